@@ -1,0 +1,112 @@
+"""Node-centric equivariant attention with every edge materialised (oracle, float64).
+
+Follows the three steps of the E2Former-V2 write-up (stapisi.com, section 3.1)
+and the attention description of the gist.science summary of arXiv 2601.16622
+(technical summary 2.2):
+
+1. source pre-coupling  h'_j = h_j (x) R(r_j)                     (tp_dense)
+2. aggregation           m_i = sum_j alpha_ij h'_j over the neighbours j of i
+3. target coupling       out_i = m_i (x) R(r_i)                     (tp_dense)
+
+Only the values carry direction; the logits use SO(3)-invariant scalars.
+Readings of what the pages leave open:
+
+* q_i = h_i[l=0, :], k_j = h_j[l=0, :] (the input features, no learned
+  projection); head h owns channels [h d, (h+1) d) with d = C / H for Q, K
+  and V; the logit is scale * <q_i, k_j> over the head's channels, with
+  scale = 1/sqrt(d) unless given.
+* V = h'_j, so alpha_ijh weights all (lmax+1)^2 components of head h's
+  channels.
+* the softmax runs over the valid (mask = 1) slots of row i only; the fused
+  kernel's online softmax (write-up section 3.2; gist.science summary 2.2)
+  equals this plain softmax up to rounding.  A row with no valid slot gives
+  m_i = 0 and out_i = 0.  Repeated indices count once per slot.
+* r_j, r_i are the atoms' own position vectors as passed.
+
+This function materialises logits [E, H] and messages [E, S, C]: it is the
+edge-centric form the pages contrast the fused kernel with.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from .sh import n_comp
+from .tp import tp_dense
+
+
+def attention_weights(h: np.ndarray, nbr_idx: np.ndarray, nbr_mask: np.ndarray, heads: int,
+                      scale: Optional[float] = None, targets: Optional[np.ndarray] = None):
+    """Edge list and softmax weights: (e_row, e_src, alpha [E, H]).
+
+    e_row indexes the target list, e_src the source atom of each valid slot.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    N, _, C = h.shape
+    if C % heads != 0:
+        raise ValueError("channels must divide into heads")
+    d = C // heads
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    tgt = np.arange(N) if targets is None else np.asarray(targets, dtype=np.int64)
+    T = tgt.shape[0]
+
+    # edge list (target row t, source j) from the mask; masked slots are never read
+    mask = np.asarray(nbr_mask)[tgt] != 0
+    idx = np.asarray(nbr_idx)[tgt]
+    e_row, e_slot = np.nonzero(mask)
+    e_src = idx[e_row, e_slot].astype(np.int64)
+    if e_src.size and (e_src.min() < 0 or e_src.max() >= N):
+        raise IndexError("a valid neighbour slot holds an out-of-range index")
+    E = e_src.shape[0]
+
+    # invariant per-head logits [E, H]
+    q = h[tgt, 0, :].reshape(T, heads, d)
+    k = h[e_src, 0, :].reshape(E, heads, d)
+    logits = scale * np.einsum("ehc,ehc->eh", q[e_row], k)
+
+    # softmax per (target, head) over that target's valid slots
+    mx = np.full((T, heads), -np.inf)
+    np.maximum.at(mx, e_row, logits)
+    p = np.exp(logits - mx[e_row])
+    z = np.zeros((T, heads))
+    np.add.at(z, e_row, p)
+    return e_row, e_src, p / z[e_row]
+
+
+def attn_forward(pos: np.ndarray, h: np.ndarray, nbr_idx: np.ndarray, nbr_mask: np.ndarray,
+                 heads: int, lmax: int, scale: Optional[float] = None,
+                 path_w: Optional[np.ndarray] = None, targets: Optional[np.ndarray] = None,
+                 return_msg: bool = False, chunk_edges: int = 1 << 16):
+    """Output [T, S, C] for the given targets (all atoms if None); optionally also m [T, S, C]."""
+    pos = np.asarray(pos, dtype=np.float64)
+    h = np.asarray(h, dtype=np.float64)
+    N, S, C = h.shape
+    if S != n_comp(lmax):
+        raise ValueError("component axis does not match lmax")
+    d = C // heads
+    tgt = np.arange(N) if targets is None else np.asarray(targets, dtype=np.int64)
+    T = tgt.shape[0]
+
+    e_row, e_src, alpha = attention_weights(h, nbr_idx, nbr_mask, heads, scale, tgt)
+    E = e_src.shape[0]
+
+    # step 1 on every source that some edge reads
+    src, src_inv = np.unique(e_src, return_inverse=True)
+    hp_src = tp_dense(h[src], pos[src], lmax, path_w)           # [n_src, S, C]
+
+    # messages alpha_ijh * h'_j, materialised in chunks, summed into m_i
+    msg = np.zeros((T, S, C))
+    for e0 in range(0, E, chunk_edges):
+        e1 = min(E, e0 + chunk_edges)
+        a = np.repeat(alpha[e0:e1], d, axis=1)                  # [e, C], channel c -> head c // d
+        m_e = a[:, None, :] * hp_src[src_inv[e0:e1]]            # [e, S, C]
+        np.add.at(msg, e_row[e0:e1], m_e)
+
+    # step 3 with the target's own harmonics
+    out = tp_dense(msg, pos[tgt], lmax, path_w)
+    if return_msg:
+        return out, msg
+    return out
