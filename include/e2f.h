@@ -1,0 +1,176 @@
+/*
+ * e2f.h -- C ABI of libe2f: E2Former-V2's on-the-fly equivariant attention
+ * (forward pass) on AMD Instinct MI355X (gfx950).
+ *
+ * Method (E2Former-V2 news write-up on stapisi.com, sections 2 and 3; the
+ * gist.science technical summary of arXiv 2601.16622, sections 2.1-2.2):
+ *
+ *   step 1  h'_j  = h_j (x) R(r_j)            EAAS tensor product per source atom
+ *   step 2  m_i   = sum_j alpha_ij h'_j       streamed over i's padded neighbour
+ *                                             list with an online softmax
+ *   step 3  out_i = m_i (x) R(r_i)            EAAS tensor product per target atom
+ *
+ * "(x) R(r)" couples each irrep block of a feature with the real solid
+ * harmonics R_lf(r) = |r|^lf C_lf(r_hat) (Racah normalisation, components
+ * m = -l..l at flat index l*l + l + m, l = 1 ordered (y, z, x)) over every
+ * path (li, lf, lo) with li, lf, lo <= lmax and |li - lf| <= lo <= li + lf,
+ * channel-wise, summed per lo.  EAAS (write-up section 2, Proposition 4.3)
+ * evaluates it exactly as: rotate the feature into the frame whose z axis
+ * lies along r, apply the sparse reindex (li + lf + lo even: m_i = m_o;
+ * odd: m_i = -m_o with a sign), rotate back.
+ *
+ * The attention logits use SO(3)-invariant scalars only (gist.science
+ * summary 2.2): q_i = h_i[l=0, :], k_j = h_j[l=0, :]; head h owns channels
+ * [h*d, (h+1)*d), d = C / H, for Q, K and V; logit = scale * <q_i, k_j>.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Buffers are device memory owned by the caller (path_w excepted: it is a
+ *   small host array folded into the kernel arguments); the library
+ *   allocates nothing and keeps no mutable global state (reentrant,
+ *   thread-safe).
+ * - Layouts are dense row-major with channels innermost:
+ *     positions   float  [n, 3]          (always fp32, angstrom, as given)
+ *     features    T      [n, S, C]       S = (lmax + 1)^2, T per `dtype`
+ *     nbr_idx     int32  [N, K]          padded neighbour list
+ *     nbr_mask    uint8  [N, K]          1 = valid slot, 0 = padded
+ *     path_w      float  [P] or NULL     HOST memory: per-path weight, NULL =
+ *                                        all 1; P = e2f_path_count(lmax),
+ *                                        paths in lexicographic (li, lf, lo)
+ *                                        order; read during the call only
+ * - `dtype` is E2F_F32 or E2F_BF16 and applies to features, workspace and
+ *   outputs; bf16 is stored round-to-nearest-even, all arithmetic is fp32.
+ * - Feature, workspace and output pointers must be 16-byte aligned;
+ *   positions, path_w and nbr_idx 4-byte aligned.
+ * - Argument errors are returned synchronously, before anything is enqueued.
+ *   Work is enqueued on `stream` and the call returns without waiting, except
+ *   under E2F_VALIDATE_INDICES.  Device faults surface at the caller's next
+ *   synchronisation, as usual for HIP.
+ * - n = 0 (or N = 0) is a successful no-op.
+ * - Supported sizes: lmax in {0, 1, 2}; C >= 1, H >= 1, C % H == 0.  The
+ *   attention kernels also need a per-lane channel count V in {1, 2, 4}
+ *   with V | d, d / V a power of two and C / V <= 64 (so C <= 256 when d is
+ *   a multiple of 4); otherwise E2F_ERR_UNSUPPORTED.
+ */
+#ifndef E2F_H_
+#define E2F_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* storage type of features, workspace and outputs */
+typedef enum e2f_dtype {
+  E2F_F32 = 0,
+  E2F_BF16 = 1
+} e2f_dtype;
+
+/* status codes */
+#define E2F_OK 0
+#define E2F_ERR_NULL (-1)        /* a required pointer is NULL */
+#define E2F_ERR_SHAPE (-2)       /* n < 0, K < 1, C < 1, H < 1, C % H != 0, lmax not in 0..2 */
+#define E2F_ERR_DTYPE (-3)       /* dtype is not an e2f_dtype value */
+#define E2F_ERR_ALIGN (-4)       /* a pointer breaks its alignment rule */
+#define E2F_ERR_WORKSPACE (-5)   /* ws_bytes < e2f_attn_workspace_bytes(...) */
+#define E2F_ERR_ALIAS (-6)       /* an output overlaps an input or another output */
+#define E2F_ERR_HIP (-7)         /* the HIP runtime reported an error at launch */
+#define E2F_ERR_INDEX (-8)       /* a valid slot holds an index outside [0, N) (validation only) */
+#define E2F_ERR_UNSUPPORTED (-9) /* channel / head layout outside the kernels' lane mapping */
+
+/* flags of the attention entry points */
+#define E2F_VALIDATE_INDICES 1u  /* check every valid slot's index before running; synchronises */
+
+/* Name of a status code ("E2F_OK", "E2F_ERR_SHAPE", ...); never NULL. */
+const char* e2f_status_string(int status);
+
+/* Number of coupling paths at this lmax (1, 5 or 15), or E2F_ERR_SHAPE. */
+int e2f_path_count(int lmax);
+
+/* The hipError_t value behind the calling thread's most recent E2F_ERR_HIP
+ * (0 if none yet); e2f_last_hip_error_name gives its HIP name. */
+int e2f_last_hip_error(void);
+const char* e2f_last_hip_error_name(void);
+
+/*
+ * e2f_eaas_couple -- the EAAS tensor product h_out_a = h_in_a (x) R(r_a).
+ * Write-up section 2 (alignment rotation, feature rotation, sparse
+ * reindex, inverse rotation; Proposition 4.3).
+ *   r      [n, 3] fp32     vectors (any length, including 0)
+ *   h_in   [n, S, C] T     features
+ *   path_w [P] fp32|NULL   host array of per-path weights (one-hot isolates a path)
+ *   h_out  [n, S, C] T     result; may equal h_in exactly (in place), must
+ *                          not overlap it otherwise
+ */
+int e2f_eaas_couple(hipStream_t stream, int64_t n, int lmax, int C, int dtype,
+                    const float* r, const void* h_in, const float* path_w, void* h_out);
+
+/*
+ * Workspace bytes that e2f_attn_precouple / _aggregate / _forward need for
+ * N atoms: the pre-coupled values of step 1, stored per atom as S + 1 rows
+ * of C elements (row 0 = k_j = h_j[l=0, :], rows 1..S = h'_j), so that each
+ * neighbour's K and V are one contiguous (S + 1) * C * sizeof(T) byte
+ * block, plus 256 bytes for a validation flag.  0 on bad arguments.
+ */
+size_t e2f_attn_workspace_bytes(int64_t N, int lmax, int C, int dtype);
+
+/*
+ * e2f_attn_precouple -- step 1 (write-up section 3.1): fills the workspace
+ * with k_j and h'_j = h_j (x) R(pos_j) for every atom.
+ *   pos [N, 3] fp32, h [N, S, C] T, workspace as above (written).
+ */
+int e2f_attn_precouple(hipStream_t stream, int64_t N, int lmax, int C, int dtype,
+                       const float* pos, const void* h, const float* path_w,
+                       void* workspace, size_t ws_bytes);
+
+/*
+ * e2f_attn_aggregate -- steps 2 and 3 (write-up sections 3.1-3.2): one
+ * wavefront per target streams its valid slots once, computes the per-head
+ * logits, keeps a running max and normaliser (online softmax) and fp32
+ * accumulators on chip, divides, and couples the result with the target's
+ * own harmonics.  No per-edge tensor is written.
+ *   pos       [N, 3] fp32
+ *   nbr_idx   [N, K] int32   index of the source atom at each slot; read only
+ *                            at mask = 1 slots; an index outside [0, N) at a
+ *                            valid slot is skipped like a masked slot, or
+ *                            reported as E2F_ERR_INDEX under
+ *                            E2F_VALIDATE_INDICES
+ *   nbr_mask  [N, K] uint8   any pattern; valid slots need not come first;
+ *                            repeated indices count once per slot
+ *   scale     logit scale; <= 0 selects 1 / sqrt(C / H)
+ *   workspace filled by e2f_attn_precouple (the flag tail is written under
+ *             E2F_VALIDATE_INDICES, hence not const)
+ *   out       [N, S, C] T    out_i; exactly 0 for a target with no valid slot
+ *   out_msg   [N, S, C] T or NULL: also store the normalised message m_i
+ *   flags     0 or E2F_VALIDATE_INDICES
+ */
+int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
+                       const float* pos, const int32_t* nbr_idx, const uint8_t* nbr_mask,
+                       float scale, const float* path_w, void* workspace, size_t ws_bytes,
+                       void* out, void* out_msg, uint32_t flags);
+
+/* e2f_attn_forward -- e2f_attn_precouple then e2f_attn_aggregate on one stream. */
+int e2f_attn_forward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
+                     const float* pos, const void* h, const int32_t* nbr_idx,
+                     const uint8_t* nbr_mask, float scale, const float* path_w,
+                     void* workspace, size_t ws_bytes, void* out, void* out_msg, uint32_t flags);
+
+/*
+ * e2f_frames -- test hook: the alignment rotation Q (Q r_hat = z_hat, write-up
+ * section 2.1) and the Wigner-D blocks D^l(Q), l = 0..lmax, exactly as the
+ * kernels build them.
+ *   r [n, 3] fp32; Q [n, 9] fp32 row-major; D [n, 35] fp32: the blocks
+ *   D^0 (1), D^1 (3x3), D^2 (5x5) row-major one after another (blocks
+ *   above lmax are left untouched).
+ */
+int e2f_frames(hipStream_t stream, int64_t n, int lmax, const float* r, float* Q, float* D);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* E2F_H_ */

@@ -1,0 +1,310 @@
+// e2f_device.hpp -- device-side building blocks of the EAAS tensor product
+// and the fused attention stream for gfx950 (wave64).
+//
+// EAAS (E2Former-V2 write-up on stapisi.com, section 2; Proposition 4.3):
+// for a vector r with polar angle t and azimuth p, the alignment rotation
+// Q = R_y(-t) R_z(-p) maps r_hat to z_hat.  The Wigner-D matrix of Q in the
+// real harmonic basis factorises the same way, D(Q) = D_y(-t) D_z(-p), and
+// both factors are sparse:
+//   * D_z(a) rotates each (m, -m) pair by the angle m a;
+//   * D_y(b) keeps the m < 0 and the m >= 0 components apart (a rotation
+//     about y preserves parity in y): a 1x1 + 2x2 block at l = 1 and a
+//     2x2 + 3x3 block at l = 2.
+// The l = 2 entries below were derived by substituting the rotated
+// coordinates into the l = 2 real solid harmonics
+//   (sqrt3 xy, sqrt3 yz, (3z^2 - r^2)/2, sqrt3 xz, sqrt3/2 (x^2 - y^2))
+// and re-expanding; with c = cos b, s = sin b the m >= 0 block is
+//   [ (3c^2-1)/2     -sqrt3 s c     sqrt3/2 s^2 ]
+//   [  sqrt3 s c      c^2 - s^2    -s c         ]
+//   [  sqrt3/2 s^2    s c          (1 + c^2)/2  ]
+// and the m < 0 block is [[c, s], [-s, c]].  In the aligned frame the
+// harmonics are |r|^lf at m_f = 0 only (Lemma 4.1 of the gist.science
+// summary, section 2.1), so the product reduces to the sparse reindex of
+// write-up section 2.2; its weights <li m lf 0 | lo m> arrive from the host.
+// All angles are handled through cosines and sines built from the
+// coordinates; no trigonometric function is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "e2f_internal.hpp"
+
+namespace e2f {
+
+__host__ __device__ constexpr int ncomp(int lmax) { return (lmax + 1) * (lmax + 1); }
+__host__ __device__ constexpr int flat(int l, int m) { return l * l + l + m; }
+
+// ---------------------------------------------------------------- frame
+
+struct Frame {
+  float ct, st;   // cos, sin of the polar angle
+  float c1, s1;   // cos, sin of the azimuth
+  float c2, s2;   // cos, sin of twice the azimuth
+  float r1, r2;   // |r|, |r|^2
+};
+
+__device__ inline Frame make_frame(float x, float y, float z) {
+  // Angles come from components scaled by the largest magnitude, so that
+  // squares of tiny components cannot lose precision in the denormal range
+  // (that would leave Q measurably non-orthogonal).
+  Frame f;
+  const float ax = fabsf(x), ay = fabsf(y), az = fabsf(z);
+  const float mxy = fmaxf(ax, ay);
+  const float m = fmaxf(mxy, az);
+  if (m > 0.0f) {
+    const float im = 1.0f / m;
+    const float xs = x * im, ys = y * im, zs = z * im;
+    const float rs = sqrtf(xs * xs + ys * ys + zs * zs);   // in [1, sqrt 3]
+    const float rhos = sqrtf(xs * xs + ys * ys);
+    const float irs = 1.0f / rs;
+    f.ct = zs * irs;
+    f.st = rhos * irs;
+    f.r1 = m * rs;
+  } else {  // r = 0: Q = identity; only lf = 0 paths survive since |r|^lf = 0
+    f.ct = 1.0f;
+    f.st = 0.0f;
+    f.r1 = 0.0f;
+  }
+  if (mxy > 0.0f) {
+    const float im = 1.0f / mxy;
+    const float xs = x * im, ys = y * im;
+    const float irho = 1.0f / sqrtf(xs * xs + ys * ys);
+    f.c1 = xs * irho;
+    f.s1 = ys * irho;
+  } else {  // on the z axis the azimuth is free; take 0
+    f.c1 = 1.0f;
+    f.s1 = 0.0f;
+  }
+  f.c2 = f.c1 * f.c1 - f.s1 * f.s1;
+  f.s2 = 2.0f * f.s1 * f.c1;
+  f.r2 = f.r1 * f.r1;
+  return f;
+}
+
+// entries of the l = 2, m >= 0 block of D_y(+t) (see the header comment)
+struct Dy2 {
+  float d00, d01, d02, d11, d12, d22;
+};
+
+__device__ inline Dy2 make_dy2(const Frame& f) {
+  const float k3 = 1.7320508075688772f;  // sqrt(3)
+  Dy2 d;
+  const float cc = f.ct * f.ct, ss = f.st * f.st, sc = f.st * f.ct;
+  d.d00 = 0.5f * (3.0f * cc - 1.0f);
+  d.d01 = k3 * sc;
+  d.d02 = 0.5f * k3 * ss;
+  d.d11 = cc - ss;
+  d.d12 = sc;
+  d.d22 = 0.5f * (1.0f + cc);
+  return d;
+}
+
+// x <- D(Q) x = D_y(-t) D_z(-p) x   (global frame -> aligned frame)
+template <int LMAX>
+__device__ inline void rotate_in(float* x, const Frame& f, const Dy2& d) {
+  if constexpr (LMAX >= 1) {
+    // D_z(-p) on the (m=1, m=-1) = (x, y) pair
+    const float a = x[flat(1, 1)], b = x[flat(1, -1)];
+    const float xp = f.c1 * a + f.s1 * b;
+    x[flat(1, -1)] = -f.s1 * a + f.c1 * b;
+    // D_y(-t): (z, x) block
+    const float zz = x[flat(1, 0)];
+    x[flat(1, 0)] = f.ct * zz + f.st * xp;
+    x[flat(1, 1)] = -f.st * zz + f.ct * xp;
+  }
+  if constexpr (LMAX >= 2) {
+    // D_z(-p): pairs (m=1, -1) with angle p and (m=2, -2) with angle 2p
+    const float a1 = x[flat(2, 1)], b1 = x[flat(2, -1)];
+    const float a2 = x[flat(2, 2)], b2 = x[flat(2, -2)];
+    const float p1 = f.c1 * a1 + f.s1 * b1;
+    const float n1 = -f.s1 * a1 + f.c1 * b1;
+    const float p2 = f.c2 * a2 + f.s2 * b2;
+    const float n2 = -f.s2 * a2 + f.c2 * b2;
+    // D_y(-t): m < 0 block [[c, -s], [s, c]] on (m=-2, m=-1)
+    x[flat(2, -2)] = f.ct * n2 - f.st * n1;
+    x[flat(2, -1)] = f.st * n2 + f.ct * n1;
+    // m >= 0 block of D_y(-t) = transpose of the D_y(+t) block
+    const float z0 = x[flat(2, 0)];
+    x[flat(2, 0)] = d.d00 * z0 + d.d01 * p1 + d.d02 * p2;
+    x[flat(2, 1)] = -d.d01 * z0 + d.d11 * p1 + d.d12 * p2;
+    x[flat(2, 2)] = d.d02 * z0 - d.d12 * p1 + d.d22 * p2;
+  }
+}
+
+// x <- D(Q)^T x = D_z(p) D_y(t) x   (aligned frame -> global frame)
+template <int LMAX>
+__device__ inline void rotate_out(float* x, const Frame& f, const Dy2& d) {
+  if constexpr (LMAX >= 1) {
+    const float zz = x[flat(1, 0)], xx = x[flat(1, 1)];
+    // D_y(t)
+    x[flat(1, 0)] = f.ct * zz - f.st * xx;
+    const float xp = f.st * zz + f.ct * xx;
+    // D_z(p)
+    const float b = x[flat(1, -1)];
+    x[flat(1, 1)] = f.c1 * xp - f.s1 * b;
+    x[flat(1, -1)] = f.s1 * xp + f.c1 * b;
+  }
+  if constexpr (LMAX >= 2) {
+    const float n2 = x[flat(2, -2)], n1 = x[flat(2, -1)];
+    const float z0 = x[flat(2, 0)], p1 = x[flat(2, 1)], p2 = x[flat(2, 2)];
+    // D_y(t): m < 0 block [[c, s], [-s, c]]
+    const float m2 = f.ct * n2 + f.st * n1;
+    const float m1 = -f.st * n2 + f.ct * n1;
+    // D_y(t): m >= 0 block
+    const float q0 = d.d00 * z0 - d.d01 * p1 + d.d02 * p2;
+    const float q1 = d.d01 * z0 + d.d11 * p1 - d.d12 * p2;
+    const float q2 = d.d02 * z0 + d.d12 * p1 + d.d22 * p2;
+    x[flat(2, 0)] = q0;
+    // D_z(p) on the pairs
+    x[flat(2, 1)] = f.c1 * q1 - f.s1 * m1;
+    x[flat(2, -1)] = f.s1 * q1 + f.c1 * m1;
+    x[flat(2, 2)] = f.c2 * q2 - f.s2 * m2;
+    x[flat(2, -2)] = f.s2 * q2 + f.c2 * m2;
+  }
+}
+
+// Per-atom reindex weights: k[p][m] = w_p <li m lf 0 | lo m> |r|^lf.
+template <int LMAX>
+struct Reindex {
+  float k[kMaxPaths][LMAX + 1];
+};
+
+template <int LMAX>
+__device__ inline Reindex<LMAX> make_reindex(const EaasCoef& cf, const Frame& f) {
+  Reindex<LMAX> R;
+  int p = 0;
+#pragma unroll
+  for (int li = 0; li <= LMAX; ++li)
+#pragma unroll
+    for (int lf = 0; lf <= LMAX; ++lf)
+#pragma unroll
+      for (int lo = 0; lo <= LMAX; ++lo) {
+        if (lo < (li > lf ? li - lf : lf - li) || lo > li + lf) continue;
+        const float rl = lf == 0 ? 1.0f : (lf == 1 ? f.r1 : f.r2);
+#pragma unroll
+        for (int m = 0; m <= LMAX; ++m) R.k[p][m] = cf.c[p][m] * rl;
+        ++p;
+      }
+  return R;
+}
+
+// y = P(x) in the aligned frame: even li+lf+lo keeps m_i = m_o, odd maps
+// m_i = -m_o with the sign (+ for m_o > 0, - for m_o < 0); y[lo, 0] gets
+// nothing from odd paths.
+template <int LMAX>
+__device__ inline void reindex(const float* x, float* y, const Reindex<LMAX>& R) {
+#pragma unroll
+  for (int s = 0; s < ncomp(LMAX); ++s) y[s] = 0.0f;
+  int p = 0;
+#pragma unroll
+  for (int li = 0; li <= LMAX; ++li)
+#pragma unroll
+    for (int lf = 0; lf <= LMAX; ++lf)
+#pragma unroll
+      for (int lo = 0; lo <= LMAX; ++lo) {
+        if (lo < (li > lf ? li - lf : lf - li) || lo > li + lf) continue;
+        const int mmax = li < lo ? li : lo;
+        if (((li + lf + lo) & 1) == 0) {
+#pragma unroll
+          for (int m = 0; m <= mmax; ++m) {
+            y[flat(lo, m)] += R.k[p][m] * x[flat(li, m)];
+            if (m > 0) y[flat(lo, -m)] += R.k[p][m] * x[flat(li, -m)];
+          }
+        } else {
+#pragma unroll
+          for (int m = 1; m <= mmax; ++m) {
+            y[flat(lo, m)] += R.k[p][m] * x[flat(li, -m)];
+            y[flat(lo, -m)] -= R.k[p][m] * x[flat(li, m)];
+          }
+        }
+        ++p;
+      }
+}
+
+// full EAAS on one channel: x (global) -> y (global)
+template <int LMAX>
+__device__ inline void eaas_channel(float* x, float* y, const Frame& f, const Dy2& d,
+                                    const Reindex<LMAX>& R) {
+  rotate_in<LMAX>(x, f, d);
+  reindex<LMAX>(x, y, R);
+  rotate_out<LMAX>(y, f, d);
+}
+
+// ------------------------------------------------------ storage types
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+__device__ inline uint16_t f32_to_bf16(float f) {  // round to nearest, ties to even
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <typename T, int V>
+struct VecIO;
+
+template <int V>
+struct VecIO<float, V> {
+  static __device__ inline void load(const float* p, float* o) {
+    if constexpr (V == 4) {
+      const float4 v = *reinterpret_cast<const float4*>(p);
+      o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    } else if constexpr (V == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(p);
+      o[0] = v.x; o[1] = v.y;
+    } else {
+      static_assert(V == 1, "fp32 vector width");
+      o[0] = *p;
+    }
+  }
+  static __device__ inline void store(float* p, const float* o) {
+    if constexpr (V == 4) {
+      *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+    } else if constexpr (V == 2) {
+      *reinterpret_cast<float2*>(p) = make_float2(o[0], o[1]);
+    } else {
+      *p = o[0];
+    }
+  }
+};
+
+template <int V>
+struct VecIO<uint16_t, V> {
+  static __device__ inline void unpack(uint32_t w, float* o) {
+    o[0] = __uint_as_float(w << 16);
+    o[1] = __uint_as_float(w & 0xffff0000u);
+  }
+  static __device__ inline uint32_t pack(float a, float b) {
+    return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+  }
+  static __device__ inline void load(const uint16_t* p, float* o) {
+    if constexpr (V == 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      unpack(v.x, o); unpack(v.y, o + 2); unpack(v.z, o + 4); unpack(v.w, o + 6);
+    } else if constexpr (V == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      unpack(v.x, o); unpack(v.y, o + 2);
+    } else if constexpr (V == 2) {
+      unpack(*reinterpret_cast<const uint32_t*>(p), o);
+    } else {
+      static_assert(V == 1, "bf16 vector width");
+      o[0] = bf16_to_f32(*p);
+    }
+  }
+  static __device__ inline void store(uint16_t* p, const float* o) {
+    if constexpr (V == 8) {
+      *reinterpret_cast<uint4*>(p) =
+          make_uint4(pack(o[0], o[1]), pack(o[2], o[3]), pack(o[4], o[5]), pack(o[6], o[7]));
+    } else if constexpr (V == 4) {
+      *reinterpret_cast<uint2*>(p) = make_uint2(pack(o[0], o[1]), pack(o[2], o[3]));
+    } else if constexpr (V == 2) {
+      *reinterpret_cast<uint32_t*>(p) = pack(o[0], o[1]);
+    } else {
+      *p = f32_to_bf16(o[0]);
+    }
+  }
+};
+
+}  // namespace e2f

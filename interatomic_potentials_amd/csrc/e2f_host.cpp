@@ -1,0 +1,356 @@
+// e2f_host.cpp -- host side of libe2f: argument checks, constant tables,
+// lane-mapping choice and kernel dispatch for the entry points of e2f.h.
+//
+// The sparse reindex weights <li m lf 0 | lo m> come from Racah's closed
+// formula for Clebsch-Gordan coefficients (Condon-Shortley phase), evaluated
+// here in double precision; the write-up (stapisi.com, section 2.2) states
+// the reindex rule, and section 5.2 warns that the CG normalisation matters.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/e2f.h"
+#include "e2f_internal.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;  // per calling thread; read by e2f_last_hip_error
+
+// a launcher's return value (0 or a hipError_t) as a status code
+int hip_status(int err) {
+  if (err == 0) return E2F_OK;
+  g_last_hip_error = err;
+  return E2F_ERR_HIP;
+}
+
+using e2f::EaasCoef;
+using e2f::kMaxPaths;
+
+double factorial(int n) {
+  double r = 1.0;
+  for (int k = 2; k <= n; ++k) r *= k;
+  return r;
+}
+
+// <j1 m1 j2 m2 | J M>, integer angular momenta, Racah's formula
+double clebsch_gordan(int j1, int m1, int j2, int m2, int J, int M) {
+  if (M != m1 + m2) return 0.0;
+  if (J < abs(j1 - j2) || J > j1 + j2) return 0.0;
+  if (abs(m1) > j1 || abs(m2) > j2 || abs(M) > J) return 0.0;
+  const double tri = factorial(J + j1 - j2) * factorial(J - j1 + j2) * factorial(j1 + j2 - J) /
+                     factorial(j1 + j2 + J + 1);
+  const double pre = sqrt((2 * J + 1) * tri * factorial(J + M) * factorial(J - M) *
+                          factorial(j1 - m1) * factorial(j1 + m1) * factorial(j2 - m2) *
+                          factorial(j2 + m2));
+  double sum = 0.0;
+  for (int k = 0; k <= j1 + j2 + J; ++k) {
+    const int a[6] = {k, j1 + j2 - J - k, j1 - m1 - k, j2 + m2 - k, J - j2 + m1 + k,
+                      J - j1 - m2 + k};
+    bool ok = true;
+    double den = 1.0;
+    for (int t = 0; t < 6; ++t) {
+      if (a[t] < 0) { ok = false; break; }
+      den *= factorial(a[t]);
+    }
+    if (ok) sum += ((k & 1) ? -1.0 : 1.0) / den;
+  }
+  return pre * sum;
+}
+
+int path_count(int lmax) {
+  int p = 0;
+  for (int li = 0; li <= lmax; ++li)
+    for (int lf = 0; lf <= lmax; ++lf)
+      for (int lo = 0; lo <= lmax; ++lo)
+        if (lo >= abs(li - lf) && lo <= li + lf) ++p;
+  return p;
+}
+
+EaasCoef make_coef(int lmax, const float* path_w) {
+  EaasCoef cf;
+  memset(&cf, 0, sizeof(cf));
+  int p = 0;
+  for (int li = 0; li <= lmax; ++li)
+    for (int lf = 0; lf <= lmax; ++lf)
+      for (int lo = 0; lo <= lmax; ++lo) {
+        if (lo < abs(li - lf) || lo > li + lf) continue;
+        const double w = path_w ? (double)path_w[p] : 1.0;
+        const int mmax = li < lo ? li : lo;
+        for (int m = 0; m <= mmax; ++m)
+          cf.c[p][m] = (float)(w * clebsch_gordan(li, m, lf, 0, lo, m));
+        ++p;
+      }
+  return cf;
+}
+
+bool bad_dtype(int dt) { return dt != E2F_F32 && dt != E2F_BF16; }
+size_t esize(int dt) { return dt == E2F_F32 ? 4 : 2; }
+int ncomp(int lmax) { return (lmax + 1) * (lmax + 1); }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int ceil_log2(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct Range {
+  const void* p;
+  size_t n;
+};
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// per-lane vector width for the element-wise EAAS kernel
+int eaas_width(int C, int dt) {
+  const int vmax = dt == E2F_F32 ? 4 : 8;
+  for (int v = vmax; v > 1; v >>= 1)
+    if (C % v == 0) return v;
+  return 1;
+}
+
+// per-lane vector width for the attention stream: V | d, d / V a power of
+// two (heads aligned to lanes), C / V <= 64 (one row per wave at most).
+// At most 4 channels per lane: with 8 the registers holding two neighbours'
+// rows in flight plus 9 x 8 accumulators exceed the register file.
+int attn_width(int C, int H, int dt) {
+  const int d = C / H;
+  const int vmax = 4;
+  (void)dt;
+  for (int v = vmax; v >= 1; v >>= 1)
+    if (d % v == 0 && is_pow2(d / v) && C / v <= 64) return v;
+  return 0;
+}
+
+size_t ws_body_bytes(int64_t N, int lmax, int C, int dt) {
+  return round256((size_t)N * (size_t)(ncomp(lmax) + 1) * (size_t)C * esize(dt));
+}
+
+int check_shape_common(int64_t n, int lmax, int C, int dt) {
+  if (bad_dtype(dt)) return E2F_ERR_DTYPE;
+  if (n < 0 || lmax < 0 || lmax > e2f::kMaxLmax || C < 1) return E2F_ERR_SHAPE;
+  return E2F_OK;
+}
+
+int check_attn_shape(int64_t N, int K, int lmax, int C, int H, int dt) {
+  const int st = check_shape_common(N, lmax, C, dt);
+  if (st != E2F_OK) return st;
+  if (K < 1 || H < 1 || C % H != 0) return E2F_ERR_SHAPE;
+  if (attn_width(C, H, dt) == 0) return E2F_ERR_UNSUPPORTED;
+  return E2F_OK;
+}
+
+int precouple_impl(hipStream_t stream, int64_t N, int lmax, int C, int dt, const float* pos,
+                   const void* h, const float* path_w, void* ws, size_t ws_bytes) {
+  const int V = eaas_width(C, dt);
+  e2f::EaasArgs a;
+  a.r = pos;
+  a.h_in = h;
+  a.h_out = ws;
+  a.n = N;
+  a.C = C;
+  const int lanes = (C + V - 1) / V;
+  a.lane_log = ceil_log2(lanes > 64 ? 64 : lanes);
+  const EaasCoef cf = make_coef(lmax, path_w);
+  (void)ws_bytes;
+  return hip_status(e2f::launch_eaas(lmax, dt, V, true, a, cf, stream));
+}
+
+int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dt,
+                   const float* pos, const int32_t* idx, const uint8_t* mask, float scale,
+                   const float* path_w, void* ws, void* out, void* out_msg, uint32_t flags) {
+  if (flags & E2F_VALIDATE_INDICES) {
+    int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                               ws_body_bytes(N, lmax, C, dt));
+    int st = hip_status(e2f::launch_validate(N, K, idx, mask, flag, stream));
+    if (st != E2F_OK) return st;
+    int32_t host_flag = 0;
+    st = hip_status(
+        hipMemcpyAsync(&host_flag, flag, sizeof(host_flag), hipMemcpyDeviceToHost, stream));
+    if (st != E2F_OK) return st;
+    st = hip_status(hipStreamSynchronize(stream));
+    if (st != E2F_OK) return st;
+    if (host_flag != 0) return E2F_ERR_INDEX;
+  }
+  const int V = attn_width(C, H, dt);
+  const int d = C / H;
+  e2f::AggArgs a;
+  a.pos = pos;
+  a.idx = idx;
+  a.mask = mask;
+  a.ws = ws;
+  a.out = out;
+  a.out_msg = out_msg;
+  a.N = N;
+  a.K = K;
+  a.C = C;
+  a.lane_log = ceil_log2(C / V);
+  a.head_lanes = d / V;
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)d);
+  a.scale_log2e = (float)(sc * 1.4426950408889634);  // log2(e)
+  const EaasCoef cf = make_coef(lmax, path_w);
+  return hip_status(e2f::launch_aggregate(lmax, dt, V, a, cf, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* e2f_status_string(int status) {
+  switch (status) {
+    case E2F_OK: return "E2F_OK";
+    case E2F_ERR_NULL: return "E2F_ERR_NULL";
+    case E2F_ERR_SHAPE: return "E2F_ERR_SHAPE";
+    case E2F_ERR_DTYPE: return "E2F_ERR_DTYPE";
+    case E2F_ERR_ALIGN: return "E2F_ERR_ALIGN";
+    case E2F_ERR_WORKSPACE: return "E2F_ERR_WORKSPACE";
+    case E2F_ERR_ALIAS: return "E2F_ERR_ALIAS";
+    case E2F_ERR_HIP: return "E2F_ERR_HIP";
+    case E2F_ERR_INDEX: return "E2F_ERR_INDEX";
+    case E2F_ERR_UNSUPPORTED: return "E2F_ERR_UNSUPPORTED";
+    default: return "E2F_ERR_UNKNOWN";
+  }
+}
+
+int e2f_last_hip_error(void) { return g_last_hip_error; }
+
+const char* e2f_last_hip_error_name(void) {
+  return hipGetErrorName(static_cast<hipError_t>(g_last_hip_error));
+}
+
+int e2f_path_count(int lmax) {
+  if (lmax < 0 || lmax > e2f::kMaxLmax) return E2F_ERR_SHAPE;
+  return path_count(lmax);
+}
+
+int e2f_eaas_couple(hipStream_t stream, int64_t n, int lmax, int C, int dtype, const float* r,
+                    const void* h_in, const float* path_w, void* h_out) {
+  int st = check_shape_common(n, lmax, C, dtype);
+  if (st != E2F_OK) return st;
+  if (n == 0) return E2F_OK;
+  if (!r || !h_in || !h_out) return E2F_ERR_NULL;
+  if (!aligned(r, 4) || !aligned(h_in, 16) || !aligned(h_out, 16) ||
+      (path_w && !aligned(path_w, 4)))
+    return E2F_ERR_ALIGN;
+  const size_t hb = (size_t)n * ncomp(lmax) * C * esize(dtype);
+  if (h_out != h_in && overlap({h_out, hb}, {h_in, hb})) return E2F_ERR_ALIAS;
+  if (overlap({h_out, hb}, {r, (size_t)n * 12})) return E2F_ERR_ALIAS;
+  const int V = eaas_width(C, dtype);
+  e2f::EaasArgs a;
+  a.r = r;
+  a.h_in = h_in;
+  a.h_out = h_out;
+  a.n = n;
+  a.C = C;
+  const int lanes = (C + V - 1) / V;
+  a.lane_log = ceil_log2(lanes > 64 ? 64 : lanes);
+  const EaasCoef cf = make_coef(lmax, path_w);
+  return hip_status(e2f::launch_eaas(lmax, dtype, V, false, a, cf, stream));
+}
+
+size_t e2f_attn_workspace_bytes(int64_t N, int lmax, int C, int dtype) {
+  if (check_shape_common(N, lmax, C, dtype) != E2F_OK) return 0;
+  return ws_body_bytes(N, lmax, C, dtype) + 256;
+}
+
+int e2f_attn_precouple(hipStream_t stream, int64_t N, int lmax, int C, int dtype,
+                       const float* pos, const void* h, const float* path_w, void* workspace,
+                       size_t ws_bytes) {
+  int st = check_shape_common(N, lmax, C, dtype);
+  if (st != E2F_OK) return st;
+  if (N == 0) return E2F_OK;
+  if (!pos || !h || !workspace) return E2F_ERR_NULL;
+  if (!aligned(pos, 4) || !aligned(h, 16) || !aligned(workspace, 16) ||
+      (path_w && !aligned(path_w, 4)))
+    return E2F_ERR_ALIGN;
+  const size_t need = e2f_attn_workspace_bytes(N, lmax, C, dtype);
+  if (ws_bytes < need) return E2F_ERR_WORKSPACE;
+  const size_t hb = (size_t)N * ncomp(lmax) * C * esize(dtype);
+  if (overlap({workspace, need}, {h, hb}) || overlap({workspace, need}, {pos, (size_t)N * 12}))
+    return E2F_ERR_ALIAS;
+  return precouple_impl(stream, N, lmax, C, dtype, pos, h, path_w, workspace, ws_bytes);
+}
+
+int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
+                       const float* pos, const int32_t* nbr_idx, const uint8_t* nbr_mask,
+                       float scale, const float* path_w, void* workspace, size_t ws_bytes,
+                       void* out, void* out_msg, uint32_t flags) {
+  int st = check_attn_shape(N, K, lmax, C, H, dtype);
+  if (st != E2F_OK) return st;
+  if (N == 0) return E2F_OK;
+  if (!pos || !nbr_idx || !nbr_mask || !workspace || !out) return E2F_ERR_NULL;
+  if (!aligned(pos, 4) || !aligned(nbr_idx, 4) || !aligned(workspace, 16) || !aligned(out, 16) ||
+      (out_msg && !aligned(out_msg, 16)) || (path_w && !aligned(path_w, 4)))
+    return E2F_ERR_ALIGN;
+  const size_t need = e2f_attn_workspace_bytes(N, lmax, C, dtype);
+  if (ws_bytes < need) return E2F_ERR_WORKSPACE;
+  const size_t ob = (size_t)N * ncomp(lmax) * C * esize(dtype);
+  const Range ins[4] = {{pos, (size_t)N * 12},
+                        {nbr_idx, (size_t)N * K * 4},
+                        {nbr_mask, (size_t)N * K},
+                        {workspace, need}};
+  for (const Range& r : ins) {
+    if (overlap({out, ob}, r)) return E2F_ERR_ALIAS;
+    if (out_msg && overlap({out_msg, ob}, r)) return E2F_ERR_ALIAS;
+  }
+  if (out_msg && overlap({out, ob}, {out_msg, ob})) return E2F_ERR_ALIAS;
+  return aggregate_impl(stream, N, K, lmax, C, H, dtype, pos, nbr_idx, nbr_mask, scale, path_w,
+                        workspace, out, out_msg, flags);
+}
+
+int e2f_attn_forward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
+                     const float* pos, const void* h, const int32_t* nbr_idx,
+                     const uint8_t* nbr_mask, float scale, const float* path_w, void* workspace,
+                     size_t ws_bytes, void* out, void* out_msg, uint32_t flags) {
+  int st = check_attn_shape(N, K, lmax, C, H, dtype);
+  if (st != E2F_OK) return st;
+  if (N == 0) return E2F_OK;
+  if (!h) return E2F_ERR_NULL;
+  if (!aligned(h, 16)) return E2F_ERR_ALIGN;
+  const size_t hb = (size_t)N * ncomp(lmax) * C * esize(dtype);
+  if (overlap({out, hb}, {h, hb}) || (out_msg && overlap({out_msg, hb}, {h, hb})))
+    return E2F_ERR_ALIAS;
+  // all remaining checks (and the workspace / h overlap) happen in the two stages,
+  // the aggregate's before anything is enqueued
+  if (!pos || !nbr_idx || !nbr_mask || !workspace || !out) return E2F_ERR_NULL;
+  const size_t need = e2f_attn_workspace_bytes(N, lmax, C, dtype);
+  if (ws_bytes < need) return E2F_ERR_WORKSPACE;
+  if (overlap({workspace, need}, {h, hb})) return E2F_ERR_ALIAS;
+  if (!aligned(pos, 4) || !aligned(nbr_idx, 4) || !aligned(workspace, 16) || !aligned(out, 16) ||
+      (out_msg && !aligned(out_msg, 16)) || (path_w && !aligned(path_w, 4)))
+    return E2F_ERR_ALIGN;
+  const Range ins[4] = {{pos, (size_t)N * 12},
+                        {nbr_idx, (size_t)N * K * 4},
+                        {nbr_mask, (size_t)N * K},
+                        {workspace, need}};
+  for (const Range& r : ins) {
+    if (overlap({out, hb}, r)) return E2F_ERR_ALIAS;
+    if (out_msg && overlap({out_msg, hb}, r)) return E2F_ERR_ALIAS;
+  }
+  if (out_msg && overlap({out, hb}, {out_msg, hb})) return E2F_ERR_ALIAS;
+  if (overlap({workspace, need}, {pos, (size_t)N * 12})) return E2F_ERR_ALIAS;
+  st = precouple_impl(stream, N, lmax, C, dtype, pos, h, path_w, workspace, ws_bytes);
+  if (st != E2F_OK) return st;
+  return aggregate_impl(stream, N, K, lmax, C, H, dtype, pos, nbr_idx, nbr_mask, scale, path_w,
+                        workspace, out, out_msg, flags);
+}
+
+int e2f_frames(hipStream_t stream, int64_t n, int lmax, const float* r, float* Q, float* D) {
+  if (n < 0 || lmax < 0 || lmax > e2f::kMaxLmax) return E2F_ERR_SHAPE;
+  if (n == 0) return E2F_OK;
+  if (!r || !Q || !D) return E2F_ERR_NULL;
+  if (!aligned(r, 4) || !aligned(Q, 4) || !aligned(D, 4)) return E2F_ERR_ALIGN;
+  if (overlap({Q, (size_t)n * 36}, {r, (size_t)n * 12}) ||
+      overlap({D, (size_t)n * 140}, {r, (size_t)n * 12}) ||
+      overlap({Q, (size_t)n * 36}, {D, (size_t)n * 140}))
+    return E2F_ERR_ALIAS;
+  return hip_status(e2f::launch_frames(lmax, n, r, Q, D, stream));
+}
+
+}  // extern "C"

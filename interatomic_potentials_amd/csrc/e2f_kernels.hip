@@ -1,0 +1,377 @@
+// e2f_kernels.hip -- gfx950 kernels of libe2f.
+//
+// k_eaas       EAAS tensor product per atom (write-up section 2): one group of
+//              2^lane_log lanes per atom, each lane owning V adjacent channels
+//              of every irrep row; rows are read and written as one coalesced
+//              vector access per lane.  In workspace mode it also copies the
+//              l = 0 row (the key) in front of h', so that a neighbour's K and
+//              V form one contiguous block for the stream below.
+// k_aggregate  steps 2 and 3 (write-up section 3; gist.science summary 2.2):
+//              one wavefront per target.  The valid slots of the target's
+//              row are compacted into LDS with a ballot; the wave then splits
+//              into 64 / 2^lane_log subgroups that stream disjoint neighbours
+//              (each neighbour's (S + 1) rows read once, coalesced), keep a
+//              running max and normaliser per head (online softmax, base-2
+//              with log2(e) folded into the scale) and fp32 accumulators in
+//              registers, merge the subgroups with cross-lane exchanges, and
+//              apply the target-side EAAS before the only store.
+// k_frames     test hook: alignment rotation and Wigner-D blocks as built here.
+// k_validate   flags a valid slot whose index lies outside [0, N).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "e2f_device.hpp"
+#include "e2f_internal.hpp"
+
+namespace e2f {
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the `hl` adjacent lanes of one head (hl a power of two, heads
+// aligned to hl).  Uniform branches; DPP within a 16-lane row.
+__device__ inline float head_sum(float x, int hl) {
+  if (hl >= 2) x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
+  if (hl >= 4) x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
+  if (hl >= 8) x += dpp<0x141>(x);   // row_half_mirror: quad 0 <-> quad 1
+  if (hl >= 16) x += dpp<0x140>(x);  // row_mirror: half-row 0 <-> 1
+  if (hl >= 32) x += __shfl_xor(x, 16);
+  if (hl >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ------------------------------------------------------------------ K1
+
+template <int LMAX, int V, typename T, bool WS>
+__global__ __launch_bounds__(256) void k_eaas(EaasArgs a, EaasCoef cf) {
+  constexpr int S = ncomp(LMAX);
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int lg = a.lane_log;
+  const int sub = lane >> lg;
+  const int gl = lane & ((1 << lg) - 1);
+  const int64_t atom = ((int64_t)blockIdx.x * kWavesPerBlock + w) * (64 >> lg) + sub;
+  if (atom >= a.n) return;
+  const int C = a.C;
+  const Frame f = make_frame(a.r[3 * atom], a.r[3 * atom + 1], a.r[3 * atom + 2]);
+  const Dy2 d = make_dy2(f);
+  const Reindex<LMAX> R = make_reindex<LMAX>(cf, f);
+  const T* src = static_cast<const T*>(a.h_in) + atom * (int64_t)S * C;
+  T* dst = static_cast<T*>(a.h_out) + atom * (int64_t)(WS ? S + 1 : S) * C;
+  for (int c0 = gl * V; c0 < C; c0 += V << lg) {
+    float x[S][V];
+#pragma unroll
+    for (int s = 0; s < S; ++s) VecIO<T, V>::load(src + s * C + c0, x[s]);
+    if constexpr (WS) VecIO<T, V>::store(dst + c0, x[0]);
+    float y[S][V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float xv[S], yv[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) xv[s] = x[s][v];
+      eaas_channel<LMAX>(xv, yv, f, d, R);
+#pragma unroll
+      for (int s = 0; s < S; ++s) y[s][v] = yv[s];
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) VecIO<T, V>::store(dst + (WS ? s + 1 : s) * C + c0, y[s]);
+  }
+}
+
+// ------------------------------------------------------------------ K2
+
+template <int LMAX, int V, typename T, int U>
+__global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
+  constexpr int S = ncomp(LMAX);
+  __shared__ int s_nb[kWavesPerBlock][kTile];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + w;
+  if (i >= a.N) return;  // whole wave: no workgroup barrier below
+  const int lg = a.lane_log;
+  const int P = 64 >> lg;
+  const int sub = lane >> lg;
+  const int c0 = (lane & ((1 << lg) - 1)) * V;
+  const bool act = c0 < a.C;
+  const int C = a.C;
+  const int K = a.K;
+  const int64_t N = a.N;
+  const int64_t row = (int64_t)(S + 1) * C;  // elements per atom in the workspace
+  const T* ws = static_cast<const T*>(a.ws);
+
+  float q[V];
+  if (act) {
+    VecIO<T, V>::load(ws + i * row + c0, q);
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) q[v] = 0.0f;
+  }
+  float mu = -1e30f;  // running max (base-2 units); finite so that empty merges stay finite
+  float z = 0.0f;     // running normaliser
+  float acc[S][V];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[s][v] = 0.0f;
+
+  const int32_t* irow = a.idx + i * K;
+  const uint8_t* mrow = a.mask + i * K;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  for (int t0 = 0; t0 < K; t0 += kTile) {
+    // compact this tile's valid slots (mask = 1 and index in range) into LDS
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < kTile; u += 64) {
+      const int slot = t0 + u + lane;
+      bool ok = false;
+      int j = 0;
+      if (slot < K && mrow[slot] != 0) {
+        j = irow[slot];
+        ok = j >= 0 && (int64_t)j < N;
+      }
+      const uint64_t b = __ballot(ok);
+      if (ok) s_nb[w][cnt + __popcll(b & below)] = j;
+      cnt += __popcll(b);
+    }
+    wave_sync();
+
+    for (int n0 = 0; n0 < cnt; n0 += P * U) {
+      float kv[U][S + 1][V];
+      bool val[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int n = n0 + u * P + sub;
+        val[u] = n < cnt;
+        if (val[u] && act) {
+          const T* src = ws + (int64_t)s_nb[w][n] * row + c0;
+#pragma unroll
+          for (int r = 0; r <= S; ++r) VecIO<T, V>::load(src + r * C, kv[u][r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r <= S; ++r)
+#pragma unroll
+            for (int v = 0; v < V; ++v) kv[u][r][v] = 0.0f;
+        }
+      }
+      float s[U];
+      float mx = mu;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float dt = 0.0f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) dt = fmaf(q[v], kv[u][0][v], dt);
+        dt = head_sum(dt, a.head_lanes);
+        s[u] = val[u] ? dt * a.scale_log2e : -INFINITY;
+        mx = fmaxf(mx, s[u]);
+      }
+      const float corr = exp2_fast(mu - mx);
+      float p[U];
+      float ps = 0.0f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        p[u] = exp2_fast(s[u] - mx);
+        ps += p[u];
+      }
+      z = fmaf(z, corr, ps);
+#pragma unroll
+      for (int r = 0; r < S; ++r)
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          float t = acc[r][v] * corr;
+#pragma unroll
+          for (int u = 0; u < U; ++u) t = fmaf(p[u], kv[u][r + 1][v], t);
+          acc[r][v] = t;
+        }
+      mu = mx;
+    }
+    wave_sync();  // every read of s_nb is done before the next tile rewrites it
+  }
+
+  // merge the subgroups' partial softmax states (same channels, other neighbours)
+  for (int o = 1 << lg; o < 64; o <<= 1) {
+    const float mo = __shfl_xor(mu, o);
+    const float zo = __shfl_xor(z, o);
+    const float mx = fmaxf(mu, mo);
+    const float ca = exp2_fast(mu - mx);
+    const float cb = exp2_fast(mo - mx);
+    z = z * ca + zo * cb;
+#pragma unroll
+    for (int r = 0; r < S; ++r)
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[r][v] = acc[r][v] * ca + __shfl_xor(acc[r][v], o) * cb;
+    mu = mx;
+  }
+
+  if (sub != 0 || !act) return;
+  const float inv = z > 0.0f ? 1.0f / z : 0.0f;  // no valid slot: m_i = 0, out_i = 0
+#pragma unroll
+  for (int r = 0; r < S; ++r)
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[r][v] *= inv;
+  if (a.out_msg != nullptr) {
+    T* mp = static_cast<T*>(a.out_msg) + i * (int64_t)S * C + c0;
+#pragma unroll
+    for (int r = 0; r < S; ++r) VecIO<T, V>::store(mp + r * C, acc[r]);
+  }
+  const Frame f = make_frame(a.pos[3 * i], a.pos[3 * i + 1], a.pos[3 * i + 2]);
+  const Dy2 d = make_dy2(f);
+  const Reindex<LMAX> R = make_reindex<LMAX>(cf, f);
+  T* op = static_cast<T*>(a.out) + i * (int64_t)S * C + c0;
+  float y[S][V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float xv[S], yv[S];
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2) xv[s2] = acc[s2][v];
+    eaas_channel<LMAX>(xv, yv, f, d, R);
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2) y[s2][v] = yv[s2];
+  }
+#pragma unroll
+  for (int r = 0; r < S; ++r) VecIO<T, V>::store(op + r * C, y[r]);
+}
+
+// ------------------------------------------------------------ helpers
+
+__global__ __launch_bounds__(256) void k_frames(int lmax, int64_t n, const float* r, float* Q,
+                                                float* D) {
+  const int64_t a = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (a >= n) return;
+  const Frame f = make_frame(r[3 * a], r[3 * a + 1], r[3 * a + 2]);
+  const Dy2 d = make_dy2(f);
+  float* q = Q + 9 * a;
+  // Q = R_y(-t) R_z(-p)
+  q[0] = f.ct * f.c1; q[1] = f.ct * f.s1; q[2] = -f.st;
+  q[3] = -f.s1;       q[4] = f.c1;        q[5] = 0.0f;
+  q[6] = f.st * f.c1; q[7] = f.st * f.s1; q[8] = f.ct;
+  float* dd = D + 35 * a;
+  dd[0] = 1.0f;
+  // column k of D(Q) = rotate_in applied to the k-th unit vector
+  for (int col = 1; col < 9; ++col) {
+    const int l = col < 4 ? 1 : 2;
+    if (l > lmax) break;
+    float e[9];
+    for (int s = 0; s < 9; ++s) e[s] = s == col ? 1.0f : 0.0f;
+    rotate_in<2>(e, f, d);
+    const int base = l == 1 ? 1 : 10;
+    const int off = l * l;  // first flat index of the block
+    const int dim = 2 * l + 1;
+    for (int row = 0; row < dim; ++row) dd[base + row * dim + (col - off)] = e[off + row];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_clear_flag(int32_t* flag) { *flag = 0; }
+
+__global__ __launch_bounds__(256) void k_validate(int64_t total, int64_t N, const int32_t* idx,
+                                                  const uint8_t* mask, int32_t* flag) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  if (mask[t] != 0) {
+    const int32_t j = idx[t];
+    if (j < 0 || (int64_t)j >= N) *flag = 1;  // every writer stores the same value
+  }
+}
+
+// ---------------------------------------------------------- launchers
+
+namespace {
+
+int last_error() { return static_cast<int>(hipGetLastError()); }
+
+template <int L, typename T, bool WS>
+int eaas_go(int V, const EaasArgs& a, const EaasCoef& cf, hipStream_t s) {
+  const int64_t per_block = (int64_t)kWavesPerBlock * (64 >> a.lane_log);
+  const dim3 grid((unsigned)((a.n + per_block - 1) / per_block));
+  (void)hipGetLastError();
+  switch (V) {
+    case 1: hipLaunchKernelGGL((k_eaas<L, 1, T, WS>), grid, dim3(256), 0, s, a, cf); break;
+    case 2: hipLaunchKernelGGL((k_eaas<L, 2, T, WS>), grid, dim3(256), 0, s, a, cf); break;
+    case 4: hipLaunchKernelGGL((k_eaas<L, 4, T, WS>), grid, dim3(256), 0, s, a, cf); break;
+    case 8:
+      if constexpr (sizeof(T) == 2) {
+        hipLaunchKernelGGL((k_eaas<L, 8, T, WS>), grid, dim3(256), 0, s, a, cf);
+        break;
+      }
+      return static_cast<int>(hipErrorInvalidValue);
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
+  return last_error();
+}
+
+template <int L, typename T>
+int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
+  constexpr int U = 2;
+  const dim3 grid((unsigned)((a.N + kWavesPerBlock - 1) / kWavesPerBlock));
+  (void)hipGetLastError();
+  switch (V) {
+    case 1: hipLaunchKernelGGL((k_aggregate<L, 1, T, U>), grid, dim3(256), 0, s, a, cf); break;
+    case 2: hipLaunchKernelGGL((k_aggregate<L, 2, T, U>), grid, dim3(256), 0, s, a, cf); break;
+    case 4: hipLaunchKernelGGL((k_aggregate<L, 4, T, U>), grid, dim3(256), 0, s, a, cf); break;
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
+  return last_error();
+}
+
+template <typename T>
+int eaas_l(int lmax, int V, bool ws, const EaasArgs& a, const EaasCoef& cf, hipStream_t s) {
+  switch (lmax) {
+    case 0: return ws ? eaas_go<0, T, true>(V, a, cf, s) : eaas_go<0, T, false>(V, a, cf, s);
+    case 1: return ws ? eaas_go<1, T, true>(V, a, cf, s) : eaas_go<1, T, false>(V, a, cf, s);
+    case 2: return ws ? eaas_go<2, T, true>(V, a, cf, s) : eaas_go<2, T, false>(V, a, cf, s);
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
+}
+
+template <typename T>
+int agg_l(int lmax, int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
+  switch (lmax) {
+    case 0: return agg_go<0, T>(V, a, cf, s);
+    case 1: return agg_go<1, T>(V, a, cf, s);
+    case 2: return agg_go<2, T>(V, a, cf, s);
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
+}
+
+}  // namespace
+
+int launch_eaas(int lmax, int dtype, int V, bool to_workspace, const EaasArgs& a,
+                const EaasCoef& cf, hipStream_t s) {
+  return dtype == 0 ? eaas_l<float>(lmax, V, to_workspace, a, cf, s)
+                    : eaas_l<uint16_t>(lmax, V, to_workspace, a, cf, s);
+}
+
+int launch_aggregate(int lmax, int dtype, int V, const AggArgs& a, const EaasCoef& cf,
+                     hipStream_t s) {
+  return dtype == 0 ? agg_l<float>(lmax, V, a, cf, s) : agg_l<uint16_t>(lmax, V, a, cf, s);
+}
+
+int launch_frames(int lmax, int64_t n, const float* r, float* Q, float* D, hipStream_t s) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_frames, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, lmax, n, r, Q,
+                     D);
+  return last_error();
+}
+
+int launch_validate(int64_t N, int K, const int32_t* idx, const uint8_t* mask, int32_t* flag,
+                    hipStream_t s) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_clear_flag, dim3(1), dim3(1), 0, s, flag);
+  const int64_t total = N * (int64_t)K;
+  hipLaunchKernelGGL(k_validate, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, total, N,
+                     idx, mask, flag);
+  return last_error();
+}
+
+}  // namespace e2f

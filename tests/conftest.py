@@ -27,3 +27,11 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_runtest_logreport(report):
+    # Print a failure's traceback the moment it happens: if a later test takes
+    # the process down, the end-of-session summary would never be written.
+    if report.failed:
+        sys.stderr.write(f"\n[failure] {report.nodeid} ({report.when})\n{report.longreprtext}\n")
+        sys.stderr.flush()

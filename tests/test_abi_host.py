@@ -1,0 +1,181 @@
+"""Host-side checks of the C ABI: no GPU needed, nothing is launched.
+
+Every call here carries exactly one argument error, so the library must
+return that error's code before touching the HIP runtime.  Fake device
+addresses are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "e2f.h")
+
+e2f = pytest.importorskip("interatomic_potentials_amd")
+lib = e2f.lib
+C = e2f.STATUS_CODES
+
+BASE = 0x7F0000000000           # fake, 256-byte aligned device addresses
+MB = 1 << 20
+
+
+def fake(k):
+    return ctypes.c_void_p(BASE + k * 64 * MB)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(e2f_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert set(syms) == set(e2f.SIGNATURES), syms
+    for name in syms:
+        assert hasattr(lib, name), name
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", e2f.LIB_PATH], capture_output=True,
+                             text=True).stdout
+        exported = set(re.findall(r"\bT (e2f_\w+)", out))
+        assert set(syms) <= exported
+
+
+def test_header_is_plain_c(tmp_path):
+    gcc = shutil.which("gcc")
+    if not gcc:
+        pytest.skip("gcc not available")
+    src = tmp_path / "use.c"
+    src.write_text('#include "e2f.h"\nint main(void){ return e2f_path_count(2) == 15 ? 0 : 1; }\n')
+    res = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                          "-I/opt/rocm/include", f"-I{os.path.dirname(HEADER)}", "-c", str(src),
+                          "-o", str(tmp_path / "use.o")], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_status_strings_and_path_counts():
+    for code, name in e2f._STATUS.items():
+        assert e2f.status_string(code) == name
+    assert e2f.status_string(12345) == "E2F_ERR_UNKNOWN"
+    assert [e2f.path_count(l) for l in (0, 1, 2)] == [1, 5, 15]
+    assert e2f.path_count(3) == C["E2F_ERR_SHAPE"]
+    assert e2f.path_count(-1) == C["E2F_ERR_SHAPE"]
+
+
+def test_workspace_bytes():
+    wb = lib.e2f_attn_workspace_bytes
+    assert wb(32768, 2, 128, 0) == 32768 * 10 * 128 * 4 + 256
+    assert wb(100000, 2, 128, 1) == 100000 * 10 * 128 * 2 + 256
+    assert wb(3, 1, 5, 0) == 512 + 256          # 3*5*5*4 = 300 B rounds up to 512
+    assert wb(0, 2, 128, 0) == 256
+    assert wb(10, 3, 128, 0) == 0
+    assert wb(10, 2, 128, 5) == 0
+    assert wb(-1, 2, 128, 0) == 0
+
+
+def _agg(**kw):
+    a = dict(stream=None, N=1000, K=64, lmax=2, C=128, H=16, dt=0, pos=fake(1), idx=fake(2),
+             mask=fake(3), scale=0.0, pw=None, ws=fake(4), ws_bytes=1 << 30, out=fake(8),
+             msg=None, flags=0)
+    a.update(kw)
+    return lib.e2f_attn_aggregate(a["stream"], a["N"], a["K"], a["lmax"], a["C"], a["H"], a["dt"],
+                                  a["pos"], a["idx"], a["mask"], a["scale"], a["pw"], a["ws"],
+                                  a["ws_bytes"], a["out"], a["msg"], a["flags"])
+
+
+def _fwd(**kw):
+    a = dict(stream=None, N=1000, K=64, lmax=2, C=128, H=16, dt=0, pos=fake(1), h=fake(9),
+             idx=fake(2), mask=fake(3), scale=0.0, pw=None, ws=fake(4), ws_bytes=1 << 30,
+             out=fake(8), msg=None, flags=0)
+    a.update(kw)
+    return lib.e2f_attn_forward(a["stream"], a["N"], a["K"], a["lmax"], a["C"], a["H"], a["dt"],
+                                a["pos"], a["h"], a["idx"], a["mask"], a["scale"], a["pw"],
+                                a["ws"], a["ws_bytes"], a["out"], a["msg"], a["flags"])
+
+
+def _eaas(**kw):
+    a = dict(stream=None, n=1000, lmax=2, C=128, dt=0, r=fake(1), h=fake(2), pw=None, out=fake(3))
+    a.update(kw)
+    return lib.e2f_eaas_couple(a["stream"], a["n"], a["lmax"], a["C"], a["dt"], a["r"], a["h"],
+                               a["pw"], a["out"])
+
+
+def _pre(**kw):
+    a = dict(stream=None, N=1000, lmax=2, C=128, dt=0, pos=fake(1), h=fake(2), pw=None, ws=fake(4),
+             ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.e2f_attn_precouple(a["stream"], a["N"], a["lmax"], a["C"], a["dt"], a["pos"], a["h"],
+                                  a["pw"], a["ws"], a["ws_bytes"])
+
+
+@pytest.mark.parametrize("fn", [_agg, _fwd])
+def test_attention_argument_errors(fn):
+    assert fn(dt=2) == C["E2F_ERR_DTYPE"]
+    assert fn(N=-1) == C["E2F_ERR_SHAPE"]
+    assert fn(K=0) == C["E2F_ERR_SHAPE"]
+    assert fn(lmax=3) == C["E2F_ERR_SHAPE"]
+    assert fn(lmax=-1) == C["E2F_ERR_SHAPE"]
+    assert fn(C=0) == C["E2F_ERR_SHAPE"]
+    assert fn(H=0) == C["E2F_ERR_SHAPE"]
+    assert fn(C=128, H=3) == C["E2F_ERR_SHAPE"]
+    assert fn(C=12, H=4) == C["E2F_ERR_UNSUPPORTED"]    # d = 3: heads cannot align to lanes
+    assert fn(C=512, H=4) == C["E2F_ERR_UNSUPPORTED"]   # 128 lanes per row
+    assert fn(N=0, pos=None, idx=None, mask=None, ws=None, out=None) == C["E2F_OK"]
+    assert fn(pos=None) == C["E2F_ERR_NULL"]
+    assert fn(idx=None) == C["E2F_ERR_NULL"]
+    assert fn(mask=None) == C["E2F_ERR_NULL"]
+    assert fn(ws=None) == C["E2F_ERR_NULL"]
+    assert fn(out=None) == C["E2F_ERR_NULL"]
+    assert fn(out=ctypes.c_void_p(BASE + 8 * 64 * MB + 8)) == C["E2F_ERR_ALIGN"]
+    assert fn(ws=ctypes.c_void_p(BASE + 4 * 64 * MB + 4)) == C["E2F_ERR_ALIGN"]
+    assert fn(msg=ctypes.c_void_p(BASE + 12 * 64 * MB + 2)) == C["E2F_ERR_ALIGN"]
+    assert fn(idx=ctypes.c_void_p(BASE + 2 * 64 * MB + 2)) == C["E2F_ERR_ALIGN"]
+    need = lib.e2f_attn_workspace_bytes(1000, 2, 128, 0)
+    assert fn(ws_bytes=need - 1) == C["E2F_ERR_WORKSPACE"]
+    assert fn(out=fake(4)) == C["E2F_ERR_ALIAS"]             # out inside the workspace
+    assert fn(out=fake(1)) == C["E2F_ERR_ALIAS"]             # out over the positions
+    assert fn(msg=fake(8)) == C["E2F_ERR_ALIAS"]             # message over the output
+    assert fn(msg=fake(2)) == C["E2F_ERR_ALIAS"]             # message over the indices
+
+
+def test_forward_specific_errors():
+    assert _fwd(h=None) == C["E2F_ERR_NULL"]
+    assert _fwd(h=ctypes.c_void_p(BASE + 9 * 64 * MB + 4)) == C["E2F_ERR_ALIGN"]
+    assert _fwd(out=fake(9)) == C["E2F_ERR_ALIAS"]           # out over h
+    assert _fwd(ws=fake(9)) == C["E2F_ERR_ALIAS"]            # workspace over h
+
+
+def test_eaas_and_precouple_errors():
+    assert _eaas(dt=9) == C["E2F_ERR_DTYPE"]
+    assert _eaas(n=-2) == C["E2F_ERR_SHAPE"]
+    assert _eaas(lmax=4) == C["E2F_ERR_SHAPE"]
+    assert _eaas(C=0) == C["E2F_ERR_SHAPE"]
+    assert _eaas(n=0, r=None, h=None, out=None) == C["E2F_OK"]
+    assert _eaas(r=None) == C["E2F_ERR_NULL"]
+    assert _eaas(h=None) == C["E2F_ERR_NULL"]
+    assert _eaas(out=None) == C["E2F_ERR_NULL"]
+    assert _eaas(h=ctypes.c_void_p(BASE + 2 * 64 * MB + 8)) == C["E2F_ERR_ALIGN"]
+    assert _eaas(r=ctypes.c_void_p(BASE + 64 * MB + 2)) == C["E2F_ERR_ALIGN"]
+    assert _eaas(out=ctypes.c_void_p(BASE + 2 * 64 * MB + 4096)) == C["E2F_ERR_ALIAS"]  # partial
+    assert _eaas(out=fake(1)) == C["E2F_ERR_ALIAS"]
+    assert _pre(dt=3) == C["E2F_ERR_DTYPE"]
+    assert _pre(lmax=5) == C["E2F_ERR_SHAPE"]
+    assert _pre(N=0, pos=None, h=None, ws=None) == C["E2F_OK"]
+    assert _pre(ws=None) == C["E2F_ERR_NULL"]
+    assert _pre(ws_bytes=100) == C["E2F_ERR_WORKSPACE"]
+    assert _pre(ws=fake(2)) == C["E2F_ERR_ALIAS"]
+    assert _pre(h=ctypes.c_void_p(BASE + 2 * 64 * MB + 2)) == C["E2F_ERR_ALIGN"]
+
+
+def test_frames_errors():
+    f = lib.e2f_frames
+    assert f(None, -1, 2, fake(1), fake(2), fake(3)) == C["E2F_ERR_SHAPE"]
+    assert f(None, 10, 3, fake(1), fake(2), fake(3)) == C["E2F_ERR_SHAPE"]
+    assert f(None, 0, 2, None, None, None) == C["E2F_OK"]
+    assert f(None, 10, 2, None, fake(2), fake(3)) == C["E2F_ERR_NULL"]
+    assert f(None, 10, 2, fake(1), fake(1), fake(3)) == C["E2F_ERR_ALIAS"]
