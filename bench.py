@@ -25,6 +25,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CALIB_COPY_MIB = 1024
 
 WORKLOADS = {
     # name -> (generator config, description)
@@ -79,6 +80,108 @@ def cpu_baseline(cfg, budget_s=15.0, seed=0):
     }
 
 
+KERNEL_SOURCES = ["interatomic_potentials_amd/csrc/e2f_kernels.hip",
+                  "interatomic_potentials_amd/csrc/e2f_device.hpp",
+                  "interatomic_potentials_amd/csrc/e2f_internal.hpp"]
+
+
+def kernel_source_hash():
+    import hashlib
+    hsh = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()[:16]
+
+
+def _counter_means(path):
+    """Mean counter value per (kernel, counter) from a rocprofv3 counter_collection.csv."""
+    import collections
+    import csv
+    acc = collections.defaultdict(list)
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            short = name.split("<")[0].replace("void ", "").strip()
+            acc[(short, row["Counter_Name"])].append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+
+def summarize_profile(pmc_dir, workload, out_path):
+    """Write the committed counter summary from a directory of rocprofv3 csv runs.
+
+    Expects sub-directories trace_<w>, fetch_<w>, write_<w>, hit_<w>, fetch_copy, write_copy
+    (each holding run_*.csv) as produced by the commands listed in the summary.
+    """
+    import csv
+    w = workload
+    stats = list(csv.DictReader(open(os.path.join(pmc_dir, f"trace_{w}", "run_kernel_stats.csv"))))
+    fetch, nf = _counter_means(os.path.join(pmc_dir, f"fetch_{w}", "run_counter_collection.csv"))
+    write, _ = _counter_means(os.path.join(pmc_dir, f"write_{w}", "run_counter_collection.csv"))
+    hit, _ = _counter_means(os.path.join(pmc_dir, f"hit_{w}", "run_counter_collection.csv"))
+    cf, _ = _counter_means(os.path.join(pmc_dir, "fetch_copy", "run_counter_collection.csv"))
+    cw, _ = _counter_means(os.path.join(pmc_dir, "write_copy", "run_counter_collection.csv"))
+    copy_bytes = CALIB_COPY_MIB << 20
+    kf = copy_bytes / (cf[("__amd_rocclr_copyBuffer", "FETCH_SIZE")] * 1024)
+    kw = copy_bytes / (cw[("__amd_rocclr_copyBuffer", "WRITE_SIZE")] * 1024)
+    lines = [f"# rocprofv3 summary: {w} workload ({WORKLOADS[w]})", "",
+             f"kernel source hash: {kernel_source_hash()}", "",
+             "Commands (run from the repository root on the GPU box; TMPDIR=/tmp):", "```"]
+    bench_cmd = "python -u bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline".format(w=w)
+    lines += [f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/pmc/trace_{w} "
+              f"-o run -- {bench_cmd}",
+              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/fetch_{w} -o run "
+              f"-- {bench_cmd}",
+              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/write_{w} -o run "
+              f"-- {bench_cmd}",
+              f"rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv -d "
+              f"gpurun_out/pmc/hit_{w} -o run -- {bench_cmd}",
+              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/fetch_copy -o run "
+              f"-- python -u bench.py --calib-copy-mib {CALIB_COPY_MIB} --steps 3",
+              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/write_copy -o run "
+              f"-- python -u bench.py --calib-copy-mib {CALIB_COPY_MIB} --steps 3",
+              f"python bench.py --summarize-profile gpurun_out/pmc --workload {w}", "```", "",
+              "## Kernel trace (--kernel-trace --stats)", "",
+              "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} |")
+    lines += ["", "## Counter calibration (plain device copy of "
+              f"{CALIB_COPY_MIB} MiB, `__amd_rocclr_copyBuffer`)", "",
+              f"- FETCH_SIZE reads {cf[('__amd_rocclr_copyBuffer', 'FETCH_SIZE')]:.0f} KiB per copy "
+              f"of {copy_bytes} B read: read factor {kf:.4f} bytes per counted byte",
+              f"- WRITE_SIZE reads {cw[('__amd_rocclr_copyBuffer', 'WRITE_SIZE')]:.0f} KiB per copy "
+              f"of {copy_bytes} B written: write factor {kw:.4f}", "",
+              "## Per-dispatch counters (mean over dispatches) and calibrated traffic", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | TCC_HIT | TCC_MISS | L2 hit rate | "
+              "traffic bytes per launch |", "|---|---|---|---|---|---|---|"]
+    for k in sorted({k for (k, c) in fetch}):
+        fb = fetch.get((k, "FETCH_SIZE"), 0.0)
+        wb = write.get((k, "WRITE_SIZE"), 0.0)
+        th = hit.get((k, "TCC_HIT_sum"), 0.0)
+        tm = hit.get((k, "TCC_MISS_sum"), 0.0)
+        traffic = fb * 1024 * kf + wb * 1024 * kw
+        lines.append(f"| `{k}` | {fb:.0f} | {wb:.0f} | {th:.4g} | {tm:.4g} | "
+                     f"{th / max(th + tm, 1):.3f} | {traffic:.6g} |")
+        lines.append(f"<!-- traffic {k} {traffic:.0f} -->")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out_path)
+
+
+def committed_traffic(workload, kernel="e2f::k_aggregate"):
+    """Calibrated HBM bytes per launch from the committed summary, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", f"k_aggregate_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if f"kernel source hash: {kernel_source_hash()}" not in text:
+        return None
+    import re
+    m = re.search(r"<!-- traffic %s (\d+) -->" % re.escape(kernel), text)
+    return float(m.group(1)) if m else None
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,7 +192,14 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+                    help="write profiles/k_aggregate_<workload>.md from rocprofv3 csv runs in DIR")
     args = ap.parse_args(argv)
+
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.workload,
+                          os.path.join(ROOT, "profiles", f"k_aggregate_{args.workload}.md"))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -198,7 +308,7 @@ def main(argv=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": k2_gbs / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": committed_traffic(args.workload),
             "algorithmic_bytes_per_launch": k2_bytes,
             "bytes_per_edge": per_edge,
             "bytes_per_target": per_target,
