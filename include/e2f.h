@@ -82,8 +82,10 @@ typedef enum e2f_dtype {
 #define E2F_ERR_INDEX (-8)       /* a valid slot holds an index outside [0, N) (validation only) */
 #define E2F_ERR_UNSUPPORTED (-9) /* channel / head layout outside the kernels' lane mapping */
 
-/* flags of the attention entry points */
+/* flags of the attention entry points (any other bit: E2F_ERR_SHAPE) */
 #define E2F_VALIDATE_INDICES 1u  /* check every valid slot's index before running; synchronises */
+#define E2F_TARGETS_IN_ORDER 2u  /* visit targets in index order: skip the spatial schedule, for
+                                    atoms already stored in a spatially coherent order */
 
 /* Name of a status code ("E2F_OK", "E2F_ERR_SHAPE", ...); never NULL. */
 const char* e2f_status_string(int status);
@@ -111,10 +113,13 @@ int e2f_eaas_couple(hipStream_t stream, int64_t n, int lmax, int C, int dtype,
 
 /*
  * Workspace bytes that e2f_attn_precouple / _aggregate / _forward need for
- * N atoms: the pre-coupled values of step 1, stored per atom as S + 1 rows
- * of C elements (row 0 = k_j = h_j[l=0, :], rows 1..S = h'_j), so that each
- * neighbour's K and V are one contiguous (S + 1) * C * sizeof(T) byte
- * block, plus 256 bytes for a validation flag.  0 on bad arguments.
+ * N atoms, 0 on bad arguments.  Layout, each part 256-byte aligned:
+ *   - the pre-coupled values of step 1, stored per atom as S + 1 rows of C
+ *     elements (row 0 = k_j = h_j[l=0, :], rows 1..S = h'_j), so that each
+ *     neighbour's K and V are one contiguous (S + 1) * C * sizeof(T) block;
+ *   - 256 bytes for the validation flag;
+ *   - the target schedule scratch (order, cells, cell counts, bounding-box
+ *     partials): about 8 N bytes plus at most 1 MiB.
  */
 size_t e2f_attn_workspace_bytes(int64_t N, int lmax, int C, int dtype);
 
@@ -142,11 +147,16 @@ int e2f_attn_precouple(hipStream_t stream, int64_t N, int lmax, int C, int dtype
  *   nbr_mask  [N, K] uint8   any pattern; valid slots need not come first;
  *                            repeated indices count once per slot
  *   scale     logit scale; <= 0 selects 1 / sqrt(C / H)
- *   workspace filled by e2f_attn_precouple (the flag tail is written under
- *             E2F_VALIDATE_INDICES, hence not const)
+ *   workspace filled by e2f_attn_precouple; its schedule scratch (and, under
+ *             E2F_VALIDATE_INDICES, its flag) is rewritten here, hence not
+ *             const.  Targets are visited in Morton order of their
+ *             positions (built on the GPU each call unless
+ *             E2F_TARGETS_IN_ORDER), each XCD taking one contiguous
+ *             stretch, so that waves sharing an L2 share neighbours; the
+ *             visiting order never changes any target's result.
  *   out       [N, S, C] T    out_i; exactly 0 for a target with no valid slot
  *   out_msg   [N, S, C] T or NULL: also store the normalised message m_i
- *   flags     0 or E2F_VALIDATE_INDICES
+ *   flags     0 or E2F_VALIDATE_INDICES | E2F_TARGETS_IN_ORDER
  */
 int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                        const float* pos, const int32_t* nbr_idx, const uint8_t* nbr_mask,

@@ -19,7 +19,7 @@ from typing import Optional
 __all__ = [
     "E2FError", "lib", "status_string", "path_count", "eaas_couple", "attn_workspace_bytes",
     "attn_precouple", "attn_aggregate", "attn_forward", "frames", "F32", "BF16",
-    "VALIDATE_INDICES",
+    "VALIDATE_INDICES", "TARGETS_IN_ORDER",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libe2f.so")
 F32 = 0
 BF16 = 1
 VALIDATE_INDICES = 1
+TARGETS_IN_ORDER = 2
 
 _STATUS = {
     0: "E2F_OK", -1: "E2F_ERR_NULL", -2: "E2F_ERR_SHAPE", -3: "E2F_ERR_DTYPE",
@@ -92,6 +93,10 @@ def status_string(code: int) -> str:
 
 def path_count(lmax: int) -> int:
     return lib.e2f_path_count(lmax)
+
+
+def _flags(validate: bool, targets_in_order: bool) -> int:
+    return (VALIDATE_INDICES if validate else 0) | (TARGETS_IN_ORDER if targets_in_order else 0)
 
 
 def _check(code: int, where: str) -> None:
@@ -214,7 +219,8 @@ def attn_precouple(pos, h, ws=None, path_w=None):
 
 def attn_aggregate(pos, nbr_idx, nbr_mask, ws, heads: int, lmax: int, C: int, dtype,
                    scale: Optional[float] = None, path_w=None, out=None,
-                   return_msg: bool = False, validate: bool = False):
+                   return_msg: bool = False, validate: bool = False,
+                   targets_in_order: bool = False):
     """Steps 2-3 from a filled workspace; returns out (and m if return_msg)."""
     torch = _torch()
     _dev(pos, "pos", torch.float32)
@@ -231,13 +237,13 @@ def attn_aggregate(pos, nbr_idx, nbr_mask, ws, heads: int, lmax: int, C: int, dt
     _check(lib.e2f_attn_aggregate(_stream(ws), N, K, lmax, C, heads, _dtype_code(out), _ptr(pos),
                                   _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0), _ptr(pw),
                                   _ptr(ws), ws.numel() * ws.element_size(), _ptr(out), _ptr(msg),
-                                  VALIDATE_INDICES if validate else 0), "e2f_attn_aggregate")
+                                  _flags(validate, targets_in_order)), "e2f_attn_aggregate")
     return (out, msg) if return_msg else out
 
 
 def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] = None,
                  path_w=None, ws=None, out=None, return_msg: bool = False,
-                 validate: bool = False):
+                 validate: bool = False, targets_in_order: bool = False):
     """Full path (steps 1-3): pos [N,3] fp32, h [N,S,C], nbr_idx [N,K] int32, nbr_mask [N,K] uint8."""
     torch = _torch()
     _dev(pos, "pos", torch.float32)
@@ -259,7 +265,7 @@ def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] =
     _check(lib.e2f_attn_forward(_stream(h), N, K, lmax, C, heads, dt, _ptr(pos), _ptr(h),
                                 _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0), _ptr(pw),
                                 _ptr(ws), ws.numel() * ws.element_size(), _ptr(out), _ptr(msg),
-                                VALIDATE_INDICES if validate else 0), "e2f_attn_forward")
+                                _flags(validate, targets_in_order)), "e2f_attn_forward")
     return (out, msg) if return_msg else out
 
 

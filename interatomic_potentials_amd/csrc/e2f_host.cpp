@@ -132,16 +132,46 @@ size_t ws_body_bytes(int64_t N, int lmax, int C, int dt) {
   return round256((size_t)N * (size_t)(ncomp(lmax) + 1) * (size_t)C * esize(dt));
 }
 
+// Morton bits per axis of the target schedule: about one cell per atom, at most 2^18 cells
+int sched_bits(int64_t N) {
+  int bits = 1;
+  while (bits < 6 && ((int64_t)1 << (3 * bits)) < N) ++bits;
+  return bits;
+}
+
+size_t sched_bytes(int64_t N) {
+  const int64_t ncell = (int64_t)1 << (3 * sched_bits(N));
+  return 2 * round256((size_t)N * 4) + round256((size_t)ncell * 4) +
+         round256((size_t)e2f::kBboxBlocks * 6 * 4);
+}
+
+// layout: [pre-coupled rows][256 B validation flag][schedule scratch]
+e2f::SchedScratch sched_scratch(void* ws, int64_t N, int lmax, int C, int dt) {
+  char* p = static_cast<char*>(ws) + ws_body_bytes(N, lmax, C, dt) + 256;
+  e2f::SchedScratch sc;
+  sc.bits = sched_bits(N);
+  const int64_t ncell = (int64_t)1 << (3 * sc.bits);
+  sc.sched = reinterpret_cast<int32_t*>(p);
+  p += round256((size_t)N * 4);
+  sc.cell = reinterpret_cast<int32_t*>(p);
+  p += round256((size_t)N * 4);
+  sc.counts = reinterpret_cast<int32_t*>(p);
+  p += round256((size_t)ncell * 4);
+  sc.partial = reinterpret_cast<float*>(p);
+  return sc;
+}
+
 int check_shape_common(int64_t n, int lmax, int C, int dt) {
   if (bad_dtype(dt)) return E2F_ERR_DTYPE;
   if (n < 0 || lmax < 0 || lmax > e2f::kMaxLmax || C < 1) return E2F_ERR_SHAPE;
   return E2F_OK;
 }
 
-int check_attn_shape(int64_t N, int K, int lmax, int C, int H, int dt) {
+int check_attn_shape(int64_t N, int K, int lmax, int C, int H, int dt, uint32_t flags) {
   const int st = check_shape_common(N, lmax, C, dt);
   if (st != E2F_OK) return st;
   if (K < 1 || H < 1 || C % H != 0) return E2F_ERR_SHAPE;
+  if (flags & ~(E2F_VALIDATE_INDICES | E2F_TARGETS_IN_ORDER)) return E2F_ERR_SHAPE;
   if (attn_width(C, H, dt) == 0) return E2F_ERR_UNSUPPORTED;
   return E2F_OK;
 }
@@ -180,6 +210,13 @@ int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
   }
   const int V = attn_width(C, H, dt);
   const int d = C / H;
+  const int32_t* sched = nullptr;
+  if (!(flags & E2F_TARGETS_IN_ORDER)) {
+    const e2f::SchedScratch sc = sched_scratch(ws, N, lmax, C, dt);
+    const int st = hip_status(e2f::launch_schedule(N, pos, sc, stream));
+    if (st != E2F_OK) return st;
+    sched = sc.sched;
+  }
   e2f::AggArgs a;
   a.pos = pos;
   a.idx = idx;
@@ -194,6 +231,7 @@ int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
   a.head_lanes = d / V;
   const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)d);
   a.scale_log2e = (float)(sc * 1.4426950408889634);  // log2(e)
+  a.sched = sched;
   const EaasCoef cf = make_coef(lmax, path_w);
   return hip_status(e2f::launch_aggregate(lmax, dt, V, a, cf, stream));
 }
@@ -256,7 +294,7 @@ int e2f_eaas_couple(hipStream_t stream, int64_t n, int lmax, int C, int dtype, c
 
 size_t e2f_attn_workspace_bytes(int64_t N, int lmax, int C, int dtype) {
   if (check_shape_common(N, lmax, C, dtype) != E2F_OK) return 0;
-  return ws_body_bytes(N, lmax, C, dtype) + 256;
+  return ws_body_bytes(N, lmax, C, dtype) + 256 + sched_bytes(N);
 }
 
 int e2f_attn_precouple(hipStream_t stream, int64_t N, int lmax, int C, int dtype,
@@ -281,7 +319,7 @@ int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, in
                        const float* pos, const int32_t* nbr_idx, const uint8_t* nbr_mask,
                        float scale, const float* path_w, void* workspace, size_t ws_bytes,
                        void* out, void* out_msg, uint32_t flags) {
-  int st = check_attn_shape(N, K, lmax, C, H, dtype);
+  int st = check_attn_shape(N, K, lmax, C, H, dtype, flags);
   if (st != E2F_OK) return st;
   if (N == 0) return E2F_OK;
   if (!pos || !nbr_idx || !nbr_mask || !workspace || !out) return E2F_ERR_NULL;
@@ -308,7 +346,7 @@ int e2f_attn_forward(hipStream_t stream, int64_t N, int K, int lmax, int C, int 
                      const float* pos, const void* h, const int32_t* nbr_idx,
                      const uint8_t* nbr_mask, float scale, const float* path_w, void* workspace,
                      size_t ws_bytes, void* out, void* out_msg, uint32_t flags) {
-  int st = check_attn_shape(N, K, lmax, C, H, dtype);
+  int st = check_attn_shape(N, K, lmax, C, H, dtype, flags);
   if (st != E2F_OK) return st;
   if (N == 0) return E2F_OK;
   if (!h) return E2F_ERR_NULL;

@@ -11,6 +11,18 @@ constexpr int kMaxLmax = 2;
 constexpr int kMaxPaths = 15;       // triangle-allowed (li, lf, lo) with all <= 2
 constexpr int kWavesPerBlock = 4;   // 256-thread workgroups, one wave per target
 constexpr int kTile = 256;          // neighbour slots compacted per pass
+constexpr int kXcds = 8;            // gfx950 (MI350 series): 8 XCDs, workgroups dealt round-robin
+constexpr int kBboxBlocks = 256;    // partial bounding boxes reduced by the schedule builder
+
+// Target schedule scratch, carved from the caller's workspace after the
+// pre-coupled rows and the validation flag.
+struct SchedScratch {
+  int32_t* sched;      // [N] target order: atoms sorted by Morton cell
+  int32_t* cell;       // [N] cell of each atom
+  int32_t* counts;     // [ncell] per-cell counts, then running offsets
+  float* partial;      // [kBboxBlocks][6] partial (min, max) of the positions
+  int bits;            // Morton bits per axis; ncell = 2^(3 bits)
+};
 
 // Sparse reindex weights, one row per path (lexicographic (li, lf, lo)):
 // c[p][m] = w_p <li m lf 0 | lo m> for m = 0..2 (Condon-Shortley).
@@ -40,6 +52,7 @@ struct AggArgs {
   int lane_log;            // log2 of the lanes serving one neighbour row
   int head_lanes;          // lanes per head = d / V (power of two)
   float scale_log2e;       // logit scale times log2(e)
+  const int32_t* sched;    // [N] processing order of the targets
 };
 
 // launchers (kernels file); return 0 or a hipError_t value
@@ -50,5 +63,6 @@ int launch_aggregate(int lmax, int dtype, int V, const AggArgs& a, const EaasCoe
 int launch_frames(int lmax, int64_t n, const float* r, float* Q, float* D, hipStream_t s);
 int launch_validate(int64_t N, int K, const int32_t* idx, const uint8_t* mask, int32_t* flag,
                     hipStream_t s);
+int launch_schedule(int64_t N, const float* pos, const SchedScratch& sc, hipStream_t s);
 
 }  // namespace e2f

@@ -97,8 +97,15 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
   __shared__ int s_nb[kWavesPerBlock][kTile];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + w;
-  if (i >= a.N) return;  // whole wave: no workgroup barrier below
+  // Workgroups are dealt to the XCDs round-robin; give XCD x the x-th
+  // contiguous stretch of the schedule so that the waves sharing an L2 work
+  // on neighbouring targets (the grid is a multiple of kXcds).
+  const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
+  const int64_t blk = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int64_t slot = blk * kWavesPerBlock + w;
+  if (slot >= a.N) return;  // whole wave: no workgroup barrier below
+  const int64_t i = a.sched ? (int64_t)a.sched[slot] : slot;
+  if (i < 0 || i >= a.N) return;
   const int lg = a.lane_log;
   const int P = 64 >> lg;
   const int sub = lane >> lg;
@@ -284,6 +291,117 @@ __global__ __launch_bounds__(256) void k_validate(int64_t total, int64_t N, cons
   }
 }
 
+// ------------------------------------------------- target schedule
+//
+// Targets are visited in Morton (Z-curve) order of a grid of 2^bits cells
+// per axis over the bounding box of the positions, built with a counting
+// sort: bounding box, per-cell counts, one scan, scatter.  The order inside
+// a cell is whatever the atomics produce; it only changes which wave takes
+// which target, never a target's arithmetic, so outputs do not depend on it.
+
+// spread the low 10 bits of v to every third bit (Morton interleave)
+__device__ inline uint32_t spread3(uint32_t v) {
+  v &= 0x3ffu;
+  v = (v | (v << 16)) & 0x030000ffu;
+  v = (v | (v << 8)) & 0x0300f00fu;
+  v = (v | (v << 4)) & 0x030c30c3u;
+  v = (v | (v << 2)) & 0x09249249u;
+  return v;
+}
+
+__global__ __launch_bounds__(256) void k_sched_bbox(int64_t N, const float* pos, float* partial,
+                                                    int32_t* counts, int64_t ncell) {
+  __shared__ float red[6][256];
+  const int t = threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + t; c < ncell; c += stride) counts[c] = 0;
+  float v[6] = {INFINITY, INFINITY, INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int64_t at = (int64_t)blockIdx.x * 256 + t; at < N; at += stride) {
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      const float x = pos[3 * at + d];
+      v[d] = fminf(v[d], x);
+      v[3 + d] = fmaxf(v[3 + d], x);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 6; ++d) red[d][t] = v[d];
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (t < o) {
+#pragma unroll
+      for (int d = 0; d < 3; ++d) {
+        red[d][t] = fminf(red[d][t], red[d][t + o]);
+        red[3 + d][t] = fmaxf(red[3 + d][t], red[3 + d][t + o]);
+      }
+    }
+    __syncthreads();
+  }
+  if (t < 6) partial[blockIdx.x * 6 + t] = red[t][0];
+}
+
+__global__ __launch_bounds__(256) void k_sched_count(int64_t N, const float* pos,
+                                                     const float* partial, int bits,
+                                                     int32_t* cell, int32_t* counts) {
+  __shared__ float bb[6];
+  const int t = threadIdx.x;
+  if (t < 6) {
+    float r = partial[t];
+    for (int b = 1; b < kBboxBlocks; ++b) {
+      const float x = partial[b * 6 + t];
+      r = t < 3 ? fminf(r, x) : fmaxf(r, x);
+    }
+    bb[t] = r;
+  }
+  __syncthreads();
+  const int64_t at = (int64_t)blockIdx.x * 256 + t;
+  if (at >= N) return;
+  const int n = 1 << bits;
+  uint32_t q[3];
+#pragma unroll
+  for (int d = 0; d < 3; ++d) {
+    const float lo = bb[d], ext = bb[3 + d] - bb[d];
+    const float u = ext > 0.0f ? (pos[3 * at + d] - lo) * ((float)n / ext) : 0.0f;
+    // comparisons keep NaN and infinities out of the integer conversion
+    q[d] = u >= 1.0f ? (u < (float)(n - 1) ? (uint32_t)u : (uint32_t)(n - 1)) : 0u;
+  }
+  const int32_t c = (int32_t)(spread3(q[0]) | (spread3(q[1]) << 1) | (spread3(q[2]) << 2));
+  cell[at] = c;
+  atomicAdd(&counts[c], 1);
+}
+
+// exclusive scan of counts[0..ncell) in place, one 1024-thread workgroup
+__global__ __launch_bounds__(1024) void k_sched_scan(int64_t ncell, int32_t* counts) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  const int64_t per = (ncell + 1023) / 1024;
+  const int64_t beg = t * per;
+  const int64_t end = beg + per < ncell ? beg + per : ncell;
+  int32_t sum = 0;
+  for (int64_t c = beg; c < end; ++c) sum += counts[c];
+  part[t] = sum;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan of the partial sums
+    const int32_t add = t >= o ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
+  }
+  int32_t run = part[t] - sum;
+  for (int64_t c = beg; c < end; ++c) {
+    const int32_t v = counts[c];
+    counts[c] = run;
+    run += v;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_sched_scatter(int64_t N, const int32_t* cell,
+                                                       int32_t* offsets, int32_t* sched) {
+  const int64_t at = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (at >= N) return;
+  sched[atomicAdd(&offsets[cell[at]], 1)] = (int32_t)at;
+}
+
 // ---------------------------------------------------------- launchers
 
 namespace {
@@ -312,8 +430,9 @@ int eaas_go(int V, const EaasArgs& a, const EaasCoef& cf, hipStream_t s) {
 
 template <int L, typename T>
 int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
-  constexpr int U = 2;
-  const dim3 grid((unsigned)((a.N + kWavesPerBlock - 1) / kWavesPerBlock));
+  constexpr int U = 4;  // neighbours per subgroup in flight per iteration
+  const int64_t blocks = (a.N + kWavesPerBlock - 1) / kWavesPerBlock;
+  const dim3 grid((unsigned)((blocks + kXcds - 1) / kXcds * kXcds));
   (void)hipGetLastError();
   switch (V) {
     case 1: hipLaunchKernelGGL((k_aggregate<L, 1, T, U>), grid, dim3(256), 0, s, a, cf); break;
@@ -371,6 +490,19 @@ int launch_validate(int64_t N, int K, const int32_t* idx, const uint8_t* mask, i
   const int64_t total = N * (int64_t)K;
   hipLaunchKernelGGL(k_validate, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, total, N,
                      idx, mask, flag);
+  return last_error();
+}
+
+int launch_schedule(int64_t N, const float* pos, const SchedScratch& sc, hipStream_t s) {
+  (void)hipGetLastError();
+  const int64_t ncell = (int64_t)1 << (3 * sc.bits);
+  const dim3 grid_n((unsigned)((N + 255) / 256));
+  hipLaunchKernelGGL(k_sched_bbox, dim3(kBboxBlocks), dim3(256), 0, s, N, pos, sc.partial,
+                     sc.counts, ncell);
+  hipLaunchKernelGGL(k_sched_count, grid_n, dim3(256), 0, s, N, pos, sc.partial, sc.bits, sc.cell,
+                     sc.counts);
+  hipLaunchKernelGGL(k_sched_scan, dim3(1), dim3(1024), 0, s, ncell, sc.counts);
+  hipLaunchKernelGGL(k_sched_scatter, grid_n, dim3(256), 0, s, N, sc.cell, sc.counts, sc.sched);
   return last_error();
 }
 

@@ -67,12 +67,26 @@ def test_status_strings_and_path_counts():
     assert e2f.path_count(-1) == C["E2F_ERR_SHAPE"]
 
 
+def _r256(b):
+    return (b + 255) // 256 * 256
+
+
+def _expected_ws(N, lmax, C, esize):
+    """Documented layout: rows | 256 B flag | order + cells (4N each) | cell counts | bbox partials."""
+    bits = 1
+    while bits < 6 and 8 ** bits < N:
+        bits += 1
+    sched = 2 * _r256(4 * N) + _r256(4 * 8 ** bits) + _r256(256 * 6 * 4)
+    return _r256(N * ((lmax + 1) ** 2 + 1) * C * esize) + 256 + sched
+
+
 def test_workspace_bytes():
     wb = lib.e2f_attn_workspace_bytes
-    assert wb(32768, 2, 128, 0) == 32768 * 10 * 128 * 4 + 256
-    assert wb(100000, 2, 128, 1) == 100000 * 10 * 128 * 2 + 256
-    assert wb(3, 1, 5, 0) == 512 + 256          # 3*5*5*4 = 300 B rounds up to 512
-    assert wb(0, 2, 128, 0) == 256
+    assert wb(32768, 2, 128, 0) == _expected_ws(32768, 2, 128, 4)
+    assert wb(32768, 2, 128, 0) - 32768 * 10 * 128 * 4 - 256 < 2 ** 20   # scratch is small
+    assert wb(100000, 2, 128, 1) == _expected_ws(100000, 2, 128, 2)
+    assert wb(3, 1, 5, 0) == _expected_ws(3, 1, 5, 4)          # 300 B of rows round up to 512
+    assert wb(0, 2, 128, 0) == _expected_ws(0, 2, 128, 4)
     assert wb(10, 3, 128, 0) == 0
     assert wb(10, 2, 128, 5) == 0
     assert wb(-1, 2, 128, 0) == 0
@@ -125,6 +139,7 @@ def test_attention_argument_errors(fn):
     assert fn(C=128, H=3) == C["E2F_ERR_SHAPE"]
     assert fn(C=12, H=4) == C["E2F_ERR_UNSUPPORTED"]    # d = 3: heads cannot align to lanes
     assert fn(C=512, H=4) == C["E2F_ERR_UNSUPPORTED"]   # 128 lanes per row
+    assert fn(flags=4) == C["E2F_ERR_SHAPE"]                  # unknown flag bit
     assert fn(N=0, pos=None, idx=None, mask=None, ws=None, out=None) == C["E2F_OK"]
     assert fn(pos=None) == C["E2F_ERR_NULL"]
     assert fn(idx=None) == C["E2F_ERR_NULL"]
