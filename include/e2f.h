@@ -118,8 +118,8 @@ int e2f_eaas_couple(hipStream_t stream, int64_t n, int lmax, int C, int dtype,
  *     elements (row 0 = k_j = h_j[l=0, :], rows 1..S = h'_j), so that each
  *     neighbour's K and V are one contiguous (S + 1) * C * sizeof(T) block;
  *   - 256 bytes for the validation flag;
- *   - the target schedule scratch (order, cells, cell counts, bounding-box
- *     partials): about 8 N bytes plus at most 1 MiB.
+ *   - the target schedule scratch (order and cell per atom, 2^15 cell
+ *     counts, bounding-box partials): 8 N bytes plus about 140 KiB.
  */
 size_t e2f_attn_workspace_bytes(int64_t N, int lmax, int C, int dtype);
 

@@ -242,11 +242,40 @@ __device__ inline uint16_t f32_to_bf16(float f) {  // round to nearest, ties to 
   return uint16_t(u >> 16);
 }
 
+// One lane's V elements of a row exactly as loaded (fp32, or bf16 pairs packed
+// in 32-bit words), widened to fp32 only where they are used.
+template <typename T, int V>
+struct Raw;
+
+template <int V>
+struct Raw<float, V> {
+  float f[V];
+  __device__ inline float get(int v) const { return f[v]; }
+  __device__ inline void zero() {
+#pragma unroll
+    for (int v = 0; v < V; ++v) f[v] = 0.0f;
+  }
+};
+
+template <int V>
+struct Raw<uint16_t, V> {
+  uint32_t w[(V + 1) / 2];
+  __device__ inline float get(int v) const {
+    const uint32_t x = w[v >> 1];
+    return __uint_as_float((v & 1) ? (x & 0xffff0000u) : (x << 16));
+  }
+  __device__ inline void zero() {
+#pragma unroll
+    for (int k = 0; k < (V + 1) / 2; ++k) w[k] = 0u;
+  }
+};
+
 template <typename T, int V>
 struct VecIO;
 
 template <int V>
 struct VecIO<float, V> {
+  static __device__ inline void load_raw(const float* p, Raw<float, V>& r) { load(p, r.f); }
   static __device__ inline void load(const float* p, float* o) {
     if constexpr (V == 4) {
       const float4 v = *reinterpret_cast<const float4*>(p);
@@ -278,6 +307,19 @@ struct VecIO<uint16_t, V> {
   }
   static __device__ inline uint32_t pack(float a, float b) {
     return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+  }
+  static __device__ inline void load_raw(const uint16_t* p, Raw<uint16_t, V>& r) {
+    if constexpr (V == 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    } else if constexpr (V == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      r.w[0] = v.x; r.w[1] = v.y;
+    } else if constexpr (V == 2) {
+      r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+      r.w[0] = *p;
+    }
   }
   static __device__ inline void load(const uint16_t* p, float* o) {
     if constexpr (V == 8) {

@@ -132,16 +132,15 @@ size_t ws_body_bytes(int64_t N, int lmax, int C, int dt) {
   return round256((size_t)N * (size_t)(ncomp(lmax) + 1) * (size_t)C * esize(dt));
 }
 
-// Morton bits per axis of the target schedule: about one cell per atom, at most 2^18 cells
+// Morton bits per axis of the target schedule: about one cell per atom, at most 2^15 cells
 int sched_bits(int64_t N) {
   int bits = 1;
-  while (bits < 6 && ((int64_t)1 << (3 * bits)) < N) ++bits;
+  while (bits < e2f::kSchedMaxBits && ((int64_t)1 << (3 * bits)) < N) ++bits;
   return bits;
 }
 
 size_t sched_bytes(int64_t N) {
-  const int64_t ncell = (int64_t)1 << (3 * sched_bits(N));
-  return 2 * round256((size_t)N * 4) + round256((size_t)ncell * 4) +
+  return 2 * round256((size_t)N * 4) + round256((size_t)e2f::kSchedCells * 4) +
          round256((size_t)e2f::kBboxBlocks * 6 * 4);
 }
 
@@ -150,13 +149,12 @@ e2f::SchedScratch sched_scratch(void* ws, int64_t N, int lmax, int C, int dt) {
   char* p = static_cast<char*>(ws) + ws_body_bytes(N, lmax, C, dt) + 256;
   e2f::SchedScratch sc;
   sc.bits = sched_bits(N);
-  const int64_t ncell = (int64_t)1 << (3 * sc.bits);
   sc.sched = reinterpret_cast<int32_t*>(p);
   p += round256((size_t)N * 4);
   sc.cell = reinterpret_cast<int32_t*>(p);
   p += round256((size_t)N * 4);
   sc.counts = reinterpret_cast<int32_t*>(p);
-  p += round256((size_t)ncell * 4);
+  p += round256((size_t)e2f::kSchedCells * 4);
   sc.partial = reinterpret_cast<float*>(p);
   return sc;
 }

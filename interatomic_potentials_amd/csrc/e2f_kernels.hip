@@ -7,8 +7,9 @@
 //              l = 0 row (the key) in front of h', so that a neighbour's K and
 //              V form one contiguous block for the stream below.
 // k_aggregate  steps 2 and 3 (write-up section 3; gist.science summary 2.2):
-//              one wavefront per target.  The valid slots of the target's
-//              row are compacted into LDS with a ballot; the wave then splits
+//              one wavefront per target, targets taken in a spatial schedule.
+//              The valid slots of the target's row are compacted into LDS
+//              with a ballot and sorted by atom index; the wave then splits
 //              into 64 / 2^lane_log subgroups that stream disjoint neighbours
 //              (each neighbour's (S + 1) rows read once, coalesced), keep a
 //              running max and normaliser per head (online softmax, base-2
@@ -136,11 +137,11 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
   const uint8_t* mrow = a.mask + i * K;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
+  int* nb = s_nb[w];
   for (int t0 = 0; t0 < K; t0 += kTile) {
     // compact this tile's valid slots (mask = 1 and index in range) into LDS
     int cnt = 0;
-#pragma unroll
-    for (int u = 0; u < kTile; u += 64) {
+    for (int u = 0; u < kTile && t0 + u < K; u += 64) {
       const int slot = t0 + u + lane;
       bool ok = false;
       int j = 0;
@@ -149,27 +150,45 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
         ok = j >= 0 && (int64_t)j < N;
       }
       const uint64_t b = __ballot(ok);
-      if (ok) s_nb[w][cnt + __popcll(b & below)] = j;
+      if (ok) nb[cnt + __popcll(b & below)] = j;
       cnt += __popcll(b);
     }
+    // Sort the tile's neighbours by atom index (bitonic network in LDS).  All
+    // waves then sweep shared neighbours in the same order, so rows fetched
+    // by one target are still in L2 when nearby targets ask for them; and the
+    // visiting order, hence the rounding, no longer depends on slot order.
+    int n2 = 1;
+    while (n2 < cnt) n2 <<= 1;
+    for (int e = cnt + lane; e < n2; e += 64) nb[e] = 0x7fffffff;
     wave_sync();
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int e = lane; e < (n2 >> 1); e += 64) {
+          const int lo = ((e & ~(jj - 1)) << 1) | (e & (jj - 1));
+          const int x = nb[lo], y = nb[lo + jj];
+          if ((x > y) == ((lo & k) == 0)) {
+            nb[lo] = y;
+            nb[lo + jj] = x;
+          }
+        }
+        wave_sync();
+      }
+    }
 
     for (int n0 = 0; n0 < cnt; n0 += P * U) {
-      float kv[U][S + 1][V];
+      Raw<T, V> kv[U][S + 1];
       bool val[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int n = n0 + u * P + sub;
         val[u] = n < cnt;
         if (val[u] && act) {
-          const T* src = ws + (int64_t)s_nb[w][n] * row + c0;
+          const T* src = ws + (int64_t)nb[n] * row + c0;
 #pragma unroll
-          for (int r = 0; r <= S; ++r) VecIO<T, V>::load(src + r * C, kv[u][r]);
+          for (int r = 0; r <= S; ++r) VecIO<T, V>::load_raw(src + r * C, kv[u][r]);
         } else {
 #pragma unroll
-          for (int r = 0; r <= S; ++r)
-#pragma unroll
-            for (int v = 0; v < V; ++v) kv[u][r][v] = 0.0f;
+          for (int r = 0; r <= S; ++r) kv[u][r].zero();
         }
       }
       float s[U];
@@ -178,7 +197,7 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
       for (int u = 0; u < U; ++u) {
         float dt = 0.0f;
 #pragma unroll
-        for (int v = 0; v < V; ++v) dt = fmaf(q[v], kv[u][0][v], dt);
+        for (int v = 0; v < V; ++v) dt = fmaf(q[v], kv[u][0].get(v), dt);
         dt = head_sum(dt, a.head_lanes);
         s[u] = val[u] ? dt * a.scale_log2e : -INFINITY;
         mx = fmaxf(mx, s[u]);
@@ -198,7 +217,7 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
         for (int v = 0; v < V; ++v) {
           float t = acc[r][v] * corr;
 #pragma unroll
-          for (int u = 0; u < U; ++u) t = fmaf(p[u], kv[u][r + 1][v], t);
+          for (int u = 0; u < U; ++u) t = fmaf(p[u], kv[u][r + 1].get(v), t);
           acc[r][v] = t;
         }
       mu = mx;
@@ -343,17 +362,25 @@ __global__ __launch_bounds__(256) void k_sched_bbox(int64_t N, const float* pos,
 __global__ __launch_bounds__(256) void k_sched_count(int64_t N, const float* pos,
                                                      const float* partial, int bits,
                                                      int32_t* cell, int32_t* counts) {
-  __shared__ float bb[6];
+  static_assert(kBboxBlocks == 256, "one partial box per thread");
+  __shared__ float red[6][256];
   const int t = threadIdx.x;
-  if (t < 6) {
-    float r = partial[t];
-    for (int b = 1; b < kBboxBlocks; ++b) {
-      const float x = partial[b * 6 + t];
-      r = t < 3 ? fminf(r, x) : fmaxf(r, x);
-    }
-    bb[t] = r;
-  }
+#pragma unroll
+  for (int d = 0; d < 6; ++d) red[d][t] = partial[t * 6 + d];
   __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (t < o) {
+#pragma unroll
+      for (int d = 0; d < 3; ++d) {
+        red[d][t] = fminf(red[d][t], red[d][t + o]);
+        red[3 + d][t] = fmaxf(red[3 + d][t], red[3 + d][t + o]);
+      }
+    }
+    __syncthreads();
+  }
+  float bb[6];
+#pragma unroll
+  for (int d = 0; d < 6; ++d) bb[d] = red[d][0];
   const int64_t at = (int64_t)blockIdx.x * 256 + t;
   if (at >= N) return;
   const int n = 1 << bits;
@@ -370,28 +397,36 @@ __global__ __launch_bounds__(256) void k_sched_count(int64_t N, const float* pos
   atomicAdd(&counts[c], 1);
 }
 
-// exclusive scan of counts[0..ncell) in place, one 1024-thread workgroup
-__global__ __launch_bounds__(1024) void k_sched_scan(int64_t ncell, int32_t* counts) {
+// exclusive scan of counts[0..kSchedCells) in place: one 1024-thread
+// workgroup, 32 consecutive counts per thread moved as 128-bit accesses
+__global__ __launch_bounds__(1024) void k_sched_scan(int32_t* counts) {
+  static_assert(kSchedCells == 1024 * 32, "32 counts per thread");
   __shared__ int32_t part[1024];
   const int t = threadIdx.x;
-  const int64_t per = (ncell + 1023) / 1024;
-  const int64_t beg = t * per;
-  const int64_t end = beg + per < ncell ? beg + per : ncell;
+  int4* p = reinterpret_cast<int4*>(counts) + t * 8;
+  int4 v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = p[k];
   int32_t sum = 0;
-  for (int64_t c = beg; c < end; ++c) sum += counts[c];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sum += v[k].x + v[k].y + v[k].z + v[k].w;
   part[t] = sum;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan of the partial sums
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan of the per-thread sums
     const int32_t add = t >= o ? part[t - o] : 0;
     __syncthreads();
     part[t] += add;
     __syncthreads();
   }
   int32_t run = part[t] - sum;
-  for (int64_t c = beg; c < end; ++c) {
-    const int32_t v = counts[c];
-    counts[c] = run;
-    run += v;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    int4 o;
+    o.x = run; run += v[k].x;
+    o.y = run; run += v[k].y;
+    o.z = run; run += v[k].z;
+    o.w = run; run += v[k].w;
+    p[k] = o;
   }
 }
 
@@ -495,13 +530,12 @@ int launch_validate(int64_t N, int K, const int32_t* idx, const uint8_t* mask, i
 
 int launch_schedule(int64_t N, const float* pos, const SchedScratch& sc, hipStream_t s) {
   (void)hipGetLastError();
-  const int64_t ncell = (int64_t)1 << (3 * sc.bits);
   const dim3 grid_n((unsigned)((N + 255) / 256));
   hipLaunchKernelGGL(k_sched_bbox, dim3(kBboxBlocks), dim3(256), 0, s, N, pos, sc.partial,
-                     sc.counts, ncell);
+                     sc.counts, (int64_t)kSchedCells);
   hipLaunchKernelGGL(k_sched_count, grid_n, dim3(256), 0, s, N, pos, sc.partial, sc.bits, sc.cell,
                      sc.counts);
-  hipLaunchKernelGGL(k_sched_scan, dim3(1), dim3(1024), 0, s, ncell, sc.counts);
+  hipLaunchKernelGGL(k_sched_scan, dim3(1), dim3(1024), 0, s, sc.counts);
   hipLaunchKernelGGL(k_sched_scatter, grid_n, dim3(256), 0, s, N, sc.cell, sc.counts, sc.sched);
   return last_error();
 }

@@ -73,10 +73,7 @@ def _r256(b):
 
 def _expected_ws(N, lmax, C, esize):
     """Documented layout: rows | 256 B flag | order + cells (4N each) | cell counts | bbox partials."""
-    bits = 1
-    while bits < 6 and 8 ** bits < N:
-        bits += 1
-    sched = 2 * _r256(4 * N) + _r256(4 * 8 ** bits) + _r256(256 * 6 * 4)
+    sched = 2 * _r256(4 * N) + _r256(4 * 2 ** 15) + _r256(256 * 6 * 4)
     return _r256(N * ((lmax + 1) ** 2 + 1) * C * esize) + 256 + sched
 
 
