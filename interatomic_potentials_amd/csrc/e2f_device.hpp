@@ -270,6 +270,37 @@ struct Raw<uint16_t, V> {
   }
 };
 
+// Raw loads through a buffer resource: the row offset goes in an SGPR, so a
+// neighbour's S + 1 rows cost one address computation (32-bit byte offsets).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+template <typename T, int V>
+__device__ inline void buffer_load_raw(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                       Raw<T, V>& r) {
+  constexpr int bytes = V * (int)sizeof(T);
+  uint32_t* w;
+  if constexpr (sizeof(T) == 4) {
+    w = reinterpret_cast<uint32_t*>(r.f);
+  } else {
+    w = r.w;
+  }
+  if constexpr (bytes == 16) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, (int)soff, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else if constexpr (bytes == 8) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)voff, (int)soff, 0);
+    w[0] = v[0]; w[1] = v[1];
+  } else if constexpr (bytes == 4) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)voff, (int)soff, 0);
+  } else {
+    static_assert(bytes == 2, "row chunk size");
+    w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)voff, (int)soff, 0);
+  }
+}
+
 template <typename T, int V>
 struct VecIO;
 

@@ -35,7 +35,24 @@ __device__ inline float dpp(float x) {
 }
 
 // Sum over the `hl` adjacent lanes of one head (hl a power of two, heads
-// aligned to hl).  Uniform branches; DPP within a 16-lane row.
+// aligned to hl).  HL > 0 fixes the width at compile time; HL = 0 takes it
+// from `hl` with uniform branches.  DPP within a 16-lane row.
+__device__ inline float head_sum(float x, int hl);
+
+template <int HL>
+__device__ inline float head_sum_t(float x, int hl) {
+  if constexpr (HL == 0) {
+    return head_sum(x, hl);
+  } else {
+    if constexpr (HL >= 2) x += dpp<0xB1>(x);
+    if constexpr (HL >= 4) x += dpp<0x4E>(x);
+    if constexpr (HL >= 8) x += dpp<0x141>(x);
+    if constexpr (HL >= 16) x += dpp<0x140>(x);
+    static_assert(HL <= 16, "wider heads take the runtime path");
+    return x;
+  }
+}
+
 __device__ inline float head_sum(float x, int hl) {
   if (hl >= 2) x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
   if (hl >= 4) x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
@@ -92,7 +109,7 @@ __global__ __launch_bounds__(256) void k_eaas(EaasArgs a, EaasCoef cf) {
 
 // ------------------------------------------------------------------ K2
 
-template <int LMAX, int V, typename T, int U>
+template <int LMAX, int V, typename T, int U, int HL, bool BUF>
 __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
   constexpr int S = ncomp(LMAX);
   __shared__ int s_nb[kWavesPerBlock][kTile];
@@ -112,11 +129,17 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
   const int sub = lane >> lg;
   const int c0 = (lane & ((1 << lg) - 1)) * V;
   const bool act = c0 < a.C;
+  const int c0_load = act ? c0 : 0;  // idle lanes read a valid column and never store
   const int C = a.C;
   const int K = a.K;
   const int64_t N = a.N;
   const int64_t row = (int64_t)(S + 1) * C;  // elements per atom in the workspace
   const T* ws = static_cast<const T*>(a.ws);
+  // buffer path: the host only selects it when N * row bytes fits 32 bits
+  const uint32_t row_bytes = (uint32_t)(row * (int64_t)sizeof(T));
+  const uint32_t cbytes = (uint32_t)C * (uint32_t)sizeof(T);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      make_rsrc(a.ws, BUF ? (uint32_t)(N * row * (int64_t)sizeof(T)) : 0u);
 
   float q[V];
   if (act) {
@@ -176,19 +199,24 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
     }
 
     for (int n0 = 0; n0 < cnt; n0 += P * U) {
+      // Past the end of the list a subgroup re-reads the tile's last valid
+      // neighbour (finite, already part of this target's sum) with weight 0,
+      // so every load is unconditional and nothing needs clearing.
       Raw<T, V> kv[U][S + 1];
       bool val[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int n = n0 + u * P + sub;
         val[u] = n < cnt;
-        if (val[u] && act) {
-          const T* src = ws + (int64_t)nb[n] * row + c0;
+        const int jn = nb[val[u] ? n : cnt - 1];
+        if constexpr (BUF) {
+          const uint32_t voff = (uint32_t)jn * row_bytes + (uint32_t)c0_load * (uint32_t)sizeof(T);
+#pragma unroll
+          for (int r = 0; r <= S; ++r) buffer_load_raw<T, V>(rsrc, voff, (uint32_t)r * cbytes, kv[u][r]);
+        } else {
+          const T* src = ws + (int64_t)jn * row + c0_load;
 #pragma unroll
           for (int r = 0; r <= S; ++r) VecIO<T, V>::load_raw(src + r * C, kv[u][r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r <= S; ++r) kv[u][r].zero();
         }
       }
       float s[U];
@@ -198,29 +226,35 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
         float dt = 0.0f;
 #pragma unroll
         for (int v = 0; v < V; ++v) dt = fmaf(q[v], kv[u][0].get(v), dt);
-        dt = head_sum(dt, a.head_lanes);
+        dt = head_sum_t<HL>(dt, a.head_lanes);
         s[u] = val[u] ? dt * a.scale_log2e : -INFINITY;
         mx = fmaxf(mx, s[u]);
       }
-      const float corr = exp2_fast(mu - mx);
+      // rescale only when some lane's running max moved (rare after the first blocks)
+      if (__any(mx > mu)) {
+        const float corr = exp2_fast(mu - mx);
+        z *= corr;
+#pragma unroll
+        for (int r = 0; r < S; ++r)
+#pragma unroll
+          for (int v = 0; v < V; ++v) acc[r][v] *= corr;
+        mu = mx;
+      }
       float p[U];
-      float ps = 0.0f;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        p[u] = exp2_fast(s[u] - mx);
-        ps += p[u];
+        p[u] = exp2_fast(s[u] - mu);
+        z += p[u];
       }
-      z = fmaf(z, corr, ps);
 #pragma unroll
       for (int r = 0; r < S; ++r)
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-          float t = acc[r][v] * corr;
+          float t = acc[r][v];
 #pragma unroll
           for (int u = 0; u < U; ++u) t = fmaf(p[u], kv[u][r + 1].get(v), t);
           acc[r][v] = t;
         }
-      mu = mx;
     }
     wave_sync();  // every read of s_nb is done before the next tile rewrites it
   }
@@ -468,12 +502,24 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
   constexpr int U = 4;  // neighbours per subgroup in flight per iteration
   const int64_t blocks = (a.N + kWavesPerBlock - 1) / kWavesPerBlock;
   const dim3 grid((unsigned)((blocks + kXcds - 1) / kXcds * kXcds));
+  const dim3 blk(256);
+  // 4 channels per lane with 1, 2 or 4 lanes per head and a workspace under
+  // 4 GiB take the specialised buffer-load kernels; anything else the general one
+  const bool buf = (int64_t)a.N * (ncomp(L) + 1) * a.C * (int64_t)sizeof(T) < ((int64_t)1 << 32);
   (void)hipGetLastError();
-  switch (V) {
-    case 1: hipLaunchKernelGGL((k_aggregate<L, 1, T, U>), grid, dim3(256), 0, s, a, cf); break;
-    case 2: hipLaunchKernelGGL((k_aggregate<L, 2, T, U>), grid, dim3(256), 0, s, a, cf); break;
-    case 4: hipLaunchKernelGGL((k_aggregate<L, 4, T, U>), grid, dim3(256), 0, s, a, cf); break;
-    default: return static_cast<int>(hipErrorInvalidValue);
+  if (V == 4 && buf && a.head_lanes == 2) {
+    hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 2, true>), grid, blk, 0, s, a, cf);
+  } else if (V == 4 && buf && a.head_lanes == 1) {
+    hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 1, true>), grid, blk, 0, s, a, cf);
+  } else if (V == 4 && buf && a.head_lanes == 4) {
+    hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 4, true>), grid, blk, 0, s, a, cf);
+  } else {
+    switch (V) {
+      case 1: hipLaunchKernelGGL((k_aggregate<L, 1, T, U, 0, false>), grid, blk, 0, s, a, cf); break;
+      case 2: hipLaunchKernelGGL((k_aggregate<L, 2, T, U, 0, false>), grid, blk, 0, s, a, cf); break;
+      case 4: hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 0, false>), grid, blk, 0, s, a, cf); break;
+      default: return static_cast<int>(hipErrorInvalidValue);
+    }
   }
   return last_error();
 }
