@@ -35,7 +35,17 @@ WORKLOADS = {
                 "C=128, H=16, bf16 storage / fp32 arithmetic",
     "water": "216 rigid H2O (648 atoms), r_c 5.0 A, K=64, lmax=2, C=128, H=16, fp32",
     "tiny": "N=64 uniform atoms, r_c 5.0 A, K=32, lmax=1, C=16, H=2, fp32",
+    "eaas": "EAAS tensor product alone: 2^20 unit vectors (uniform on S^2), h [2^20, 9, 128], "
+            "all 15 paths of lmax=2, fp32",
 }
+
+# Per-CU vector-memory path of gfx950: one 64-lane 16-byte-per-lane load per
+# 16 cycles through the texture addresser / data return units, i.e. 64 B/clk
+# per CU; 256 CUs at 2.4 GHz.  The aggregate kernel's counters show these
+# units >90% busy, so this is the ceiling it runs against once the gathered
+# rows hit in L2.
+VMEM_PATH_PEAK_GBS = 64 * 256 * 2.4
+
 
 
 def algorithmic_bytes(N, K, E, S, C, b):
@@ -118,7 +128,8 @@ def summarize_profile(pmc_dir, workload, out_path):
     stats = list(csv.DictReader(open(os.path.join(pmc_dir, f"trace_{w}", "run_kernel_stats.csv"))))
     fetch, nf = _counter_means(os.path.join(pmc_dir, f"fetch_{w}", "run_counter_collection.csv"))
     write, _ = _counter_means(os.path.join(pmc_dir, f"write_{w}", "run_counter_collection.csv"))
-    hit, _ = _counter_means(os.path.join(pmc_dir, f"hit_{w}", "run_counter_collection.csv"))
+    hit_path = os.path.join(pmc_dir, f"hit_{w}", "run_counter_collection.csv")
+    hit = _counter_means(hit_path)[0] if os.path.exists(hit_path) else {}
     cf, _ = _counter_means(os.path.join(pmc_dir, "fetch_copy", "run_counter_collection.csv"))
     cw, _ = _counter_means(os.path.join(pmc_dir, "write_copy", "run_counter_collection.csv"))
     copy_bytes = CALIB_COPY_MIB << 20
@@ -182,6 +193,47 @@ def committed_traffic(workload, kernel="e2f::k_aggregate"):
     return float(m.group(1)) if m else None
 
 
+def bench_eaas(args, e2f, dev):
+    """The EAAS tensor product on its own (e2f_eaas_couple over 2^20 vectors)."""
+    import numpy as np
+    import torch
+
+    from gen import make_micro
+
+    r_np, h_np, _ = make_micro()
+    B, S, C = h_np.shape
+    r = torch.from_numpy(r_np).to(dev)
+    h = torch.from_numpy(h_np).to(dev)
+    out = torch.empty_like(h)
+    del h_np
+    for _ in range(args.warmup):
+        e2f.eaas_couple(r, h, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record(stream)
+        e2f.eaas_couple(r, h, out=out)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    per_vec = 2 * S * C * 4 + 12
+    gbs = B * per_vec / (ms * 1e-3) / 1e9
+    print(f"[bench] eaas: {B} vectors, {ms:.3f} ms, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    result = {
+        "metric": "EAAS tensor-product vectors/s (lmax=2, C=128, all 15 paths)",
+        "value": B / (ms * 1e-3), "unit": "vectors/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded generator)",
+        "config": {"workload": WORKLOADS["eaas"], "vectors": B, "lmax": 2, "channels": C},
+        "roofline": {"kernel": "k_eaas", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": B * per_vec, "bytes_per_vector": per_vec},
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,8 +251,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.summarize_profile:
+        kernel = "k_eaas" if args.workload == "eaas" else "k_aggregate"
         summarize_profile(args.summarize_profile, args.workload,
-                          os.path.join(ROOT, "profiles", f"k_aggregate_{args.workload}.md"))
+                          os.path.join(ROOT, "profiles", f"{kernel}_{args.workload}.md"))
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -225,6 +278,9 @@ def main(argv=None):
 
     import interatomic_potentials_amd as e2f
     from gen import make_config
+
+    if args.workload == "eaas":
+        return bench_eaas(args, e2f, dev)
 
     t_gen = time.perf_counter()
     cfg = make_config(args.workload)
@@ -327,6 +383,8 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": k2_bytes,
             "bytes_per_edge": per_edge,
             "bytes_per_target": per_target,
+            "vmem_path_peak": VMEM_PATH_PEAK_GBS,
+            "vmem_path_frac": k2_gbs / VMEM_PATH_PEAK_GBS,
         },
     }
     if not args.no_cpu_baseline:

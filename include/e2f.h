@@ -49,8 +49,9 @@
  * - n = 0 (or N = 0) is a successful no-op.
  * - Supported sizes: lmax in {0, 1, 2}; C >= 1, H >= 1, C % H == 0.  The
  *   attention kernels also need a per-lane channel count V in {1, 2, 4}
- *   with V | d, d / V a power of two and C / V <= 64 (so C <= 256 when d is
- *   a multiple of 4); otherwise E2F_ERR_UNSUPPORTED.
+ *   (fp32) or {1, 2, 4, 8} (bf16) with V | d, d / V a power of two and
+ *   C / V <= 64 (so C <= 256 at fp32 when d is a multiple of 4, C <= 512 at
+ *   bf16 when d is a multiple of 8); otherwise E2F_ERR_UNSUPPORTED.
  */
 #ifndef E2F_H_
 #define E2F_H_

@@ -117,12 +117,12 @@ int eaas_width(int C, int dt) {
 
 // per-lane vector width for the attention stream: V | d, d / V a power of
 // two (heads aligned to lanes), C / V <= 64 (one row per wave at most).
-// At most 4 channels per lane: with 8 the registers holding two neighbours'
-// rows in flight plus 9 x 8 accumulators exceed the register file.
+// 16-byte loads where possible: 4 fp32 channels or 8 bf16 channels per lane.
+// bf16 with 8 channels keeps loaded rows packed (one 32-bit register per two
+// channels), so one neighbour per subgroup in flight fits the registers.
 int attn_width(int C, int H, int dt) {
   const int d = C / H;
-  const int vmax = 4;
-  (void)dt;
+  const int vmax = dt == E2F_BF16 ? 8 : 4;
   for (int v = vmax; v >= 1; v >>= 1)
     if (d % v == 0 && is_pow2(d / v) && C / v <= 64) return v;
   return 0;

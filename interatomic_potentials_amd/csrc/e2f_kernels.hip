@@ -507,6 +507,21 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
   // 4 GiB take the specialised buffer-load kernels; anything else the general one
   const bool buf = (int64_t)a.N * (ncomp(L) + 1) * a.C * (int64_t)sizeof(T) < ((int64_t)1 << 32);
   (void)hipGetLastError();
+  if constexpr (sizeof(T) == 2) {
+    // bf16, 8 channels per lane: one neighbour per subgroup per iteration
+    if (V == 8 && buf && a.head_lanes == 1) {
+      hipLaunchKernelGGL((k_aggregate<L, 8, T, 1, 1, true>), grid, blk, 0, s, a, cf);
+      return last_error();
+    }
+    if (V == 8 && buf && a.head_lanes == 2) {
+      hipLaunchKernelGGL((k_aggregate<L, 8, T, 1, 2, true>), grid, blk, 0, s, a, cf);
+      return last_error();
+    }
+    if (V == 8) {
+      hipLaunchKernelGGL((k_aggregate<L, 8, T, 1, 0, false>), grid, blk, 0, s, a, cf);
+      return last_error();
+    }
+  }
   if (V == 4 && buf && a.head_lanes == 2) {
     hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 2, true>), grid, blk, 0, s, a, cf);
   } else if (V == 4 && buf && a.head_lanes == 1) {

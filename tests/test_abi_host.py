@@ -135,7 +135,8 @@ def test_attention_argument_errors(fn):
     assert fn(H=0) == C["E2F_ERR_SHAPE"]
     assert fn(C=128, H=3) == C["E2F_ERR_SHAPE"]
     assert fn(C=12, H=4) == C["E2F_ERR_UNSUPPORTED"]    # d = 3: heads cannot align to lanes
-    assert fn(C=512, H=4) == C["E2F_ERR_UNSUPPORTED"]   # 128 lanes per row
+    assert fn(C=512, H=4) == C["E2F_ERR_UNSUPPORTED"]   # fp32: 128 lanes per row
+    assert fn(C=1024, H=8, dt=1) == C["E2F_ERR_UNSUPPORTED"]   # bf16: 128 lanes per row
     assert fn(flags=4) == C["E2F_ERR_SHAPE"]                  # unknown flag bit
     assert fn(N=0, pos=None, idx=None, mask=None, ws=None, out=None) == C["E2F_OK"]
     assert fn(pos=None) == C["E2F_ERR_NULL"]

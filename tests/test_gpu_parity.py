@@ -338,3 +338,24 @@ def test_schedule_covers_every_target_bit_exact(e2f, dev, name):
     e2f.attn_forward(pos, h, idx, mask, s.H, out=b, targets_in_order=True)
     assert torch.isfinite(a).all() and torch.isfinite(b).all()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("lmax,C,H,K", [(2, 128, 16, 64), (2, 128, 8, 40), (1, 64, 16, 30),
+                                        (2, 24, 8, 20), (2, 512, 64, 16), (0, 16, 2, 300)])
+def test_attention_bf16_shapes_vs_oracle(e2f, dev, lmax, C, H, K):
+    """bf16 storage over every lane mapping: 8, 4 and 1 channels per lane, 1 or 2 lanes per head."""
+    say(f"attention bf16 shapes: lmax={lmax} C={C} H={H} K={K}")
+    rng = np.random.default_rng(7000 + lmax * 100 + C + K)
+    N = 120
+    S = (lmax + 1) ** 2
+    pos = (rng.standard_normal((N, 3)) * 4).astype(np.float32)
+    h = bf16_bits_to_f32(f32_to_bf16_bits(rng.standard_normal((N, S, C)).astype(np.float32)))
+    idx = rng.integers(0, N, size=(N, K)).astype(np.int32)
+    mask = (rng.random((N, K)) < 0.6).astype(np.uint8)
+    mask[3] = 0
+    out, msg = e2f.attn_forward(T(pos, dev), T(h, dev, torch.bfloat16), T(idx, dev), T(mask, dev),
+                                H, return_msg=True)
+    ref, ref_msg = oracle_attn(pos, h, idx, mask, H, lmax, return_msg=True)
+    assert block_rel_err(to_host(msg), ref_msg, lmax) <= TOL_BF16
+    assert block_rel_err(to_host(out), ref, lmax) <= TOL_BF16
+    assert (out[3].float() == 0).all()
