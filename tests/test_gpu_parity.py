@@ -341,7 +341,7 @@ def test_schedule_covers_every_target_bit_exact(e2f, dev, name):
 
 
 @pytest.mark.parametrize("lmax,C,H,K", [(2, 128, 16, 64), (2, 128, 8, 40), (1, 64, 16, 30),
-                                        (2, 24, 8, 20), (2, 512, 64, 16), (0, 16, 2, 300)])
+                                        (2, 8, 8, 20), (2, 512, 64, 16), (0, 16, 2, 300)])
 def test_attention_bf16_shapes_vs_oracle(e2f, dev, lmax, C, H, K):
     """bf16 storage over every lane mapping: 8, 4 and 1 channels per lane, 1 or 2 lanes per head."""
     say(f"attention bf16 shapes: lmax={lmax} C={C} H={H} K={K}")
@@ -359,3 +359,13 @@ def test_attention_bf16_shapes_vs_oracle(e2f, dev, lmax, C, H, K):
     assert block_rel_err(to_host(msg), ref_msg, lmax) <= TOL_BF16
     assert block_rel_err(to_host(out), ref, lmax) <= TOL_BF16
     assert (out[3].float() == 0).all()
+
+
+def test_unsupported_head_layout_is_reported(e2f, dev):
+    """d = 3 channels per head cannot align heads to lanes: a clear error, nothing launched."""
+    h = torch.zeros((4, 9, 24), device=dev)
+    with pytest.raises(e2f.E2FError) as ei:
+        e2f.attn_forward(torch.zeros((4, 3), device=dev), h,
+                         torch.zeros((4, 2), dtype=torch.int32, device=dev),
+                         torch.zeros((4, 2), dtype=torch.uint8, device=dev), 8)
+    assert ei.value.name == "E2F_ERR_UNSUPPORTED"
