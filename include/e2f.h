@@ -157,18 +157,59 @@ int e2f_attn_precouple(hipStream_t stream, int64_t N, int lmax, int C, int dtype
  *             visiting order never changes any target's result.
  *   out       [N, S, C] T    out_i; exactly 0 for a target with no valid slot
  *   out_msg   [N, S, C] T or NULL: also store the normalised message m_i
+ *   lse       [N, H] fp32 or NULL: also store each head's natural log-sum-exp
+ *             of the logits over the valid slots (-inf with no valid slot);
+ *             with out_msg, this is what e2f_attn_backward needs
  *   flags     0 or E2F_VALIDATE_INDICES | E2F_TARGETS_IN_ORDER
  */
 int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                        const float* pos, const int32_t* nbr_idx, const uint8_t* nbr_mask,
                        float scale, const float* path_w, void* workspace, size_t ws_bytes,
-                       void* out, void* out_msg, uint32_t flags);
+                       void* out, void* out_msg, float* lse, uint32_t flags);
 
 /* e2f_attn_forward -- e2f_attn_precouple then e2f_attn_aggregate on one stream. */
 int e2f_attn_forward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                      const float* pos, const void* h, const int32_t* nbr_idx,
                      const uint8_t* nbr_mask, float scale, const float* path_w,
-                     void* workspace, size_t ws_bytes, void* out, void* out_msg, uint32_t flags);
+                     void* workspace, size_t ws_bytes, void* out, void* out_msg, float* lse,
+                     uint32_t flags);
+
+/*
+ * Backward pass (vector-Jacobian product) of the attention, for forces as
+ * derivatives of an energy with respect to positions (the write-up's
+ * "Conservative" variant, section 4.2): given G = dL/d out it returns
+ * dL/dh and dL/dpos.  Softmax weights are recomputed from the forward's
+ * log-sum-exp (no per-edge tensor is stored); feature gradients use the
+ * adjoint EAAS map and position gradients its derivative with respect to
+ * r (radial part and rotation generators in the aligned frame).
+ *
+ * e2f_attn_backward_workspace_bytes -- scratch bytes for N atoms and K slots:
+ * (S + 1) C + C + H floats per atom, the reverse neighbour list (8 N + 4 N K
+ * bytes) and the target schedule scratch.  0 on bad arguments.
+ */
+size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int H, int dtype);
+
+/*
+ * e2f_attn_backward -- fp32 storage only (E2F_ERR_UNSUPPORTED for bf16, for
+ * N above 2^24 or N K at or above 2^31).
+ *   pos, h, nbr_idx, nbr_mask, scale, path_w: as given to the forward
+ *   workspace   the forward's workspace after e2f_attn_precouple (read only)
+ *   msg, lse    the forward's out_msg and lse outputs
+ *   grad_out    [N, S, C] fp32  dL/d out
+ *   grad_h      [N, S, C] fp32  dL/dh (written)
+ *   grad_pos    [N, 3] fp32     dL/dpos (written)
+ *   bwd_workspace, bwd_ws_bytes  scratch of e2f_attn_backward_workspace_bytes
+ *   flags       0 or E2F_TARGETS_IN_ORDER
+ * The result does not depend on the order of a target's slots, nor on the
+ * order in which the reverse list is filled for sources listed by at most
+ * 1024 targets (each source's list is sorted before it is summed).
+ */
+int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
+                      const float* pos, const void* h, const int32_t* nbr_idx,
+                      const uint8_t* nbr_mask, float scale, const float* path_w,
+                      const void* workspace, size_t ws_bytes, const void* msg, const float* lse,
+                      const void* grad_out, void* grad_h, float* grad_pos,
+                      void* bwd_workspace, size_t bwd_ws_bytes, uint32_t flags);
 
 /*
  * e2f_frames -- test hook: the alignment rotation Q (Q r_hat = z_hat, write-up

@@ -18,7 +18,8 @@ from typing import Optional
 
 __all__ = [
     "E2FError", "lib", "status_string", "path_count", "eaas_couple", "attn_workspace_bytes",
-    "attn_precouple", "attn_aggregate", "attn_forward", "frames", "F32", "BF16",
+    "attn_precouple", "attn_aggregate", "attn_forward", "attn_backward",
+    "attn_backward_workspace_bytes", "frames", "F32", "BF16",
     "VALIDATE_INDICES", "TARGETS_IN_ORDER",
 ]
 
@@ -49,9 +50,12 @@ SIGNATURES = {
     "e2f_attn_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
     "e2f_attn_precouple": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz]),
     "e2f_attn_aggregate": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _f32,
-                                  _vp, _vp, _sz, _vp, _vp, _u32]),
+                                  _vp, _vp, _sz, _vp, _vp, _vp, _u32]),
     "e2f_attn_forward": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
-                                _f32, _vp, _vp, _sz, _vp, _vp, _u32]),
+                                _f32, _vp, _vp, _sz, _vp, _vp, _vp, _u32]),
+    "e2f_attn_backward_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32]),
+    "e2f_attn_backward": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                 _f32, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _u32]),
     "e2f_frames": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp]),
 }
 
@@ -217,11 +221,16 @@ def attn_precouple(pos, h, ws=None, path_w=None):
     return ws
 
 
+def _results(out, msg, lse):
+    extra = tuple(t for t in (msg, lse) if t is not None)
+    return (out,) + extra if extra else out
+
+
 def attn_aggregate(pos, nbr_idx, nbr_mask, ws, heads: int, lmax: int, C: int, dtype,
                    scale: Optional[float] = None, path_w=None, out=None,
                    return_msg: bool = False, validate: bool = False,
-                   targets_in_order: bool = False):
-    """Steps 2-3 from a filled workspace; returns out (and m if return_msg)."""
+                   targets_in_order: bool = False, return_lse: bool = False):
+    """Steps 2-3 from a filled workspace; returns out, or (out[, m][, lse]) when asked."""
     torch = _torch()
     _dev(pos, "pos", torch.float32)
     _dev(nbr_idx, "nbr_idx", torch.int32)
@@ -233,18 +242,24 @@ def attn_aggregate(pos, nbr_idx, nbr_mask, ws, heads: int, lmax: int, C: int, dt
         out = torch.empty((N, S, C), dtype=dtype, device=ws.device)
     _dev(out, "out", dtype)
     msg = torch.empty_like(out) if return_msg else None
+    lse = torch.empty((N, heads), dtype=torch.float32, device=ws.device) if return_lse else None
     pw = _path_w(path_w, ws.device)
     _check(lib.e2f_attn_aggregate(_stream(ws), N, K, lmax, C, heads, _dtype_code(out), _ptr(pos),
                                   _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0), _ptr(pw),
                                   _ptr(ws), ws.numel() * ws.element_size(), _ptr(out), _ptr(msg),
-                                  _flags(validate, targets_in_order)), "e2f_attn_aggregate")
-    return (out, msg) if return_msg else out
+                                  _ptr(lse), _flags(validate, targets_in_order)),
+           "e2f_attn_aggregate")
+    return _results(out, msg, lse)
 
 
 def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] = None,
                  path_w=None, ws=None, out=None, return_msg: bool = False,
-                 validate: bool = False, targets_in_order: bool = False):
-    """Full path (steps 1-3): pos [N,3] fp32, h [N,S,C], nbr_idx [N,K] int32, nbr_mask [N,K] uint8."""
+                 validate: bool = False, targets_in_order: bool = False,
+                 return_lse: bool = False):
+    """Full path (steps 1-3): pos [N,3] fp32, h [N,S,C], nbr_idx [N,K] int32, nbr_mask [N,K] uint8.
+
+    Returns out, or (out[, m][, lse]) when return_msg / return_lse ask for them.
+    """
     torch = _torch()
     _dev(pos, "pos", torch.float32)
     _dev(h, "h")
@@ -261,12 +276,52 @@ def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] =
         out = torch.empty_like(h)
     _dev(out, "out", h.dtype)
     msg = torch.empty_like(h) if return_msg else None
+    lse = torch.empty((N, heads), dtype=torch.float32, device=h.device) if return_lse else None
     pw = _path_w(path_w, h.device)
     _check(lib.e2f_attn_forward(_stream(h), N, K, lmax, C, heads, dt, _ptr(pos), _ptr(h),
                                 _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0), _ptr(pw),
                                 _ptr(ws), ws.numel() * ws.element_size(), _ptr(out), _ptr(msg),
-                                _flags(validate, targets_in_order)), "e2f_attn_forward")
-    return (out, msg) if return_msg else out
+                                _ptr(lse), _flags(validate, targets_in_order)), "e2f_attn_forward")
+    return _results(out, msg, lse)
+
+
+def attn_backward_workspace_bytes(N: int, K: int, lmax: int, C: int, H: int,
+                                  dtype: int = F32) -> int:
+    return int(lib.e2f_attn_backward_workspace_bytes(N, K, lmax, C, H, dtype))
+
+
+def attn_backward(pos, h, nbr_idx, nbr_mask, heads: int, ws, msg, lse, grad_out,
+                  scale: Optional[float] = None, path_w=None, targets_in_order: bool = False,
+                  bwd_ws=None, grad_h=None, grad_pos=None):
+    """(dL/dh, dL/dpos) for L = <grad_out, out>; ws, msg, lse from the forward (fp32 only)."""
+    torch = _torch()
+    _dev(pos, "pos", torch.float32)
+    _dev(h, "h", torch.float32)
+    _dev(nbr_idx, "nbr_idx", torch.int32)
+    _dev(nbr_mask, "nbr_mask", torch.uint8)
+    _dev(ws, "ws")
+    _dev(msg, "msg", torch.float32)
+    _dev(lse, "lse", torch.float32)
+    _dev(grad_out, "grad_out", torch.float32)
+    N, S, C = h.shape
+    K = nbr_idx.shape[1]
+    lmax = _lmax_of(S)
+    if bwd_ws is None:
+        nbytes = attn_backward_workspace_bytes(N, K, lmax, C, heads, F32)
+        bwd_ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=h.device)
+    _dev(bwd_ws, "bwd_ws")
+    grad_h = torch.empty_like(h) if grad_h is None else _dev(grad_h, "grad_h", torch.float32)
+    grad_pos = (torch.empty_like(pos) if grad_pos is None
+                else _dev(grad_pos, "grad_pos", torch.float32))
+    pw = _path_w(path_w, h.device)
+    _check(lib.e2f_attn_backward(_stream(h), N, K, lmax, C, heads, F32, _ptr(pos), _ptr(h),
+                                 _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0), _ptr(pw),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _ptr(msg), _ptr(lse),
+                                 _ptr(grad_out), _ptr(grad_h), _ptr(grad_pos), _ptr(bwd_ws),
+                                 bwd_ws.numel() * bwd_ws.element_size(),
+                                 TARGETS_IN_ORDER if targets_in_order else 0),
+           "e2f_attn_backward")
+    return grad_h, grad_pos
 
 
 def frames(r, lmax: int = 2):

@@ -25,7 +25,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libe2f.so")
 ARCH = os.environ.get("E2F_OFFLOAD_ARCH", "gfx950")
 
-HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = shutil.which("hipcc") or f"{ROCM}/bin/hipcc"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -33,6 +34,7 @@ DEVICE = ["-x", "hip", f"--offload-arch={ARCH}",
 
 SOURCES = [
     ("e2f_kernels.hip", True),
+    ("e2f_backward.hip", True),
     ("e2f_host.cpp", False),
 ]
 
@@ -54,7 +56,9 @@ def build(verbose: bool = False) -> str:
     for name, is_hip in SOURCES:
         src = os.path.join(CSRC, name)
         obj = os.path.join(BUILD, name + ".o")
-        cmd = [HIPCC] + COMMON + (DEVICE if is_hip else []) + ["-c", src, "-o", obj]
+        host = ["-x", "c++", "-D__HIP_PLATFORM_AMD__",  # plain C++ against the HIP runtime API
+                f"-I{ROCM}/include"]
+        cmd = [HIPCC] + COMMON + (DEVICE if is_hip else host) + ["-c", src, "-o", obj]
         jobs.append((cmd, obj))
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
         list(ex.map(lambda j: _run(j[0], verbose), jobs))

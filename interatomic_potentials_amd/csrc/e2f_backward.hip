@@ -1,0 +1,537 @@
+// e2f_backward.hip -- vector-Jacobian product of the on-the-fly attention (fp32).
+//
+// For L = <G, out> with out_i = T(r_i) m_i, m_i = sum_j a_ij h'_j and
+// h'_j = T(r_j) h_j (T(r) = the EAAS coupling with R(r)), the gradients are
+//   dm_i   = T(r_i)^T G_i                                   (adjoint EAAS)
+//   D_ih   = <dm_i, m_i>_h                                  (per head)
+//   ds_ijh = a_ijh (<dm_i, h'_j>_h - D_ih)                  (softmax backward)
+//   dq_i   = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i
+//   dh'_j  = sum_i a_ij dm_i
+//   dh_j   = T(r_j)^T dh'_j + e_(l=0) (dq_j + dk_j)
+//   dpos_i = grad_r <G_i, T(r) m_i> at r_i + grad_r <dh'_i, T(r) h_i> at r_i
+// with a_ij recomputed from the forward's saved log-sum-exp, as in the
+// recompute scheme of FlashAttention-2, so no per-edge tensor is stored.
+//
+// k_bwd_prep  per atom: dm, D, the step-3 part of dpos
+// k_bwd_q     per target, streaming its sorted neighbours: dq
+// k_bwd_src   per source, streaming the targets that list it (reverse list,
+//             sorted): dh', dk, then dh and the step-1 part of dpos
+// The reverse list is a CSR built with a count, a scan and a fill; the
+// per-source sort makes the summation order independent of the fill order
+// for sources listed by up to kRevTile targets.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "e2f_device.hpp"
+#include "e2f_internal.hpp"
+
+namespace e2f {
+namespace {
+
+__device__ inline float exp2_b(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ inline float dpp_b(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+template <int HL>
+__device__ inline float head_sum_b(float x, int hl) {
+  if constexpr (HL > 0) {
+    if constexpr (HL >= 2) x += dpp_b<0xB1>(x);
+    if constexpr (HL >= 4) x += dpp_b<0x4E>(x);
+    if constexpr (HL >= 8) x += dpp_b<0x141>(x);
+    if constexpr (HL >= 16) x += dpp_b<0x140>(x);
+    return x;
+  } else {
+    if (hl >= 2) x += dpp_b<0xB1>(x);
+    if (hl >= 4) x += dpp_b<0x4E>(x);
+    if (hl >= 8) x += dpp_b<0x141>(x);
+    if (hl >= 16) x += dpp_b<0x140>(x);
+    if (hl >= 32) x += __shfl_xor(x, 16);
+    if (hl >= 64) x += __shfl_xor(x, 32);
+    return x;
+  }
+}
+
+__device__ inline void wave_sync_b() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int V>
+__device__ inline void ld(const float* p, float* o) {
+  VecIO<float, V>::load(p, o);
+}
+template <int V>
+__device__ inline void st(float* p, const float* o) {
+  VecIO<float, V>::store(p, o);
+}
+
+// bitonic sort of nb[0..cnt) ascending (one wave, LDS), padding to a power of two
+__device__ inline void sort_list(int* nb, int cnt, int lane) {
+  int n2 = 1;
+  while (n2 < cnt) n2 <<= 1;
+  for (int e = cnt + lane; e < n2; e += 64) nb[e] = 0x7fffffff;
+  wave_sync_b();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int e = lane; e < (n2 >> 1); e += 64) {
+        const int lo = ((e & ~(jj - 1)) << 1) | (e & (jj - 1));
+        const int x = nb[lo], y = nb[lo + jj];
+        if ((x > y) == ((lo & k) == 0)) {
+          nb[lo] = y;
+          nb[lo + jj] = x;
+        }
+      }
+      wave_sync_b();
+    }
+  }
+}
+
+// the target or source handled by this wave (Morton schedule, XCD-aware order)
+__device__ inline int64_t scheduled_atom(const int32_t* sched, int64_t N, int w) {
+  const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
+  const int64_t blk = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int64_t slot = blk * kWavesPerBlock + w;
+  if (slot >= N) return -1;
+  const int64_t i = sched ? (int64_t)sched[slot] : slot;
+  return (i >= 0 && i < N) ? i : -1;
+}
+
+// ---------------------------------------------------------------- prep
+
+template <int LMAX, int V, int HL>
+__global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a, EaasCoef cf) {
+  constexpr int S = ncomp(LMAX);
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int lg = a.lane_log;
+  const int G2 = 1 << lg;
+  const int sub = lane >> lg;
+  const int gl = lane & (G2 - 1);
+  const int64_t atom = ((int64_t)blockIdx.x * kWavesPerBlock + w) * (64 >> lg) + sub;
+  if (atom >= a.N) return;  // whole subgroup: the reductions below stay inside it
+  const int C = a.C;
+  const int c0 = gl * V;
+  const bool act = c0 < C;
+  const int cl = act ? c0 : 0;
+  const Frame f = make_frame(a.pos[3 * atom], a.pos[3 * atom + 1], a.pos[3 * atom + 2]);
+  const Dy2 d = make_dy2(f);
+  const Reindex<LMAX> R = make_reindex<LMAX>(cf, f);
+  Reindex<LMAX> Rrad, Rhat;
+  make_grad_reindex<LMAX>(cf, f, Rrad, Rhat);
+
+  const int64_t base = atom * (int64_t)S * C;
+  float g[S][V], m[S][V], dm[S][V], q[V];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    ld<V>(a.gout + base + s * C + cl, g[s]);
+    ld<V>(a.msg + base + s * C + cl, m[s]);
+  }
+  ld<V>(a.h + base + cl, q);
+  float Dp = 0.0f;
+  float acc[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float gv[S], mv[S], out[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      gv[s] = g[s][v];
+      mv[s] = m[s][v];
+    }
+    eaas_channel_t<LMAX>(gv, out, f, d, R);  // gv is rotated in place
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      dm[s][v] = out[s];
+      Dp = fmaf(out[s], mv[s], Dp);
+    }
+    // position gradient of <G, T(r) m>: both in the aligned frame (gv already is)
+    rotate_in<LMAX>(mv, f, d);
+    pos_grad_channel<LMAX>(mv, gv, Rrad, Rhat, acc);
+  }
+  if (!act) {
+    Dp = 0.0f;
+    acc[0] = acc[1] = acc[2] = 0.0f;
+  }
+  Dp = head_sum_b<HL>(Dp, a.head_lanes);
+  if (act && (gl & (a.head_lanes - 1)) == 0) a.dh[atom * a.heads + c0 / (C / a.heads)] = Dp;
+  for (int o = 1; o < G2; o <<= 1) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) acc[k] += __shfl_xor(acc[k], o);
+  }
+  if (gl == 0) {
+    float gp[3];
+    frame_to_global(f, acc, gp);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) a.grad_pos[3 * atom + k] = gp[k];
+  }
+  if (act) {
+    float* row = a.brows + atom * (int64_t)(S + 1) * C;
+    st<V>(row + c0, q);
+#pragma unroll
+    for (int s = 0; s < S; ++s) st<V>(row + (s + 1) * C + c0, dm[s]);
+  }
+}
+
+// -------------------------------------------------- target-centric dq
+
+template <int LMAX, int V, int U, int HL>
+__global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
+  constexpr int S = ncomp(LMAX);
+  __shared__ int s_nb[kWavesPerBlock][kTile];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t i = scheduled_atom(a.sched, a.N, w);
+  if (i < 0) return;
+  const int lg = a.lane_log;
+  const int P = 64 >> lg;
+  const int sub = lane >> lg;
+  const int c0 = (lane & ((1 << lg) - 1)) * V;
+  const bool act = c0 < a.C;
+  const int cl = act ? c0 : 0;
+  const int C = a.C, K = a.K;
+  const int64_t N = a.N;
+  const int64_t row = (int64_t)(S + 1) * C;
+  const int head = cl / (C / a.heads);
+
+  float q[V], dm[S][V];
+  ld<V>(a.brows + i * row + cl, q);
+#pragma unroll
+  for (int s = 0; s < S; ++s) ld<V>(a.brows + i * row + (s + 1) * C + cl, dm[s]);
+  const float L2 = a.lse[i * a.heads + head] * 1.4426950408889634f;
+  const float Dv = a.dh[i * a.heads + head];
+  float dq[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) dq[v] = 0.0f;
+
+  const int32_t* irow = a.idx + i * K;
+  const uint8_t* mrow = a.mask + i * K;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int* nb = s_nb[w];
+  for (int t0 = 0; t0 < K; t0 += kTile) {
+    int cnt = 0;
+    for (int u = 0; u < kTile && t0 + u < K; u += 64) {
+      const int slot = t0 + u + lane;
+      bool ok = false;
+      int j = 0;
+      if (slot < K && mrow[slot] != 0) {
+        j = irow[slot];
+        ok = j >= 0 && (int64_t)j < N;
+      }
+      const uint64_t b = __ballot(ok);
+      if (ok) nb[cnt + __popcll(b & below)] = j;
+      cnt += __popcll(b);
+    }
+    sort_list(nb, cnt, lane);
+    for (int n0 = 0; n0 < cnt; n0 += P * U) {
+      float kv[U][S + 1][V];
+      bool val[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int n = n0 + u * P + sub;
+        val[u] = n < cnt;
+        const float* src = a.ws + (int64_t)nb[val[u] ? n : cnt - 1] * row + cl;
+#pragma unroll
+        for (int r = 0; r <= S; ++r) ld<V>(src + r * C, kv[u][r]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float qk = 0.0f, dp = 0.0f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) qk = fmaf(q[v], kv[u][0][v], qk);
+#pragma unroll
+        for (int r = 0; r < S; ++r)
+#pragma unroll
+          for (int v = 0; v < V; ++v) dp = fmaf(dm[r][v], kv[u][r + 1][v], dp);
+        qk = head_sum_b<HL>(qk, a.head_lanes);
+        dp = head_sum_b<HL>(dp, a.head_lanes);
+        const float alpha = val[u] ? exp2_b(qk * a.scale_log2e - L2) : 0.0f;
+        const float ds = alpha * (dp - Dv) * a.scale;
+#pragma unroll
+        for (int v = 0; v < V; ++v) dq[v] = fmaf(ds, kv[u][0][v], dq[v]);
+      }
+    }
+    wave_sync_b();
+  }
+  for (int o = 1 << lg; o < 64; o <<= 1) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) dq[v] += __shfl_xor(dq[v], o);
+  }
+  if (sub == 0 && act) st<V>(a.dq + i * C + c0, dq);
+}
+
+// ------------------------------------------ source-centric dh', dk, dh, dpos
+
+template <int LMAX, int V, int U, int HL>
+__global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf) {
+  constexpr int S = ncomp(LMAX);
+  __shared__ int s_nb[kWavesPerBlock][kRevTile];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t j = scheduled_atom(a.sched, a.N, w);
+  if (j < 0) return;
+  const int lg = a.lane_log;
+  const int P = 64 >> lg;
+  const int sub = lane >> lg;
+  const int gl = lane & ((1 << lg) - 1);
+  const int c0 = gl * V;
+  const bool act = c0 < a.C;
+  const int cl = act ? c0 : 0;
+  const int C = a.C;
+  const int64_t row = (int64_t)(S + 1) * C;
+  const int head = cl / (C / a.heads);
+
+  float k[V], hp[S][V];
+  ld<V>(a.ws + j * row + cl, k);
+#pragma unroll
+  for (int s = 0; s < S; ++s) ld<V>(a.ws + j * row + (s + 1) * C + cl, hp[s]);
+  float dhp[S][V], dk[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    dk[v] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) dhp[s][v] = 0.0f;
+  }
+
+  const int beg = a.rev_off[j], end = a.rev_off[j + 1];
+  int* nb = s_nb[w];
+  for (int t0 = beg; t0 < end; t0 += kRevTile) {
+    const int cnt = end - t0 < kRevTile ? end - t0 : kRevTile;
+    for (int e = lane; e < cnt; e += 64) nb[e] = a.rev_idx[t0 + e];
+    sort_list(nb, cnt, lane);
+    for (int n0 = 0; n0 < cnt; n0 += P * U) {
+      float qd[U][S + 1][V];
+      float L2[U], Dv[U];
+      bool val[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int n = n0 + u * P + sub;
+        val[u] = n < cnt;
+        const int64_t ti = nb[val[u] ? n : cnt - 1];
+        const float* src = a.brows + ti * row + cl;
+#pragma unroll
+        for (int r = 0; r <= S; ++r) ld<V>(src + r * C, qd[u][r]);
+        L2[u] = a.lse[ti * a.heads + head] * 1.4426950408889634f;
+        Dv[u] = a.dh[ti * a.heads + head];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float qk = 0.0f, dp = 0.0f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) qk = fmaf(qd[u][0][v], k[v], qk);
+#pragma unroll
+        for (int r = 0; r < S; ++r)
+#pragma unroll
+          for (int v = 0; v < V; ++v) dp = fmaf(qd[u][r + 1][v], hp[r][v], dp);
+        qk = head_sum_b<HL>(qk, a.head_lanes);
+        dp = head_sum_b<HL>(dp, a.head_lanes);
+        const float alpha = val[u] ? exp2_b(qk * a.scale_log2e - L2[u]) : 0.0f;
+        const float ds = alpha * (dp - Dv[u]) * a.scale;
+#pragma unroll
+        for (int v = 0; v < V; ++v) dk[v] = fmaf(ds, qd[u][0][v], dk[v]);
+#pragma unroll
+        for (int r = 0; r < S; ++r)
+#pragma unroll
+          for (int v = 0; v < V; ++v) dhp[r][v] = fmaf(alpha, qd[u][r + 1][v], dhp[r][v]);
+      }
+    }
+    wave_sync_b();
+  }
+  for (int o = 1 << lg; o < 64; o <<= 1) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      dk[v] += __shfl_xor(dk[v], o);
+#pragma unroll
+      for (int s = 0; s < S; ++s) dhp[s][v] += __shfl_xor(dhp[s][v], o);
+    }
+  }
+  if (sub != 0) return;
+
+  const Frame f = make_frame(a.pos[3 * j], a.pos[3 * j + 1], a.pos[3 * j + 2]);
+  const Dy2 d = make_dy2(f);
+  const Reindex<LMAX> R = make_reindex<LMAX>(cf, f);
+  Reindex<LMAX> Rrad, Rhat;
+  make_grad_reindex<LMAX>(cf, f, Rrad, Rhat);
+  const int64_t base = j * (int64_t)S * C;
+  float hj[S][V], dqj[V], gh[S][V];
+#pragma unroll
+  for (int s = 0; s < S; ++s) ld<V>(a.h + base + s * C + cl, hj[s]);
+  ld<V>(a.dq + j * C + cl, dqj);
+  float acc[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float gv[S], xv[S], out[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      gv[s] = dhp[s][v];
+      xv[s] = hj[s][v];
+    }
+    eaas_channel_t<LMAX>(gv, out, f, d, R);  // gv is rotated in place
+    out[0] += dqj[v] + dk[v];
+#pragma unroll
+    for (int s = 0; s < S; ++s) gh[s][v] = out[s];
+    rotate_in<LMAX>(xv, f, d);
+    pos_grad_channel<LMAX>(xv, gv, Rrad, Rhat, acc);
+  }
+  if (!act) acc[0] = acc[1] = acc[2] = 0.0f;
+  for (int o = 1; o < (1 << lg); o <<= 1) {
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) acc[kk] += __shfl_xor(acc[kk], o);
+  }
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) st<V>(a.grad_h + base + s * C + c0, gh[s]);
+  }
+  if (gl == 0) {
+    float gp[3];
+    frame_to_global(f, acc, gp);
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) a.grad_pos[3 * j + kk] += gp[kk];  // prep wrote the step-3 part
+  }
+}
+
+// -------------------------------------------------------- reverse list
+
+__global__ __launch_bounds__(256) void k_fill_i32(int64_t n, int32_t* p, int32_t v) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < n) p[t] = v;
+}
+
+__global__ __launch_bounds__(256) void k_rev_count(int64_t total, int64_t N, const int32_t* idx,
+                                                   const uint8_t* mask, int32_t* cnt) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total || mask[t] == 0) return;
+  const int32_t j = idx[t];
+  if (j >= 0 && (int64_t)j < N) atomicAdd(&cnt[j], 1);
+}
+
+__global__ __launch_bounds__(256) void k_rev_fill(int64_t total, int64_t N, int K,
+                                                  const int32_t* idx, const uint8_t* mask,
+                                                  int32_t* cur, int32_t* entries) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total || mask[t] == 0) return;
+  const int32_t j = idx[t];
+  if (j >= 0 && (int64_t)j < N) entries[atomicAdd(&cur[j], 1)] = (int32_t)(t / K);
+}
+
+// exclusive scan, pass 1: each 1024-thread block scans kScanTile elements in place
+__global__ __launch_bounds__(1024) void k_scan_tiles(int64_t n, int32_t* a, int32_t* tile_sums) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  const int64_t e0 = (int64_t)blockIdx.x * kScanTile + 4 * t;
+  int32_t v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] = e0 + k < n ? a[e0 + k] : 0;
+  const int32_t sum = v[0] + v[1] + v[2] + v[3];
+  part[t] = sum;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int32_t add = t >= o ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
+  }
+  int32_t run = part[t] - sum;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (e0 + k < n) a[e0 + k] = run;
+    run += v[k];
+  }
+  if (t == 1023) tile_sums[blockIdx.x] = part[1023];
+}
+
+// pass 2: one block scans the tile totals (at most kScanTile of them); a[n] = total
+__global__ __launch_bounds__(1024) void k_scan_top(int64_t n, int ntiles, int32_t* tile_sums,
+                                                   int32_t* a) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  int32_t v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] = 4 * t + k < ntiles ? tile_sums[4 * t + k] : 0;
+  const int32_t sum = v[0] + v[1] + v[2] + v[3];
+  part[t] = sum;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int32_t add = t >= o ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
+  }
+  int32_t run = part[t] - sum;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (4 * t + k < ntiles) tile_sums[4 * t + k] = run;
+    run += v[k];
+  }
+  if (t == 1023) a[n] = part[1023];
+}
+
+// pass 3: add the tile offsets; keep a copy as the fill cursors
+__global__ __launch_bounds__(256) void k_scan_fix(int64_t n, int32_t* a, const int32_t* tile_sums,
+                                                  int32_t* cur) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  const int32_t v = a[e] + tile_sums[e / kScanTile];
+  a[e] = v;
+  cur[e] = v;
+}
+
+int last_err() { return static_cast<int>(hipGetLastError()); }
+
+template <int L, int V, int HL>
+int bwd_go(const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
+  constexpr int U = 2;
+  const int64_t per_block = (int64_t)kWavesPerBlock * (64 >> a.lane_log);
+  const dim3 grid_prep((unsigned)((a.N + per_block - 1) / per_block));
+  const int64_t blocks = (a.N + kWavesPerBlock - 1) / kWavesPerBlock;
+  const dim3 grid((unsigned)((blocks + kXcds - 1) / kXcds * kXcds));
+  hipLaunchKernelGGL((k_bwd_prep<L, V, HL>), grid_prep, dim3(256), 0, s, a, cf);
+  hipLaunchKernelGGL((k_bwd_q<L, V, U, HL>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_bwd_src<L, V, U, HL>), grid, dim3(256), 0, s, a, cf);
+  return last_err();
+}
+
+template <int L>
+int bwd_l(int V, const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
+  if (V == 4 && a.head_lanes == 2) return bwd_go<L, 4, 2>(a, cf, s);
+  if (V == 4 && a.head_lanes == 1) return bwd_go<L, 4, 1>(a, cf, s);
+  switch (V) {
+    case 1: return bwd_go<L, 1, 0>(a, cf, s);
+    case 2: return bwd_go<L, 2, 0>(a, cf, s);
+    case 4: return bwd_go<L, 4, 0>(a, cf, s);
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
+}
+
+}  // namespace
+
+int launch_reverse_list(int64_t N, int K, const int32_t* idx, const uint8_t* mask, int32_t* off,
+                        int32_t* cur, int32_t* tile_sums, int32_t* entries, hipStream_t s) {
+  (void)hipGetLastError();
+  const int64_t total = N * (int64_t)K;
+  const unsigned gt = (unsigned)((total + 255) / 256);
+  const unsigned gn = (unsigned)((N + 255) / 256);
+  const int ntiles = (int)((N + kScanTile - 1) / kScanTile);
+  hipLaunchKernelGGL(k_fill_i32, dim3(gn), dim3(256), 0, s, N, off, 0);
+  hipLaunchKernelGGL(k_rev_count, dim3(gt), dim3(256), 0, s, total, N, idx, mask, off);
+  hipLaunchKernelGGL(k_scan_tiles, dim3((unsigned)ntiles), dim3(1024), 0, s, N, off, tile_sums);
+  hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(1024), 0, s, N, ntiles, tile_sums, off);
+  hipLaunchKernelGGL(k_scan_fix, dim3(gn), dim3(256), 0, s, N, off, tile_sums, cur);
+  hipLaunchKernelGGL(k_rev_fill, dim3(gt), dim3(256), 0, s, total, N, K, idx, mask, cur, entries);
+  return last_err();
+}
+
+int launch_backward(int lmax, int V, const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
+  (void)hipGetLastError();
+  switch (lmax) {
+    case 0: return bwd_l<0>(V, a, cf, s);
+    case 1: return bwd_l<1>(V, a, cf, s);
+    case 2: return bwd_l<2>(V, a, cf, s);
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
+}
+
+}  // namespace e2f

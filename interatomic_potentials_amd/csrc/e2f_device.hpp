@@ -222,6 +222,150 @@ __device__ inline void reindex(const float* x, float* y, const Reindex<LMAX>& R)
       }
 }
 
+// x = P^T(y): the transpose of the reindex (adjoint of the aligned-frame map)
+template <int LMAX>
+__device__ inline void reindex_t(const float* y, float* x, const Reindex<LMAX>& R) {
+#pragma unroll
+  for (int s = 0; s < ncomp(LMAX); ++s) x[s] = 0.0f;
+  int p = 0;
+#pragma unroll
+  for (int li = 0; li <= LMAX; ++li)
+#pragma unroll
+    for (int lf = 0; lf <= LMAX; ++lf)
+#pragma unroll
+      for (int lo = 0; lo <= LMAX; ++lo) {
+        if (lo < (li > lf ? li - lf : lf - li) || lo > li + lf) continue;
+        const int mmax = li < lo ? li : lo;
+        if (((li + lf + lo) & 1) == 0) {
+#pragma unroll
+          for (int m = 0; m <= mmax; ++m) {
+            x[flat(li, m)] += R.k[p][m] * y[flat(lo, m)];
+            if (m > 0) x[flat(li, -m)] += R.k[p][m] * y[flat(lo, -m)];
+          }
+        } else {
+#pragma unroll
+          for (int m = 1; m <= mmax; ++m) {
+            x[flat(li, -m)] += R.k[p][m] * y[flat(lo, m)];
+            x[flat(li, m)] -= R.k[p][m] * y[flat(lo, -m)];
+          }
+        }
+        ++p;
+      }
+}
+
+// Reindex weights for the position gradient (no path to l_f = 0 moves with r):
+//   radial: w_p c_m l_f |r|^(l_f - 1)   (d/d|r| of the value weights)
+//   hat:    w_p c_m |r|^(l_f - 1)       (value weights over |r|, for the torque terms)
+template <int LMAX>
+__device__ inline void make_grad_reindex(const EaasCoef& cf, const Frame& f, Reindex<LMAX>& rad,
+                                         Reindex<LMAX>& hat) {
+  int p = 0;
+#pragma unroll
+  for (int li = 0; li <= LMAX; ++li)
+#pragma unroll
+    for (int lf = 0; lf <= LMAX; ++lf)
+#pragma unroll
+      for (int lo = 0; lo <= LMAX; ++lo) {
+        if (lo < (li > lf ? li - lf : lf - li) || lo > li + lf) continue;
+        const float rl1 = lf == 2 ? f.r1 : 1.0f;  // |r|^(l_f - 1) for l_f = 1, 2
+#pragma unroll
+        for (int m = 0; m <= LMAX; ++m) {
+          hat.k[p][m] = lf == 0 ? 0.0f : cf.c[p][m] * rl1;
+          rad.k[p][m] = hat.k[p][m] * (float)lf;
+        }
+        ++p;
+      }
+}
+
+// Generators of rotations about the x and y axes in the real harmonic basis
+// (D(R_a(e)) = 1 + e J_a + O(e^2)); at l = 1 the basis is (y, z, x), at l = 2
+// the entries follow from differentiating the D_y blocks above at zero angle
+// and J_x = J_y J_z - J_z J_y.
+template <int LMAX>
+__device__ inline void apply_jx(const float* x, float* y) {
+  y[0] = 0.0f;
+  if constexpr (LMAX >= 1) {
+    y[flat(1, -1)] = -x[flat(1, 0)];
+    y[flat(1, 0)] = x[flat(1, -1)];
+    y[flat(1, 1)] = 0.0f;
+  }
+  if constexpr (LMAX >= 2) {
+    const float k3 = 1.7320508075688772f;
+    y[flat(2, -2)] = -x[flat(2, 1)];
+    y[flat(2, -1)] = -k3 * x[flat(2, 0)] - x[flat(2, 2)];
+    y[flat(2, 0)] = k3 * x[flat(2, -1)];
+    y[flat(2, 1)] = x[flat(2, -2)];
+    y[flat(2, 2)] = x[flat(2, -1)];
+  }
+}
+
+template <int LMAX>
+__device__ inline void apply_jy(const float* x, float* y) {
+  y[0] = 0.0f;
+  if constexpr (LMAX >= 1) {
+    y[flat(1, -1)] = 0.0f;
+    y[flat(1, 0)] = -x[flat(1, 1)];
+    y[flat(1, 1)] = x[flat(1, 0)];
+  }
+  if constexpr (LMAX >= 2) {
+    const float k3 = 1.7320508075688772f;
+    y[flat(2, -2)] = x[flat(2, -1)];
+    y[flat(2, -1)] = -x[flat(2, -2)];
+    y[flat(2, 0)] = -k3 * x[flat(2, 1)];
+    y[flat(2, 1)] = k3 * x[flat(2, 0)] - x[flat(2, 2)];
+    y[flat(2, 2)] = x[flat(2, 1)];
+  }
+}
+
+// Position gradient of f(r) = <g, x (x) R(r)> for one channel, in the aligned
+// frame.  With xt = D(Q) x and gt = D(Q) g the product is <gt, P xt>:
+//   * moving r along r_hat changes only |r|:        df/d|r| = <gt, P_rad xt>;
+//   * rotating r about a local axis a (a = x, y) conjugates the map by that
+//     rotation, so its derivative is the torque <gt, [J_a, P] xt>; rotating about
+//     r itself changes nothing.  Torque about local a = (r' x grad')_a with
+//     r' = |r| z, which gives grad'_x = t_y / |r| and grad'_y = -t_x / |r|.
+// `hat` already carries the 1/|r|, so no division happens (also fine at r = 0).
+// Adds (grad'_x, grad'_y, grad'_z) of this channel to acc; the caller rotates
+// the channel sum back with Q^T.
+template <int LMAX>
+__device__ inline void pos_grad_channel(float* xt, float* gt, const Reindex<LMAX>& rad,
+                                        const Reindex<LMAX>& hat, float* acc) {
+  constexpr int S = ncomp(LMAX);
+  float t[S], u[S], v[S];
+  reindex<LMAX>(xt, t, rad);
+  float dr = 0.0f;
+#pragma unroll
+  for (int s = 0; s < S; ++s) dr = fmaf(gt[s], t[s], dr);
+  reindex<LMAX>(xt, t, hat);  // P_hat xt
+  // t_a = -<J_a gt, P_hat xt> - <gt, P_hat J_a xt>
+  float tx = 0.0f, ty = 0.0f;
+  apply_jx<LMAX>(gt, u);
+#pragma unroll
+  for (int s = 0; s < S; ++s) tx = fmaf(-u[s], t[s], tx);
+  apply_jx<LMAX>(xt, u);
+  reindex<LMAX>(u, v, hat);
+#pragma unroll
+  for (int s = 0; s < S; ++s) tx = fmaf(-gt[s], v[s], tx);
+  apply_jy<LMAX>(gt, u);
+#pragma unroll
+  for (int s = 0; s < S; ++s) ty = fmaf(-u[s], t[s], ty);
+  apply_jy<LMAX>(xt, u);
+  reindex<LMAX>(u, v, hat);
+#pragma unroll
+  for (int s = 0; s < S; ++s) ty = fmaf(-gt[s], v[s], ty);
+  acc[0] += ty;
+  acc[1] -= tx;
+  acc[2] += dr;
+}
+
+// v = Q^T v' for the alignment rotation of the frame (local -> global vector)
+__device__ inline void frame_to_global(const Frame& f, const float* l, float* g) {
+  // rows of Q = R_y(-t) R_z(-p)
+  g[0] = f.ct * f.c1 * l[0] - f.s1 * l[1] + f.st * f.c1 * l[2];
+  g[1] = f.ct * f.s1 * l[0] + f.c1 * l[1] + f.st * f.s1 * l[2];
+  g[2] = -f.st * l[0] + f.ct * l[2];
+}
+
 // full EAAS on one channel: x (global) -> y (global)
 template <int LMAX>
 __device__ inline void eaas_channel(float* x, float* y, const Frame& f, const Dy2& d,
@@ -229,6 +373,15 @@ __device__ inline void eaas_channel(float* x, float* y, const Frame& f, const Dy
   rotate_in<LMAX>(x, f, d);
   reindex<LMAX>(x, y, R);
   rotate_out<LMAX>(y, f, d);
+}
+
+// adjoint EAAS on one channel: x = D^T P^T D y (y is overwritten)
+template <int LMAX>
+__device__ inline void eaas_channel_t(float* y, float* x, const Frame& f, const Dy2& d,
+                                      const Reindex<LMAX>& R) {
+  rotate_in<LMAX>(y, f, d);
+  reindex_t<LMAX>(y, x, R);
+  rotate_out<LMAX>(x, f, d);
 }
 
 // ------------------------------------------------------ storage types

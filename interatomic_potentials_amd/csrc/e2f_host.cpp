@@ -144,6 +144,35 @@ size_t sched_bytes(int64_t N) {
          round256((size_t)e2f::kBboxBlocks * 6 * 4);
 }
 
+// backward workspace: [q / dm rows][dq][per-head D][reverse list offsets, cursors,
+// scan tile sums, entries][schedule scratch]; every part 256-byte aligned
+struct BwdLayout {
+  size_t brows, dq, dh, off, cur, tiles, entries, sched, cell, counts, partial, total;
+};
+
+BwdLayout bwd_layout(int64_t N, int K, int lmax, int C, int H) {
+  BwdLayout L;
+  size_t p = 0;
+  auto take = [&p](size_t bytes) {
+    const size_t at = p;
+    p += round256(bytes);
+    return at;
+  };
+  L.brows = take((size_t)N * (ncomp(lmax) + 1) * C * 4);
+  L.dq = take((size_t)N * C * 4);
+  L.dh = take((size_t)N * H * 4);
+  L.off = take((size_t)(N + 1) * 4);
+  L.cur = take((size_t)N * 4);
+  L.tiles = take((size_t)e2f::kScanTile * 4);
+  L.entries = take((size_t)N * K * 4);
+  L.sched = take((size_t)N * 4);
+  L.cell = take((size_t)N * 4);
+  L.counts = take((size_t)e2f::kSchedCells * 4);
+  L.partial = take((size_t)e2f::kBboxBlocks * 6 * 4);
+  L.total = p;
+  return L;
+}
+
 // layout: [pre-coupled rows][256 B validation flag][schedule scratch]
 e2f::SchedScratch sched_scratch(void* ws, int64_t N, int lmax, int C, int dt) {
   char* p = static_cast<char*>(ws) + ws_body_bytes(N, lmax, C, dt) + 256;
@@ -192,7 +221,8 @@ int precouple_impl(hipStream_t stream, int64_t N, int lmax, int C, int dt, const
 
 int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dt,
                    const float* pos, const int32_t* idx, const uint8_t* mask, float scale,
-                   const float* path_w, void* ws, void* out, void* out_msg, uint32_t flags) {
+                   const float* path_w, void* ws, void* out, void* out_msg, float* lse,
+                   uint32_t flags) {
   if (flags & E2F_VALIDATE_INDICES) {
     int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
                                                ws_body_bytes(N, lmax, C, dt));
@@ -230,6 +260,8 @@ int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
   const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)d);
   a.scale_log2e = (float)(sc * 1.4426950408889634);  // log2(e)
   a.sched = sched;
+  a.lse = lse;
+  a.heads = H;
   const EaasCoef cf = make_coef(lmax, path_w);
   return hip_status(e2f::launch_aggregate(lmax, dt, V, a, cf, stream));
 }
@@ -316,17 +348,19 @@ int e2f_attn_precouple(hipStream_t stream, int64_t N, int lmax, int C, int dtype
 int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                        const float* pos, const int32_t* nbr_idx, const uint8_t* nbr_mask,
                        float scale, const float* path_w, void* workspace, size_t ws_bytes,
-                       void* out, void* out_msg, uint32_t flags) {
+                       void* out, void* out_msg, float* lse, uint32_t flags) {
   int st = check_attn_shape(N, K, lmax, C, H, dtype, flags);
   if (st != E2F_OK) return st;
   if (N == 0) return E2F_OK;
   if (!pos || !nbr_idx || !nbr_mask || !workspace || !out) return E2F_ERR_NULL;
   if (!aligned(pos, 4) || !aligned(nbr_idx, 4) || !aligned(workspace, 16) || !aligned(out, 16) ||
-      (out_msg && !aligned(out_msg, 16)) || (path_w && !aligned(path_w, 4)))
+      (out_msg && !aligned(out_msg, 16)) || (path_w && !aligned(path_w, 4)) ||
+      (lse && !aligned(lse, 4)))
     return E2F_ERR_ALIGN;
   const size_t need = e2f_attn_workspace_bytes(N, lmax, C, dtype);
   if (ws_bytes < need) return E2F_ERR_WORKSPACE;
   const size_t ob = (size_t)N * ncomp(lmax) * C * esize(dtype);
+  const size_t lb = (size_t)N * H * 4;
   const Range ins[4] = {{pos, (size_t)N * 12},
                         {nbr_idx, (size_t)N * K * 4},
                         {nbr_mask, (size_t)N * K},
@@ -334,16 +368,19 @@ int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, in
   for (const Range& r : ins) {
     if (overlap({out, ob}, r)) return E2F_ERR_ALIAS;
     if (out_msg && overlap({out_msg, ob}, r)) return E2F_ERR_ALIAS;
+    if (lse && overlap({lse, lb}, r)) return E2F_ERR_ALIAS;
   }
   if (out_msg && overlap({out, ob}, {out_msg, ob})) return E2F_ERR_ALIAS;
+  if (lse && (overlap({lse, lb}, {out, ob}) || (out_msg && overlap({lse, lb}, {out_msg, ob}))))
+    return E2F_ERR_ALIAS;
   return aggregate_impl(stream, N, K, lmax, C, H, dtype, pos, nbr_idx, nbr_mask, scale, path_w,
-                        workspace, out, out_msg, flags);
+                        workspace, out, out_msg, lse, flags);
 }
 
 int e2f_attn_forward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                      const float* pos, const void* h, const int32_t* nbr_idx,
                      const uint8_t* nbr_mask, float scale, const float* path_w, void* workspace,
-                     size_t ws_bytes, void* out, void* out_msg, uint32_t flags) {
+                     size_t ws_bytes, void* out, void* out_msg, float* lse, uint32_t flags) {
   int st = check_attn_shape(N, K, lmax, C, H, dtype, flags);
   if (st != E2F_OK) return st;
   if (N == 0) return E2F_OK;
@@ -359,22 +396,119 @@ int e2f_attn_forward(hipStream_t stream, int64_t N, int K, int lmax, int C, int 
   if (ws_bytes < need) return E2F_ERR_WORKSPACE;
   if (overlap({workspace, need}, {h, hb})) return E2F_ERR_ALIAS;
   if (!aligned(pos, 4) || !aligned(nbr_idx, 4) || !aligned(workspace, 16) || !aligned(out, 16) ||
-      (out_msg && !aligned(out_msg, 16)) || (path_w && !aligned(path_w, 4)))
+      (out_msg && !aligned(out_msg, 16)) || (path_w && !aligned(path_w, 4)) ||
+      (lse && !aligned(lse, 4)))
     return E2F_ERR_ALIGN;
-  const Range ins[4] = {{pos, (size_t)N * 12},
+  const size_t lb = (size_t)N * H * 4;
+  const Range ins[5] = {{pos, (size_t)N * 12},
                         {nbr_idx, (size_t)N * K * 4},
                         {nbr_mask, (size_t)N * K},
-                        {workspace, need}};
+                        {workspace, need},
+                        {h, hb}};
   for (const Range& r : ins) {
     if (overlap({out, hb}, r)) return E2F_ERR_ALIAS;
     if (out_msg && overlap({out_msg, hb}, r)) return E2F_ERR_ALIAS;
+    if (lse && overlap({lse, lb}, r)) return E2F_ERR_ALIAS;
   }
   if (out_msg && overlap({out, hb}, {out_msg, hb})) return E2F_ERR_ALIAS;
+  if (lse && (overlap({lse, lb}, {out, hb}) || (out_msg && overlap({lse, lb}, {out_msg, hb}))))
+    return E2F_ERR_ALIAS;
   if (overlap({workspace, need}, {pos, (size_t)N * 12})) return E2F_ERR_ALIAS;
   st = precouple_impl(stream, N, lmax, C, dtype, pos, h, path_w, workspace, ws_bytes);
   if (st != E2F_OK) return st;
   return aggregate_impl(stream, N, K, lmax, C, H, dtype, pos, nbr_idx, nbr_mask, scale, path_w,
-                        workspace, out, out_msg, flags);
+                        workspace, out, out_msg, lse, flags);
+}
+
+size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int H, int dtype) {
+  if (check_attn_shape(N, K, lmax, C, H, dtype, 0) != E2F_OK) return 0;
+  return bwd_layout(N, K, lmax, C, H).total;
+}
+
+int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
+                      const float* pos, const void* h, const int32_t* nbr_idx,
+                      const uint8_t* nbr_mask, float scale, const float* path_w,
+                      const void* workspace, size_t ws_bytes, const void* msg, const float* lse,
+                      const void* grad_out, void* grad_h, float* grad_pos,
+                      void* bwd_workspace, size_t bwd_ws_bytes, uint32_t flags) {
+  int st = check_attn_shape(N, K, lmax, C, H, dtype, flags);
+  if (st != E2F_OK) return st;
+  if (flags & E2F_VALIDATE_INDICES) return E2F_ERR_SHAPE;  // not offered for the backward
+  if (dtype != E2F_F32) return E2F_ERR_UNSUPPORTED;         // fp32 storage only
+  if (N == 0) return E2F_OK;
+  if (N > (int64_t)e2f::kScanTile * e2f::kScanTile || N * (int64_t)K >= ((int64_t)1 << 31))
+    return E2F_ERR_UNSUPPORTED;
+  if (!pos || !h || !nbr_idx || !nbr_mask || !workspace || !msg || !lse || !grad_out || !grad_h ||
+      !grad_pos || !bwd_workspace)
+    return E2F_ERR_NULL;
+  if (!aligned(pos, 4) || !aligned(h, 16) || !aligned(nbr_idx, 4) || !aligned(workspace, 16) ||
+      !aligned(msg, 16) || !aligned(lse, 4) || !aligned(grad_out, 16) || !aligned(grad_h, 16) ||
+      !aligned(grad_pos, 4) || !aligned(bwd_workspace, 16) || (path_w && !aligned(path_w, 4)))
+    return E2F_ERR_ALIGN;
+  const size_t need = e2f_attn_workspace_bytes(N, lmax, C, dtype);
+  if (ws_bytes < need) return E2F_ERR_WORKSPACE;
+  const BwdLayout L = bwd_layout(N, K, lmax, C, H);
+  if (bwd_ws_bytes < L.total) return E2F_ERR_WORKSPACE;
+  const size_t hb = (size_t)N * ncomp(lmax) * C * 4;
+  const Range ins[8] = {{pos, (size_t)N * 12}, {h, hb},       {nbr_idx, (size_t)N * K * 4},
+                        {nbr_mask, (size_t)N * K}, {workspace, need}, {msg, hb},
+                        {lse, (size_t)N * H * 4}, {grad_out, hb}};
+  const Range outs[3] = {{grad_h, hb}, {grad_pos, (size_t)N * 12}, {bwd_workspace, L.total}};
+  for (const Range& o : outs)
+    for (const Range& r : ins)
+      if (overlap(o, r)) return E2F_ERR_ALIAS;
+  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
+    return E2F_ERR_ALIAS;
+
+  char* b = static_cast<char*>(bwd_workspace);
+  e2f::BwdArgs a;
+  a.pos = pos;
+  a.h = static_cast<const float*>(h);
+  a.idx = nbr_idx;
+  a.mask = nbr_mask;
+  a.ws = static_cast<const float*>(workspace);
+  a.msg = static_cast<const float*>(msg);
+  a.lse = lse;
+  a.gout = static_cast<const float*>(grad_out);
+  a.grad_h = static_cast<float*>(grad_h);
+  a.grad_pos = grad_pos;
+  a.brows = reinterpret_cast<float*>(b + L.brows);
+  a.dq = reinterpret_cast<float*>(b + L.dq);
+  a.dh = reinterpret_cast<float*>(b + L.dh);
+  int32_t* off = reinterpret_cast<int32_t*>(b + L.off);
+  int32_t* cur = reinterpret_cast<int32_t*>(b + L.cur);
+  int32_t* tiles = reinterpret_cast<int32_t*>(b + L.tiles);
+  int32_t* entries = reinterpret_cast<int32_t*>(b + L.entries);
+  a.rev_off = off;
+  a.rev_idx = entries;
+  a.sched = nullptr;
+  if (!(flags & E2F_TARGETS_IN_ORDER)) {
+    e2f::SchedScratch sc;
+    sc.bits = sched_bits(N);
+    sc.sched = reinterpret_cast<int32_t*>(b + L.sched);
+    sc.cell = reinterpret_cast<int32_t*>(b + L.cell);
+    sc.counts = reinterpret_cast<int32_t*>(b + L.counts);
+    sc.partial = reinterpret_cast<float*>(b + L.partial);
+    st = hip_status(e2f::launch_schedule(N, pos, sc, stream));
+    if (st != E2F_OK) return st;
+    a.sched = sc.sched;
+  }
+  st = hip_status(e2f::launch_reverse_list(N, K, nbr_idx, nbr_mask, off, cur, tiles, entries,
+                                           stream));
+  if (st != E2F_OK) return st;
+  const int V = attn_width(C, H, dtype);
+  const int d = C / H;
+  a.N = N;
+  a.K = K;
+  a.C = C;
+  a.heads = H;
+  a.lane_log = ceil_log2(C / V);
+  a.head_lanes = d / V;
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)d);
+  a.scale = (float)sc;
+  a.scale_log2e = (float)(sc * 1.4426950408889634);
+  const EaasCoef cf = make_coef(lmax, path_w);
+  return hip_status(e2f::launch_backward(lmax, V, a, cf, stream));
 }
 
 int e2f_frames(hipStream_t stream, int64_t n, int lmax, const float* r, float* Q, float* D) {

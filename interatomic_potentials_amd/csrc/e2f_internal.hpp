@@ -55,6 +55,36 @@ struct AggArgs {
   int head_lanes;          // lanes per head = d / V (power of two)
   float scale_log2e;       // logit scale times log2(e)
   const int32_t* sched;    // [N] processing order of the targets
+  float* lse;              // [N, H] natural log-sum-exp of each target's logits, or nullptr
+  int heads;               // H
+};
+
+// Backward pass (vector-Jacobian product) arguments, fp32 storage.
+struct BwdArgs {
+  const float* pos;        // [N, 3]
+  const float* h;          // [N, S, C] forward input
+  const int32_t* idx;      // [N, K]
+  const uint8_t* mask;     // [N, K]
+  const float* ws;         // forward workspace rows [N, S + 1, C] (k, h')
+  const float* msg;        // [N, S, C] forward message m
+  const float* lse;        // [N, H] forward log-sum-exp
+  const float* gout;       // [N, S, C] upstream gradient of out
+  float* grad_h;           // [N, S, C]
+  float* grad_pos;         // [N, 3]
+  float* brows;            // [N, S + 1, C] scratch: row 0 = q_i, rows 1..S = dm_i
+  float* dq;               // [N, C] scratch
+  float* dh;               // [N, H] scratch: per-head <dm_i, m_i>
+  const int32_t* rev_off;  // [N + 1] reverse list offsets (targets of each source)
+  const int32_t* rev_idx;  // [E] reverse list entries
+  const int32_t* sched;    // [N] visiting order
+  int64_t N;
+  int K;
+  int C;
+  int heads;
+  int lane_log;
+  int head_lanes;
+  float scale;
+  float scale_log2e;
 };
 
 // launchers (kernels file); return 0 or a hipError_t value
@@ -66,5 +96,11 @@ int launch_frames(int lmax, int64_t n, const float* r, float* Q, float* D, hipSt
 int launch_validate(int64_t N, int K, const int32_t* idx, const uint8_t* mask, int32_t* flag,
                     hipStream_t s);
 int launch_schedule(int64_t N, const float* pos, const SchedScratch& sc, hipStream_t s);
+// reverse neighbour list (CSR by source) and the three backward passes
+int launch_reverse_list(int64_t N, int K, const int32_t* idx, const uint8_t* mask, int32_t* off,
+                        int32_t* cur, int32_t* tile_sums, int32_t* entries, hipStream_t s);
+int launch_backward(int lmax, int V, const BwdArgs& a, const EaasCoef& cf, hipStream_t s);
+constexpr int kScanTile = 4096;     // elements per block of the generic scan
+constexpr int kRevTile = 1024;      // reverse-list entries sorted per pass
 
 }  // namespace e2f

@@ -275,6 +275,12 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
   }
 
   if (sub != 0 || !act) return;
+  if (a.lse != nullptr && (lane & (a.head_lanes - 1)) == 0) {
+    // natural log-sum-exp of this head's logits (base-2 running state times ln 2)
+    const int d = a.C / a.heads;
+    a.lse[i * a.heads + c0 / d] =
+        z > 0.0f ? (mu + log2f(z)) * 0.6931471805599453f : -INFINITY;
+  }
   const float inv = z > 0.0f ? 1.0f / z : 0.0f;  // no valid slot: m_i = 0, out_i = 0
 #pragma unroll
   for (int r = 0; r < S; ++r)

@@ -92,21 +92,21 @@ def test_workspace_bytes():
 def _agg(**kw):
     a = dict(stream=None, N=1000, K=64, lmax=2, C=128, H=16, dt=0, pos=fake(1), idx=fake(2),
              mask=fake(3), scale=0.0, pw=None, ws=fake(4), ws_bytes=1 << 30, out=fake(8),
-             msg=None, flags=0)
+             msg=None, lse=None, flags=0)
     a.update(kw)
     return lib.e2f_attn_aggregate(a["stream"], a["N"], a["K"], a["lmax"], a["C"], a["H"], a["dt"],
                                   a["pos"], a["idx"], a["mask"], a["scale"], a["pw"], a["ws"],
-                                  a["ws_bytes"], a["out"], a["msg"], a["flags"])
+                                  a["ws_bytes"], a["out"], a["msg"], a["lse"], a["flags"])
 
 
 def _fwd(**kw):
     a = dict(stream=None, N=1000, K=64, lmax=2, C=128, H=16, dt=0, pos=fake(1), h=fake(9),
              idx=fake(2), mask=fake(3), scale=0.0, pw=None, ws=fake(4), ws_bytes=1 << 30,
-             out=fake(8), msg=None, flags=0)
+             out=fake(8), msg=None, lse=None, flags=0)
     a.update(kw)
     return lib.e2f_attn_forward(a["stream"], a["N"], a["K"], a["lmax"], a["C"], a["H"], a["dt"],
                                 a["pos"], a["h"], a["idx"], a["mask"], a["scale"], a["pw"],
-                                a["ws"], a["ws_bytes"], a["out"], a["msg"], a["flags"])
+                                a["ws"], a["ws_bytes"], a["out"], a["msg"], a["lse"], a["flags"])
 
 
 def _eaas(**kw):
@@ -154,6 +154,8 @@ def test_attention_argument_errors(fn):
     assert fn(out=fake(1)) == C["E2F_ERR_ALIAS"]             # out over the positions
     assert fn(msg=fake(8)) == C["E2F_ERR_ALIAS"]             # message over the output
     assert fn(msg=fake(2)) == C["E2F_ERR_ALIAS"]             # message over the indices
+    assert fn(lse=fake(8)) == C["E2F_ERR_ALIAS"]             # lse over the output
+    assert fn(lse=ctypes.c_void_p(BASE + 13 * 64 * MB + 2)) == C["E2F_ERR_ALIGN"]
 
 
 def test_forward_specific_errors():
@@ -192,3 +194,34 @@ def test_frames_errors():
     assert f(None, 0, 2, None, None, None) == C["E2F_OK"]
     assert f(None, 10, 2, None, fake(2), fake(3)) == C["E2F_ERR_NULL"]
     assert f(None, 10, 2, fake(1), fake(1), fake(3)) == C["E2F_ERR_ALIAS"]
+
+
+def _bwd(**kw):
+    a = dict(stream=None, N=1000, K=64, lmax=2, C=128, H=16, dt=0, pos=fake(1), h=fake(9),
+             idx=fake(2), mask=fake(3), scale=0.0, pw=None, ws=fake(4), ws_bytes=1 << 30,
+             msg=fake(10), lse=fake(11), gout=fake(12), gh=fake(13), gp=fake(14), bws=fake(16),
+             bws_bytes=1 << 30, flags=0)
+    a.update(kw)
+    return lib.e2f_attn_backward(a["stream"], a["N"], a["K"], a["lmax"], a["C"], a["H"], a["dt"],
+                                 a["pos"], a["h"], a["idx"], a["mask"], a["scale"], a["pw"],
+                                 a["ws"], a["ws_bytes"], a["msg"], a["lse"], a["gout"], a["gh"],
+                                 a["gp"], a["bws"], a["bws_bytes"], a["flags"])
+
+
+def test_backward_argument_errors():
+    wb = lib.e2f_attn_backward_workspace_bytes
+    assert wb(1000, 64, 2, 128, 16, 0) > 1000 * 11 * 128 * 4 + 1000 * 64 * 4
+    assert wb(1000, 64, 3, 128, 16, 0) == 0
+    assert _bwd(dt=1) == C["E2F_ERR_UNSUPPORTED"]            # bf16 backward not offered
+    assert _bwd(dt=5) == C["E2F_ERR_DTYPE"]
+    assert _bwd(K=0) == C["E2F_ERR_SHAPE"]
+    assert _bwd(flags=1) == C["E2F_ERR_SHAPE"]               # no index validation here
+    assert _bwd(N=0, pos=None, h=None) == C["E2F_OK"]
+    for name in ("pos", "h", "idx", "mask", "ws", "msg", "lse", "gout", "gh", "gp", "bws"):
+        assert _bwd(**{name: None}) == C["E2F_ERR_NULL"], name
+    assert _bwd(gh=ctypes.c_void_p(BASE + 13 * 64 * MB + 4)) == C["E2F_ERR_ALIGN"]
+    assert _bwd(bws_bytes=wb(1000, 64, 2, 128, 16, 0) - 1) == C["E2F_ERR_WORKSPACE"]
+    assert _bwd(ws_bytes=100) == C["E2F_ERR_WORKSPACE"]
+    assert _bwd(gh=fake(9)) == C["E2F_ERR_ALIAS"]             # grad_h over h
+    assert _bwd(gp=fake(12)) == C["E2F_ERR_ALIAS"]            # grad_pos over grad_out
+    assert _bwd(bws=fake(13)) == C["E2F_ERR_ALIAS"]           # scratch over grad_h

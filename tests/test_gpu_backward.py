@@ -1,0 +1,136 @@
+"""GPU backward pass (dL/dh, dL/dpos) against the oracle's float64 autograd gradients.
+
+Errors: dL/dh uses the forward's block-relative metric; dL/dpos uses, per atom,
+|gpu - ref| / max(|ref|, 1e-3 max_atoms |ref|).  Both at 1e-4 (fp32).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from gen import make_config
+from oracle.grad import attn_backward as oracle_backward
+from tests.helpers import TOL_F32, block_rel_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def e2f():
+    import interatomic_potentials_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return torch.device("cuda:0")
+
+
+def T(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def pos_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    nr = np.linalg.norm(ref, axis=1)
+    den = np.maximum(nr, 1e-3 * nr.max() + 1e-300)
+    return float((np.linalg.norm(got - ref, axis=1) / den).max())
+
+
+def gpu_backward(e2f, dev, pos, h, idx, mask, H, g, **kw):
+    p, hh, ii, mm = T(pos, dev), T(h, dev), T(idx, dev), T(mask, dev)
+    ws = e2f.attn_precouple(p, hh)
+    out, msg, lse = e2f.attn_aggregate(p, ii, mm, ws, H, int(round(h.shape[1] ** 0.5)) - 1,
+                                       h.shape[2], torch.float32, return_msg=True, return_lse=True)
+    gh, gp = e2f.attn_backward(p, hh, ii, mm, H, ws, msg, lse, T(g, dev), **kw)
+    torch.cuda.synchronize()
+    return gh.cpu().numpy(), gp.cpu().numpy(), lse
+
+
+@pytest.mark.parametrize("lmax,C,H,K", [(0, 16, 2, 12), (1, 16, 2, 20), (2, 32, 4, 24),
+                                        (2, 128, 16, 64), (2, 64, 4, 300), (1, 8, 8, 10)])
+def test_backward_random_graphs(e2f, dev, lmax, C, H, K):
+    say(f"backward random graph: lmax={lmax} C={C} H={H} K={K}")
+    rng = np.random.default_rng(lmax * 31 + C + K)
+    N = 80
+    S = (lmax + 1) ** 2
+    pos = (rng.standard_normal((N, 3)) * 3).astype(np.float32)
+    h = rng.standard_normal((N, S, C)).astype(np.float32)
+    idx = rng.integers(0, N, size=(N, K)).astype(np.int32)
+    mask = (rng.random((N, K)) < 0.6).astype(np.uint8)
+    mask[7] = 0                                          # a target with no valid slot
+    g = rng.standard_normal((N, S, C)).astype(np.float32)
+    gh, gp, _ = gpu_backward(e2f, dev, pos, h, idx, mask, H, g)
+    rh, rp = oracle_backward(pos, h, idx, mask, H, lmax, g)
+    assert block_rel_err(gh, rh, lmax) <= TOL_F32
+    assert pos_err(gp, rp) <= TOL_F32
+
+
+@pytest.mark.parametrize("name", ["tiny", "water"])
+def test_backward_small_configs(e2f, dev, name):
+    cfg = make_config(name)
+    s = cfg.spec
+    say(f"backward {name}: N={cfg.N} E={cfg.nl.n_edges}")
+    g = np.random.default_rng(5).standard_normal(cfg.h.shape).astype(np.float32)
+    gh, gp, lse = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g)
+    rh, rp = oracle_backward(cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, s.lmax, g)
+    assert block_rel_err(gh, rh, s.lmax) <= TOL_F32
+    assert pos_err(gp, rp) <= TOL_F32
+    # the forward's log-sum-exp output itself
+    from oracle.attn import attention_weights  # noqa: F401  (same edge list as the oracle)
+    hh = cfg.h.astype(np.float64)
+    d = s.C // s.H
+    q = hh[:, 0, :].reshape(cfg.N, s.H, d)
+    ref_lse = np.full((cfg.N, s.H), -np.inf)
+    for i in range(cfg.N):
+        js = cfg.idx[i][cfg.mask[i] != 0]
+        if js.size:
+            logits = (q[i][None] * q[js]).sum(-1) / np.sqrt(d)
+            mx = logits.max(0)
+            ref_lse[i] = mx + np.log(np.exp(logits - mx).sum(0))
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=1e-5)
+
+
+def test_backward_large_sampled(e2f, dev):
+    """Large workload: the upstream gradient lives on a few targets, so the oracle needs only their edges."""
+    cfg = make_config("large")
+    s = cfg.spec
+    rng = np.random.default_rng(9)
+    tg = rng.choice(cfg.N, 24, replace=False)
+    g = np.zeros(cfg.h.shape, np.float32)
+    g[tg] = rng.standard_normal((tg.size,) + cfg.h.shape[1:]).astype(np.float32)
+    say(f"backward large, gradient on {tg.size} targets")
+    gh, gp, _ = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g)
+    mask_t = np.zeros_like(cfg.mask)
+    mask_t[tg] = cfg.mask[tg]
+    rh, rp = oracle_backward(cfg.pos, cfg.h, cfg.idx, mask_t, s.H, s.lmax, g)
+    touched = np.unique(np.concatenate([tg, cfg.idx[tg][cfg.mask[tg] != 0]]))
+    assert block_rel_err(gh[touched], rh[touched], s.lmax) <= TOL_F32
+    assert pos_err(gp[touched], rp[touched]) <= TOL_F32
+    untouched = np.setdiff1d(np.arange(cfg.N), touched)
+    assert np.all(gh[untouched] == 0) and np.all(gp[untouched] == 0)
+
+
+def test_backward_deterministic_and_linear(e2f, dev):
+    cfg = make_config("water")
+    s = cfg.spec
+    say("backward determinism, zero and scaled upstream gradients")
+    g = np.random.default_rng(6).standard_normal(cfg.h.shape).astype(np.float32)
+    a = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g)
+    b = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    c = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g,
+                     targets_in_order=True)
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+    z = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, np.zeros_like(g))
+    assert np.all(z[0] == 0) and np.all(z[1] == 0)
+    two = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, 2 * g)
+    assert np.array_equal(two[0], 2 * a[0]) and np.array_equal(two[1], 2 * a[1])
