@@ -91,6 +91,7 @@ def cpu_baseline(cfg, budget_s=15.0, seed=0):
 
 
 KERNEL_SOURCES = ["interatomic_potentials_amd/csrc/e2f_kernels.hip",
+                  "interatomic_potentials_amd/csrc/e2f_backward.hip",
                   "interatomic_potentials_amd/csrc/e2f_device.hpp",
                   "interatomic_potentials_amd/csrc/e2f_internal.hpp"]
 
@@ -138,7 +139,9 @@ def summarize_profile(pmc_dir, workload, out_path):
     lines = [f"# rocprofv3 summary: {w} workload ({WORKLOADS[w]})", "",
              f"kernel source hash: {kernel_source_hash()}", "",
              "Commands (run from the repository root on the GPU box; TMPDIR=/tmp):", "```"]
-    bench_cmd = "python -u bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline".format(w=w)
+    extra = " --backward" if w == "large" else ""
+    bench_cmd = ("python -u bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline"
+                 "{x}").format(w=w, x=extra)
     lines += [f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/pmc/trace_{w} "
               f"-o run -- {bench_cmd}",
               f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/fetch_{w} -o run "
@@ -193,6 +196,52 @@ def committed_traffic(workload, kernel="e2f::k_aggregate"):
     return float(m.group(1)) if m else None
 
 
+def bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream):
+    """Time e2f_attn_backward (dL/dh, dL/dpos) after a forward that saves m and the lse."""
+    import numpy as np
+    import torch
+
+    s = cfg.spec
+    N, K, S, C, H, E = cfg.N, s.K, cfg.S, s.C, s.H, cfg.nl.n_edges
+    if h.dtype != torch.float32:
+        return {"skipped": "backward is fp32-only"}
+    out, msg, lse = e2f.attn_aggregate(pos, idx, mask, ws, H, s.lmax, C, torch.float32, out=out,
+                                       return_msg=True, return_lse=True)
+    g = torch.randn_like(out)
+    bws = torch.empty(e2f.attn_backward_workspace_bytes(N, K, s.lmax, C, H), dtype=torch.uint8,
+                      device=h.device)
+    gh = torch.empty_like(h)
+    gp = torch.empty_like(pos)
+
+    def run():
+        e2f.attn_backward(pos, h, idx, mask, H, ws, msg, lse, g, bwd_ws=bws, grad_h=gh,
+                          grad_pos=gp)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    row = (S + 1) * C * 4
+    # prep reads G, m, h row 0 and writes q + dm rows; each stream reads one row block per edge
+    # (k + h' for the target pass; q + dm plus lse and D for the source pass) and per atom
+    # its own rows; the source pass also writes grad_h and reads h
+    b_prep = N * (2 * S * C * 4 + C * 4 + row + H * 4 + 12 + 12)
+    b_q = E * row + N * (K * 5 + row + C * 4 + 2 * H * 4)
+    b_src = E * (row + 2 * 4) + N * (row + S * C * 4 + S * C * 4 + C * 4 + 12 + 12)
+    total = b_prep + b_q + b_src
+    print(f"[bench] backward: {ms:.3f} ms, {total / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic",
+          file=sys.stderr, flush=True)
+    return {"ms": ms, "edges_per_s": E / (ms * 1e-3), "algorithmic_bytes": total,
+            "algorithmic_GBps": total / (ms * 1e-3) / 1e9,
+            "bytes_per_edge": 2 * row + 8}
+
+
 def bench_eaas(args, e2f, dev):
     """The EAAS tensor product on its own (e2f_eaas_couple over 2^20 vectors)."""
     import numpy as np
@@ -241,6 +290,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="large", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward pass (dL/dh, dL/dpos) of the same workload")
     ap.add_argument("--index-order-reference", action="store_true",
                     help="also time the aggregate visiting targets in index order (no schedule)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
@@ -387,6 +438,8 @@ def main(argv=None):
             "vmem_path_frac": k2_gbs / VMEM_PATH_PEAK_GBS,
         },
     }
+    if args.backward:
+        result["backward"] = bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, budget_s=args.cpu_budget)

@@ -191,7 +191,7 @@ size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int 
 
 /*
  * e2f_attn_backward -- fp32 storage only (E2F_ERR_UNSUPPORTED for bf16, for
- * N above 2^24 or N K at or above 2^31).
+ * N above 2^24, K above 2048 or N K at or above 2^31).
  *   pos, h, nbr_idx, nbr_mask, scale, path_w: as given to the forward
  *   workspace   the forward's workspace after e2f_attn_precouple (read only)
  *   msg, lse    the forward's out_msg and lse outputs

@@ -16,9 +16,11 @@
 // k_bwd_q     per target, streaming its sorted neighbours: dq
 // k_bwd_src   per source, streaming the targets that list it (reverse list,
 //             sorted): dh', dk, then dh and the step-1 part of dpos
-// The reverse list is a CSR built with a count, a scan and a fill; the
-// per-source sort makes the summation order independent of the fill order
-// for sources listed by up to kRevTile targets.
+// The reverse list is a CSR built with a count, a scan and a fill (atomics
+// aggregated in LDS per group of spatially adjacent targets); the per-source
+// sort makes the summation order independent of the fill order for sources
+// listed by up to kRevTile targets.  Rows are read through buffer resources
+// (32-bit offsets) when the row arrays fit 4 GiB.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a, EaasCoef cf) {
 
 // -------------------------------------------------- target-centric dq
 
-template <int LMAX, int V, int U, int HL>
+template <int LMAX, int V, int U, int HL, bool BUF>
 __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
   constexpr int S = ncomp(LMAX);
   __shared__ int s_nb[kWavesPerBlock][kTile];
@@ -196,6 +198,9 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
   const int64_t N = a.N;
   const int64_t row = (int64_t)(S + 1) * C;
   const int head = cl / (C / a.heads);
+  const uint32_t row_bytes = (uint32_t)(row * 4);
+  const uint32_t cbytes = (uint32_t)C * 4u;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(a.ws, BUF ? (uint32_t)(N * row * 4) : 0u);
 
   float q[V], dm[S][V];
   ld<V>(a.brows + i * row + cl, q);
@@ -227,31 +232,40 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
     }
     sort_list(nb, cnt, lane);
     for (int n0 = 0; n0 < cnt; n0 += P * U) {
-      float kv[U][S + 1][V];
+      Raw<float, V> kv[U][S + 1];
       bool val[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int n = n0 + u * P + sub;
         val[u] = n < cnt;
-        const float* src = a.ws + (int64_t)nb[val[u] ? n : cnt - 1] * row + cl;
+        const int jn = nb[val[u] ? n : cnt - 1];
+        if constexpr (BUF) {
+          const uint32_t voff = (uint32_t)jn * row_bytes + (uint32_t)cl * 4u;
 #pragma unroll
-        for (int r = 0; r <= S; ++r) ld<V>(src + r * C, kv[u][r]);
+          for (int r = 0; r <= S; ++r) buffer_load_raw<float, V>(rsrc, voff, (uint32_t)r * cbytes, kv[u][r]);
+        } else {
+          const float* src = a.ws + (int64_t)jn * row + cl;
+#pragma unroll
+          for (int r = 0; r <= S; ++r) ld<V>(src + r * C, kv[u][r].f);
+        }
       }
+      // keep every neighbour's loads in flight before the first use
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float qk = 0.0f, dp = 0.0f;
 #pragma unroll
-        for (int v = 0; v < V; ++v) qk = fmaf(q[v], kv[u][0][v], qk);
+        for (int v = 0; v < V; ++v) qk = fmaf(q[v], kv[u][0].f[v], qk);
 #pragma unroll
         for (int r = 0; r < S; ++r)
 #pragma unroll
-          for (int v = 0; v < V; ++v) dp = fmaf(dm[r][v], kv[u][r + 1][v], dp);
+          for (int v = 0; v < V; ++v) dp = fmaf(dm[r][v], kv[u][r + 1].f[v], dp);
         qk = head_sum_b<HL>(qk, a.head_lanes);
         dp = head_sum_b<HL>(dp, a.head_lanes);
         const float alpha = val[u] ? exp2_b(qk * a.scale_log2e - L2) : 0.0f;
         const float ds = alpha * (dp - Dv) * a.scale;
 #pragma unroll
-        for (int v = 0; v < V; ++v) dq[v] = fmaf(ds, kv[u][0][v], dq[v]);
+        for (int v = 0; v < V; ++v) dq[v] = fmaf(ds, kv[u][0].f[v], dq[v]);
       }
     }
     wave_sync_b();
@@ -265,7 +279,7 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
 
 // ------------------------------------------ source-centric dh', dk, dh, dpos
 
-template <int LMAX, int V, int U, int HL>
+template <int LMAX, int V, int U, int HL, bool BUF>
 __global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf) {
   constexpr int S = ncomp(LMAX);
   __shared__ int s_nb[kWavesPerBlock][kRevTile];
@@ -283,6 +297,9 @@ __global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf) {
   const int C = a.C;
   const int64_t row = (int64_t)(S + 1) * C;
   const int head = cl / (C / a.heads);
+  const uint32_t row_bytes = (uint32_t)(row * 4);
+  const uint32_t cbytes = (uint32_t)C * 4u;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(a.brows, BUF ? (uint32_t)(a.N * row * 4) : 0u);
 
   float k[V], hp[S][V];
   ld<V>(a.ws + j * row + cl, k);
@@ -303,7 +320,7 @@ __global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf) {
     for (int e = lane; e < cnt; e += 64) nb[e] = a.rev_idx[t0 + e];
     sort_list(nb, cnt, lane);
     for (int n0 = 0; n0 < cnt; n0 += P * U) {
-      float qd[U][S + 1][V];
+      Raw<float, V> qd[U][S + 1];
       float L2[U], Dv[U];
       bool val[U];
 #pragma unroll
@@ -311,31 +328,38 @@ __global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf) {
         const int n = n0 + u * P + sub;
         val[u] = n < cnt;
         const int64_t ti = nb[val[u] ? n : cnt - 1];
-        const float* src = a.brows + ti * row + cl;
+        if constexpr (BUF) {
+          const uint32_t voff = (uint32_t)ti * row_bytes + (uint32_t)cl * 4u;
 #pragma unroll
-        for (int r = 0; r <= S; ++r) ld<V>(src + r * C, qd[u][r]);
+          for (int r = 0; r <= S; ++r) buffer_load_raw<float, V>(rsrc, voff, (uint32_t)r * cbytes, qd[u][r]);
+        } else {
+          const float* src = a.brows + ti * row + cl;
+#pragma unroll
+          for (int r = 0; r <= S; ++r) ld<V>(src + r * C, qd[u][r].f);
+        }
         L2[u] = a.lse[ti * a.heads + head] * 1.4426950408889634f;
         Dv[u] = a.dh[ti * a.heads + head];
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float qk = 0.0f, dp = 0.0f;
 #pragma unroll
-        for (int v = 0; v < V; ++v) qk = fmaf(qd[u][0][v], k[v], qk);
+        for (int v = 0; v < V; ++v) qk = fmaf(qd[u][0].f[v], k[v], qk);
 #pragma unroll
         for (int r = 0; r < S; ++r)
 #pragma unroll
-          for (int v = 0; v < V; ++v) dp = fmaf(qd[u][r + 1][v], hp[r][v], dp);
+          for (int v = 0; v < V; ++v) dp = fmaf(qd[u][r + 1].f[v], hp[r][v], dp);
         qk = head_sum_b<HL>(qk, a.head_lanes);
         dp = head_sum_b<HL>(dp, a.head_lanes);
         const float alpha = val[u] ? exp2_b(qk * a.scale_log2e - L2[u]) : 0.0f;
         const float ds = alpha * (dp - Dv[u]) * a.scale;
 #pragma unroll
-        for (int v = 0; v < V; ++v) dk[v] = fmaf(ds, qd[u][0][v], dk[v]);
+        for (int v = 0; v < V; ++v) dk[v] = fmaf(ds, qd[u][0].f[v], dk[v]);
 #pragma unroll
         for (int r = 0; r < S; ++r)
 #pragma unroll
-          for (int v = 0; v < V; ++v) dhp[r][v] = fmaf(alpha, qd[u][r + 1][v], dhp[r][v]);
+          for (int v = 0; v < V; ++v) dhp[r][v] = fmaf(alpha, qd[u][r + 1].f[v], dhp[r][v]);
       }
     }
     wave_sync_b();
@@ -400,21 +424,71 @@ __global__ __launch_bounds__(256) void k_fill_i32(int64_t n, int32_t* p, int32_t
   if (t < n) p[t] = v;
 }
 
-__global__ __launch_bounds__(256) void k_rev_count(int64_t total, int64_t N, const int32_t* idx,
-                                                   const uint8_t* mask, int32_t* cnt) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= total || mask[t] == 0) return;
-  const int32_t j = idx[t];
-  if (j >= 0 && (int64_t)j < N) atomicAdd(&cnt[j], 1);
+// Reverse-list count and fill, aggregated in LDS.  A 256-thread workgroup
+// takes `per` consecutive targets of the schedule (at most kRevSlots slots);
+// spatially adjacent targets share most sources, so an LDS hash table of
+// (source, count) turns most global atomics into LDS atomics: one global atomic
+// per distinct source per workgroup.  The fill also returns each slot's rank
+// within its source and workgroup, so one atomic per source reserves the
+// workgroup's block of entries.
+constexpr int kRevSlots = 2048;   // slots per workgroup (8 per thread)
+constexpr int kRevHash = 4096;    // hash table entries (load factor <= 1/2)
+
+__device__ inline int rev_hash_insert(int* keys, int* vals, int j, int* rank) {
+  unsigned hh = ((unsigned)j * 2654435761u) >> (32 - 12);
+  while (true) {
+    const int k = atomicCAS(&keys[hh], -1, j);
+    if (k == -1 || k == j) {
+      *rank = atomicAdd(&vals[hh], 1);
+      return (int)hh;
+    }
+    hh = (hh + 1) & (kRevHash - 1);
+  }
 }
 
-__global__ __launch_bounds__(256) void k_rev_fill(int64_t total, int64_t N, int K,
-                                                  const int32_t* idx, const uint8_t* mask,
-                                                  int32_t* cur, int32_t* entries) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= total || mask[t] == 0) return;
-  const int32_t j = idx[t];
-  if (j >= 0 && (int64_t)j < N) entries[atomicAdd(&cur[j], 1)] = (int32_t)(t / K);
+template <bool FILL>
+__global__ __launch_bounds__(256) void k_rev_pass(int64_t N, int K, int per, const int32_t* idx,
+                                                  const uint8_t* mask, const int32_t* sched,
+                                                  int32_t* cnt_or_cur, int32_t* entries) {
+  static_assert(kRevSlots == 256 * 8, "8 slots per thread");
+  __shared__ int keys[kRevHash];
+  __shared__ int vals[kRevHash];
+  __shared__ int base[FILL ? kRevHash : 1];
+  const int t = threadIdx.x;
+  for (int e = t; e < kRevHash; e += 256) {
+    keys[e] = -1;
+    vals[e] = 0;
+  }
+  __syncthreads();
+  const int64_t g0 = (int64_t)blockIdx.x * per;
+  int hs[8], rk[8], tg[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    hs[u] = -1;
+    const int e = t + 256 * u;
+    const int64_t slot_t = g0 + e / K;
+    if (e >= per * K || slot_t >= N) continue;
+    const int64_t i = sched ? (int64_t)sched[slot_t] : slot_t;
+    const int64_t sl = i * K + e % K;
+    if (mask[sl] == 0) continue;
+    const int32_t j = idx[sl];
+    if (j < 0 || (int64_t)j >= N) continue;
+    hs[u] = rev_hash_insert(keys, vals, j, &rk[u]);
+    tg[u] = (int)i;
+  }
+  __syncthreads();
+  for (int e = t; e < kRevHash; e += 256) {
+    if (keys[e] >= 0) {
+      const int b = atomicAdd(&cnt_or_cur[keys[e]], vals[e]);
+      if constexpr (FILL) base[e] = b;
+    }
+  }
+  if constexpr (FILL) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (hs[u] >= 0) entries[base[hs[u]] + rk[u]] = tg[u];
+  }
 }
 
 // exclusive scan, pass 1: each 1024-thread block scans kScanTile elements in place
@@ -483,14 +557,22 @@ int last_err() { return static_cast<int>(hipGetLastError()); }
 
 template <int L, int V, int HL>
 int bwd_go(const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
-  constexpr int U = 2;
+  constexpr int UQ = 4;  // neighbours per subgroup in flight, target pass
+  constexpr int US = 2;  // targets per subgroup in flight, source pass (more live registers)
   const int64_t per_block = (int64_t)kWavesPerBlock * (64 >> a.lane_log);
   const dim3 grid_prep((unsigned)((a.N + per_block - 1) / per_block));
   const int64_t blocks = (a.N + kWavesPerBlock - 1) / kWavesPerBlock;
   const dim3 grid((unsigned)((blocks + kXcds - 1) / kXcds * kXcds));
+  // 32-bit buffer offsets when the row arrays fit 4 GiB
+  const bool buf = a.N * (ncomp(L) + 1) * (int64_t)a.C * 4 < ((int64_t)1 << 32);
   hipLaunchKernelGGL((k_bwd_prep<L, V, HL>), grid_prep, dim3(256), 0, s, a, cf);
-  hipLaunchKernelGGL((k_bwd_q<L, V, U, HL>), grid, dim3(256), 0, s, a);
-  hipLaunchKernelGGL((k_bwd_src<L, V, U, HL>), grid, dim3(256), 0, s, a, cf);
+  if (buf) {
+    hipLaunchKernelGGL((k_bwd_q<L, V, UQ, HL, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, true>), grid, dim3(256), 0, s, a, cf);
+  } else {
+    hipLaunchKernelGGL((k_bwd_q<L, V, UQ, HL, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, false>), grid, dim3(256), 0, s, a, cf);
+  }
   return last_err();
 }
 
@@ -508,19 +590,25 @@ int bwd_l(int V, const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
 
 }  // namespace
 
-int launch_reverse_list(int64_t N, int K, const int32_t* idx, const uint8_t* mask, int32_t* off,
-                        int32_t* cur, int32_t* tile_sums, int32_t* entries, hipStream_t s) {
+int launch_reverse_list(int64_t N, int K, const int32_t* idx, const uint8_t* mask,
+                        const int32_t* sched, int32_t* off, int32_t* cur, int32_t* tile_sums,
+                        int32_t* entries, hipStream_t s) {
   (void)hipGetLastError();
-  const int64_t total = N * (int64_t)K;
-  const unsigned gt = (unsigned)((total + 255) / 256);
   const unsigned gn = (unsigned)((N + 255) / 256);
   const int ntiles = (int)((N + kScanTile - 1) / kScanTile);
+  // targets per workgroup: as many whole rows as fit kRevSlots (rows longer than
+  // that are split over several workgroups by the slot range below)
+  const int per = K <= kRevSlots ? kRevSlots / K : 1;
+  if (K > kRevSlots) return static_cast<int>(hipErrorInvalidValue);
+  const unsigned gr = (unsigned)((N + per - 1) / per);
   hipLaunchKernelGGL(k_fill_i32, dim3(gn), dim3(256), 0, s, N, off, 0);
-  hipLaunchKernelGGL(k_rev_count, dim3(gt), dim3(256), 0, s, total, N, idx, mask, off);
+  hipLaunchKernelGGL(k_rev_pass<false>, dim3(gr), dim3(256), 0, s, N, K, per, idx, mask, sched,
+                     off, (int32_t*)nullptr);
   hipLaunchKernelGGL(k_scan_tiles, dim3((unsigned)ntiles), dim3(1024), 0, s, N, off, tile_sums);
   hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(1024), 0, s, N, ntiles, tile_sums, off);
   hipLaunchKernelGGL(k_scan_fix, dim3(gn), dim3(256), 0, s, N, off, tile_sums, cur);
-  hipLaunchKernelGGL(k_rev_fill, dim3(gt), dim3(256), 0, s, total, N, K, idx, mask, cur, entries);
+  hipLaunchKernelGGL(k_rev_pass<true>, dim3(gr), dim3(256), 0, s, N, K, per, idx, mask, sched,
+                     cur, entries);
   return last_err();
 }
 

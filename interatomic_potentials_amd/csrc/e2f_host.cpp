@@ -436,7 +436,8 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
   if (flags & E2F_VALIDATE_INDICES) return E2F_ERR_SHAPE;  // not offered for the backward
   if (dtype != E2F_F32) return E2F_ERR_UNSUPPORTED;         // fp32 storage only
   if (N == 0) return E2F_OK;
-  if (N > (int64_t)e2f::kScanTile * e2f::kScanTile || N * (int64_t)K >= ((int64_t)1 << 31))
+  if (N > (int64_t)e2f::kScanTile * e2f::kScanTile || N * (int64_t)K >= ((int64_t)1 << 31) ||
+      K > e2f::kRevMaxK)
     return E2F_ERR_UNSUPPORTED;
   if (!pos || !h || !nbr_idx || !nbr_mask || !workspace || !msg || !lse || !grad_out || !grad_h ||
       !grad_pos || !bwd_workspace)
@@ -493,8 +494,8 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
     if (st != E2F_OK) return st;
     a.sched = sc.sched;
   }
-  st = hip_status(e2f::launch_reverse_list(N, K, nbr_idx, nbr_mask, off, cur, tiles, entries,
-                                           stream));
+  st = hip_status(e2f::launch_reverse_list(N, K, nbr_idx, nbr_mask, a.sched, off, cur, tiles,
+                                           entries, stream));
   if (st != E2F_OK) return st;
   const int V = attn_width(C, H, dtype);
   const int d = C / H;

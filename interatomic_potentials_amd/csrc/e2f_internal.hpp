@@ -97,8 +97,10 @@ int launch_validate(int64_t N, int K, const int32_t* idx, const uint8_t* mask, i
                     hipStream_t s);
 int launch_schedule(int64_t N, const float* pos, const SchedScratch& sc, hipStream_t s);
 // reverse neighbour list (CSR by source) and the three backward passes
-int launch_reverse_list(int64_t N, int K, const int32_t* idx, const uint8_t* mask, int32_t* off,
-                        int32_t* cur, int32_t* tile_sums, int32_t* entries, hipStream_t s);
+int launch_reverse_list(int64_t N, int K, const int32_t* idx, const uint8_t* mask,
+                        const int32_t* sched, int32_t* off, int32_t* cur, int32_t* tile_sums,
+                        int32_t* entries, hipStream_t s);
+constexpr int kRevMaxK = 2048;      // longest neighbour row the reverse-list build takes
 int launch_backward(int lmax, int V, const BwdArgs& a, const EaasCoef& cf, hipStream_t s);
 constexpr int kScanTile = 4096;     // elements per block of the generic scan
 constexpr int kRevTile = 1024;      // reverse-list entries sorted per pass
