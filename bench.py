@@ -158,7 +158,10 @@ def summarize_profile(pmc_dir, workload, out_path):
               "## Kernel trace (--kernel-trace --stats)", "",
               "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in stats:
-        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+        name = r["Name"]
+        if len(name) > 200:     # library kernels with long template argument lists
+            name = name.split("<")[0].replace("void ", "").strip() + "<...>"
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                      f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} |")
     lines += ["", "## Counter calibration (plain device copy of "
               f"{CALIB_COPY_MIB} MiB, `__amd_rocclr_copyBuffer`)", "",
