@@ -23,6 +23,15 @@ Readings of what the pages leave open:
   m_i = 0 and out_i = 0.  Repeated indices count once per slot.
 * r_j, r_i are the atoms' own position vectors as passed.
 
+Optional learned projections (``project``).  The gist.science summary (2.2,
+Eq. 6) builds Q and K with SO(3)-invariant scalar projections; the equation
+itself is not printed.  Reading: q_i = h_i[l=0] W_Q and k_j = h_j[l=0] W_K
+with W_Q, W_K [C, C] acting on the channel axis from the right.  For the
+values the pages print no projection; the reading is per-degree channel
+mixing v_j[l] = h_j[l] W_V[l] (W_V [lmax+1, C, C]), the most general linear
+map of irrep features that commutes with rotations (Schur's lemma), applied
+before the pre-coupling: h'_j = v_j (x) R(r_j).
+
 This function materialises logits [E, H] and messages [E, S, C]: it is the
 edge-centric form the pages contrast the fused kernel with.
 """
@@ -37,11 +46,29 @@ from .sh import n_comp
 from .tp import tp_dense
 
 
+def project(h: np.ndarray, w_q: np.ndarray, w_k: np.ndarray, w_v: np.ndarray):
+    """(q [N, C], k [N, C], v [N, S, C]) of the learned projections (reading in the header)."""
+    h = np.asarray(h, dtype=np.float64)
+    N, S, C = h.shape
+    lmax = int(round(S ** 0.5)) - 1
+    w_v = np.asarray(w_v, dtype=np.float64)
+    if w_v.shape != (lmax + 1, C, C):
+        raise ValueError("w_v must be [lmax + 1, C, C]")
+    q = h[:, 0, :] @ np.asarray(w_q, dtype=np.float64)
+    k = h[:, 0, :] @ np.asarray(w_k, dtype=np.float64)
+    v = np.empty_like(h)
+    for l in range(lmax + 1):
+        v[:, l * l:(l + 1) ** 2, :] = h[:, l * l:(l + 1) ** 2, :] @ w_v[l]
+    return q, k, v
+
+
 def attention_weights(h: np.ndarray, nbr_idx: np.ndarray, nbr_mask: np.ndarray, heads: int,
-                      scale: Optional[float] = None, targets: Optional[np.ndarray] = None):
+                      scale: Optional[float] = None, targets: Optional[np.ndarray] = None,
+                      qk: Optional[tuple] = None):
     """Edge list and softmax weights: (e_row, e_src, alpha [E, H]).
 
     e_row indexes the target list, e_src the source atom of each valid slot.
+    ``qk`` = (q [N, C], k [N, C]) replaces the default q = k = h[:, l=0, :].
     """
     h = np.asarray(h, dtype=np.float64)
     N, _, C = h.shape
@@ -63,8 +90,10 @@ def attention_weights(h: np.ndarray, nbr_idx: np.ndarray, nbr_mask: np.ndarray, 
     E = e_src.shape[0]
 
     # invariant per-head logits [E, H]
-    q = h[tgt, 0, :].reshape(T, heads, d)
-    k = h[e_src, 0, :].reshape(E, heads, d)
+    qa, ka = (h[:, 0, :], h[:, 0, :]) if qk is None else (np.asarray(qk[0], dtype=np.float64),
+                                                         np.asarray(qk[1], dtype=np.float64))
+    q = qa[tgt].reshape(T, heads, d)
+    k = ka[e_src].reshape(E, heads, d)
     logits = scale * np.einsum("ehc,ehc->eh", q[e_row], k)
 
     # softmax per (target, head) over that target's valid slots
@@ -79,8 +108,12 @@ def attention_weights(h: np.ndarray, nbr_idx: np.ndarray, nbr_mask: np.ndarray, 
 def attn_forward(pos: np.ndarray, h: np.ndarray, nbr_idx: np.ndarray, nbr_mask: np.ndarray,
                  heads: int, lmax: int, scale: Optional[float] = None,
                  path_w: Optional[np.ndarray] = None, targets: Optional[np.ndarray] = None,
-                 return_msg: bool = False, chunk_edges: int = 1 << 16):
-    """Output [T, S, C] for the given targets (all atoms if None); optionally also m [T, S, C]."""
+                 return_msg: bool = False, chunk_edges: int = 1 << 16,
+                 proj: Optional[tuple] = None):
+    """Output [T, S, C] for the given targets (all atoms if None); optionally also m [T, S, C].
+
+    ``proj`` = (W_Q, W_K, W_V) switches on the learned projections (see ``project``).
+    """
     pos = np.asarray(pos, dtype=np.float64)
     h = np.asarray(h, dtype=np.float64)
     N, S, C = h.shape
@@ -90,12 +123,17 @@ def attn_forward(pos: np.ndarray, h: np.ndarray, nbr_idx: np.ndarray, nbr_mask: 
     tgt = np.arange(N) if targets is None else np.asarray(targets, dtype=np.int64)
     T = tgt.shape[0]
 
-    e_row, e_src, alpha = attention_weights(h, nbr_idx, nbr_mask, heads, scale, tgt)
+    if proj is None:
+        qk, v = None, h
+    else:
+        q, k, v = project(h, *proj)
+        qk = (q, k)
+    e_row, e_src, alpha = attention_weights(h, nbr_idx, nbr_mask, heads, scale, tgt, qk)
     E = e_src.shape[0]
 
     # step 1 on every source that some edge reads
     src, src_inv = np.unique(e_src, return_inverse=True)
-    hp_src = tp_dense(h[src], pos[src], lmax, path_w)           # [n_src, S, C]
+    hp_src = tp_dense(v[src], pos[src], lmax, path_w)           # [n_src, S, C]
 
     # messages alpha_ijh * h'_j, materialised in chunks, summed into m_i
     msg = np.zeros((T, S, C))

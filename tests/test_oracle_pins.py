@@ -385,3 +385,76 @@ def test_masked_slots_ignored_and_empty_rows_zero():
     assert np.all(out[3] == 0.0)
     sub = attn_forward(pos, h, idx, mask, H, lmax, targets=np.array([7, 3, 1]))
     np.testing.assert_array_equal(sub, out[[7, 3, 1]])
+
+
+# ------------------------------------------------------- learned projections
+
+def _torch_mha(x_qk, x_v, idx, mask, heads, w_q, w_k, w_v):
+    """torch's multi-head attention with separate input projections and an identity output map.
+
+    torch's linear maps compute x @ weight.T, so the oracle's right-multiplied weights
+    go in transposed; a transposed operand on the oracle side fails this comparison.
+    """
+    import torch
+    N, C = x_qk.shape
+    adj = np.zeros((N, N), dtype=bool)
+    rows = np.repeat(np.arange(N), idx.shape[1])
+    ok = mask.ravel() != 0
+    adj[rows[ok], idx.ravel()[ok]] = True
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))  # noqa: E731
+    out, _ = torch.nn.functional.multi_head_attention_forward(
+        t(x_qk)[:, None, :], t(x_qk)[:, None, :], t(x_v)[:, None, :], C, heads,
+        in_proj_weight=None, in_proj_bias=None, bias_k=None, bias_v=None, add_zero_attn=False,
+        dropout_p=0.0, out_proj_weight=torch.eye(C, dtype=torch.float64), out_proj_bias=None,
+        training=False, need_weights=False, attn_mask=torch.from_numpy(~adj),
+        use_separate_proj_weight=True, q_proj_weight=t(w_q.T), k_proj_weight=t(w_k.T),
+        v_proj_weight=t(w_v.T))
+    return out[:, 0, :].numpy()
+
+
+def _weights(rng, lmax, C):
+    return (rng.standard_normal((C, C)) / math.sqrt(C), rng.standard_normal((C, C)) / math.sqrt(C),
+            rng.standard_normal((lmax + 1, C, C)) / math.sqrt(C))
+
+
+def test_projections_lmax0_match_torch_mha():
+    rng = np.random.default_rng(26)
+    N, K, C, H = 36, 10, 32, 4
+    pos = rng.standard_normal((N, 3)) * 4
+    h = rng.standard_normal((N, 1, C))
+    idx, mask = _random_graph(rng, N, K)
+    wq, wk, wv = _weights(rng, 0, C)
+    out = attn_forward(pos, h, idx, mask, H, 0, proj=(wq, wk, wv))
+    ref = _torch_mha(h[:, 0, :], h[:, 0, :], idx, mask, H, wq, wk, wv[0])
+    np.testing.assert_allclose(out[:, 0, :], ref, atol=1e-12 * np.abs(ref).max())
+
+
+def test_projections_at_origin_match_torch_mha_per_component():
+    """All atoms at r = 0: each component s is multi-head attention over v = h[:, s] W_V[l(s)]."""
+    rng = np.random.default_rng(27)
+    N, K, C, H, lmax = 30, 9, 16, 2, 2
+    h = rng.standard_normal((N, 9, C))
+    idx, mask = _random_graph(rng, N, K)
+    wq, wk, wv = _weights(rng, lmax, C)
+    out = attn_forward(np.zeros((N, 3)), h, idx, mask, H, lmax, proj=(wq, wk, wv))
+    for s in range(9):
+        l = int(math.isqrt(s))
+        ref = _torch_mha(h[:, 0, :], h[:, s, :], idx, mask, H, wq, wk, wv[l])
+        np.testing.assert_allclose(out[:, s, :], ref, atol=1e-12 * np.abs(ref).max())
+
+
+def test_projections_keep_equivariance_and_identity_weights_change_nothing():
+    rng = np.random.default_rng(28)
+    N, K, C, H, lmax = 24, 8, 16, 2, 2
+    h = rng.standard_normal((N, 9, C))
+    pos = rng.standard_normal((N, 3)) * 3
+    idx, mask = _random_graph(rng, N, K)
+    w = _weights(rng, lmax, C)
+    out = attn_forward(pos, h, idx, mask, H, lmax, proj=w)
+    R = wigner.random_rotation(rng)
+    D = wigner.wigner_d_full(lmax, R)
+    out_r = attn_forward(pos @ R.T, np.einsum("ab,nbc->nac", D, h), idx, mask, H, lmax, proj=w)
+    np.testing.assert_allclose(out_r, np.einsum("ab,nbc->nac", D, out), atol=1e-10 * np.abs(out).max())
+    eye = np.eye(C)
+    same = attn_forward(pos, h, idx, mask, H, lmax, proj=(eye, eye, np.stack([eye] * 3)))
+    np.testing.assert_allclose(same, attn_forward(pos, h, idx, mask, H, lmax), atol=1e-13)
