@@ -53,7 +53,7 @@ def algorithmic_bytes(N, K, E, S, C, b):
     per_edge = (S + 1) * C * b                      # k_j row + S rows of h'_j
     per_target = K * 5 + C * b + S * C * b + 12     # idx + mask row, q_i, out_i, pos_i
     k2 = E * per_edge + N * per_target
-    k1 = N * (S * C * b + (S + 1) * C * b + 12)     # read h, write k + h', read pos
+    k1 = N * (S * C * b + (S + 2) * C * b + 12)     # read h, write k + h' + q, read pos
     return k1, k2, per_edge, per_target
 
 
@@ -92,6 +92,7 @@ def cpu_baseline(cfg, budget_s=15.0, seed=0):
 
 KERNEL_SOURCES = ["interatomic_potentials_amd/csrc/e2f_kernels.hip",
                   "interatomic_potentials_amd/csrc/e2f_backward.hip",
+                  "interatomic_potentials_amd/csrc/e2f_project.hip",
                   "interatomic_potentials_amd/csrc/e2f_device.hpp",
                   "interatomic_potentials_amd/csrc/e2f_internal.hpp"]
 
@@ -245,6 +246,59 @@ def bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream):
             "bytes_per_edge": 2 * row + 8}
 
 
+# published dense peaks of MI355X (TFLOP/s) for the matrix-core dtypes used here
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+
+
+def bench_proj(args, e2f, cfg, pos, h, idx, mask, ws, out, stream):
+    """Learned projections on the matrix cores, fused with the pre-coupling (and the full step)."""
+    import numpy as np
+    import torch
+
+    from gen import proj_weights
+
+    s = cfg.spec
+    N, S, C, H, E = cfg.N, cfg.S, s.C, s.H, cfg.nl.n_edges
+    bf16 = s.dtype == "bf16"
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    b = 2 if bf16 else 4
+    w = tuple(torch.from_numpy(x).to(h.device).to(tdt)
+              for x in proj_weights(s.lmax, C, seed=13, dtype=s.dtype))
+
+    def pre():
+        e2f.attn_precouple(pos, h, ws, proj=w)
+
+    for _ in range(args.warmup):
+        pre()
+        e2f.attn_aggregate(pos, idx, mask, ws, H, s.lmax, C, tdt, out=out)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record(stream)
+        pre()
+        e[1].record(stream)
+        e2f.attn_aggregate(pos, idx, mask, ws, H, s.lmax, C, tdt, out=out)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    step_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
+    flops = 2.0 * N * (S + 2) * C * C                 # S value rows + q + k per atom
+    nbytes = N * (S * C * b + 12 + (S + 2) * C * b) + (s.lmax + 3) * C * C * b  # + weights
+    tflops = flops / (k_ms * 1e-3) / 1e12
+    gbs = nbytes / (k_ms * 1e-3) / 1e9
+    peak = MFMA_PEAK_TFLOPS["bf16" if bf16 else "f32"]
+    mfma_frac, hbm_frac = tflops / peak, gbs / HBM_PEAK_GBS
+    bound = "mfma" if flops / nbytes > peak * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+    print(f"[bench] projected: precouple+projections {k_ms:.3f} ms ({tflops:.1f} TFLOP/s = "
+          f"{mfma_frac:.2f} of MFMA peak, {gbs:.0f} GB/s), step {step_ms:.3f} ms",
+          file=sys.stderr, flush=True)
+    return {"kernel": "k_proj_eaas (projections on MFMA fused with the pre-coupling)",
+            "ms_per_step": step_ms, "edges_per_s": E / (step_ms * 1e-3), "kernel_ms": k_ms,
+            "bound": bound, "flops": flops, "achieved_tflops": tflops, "mfma_peak_tflops": peak,
+            "mfma_frac": mfma_frac, "algorithmic_bytes": nbytes, "achieved_GBps": gbs,
+            "hbm_frac": hbm_frac, "weights": "seeded N(0, 1/C), proj_weights(seed=13)"}
+
+
 def bench_eaas(args, e2f, dev):
     """The EAAS tensor product on its own (e2f_eaas_couple over 2^20 vectors)."""
     import numpy as np
@@ -293,6 +347,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="large", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-proj", action="store_true",
+                    help="skip the learned-projection variant (MFMA) timed after the main step")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward pass (dL/dh, dL/dpos) of the same workload")
     ap.add_argument("--index-order-reference", action="store_true",
@@ -441,6 +497,8 @@ def main(argv=None):
             "vmem_path_frac": k2_gbs / VMEM_PATH_PEAK_GBS,
         },
     }
+    if not args.no_proj:
+        result["projected"] = bench_proj(args, e2f, cfg, pos, h, idx, mask, ws, out, stream)
     if args.backward:
         result["backward"] = bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream)
     if not args.no_cpu_baseline:

@@ -2,8 +2,8 @@
 
 This package is the only code shared by the CPU oracle and the HIP path.  It
 holds no arithmetic of the method itself: it draws positions and irrep
-features, rounds features to bfloat16 storage when asked, and builds padded
-neighbour lists with a k-d tree.  Every array it returns is plain numpy.
+features and projection weights, rounds them to bfloat16 storage when asked,
+and builds padded neighbour lists with a k-d tree.  Every array it returns is plain numpy.
 """
 
 from .configs import (  # noqa: F401
@@ -14,4 +14,5 @@ from .configs import (  # noqa: F401
     make_config,
     make_micro,
     neighbour_list,
+    proj_weights,
 )

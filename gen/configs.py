@@ -277,3 +277,19 @@ def make_micro(B: int = MICRO_B, C: int = 128, lmax: int = 2, seed: int = MICRO_
     r = unit_vectors(rng, B)
     h, bits = features(rng, B, (lmax + 1) ** 2, C, dtype)
     return r, h, bits
+
+
+def proj_weights(lmax: int, C: int, seed: int, dtype: str = "f32"):
+    """Random projection weights (W_Q [C, C], W_K [C, C], W_V [lmax + 1, C, C]), i.i.d.
+    N(0, 1/C) so that projected features keep unit scale; bf16 rounds them (RNE).
+    Returns float32 arrays (already rounded for bf16)."""
+    rng = np.random.default_rng(seed)
+    scale = np.float32(1.0 / np.sqrt(C))
+    ws = [rng.standard_normal((C, C), dtype=np.float32) * scale,
+          rng.standard_normal((C, C), dtype=np.float32) * scale,
+          rng.standard_normal((lmax + 1, C, C), dtype=np.float32) * scale]
+    if dtype == "bf16":
+        ws = [bf16_bits_to_f32(f32_to_bf16_bits(w)) for w in ws]
+    elif dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return tuple(ws)

@@ -118,6 +118,7 @@ int e2f_eaas_couple(hipStream_t stream, int64_t n, int lmax, int C, int dtype,
  *   - the pre-coupled values of step 1, stored per atom as S + 1 rows of C
  *     elements (row 0 = k_j = h_j[l=0, :], rows 1..S = h'_j), so that each
  *     neighbour's K and V are one contiguous (S + 1) * C * sizeof(T) block;
+ *   - the query rows q_i, N rows of C elements (h_i[l=0, :]);
  *   - 256 bytes for the validation flag;
  *   - the target schedule scratch (order and cell per atom, 2^15 cell
  *     counts, bounding-box partials): 8 N bytes plus about 140 KiB.
@@ -134,6 +135,27 @@ int e2f_attn_precouple(hipStream_t stream, int64_t N, int lmax, int C, int dtype
                        void* workspace, size_t ws_bytes);
 
 /*
+ * e2f_attn_precouple_proj -- step 1 with learned projections, the queries and
+ * keys as invariant scalar projections (gist.science summary of arXiv
+ * 2601.16622, technical summary 2.2, Eq. 6) and the values mixed per degree:
+ *   q_i = h_i[l=0] W_Q,  k_i = h_i[l=0] W_K,  v_i[l] = h_i[l] W_V[l],
+ *   h'_i = v_i (x) R(pos_i)   (EAAS, write-up section 2),
+ * written to the same workspace layout, so e2f_attn_aggregate follows as
+ * without projections.  The products run on the matrix cores (MFMA) with
+ * fp32 accumulation.
+ *   w_q, w_k  [C, C] device arrays of the storage type, row-major
+ *             [C_in, C_out], applied from the right
+ *   w_v       [lmax + 1, C, C] device array, one matrix per degree
+ * Supported C: 16, 32, 64, 128 (fp32) and 32, 64, 128 (bf16); other C give
+ * E2F_ERR_UNSUPPORTED.  Weights must be 16-byte aligned and must not overlap
+ * the workspace.
+ */
+int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int dtype,
+                            const float* pos, const void* h, const void* w_q, const void* w_k,
+                            const void* w_v, const float* path_w, void* workspace,
+                            size_t ws_bytes);
+
+/*
  * e2f_attn_aggregate -- steps 2 and 3 (write-up sections 3.1-3.2): one
  * wavefront per target streams its valid slots once, computes the per-head
  * logits, keeps a running max and normaliser (online softmax) and fp32
@@ -148,7 +170,7 @@ int e2f_attn_precouple(hipStream_t stream, int64_t N, int lmax, int C, int dtype
  *   nbr_mask  [N, K] uint8   any pattern; valid slots need not come first;
  *                            repeated indices count once per slot
  *   scale     logit scale; <= 0 selects 1 / sqrt(C / H)
- *   workspace filled by e2f_attn_precouple; its schedule scratch (and, under
+ *   workspace filled by e2f_attn_precouple (or _proj); its schedule scratch (and, under
  *             E2F_VALIDATE_INDICES, its flag) is rewritten here, hence not
  *             const.  Targets are visited in Morton order of their
  *             positions (built on the GPU each call unless
@@ -174,6 +196,13 @@ int e2f_attn_forward(hipStream_t stream, int64_t N, int K, int lmax, int C, int 
                      void* workspace, size_t ws_bytes, void* out, void* out_msg, float* lse,
                      uint32_t flags);
 
+/* e2f_attn_forward_proj -- e2f_attn_precouple_proj then e2f_attn_aggregate. */
+int e2f_attn_forward_proj(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
+                          const float* pos, const void* h, const void* w_q, const void* w_k,
+                          const void* w_v, const int32_t* nbr_idx, const uint8_t* nbr_mask,
+                          float scale, const float* path_w, void* workspace, size_t ws_bytes,
+                          void* out, void* out_msg, float* lse, uint32_t flags);
+
 /*
  * Backward pass (vector-Jacobian product) of the attention, for forces as
  * derivatives of an energy with respect to positions (the write-up's
@@ -193,7 +222,8 @@ size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int 
  * e2f_attn_backward -- fp32 storage only (E2F_ERR_UNSUPPORTED for bf16, for
  * N above 2^24, K above 2048 or N K at or above 2^31).
  *   pos, h, nbr_idx, nbr_mask, scale, path_w: as given to the forward
- *   workspace   the forward's workspace after e2f_attn_precouple (read only)
+ *   workspace   the forward's workspace after e2f_attn_precouple (read only;
+ *               the layer without projections is differentiated)
  *   msg, lse    the forward's out_msg and lse outputs
  *   grad_out    [N, S, C] fp32  dL/d out
  *   grad_h      [N, S, C] fp32  dL/dh (written)

@@ -49,6 +49,10 @@ SIGNATURES = {
     "e2f_eaas_couple": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "e2f_attn_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
     "e2f_attn_precouple": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz]),
+    "e2f_attn_precouple_proj": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _sz]),
+    "e2f_attn_forward_proj": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                     _vp, _vp, _vp, _f32, _vp, _vp, _sz, _vp, _vp, _vp, _u32]),
     "e2f_attn_aggregate": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _f32,
                                   _vp, _vp, _sz, _vp, _vp, _vp, _u32]),
     "e2f_attn_forward": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
@@ -204,8 +208,26 @@ def _new_workspace(N, lmax, C, dt, device):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def attn_precouple(pos, h, ws=None, path_w=None):
-    """Step 1 into the workspace (allocated here if not given); returns it."""
+def _proj_weights(proj, h, lmax):
+    """(w_q, w_k, w_v) as device tensors of h's dtype: [C, C], [C, C], [lmax + 1, C, C]."""
+    if proj is None:
+        return None
+    w_q, w_k, w_v = proj
+    C = h.shape[2]
+    for t, name, shape in ((w_q, "w_q", (C, C)), (w_k, "w_k", (C, C)),
+                           (w_v, "w_v", (lmax + 1, C, C))):
+        _dev(t, name, h.dtype)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+    return w_q, w_k, w_v
+
+
+def attn_precouple(pos, h, ws=None, path_w=None, proj=None):
+    """Step 1 into the workspace (allocated here if not given); returns it.
+
+    ``proj`` = (w_q, w_k, w_v) adds the learned projections (q = h[l=0] w_q,
+    k = h[l=0] w_k, v[l] = h[l] w_v[l] before the coupling) on the matrix cores.
+    """
     torch = _torch()
     _dev(pos, "pos", torch.float32)
     _dev(h, "h")
@@ -216,8 +238,16 @@ def attn_precouple(pos, h, ws=None, path_w=None):
         ws = _new_workspace(N, lmax, C, dt, h.device)
     _dev(ws, "ws")
     pw = _path_w(path_w, h.device)
-    _check(lib.e2f_attn_precouple(_stream(h), N, lmax, C, dt, _ptr(pos), _ptr(h), _ptr(pw),
-                                  _ptr(ws), ws.numel() * ws.element_size()), "e2f_attn_precouple")
+    w = _proj_weights(proj, h, lmax)
+    if w is None:
+        _check(lib.e2f_attn_precouple(_stream(h), N, lmax, C, dt, _ptr(pos), _ptr(h), _ptr(pw),
+                                      _ptr(ws), ws.numel() * ws.element_size()),
+               "e2f_attn_precouple")
+    else:
+        _check(lib.e2f_attn_precouple_proj(_stream(h), N, lmax, C, dt, _ptr(pos), _ptr(h),
+                                           _ptr(w[0]), _ptr(w[1]), _ptr(w[2]), _ptr(pw), _ptr(ws),
+                                           ws.numel() * ws.element_size()),
+               "e2f_attn_precouple_proj")
     return ws
 
 
@@ -255,10 +285,11 @@ def attn_aggregate(pos, nbr_idx, nbr_mask, ws, heads: int, lmax: int, C: int, dt
 def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] = None,
                  path_w=None, ws=None, out=None, return_msg: bool = False,
                  validate: bool = False, targets_in_order: bool = False,
-                 return_lse: bool = False):
+                 return_lse: bool = False, proj=None):
     """Full path (steps 1-3): pos [N,3] fp32, h [N,S,C], nbr_idx [N,K] int32, nbr_mask [N,K] uint8.
 
     Returns out, or (out[, m][, lse]) when return_msg / return_lse ask for them.
+    ``proj`` = (w_q, w_k, w_v) adds the learned projections (see attn_precouple).
     """
     torch = _torch()
     _dev(pos, "pos", torch.float32)
@@ -278,10 +309,20 @@ def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] =
     msg = torch.empty_like(h) if return_msg else None
     lse = torch.empty((N, heads), dtype=torch.float32, device=h.device) if return_lse else None
     pw = _path_w(path_w, h.device)
-    _check(lib.e2f_attn_forward(_stream(h), N, K, lmax, C, heads, dt, _ptr(pos), _ptr(h),
-                                _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0), _ptr(pw),
-                                _ptr(ws), ws.numel() * ws.element_size(), _ptr(out), _ptr(msg),
-                                _ptr(lse), _flags(validate, targets_in_order)), "e2f_attn_forward")
+    w = _proj_weights(proj, h, lmax)
+    if w is None:
+        _check(lib.e2f_attn_forward(_stream(h), N, K, lmax, C, heads, dt, _ptr(pos), _ptr(h),
+                                    _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0), _ptr(pw),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _ptr(out), _ptr(msg),
+                                    _ptr(lse), _flags(validate, targets_in_order)),
+               "e2f_attn_forward")
+    else:
+        _check(lib.e2f_attn_forward_proj(_stream(h), N, K, lmax, C, heads, dt, _ptr(pos), _ptr(h),
+                                         _ptr(w[0]), _ptr(w[1]), _ptr(w[2]), _ptr(nbr_idx),
+                                         _ptr(nbr_mask), float(scale or 0.0), _ptr(pw), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _ptr(out), _ptr(msg),
+                                         _ptr(lse), _flags(validate, targets_in_order)),
+               "e2f_attn_forward_proj")
     return _results(out, msg, lse)
 
 

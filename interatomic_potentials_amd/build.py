@@ -35,6 +35,7 @@ DEVICE = ["-x", "hip", f"--offload-arch={ARCH}",
 SOURCES = [
     ("e2f_kernels.hip", True),
     ("e2f_backward.hip", True),
+    ("e2f_project.hip", True),
     ("e2f_host.cpp", False),
 ]
 

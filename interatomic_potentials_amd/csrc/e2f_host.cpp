@@ -128,8 +128,18 @@ int attn_width(int C, int H, int dt) {
   return 0;
 }
 
-size_t ws_body_bytes(int64_t N, int lmax, int C, int dt) {
+// workspace: [rows [N, S + 1, C]: k, h'][query rows [N, C]][256 B validation flag]
+//            [schedule scratch], every part 256-byte aligned
+size_t ws_rows_bytes(int64_t N, int lmax, int C, int dt) {
   return round256((size_t)N * (size_t)(ncomp(lmax) + 1) * (size_t)C * esize(dt));
+}
+
+size_t ws_body_bytes(int64_t N, int lmax, int C, int dt) {
+  return ws_rows_bytes(N, lmax, C, dt) + round256((size_t)N * (size_t)C * esize(dt));
+}
+
+void* ws_query_rows(void* ws, int64_t N, int lmax, int C, int dt) {
+  return static_cast<char*>(ws) + ws_rows_bytes(N, lmax, C, dt);
 }
 
 // Morton bits per axis of the target schedule: about one cell per atom, at most 2^15 cells
@@ -173,7 +183,6 @@ BwdLayout bwd_layout(int64_t N, int K, int lmax, int C, int H) {
   return L;
 }
 
-// layout: [pre-coupled rows][256 B validation flag][schedule scratch]
 e2f::SchedScratch sched_scratch(void* ws, int64_t N, int lmax, int C, int dt) {
   char* p = static_cast<char*>(ws) + ws_body_bytes(N, lmax, C, dt) + 256;
   e2f::SchedScratch sc;
@@ -210,6 +219,7 @@ int precouple_impl(hipStream_t stream, int64_t N, int lmax, int C, int dt, const
   a.r = pos;
   a.h_in = h;
   a.h_out = ws;
+  a.q_out = ws_query_rows(ws, N, lmax, C, dt);
   a.n = N;
   a.C = C;
   const int lanes = (C + V - 1) / V;
@@ -250,6 +260,7 @@ int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
   a.idx = idx;
   a.mask = mask;
   a.ws = ws;
+  a.q = ws_query_rows(ws, N, lmax, C, dt);
   a.out = out;
   a.out_msg = out_msg;
   a.N = N;
@@ -314,6 +325,7 @@ int e2f_eaas_couple(hipStream_t stream, int64_t n, int lmax, int C, int dtype, c
   a.r = r;
   a.h_in = h_in;
   a.h_out = h_out;
+  a.q_out = nullptr;
   a.n = n;
   a.C = C;
   const int lanes = (C + V - 1) / V;
@@ -377,10 +389,46 @@ int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, in
                         workspace, out, out_msg, lse, flags);
 }
 
-int e2f_attn_forward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
-                     const float* pos, const void* h, const int32_t* nbr_idx,
-                     const uint8_t* nbr_mask, float scale, const float* path_w, void* workspace,
-                     size_t ws_bytes, void* out, void* out_msg, float* lse, uint32_t flags) {
+}  // extern "C"
+
+namespace {
+
+// weights of the projected variants: present, aligned, a supported C, and
+// clear of the workspace
+int check_proj(int lmax, int C, int dtype, const void* w_q, const void* w_k, const void* w_v,
+               const void* workspace, size_t need) {
+  if (!w_q || !w_k || !w_v) return E2F_ERR_NULL;
+  if (!aligned(w_q, 16) || !aligned(w_k, 16) || !aligned(w_v, 16)) return E2F_ERR_ALIGN;
+  if (!e2f::proj_supported(C, dtype)) return E2F_ERR_UNSUPPORTED;
+  const size_t wb = (size_t)C * C * esize(dtype);
+  if (overlap({workspace, need}, {w_q, wb}) || overlap({workspace, need}, {w_k, wb}) ||
+      overlap({workspace, need}, {w_v, (size_t)(lmax + 1) * wb}))
+    return E2F_ERR_ALIAS;
+  return E2F_OK;
+}
+
+int precouple_proj_impl(hipStream_t stream, int64_t N, int lmax, int C, int dt, const float* pos,
+                        const void* h, const void* w_q, const void* w_k, const void* w_v,
+                        const float* path_w, void* ws) {
+  e2f::ProjArgs a;
+  a.r = pos;
+  a.h = h;
+  a.w_q = w_q;
+  a.w_k = w_k;
+  a.w_v = w_v;
+  a.ws = ws;
+  a.q_out = ws_query_rows(ws, N, lmax, C, dt);
+  a.n = N;
+  const EaasCoef cf = make_coef(lmax, path_w);
+  return hip_status(e2f::launch_proj(lmax, dt, C, a, cf, stream));
+}
+
+// e2f_attn_forward and e2f_attn_forward_proj (w_q == nullptr: no projections)
+int forward_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
+                 const float* pos, const void* h, const void* w_q, const void* w_k,
+                 const void* w_v, const int32_t* nbr_idx, const uint8_t* nbr_mask, float scale,
+                 const float* path_w, void* workspace, size_t ws_bytes, void* out, void* out_msg,
+                 float* lse, uint32_t flags, bool proj) {
   int st = check_attn_shape(N, K, lmax, C, H, dtype, flags);
   if (st != E2F_OK) return st;
   if (N == 0) return E2F_OK;
@@ -414,10 +462,61 @@ int e2f_attn_forward(hipStream_t stream, int64_t N, int K, int lmax, int C, int 
   if (lse && (overlap({lse, lb}, {out, hb}) || (out_msg && overlap({lse, lb}, {out_msg, hb}))))
     return E2F_ERR_ALIAS;
   if (overlap({workspace, need}, {pos, (size_t)N * 12})) return E2F_ERR_ALIAS;
-  st = precouple_impl(stream, N, lmax, C, dtype, pos, h, path_w, workspace, ws_bytes);
+  if (proj) {
+    st = check_proj(lmax, C, dtype, w_q, w_k, w_v, workspace, need);
+    if (st != E2F_OK) return st;
+    st = precouple_proj_impl(stream, N, lmax, C, dtype, pos, h, w_q, w_k, w_v, path_w,
+                             workspace);
+  } else {
+    st = precouple_impl(stream, N, lmax, C, dtype, pos, h, path_w, workspace, ws_bytes);
+  }
   if (st != E2F_OK) return st;
   return aggregate_impl(stream, N, K, lmax, C, H, dtype, pos, nbr_idx, nbr_mask, scale, path_w,
                         workspace, out, out_msg, lse, flags);
+}
+
+}  // namespace
+
+extern "C" {
+
+int e2f_attn_forward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
+                     const float* pos, const void* h, const int32_t* nbr_idx,
+                     const uint8_t* nbr_mask, float scale, const float* path_w, void* workspace,
+                     size_t ws_bytes, void* out, void* out_msg, float* lse, uint32_t flags) {
+  return forward_impl(stream, N, K, lmax, C, H, dtype, pos, h, nullptr, nullptr, nullptr,
+                      nbr_idx, nbr_mask, scale, path_w, workspace, ws_bytes, out, out_msg, lse,
+                      flags, false);
+}
+
+int e2f_attn_forward_proj(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
+                          const float* pos, const void* h, const void* w_q, const void* w_k,
+                          const void* w_v, const int32_t* nbr_idx, const uint8_t* nbr_mask,
+                          float scale, const float* path_w, void* workspace, size_t ws_bytes,
+                          void* out, void* out_msg, float* lse, uint32_t flags) {
+  return forward_impl(stream, N, K, lmax, C, H, dtype, pos, h, w_q, w_k, w_v, nbr_idx, nbr_mask,
+                      scale, path_w, workspace, ws_bytes, out, out_msg, lse, flags, true);
+}
+
+int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int dtype,
+                            const float* pos, const void* h, const void* w_q, const void* w_k,
+                            const void* w_v, const float* path_w, void* workspace,
+                            size_t ws_bytes) {
+  int st = check_shape_common(N, lmax, C, dtype);
+  if (st != E2F_OK) return st;
+  if (N == 0) return E2F_OK;
+  if (!pos || !h || !workspace) return E2F_ERR_NULL;
+  if (!aligned(pos, 4) || !aligned(h, 16) || !aligned(workspace, 16) ||
+      (path_w && !aligned(path_w, 4)))
+    return E2F_ERR_ALIGN;
+  const size_t need = e2f_attn_workspace_bytes(N, lmax, C, dtype);
+  if (ws_bytes < need) return E2F_ERR_WORKSPACE;
+  const size_t hb = (size_t)N * ncomp(lmax) * C * esize(dtype);
+  if (overlap({workspace, need}, {h, hb}) || overlap({workspace, need}, {pos, (size_t)N * 12}))
+    return E2F_ERR_ALIAS;
+  st = check_proj(lmax, C, dtype, w_q, w_k, w_v, workspace, need);
+  if (st != E2F_OK) return st;
+  return precouple_proj_impl(stream, N, lmax, C, dtype, pos, h, w_q, w_k, w_v, path_w,
+                             workspace);
 }
 
 size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int H, int dtype) {

@@ -36,6 +36,7 @@ struct EaasArgs {
   const float* r;      // [n, 3]
   const void* h_in;    // [n, S, C]
   void* h_out;         // [n, S, C] or workspace [n, S + 1, C]
+  void* q_out;         // workspace mode: query rows [n, C] (a copy of the l = 0 row)
   int64_t n;
   int C;
   int lane_log;        // log2 of the lanes serving one atom (power of two <= 64)
@@ -46,6 +47,7 @@ struct AggArgs {
   const int32_t* idx;      // [N, K]
   const uint8_t* mask;     // [N, K]
   const void* ws;          // [N, S + 1, C]: row 0 = k, rows 1..S = h'
+  const void* q;           // [N, C] query rows
   void* out;               // [N, S, C]
   void* out_msg;           // [N, S, C] or nullptr
   int64_t N;
@@ -87,11 +89,28 @@ struct BwdArgs {
   float scale_log2e;
 };
 
+// Learned projections fused with the pre-coupling (storage type T for h and
+// the weights, row-major [C_in, C_out] matrices applied from the right).
+struct ProjArgs {
+  const float* r;          // [n, 3]
+  const void* h;           // [n, S, C]
+  const void* w_q;         // [C, C]
+  const void* w_k;         // [C, C]
+  const void* w_v;         // [lmax + 1, C, C]
+  void* ws;                // workspace rows [n, S + 1, C]: k, then h' = (h W_V) (x) R(r)
+  void* q_out;             // [n, C] query rows h[l=0] W_Q
+  int64_t n;
+};
+constexpr int kProjTileAtoms = 16;  // atoms per MFMA row tile
+
 // launchers (kernels file); return 0 or a hipError_t value
 int launch_eaas(int lmax, int dtype, int V, bool to_workspace, const EaasArgs& a,
                 const EaasCoef& cf, hipStream_t s);
 int launch_aggregate(int lmax, int dtype, int V, const AggArgs& a, const EaasCoef& cf,
                      hipStream_t s);
+// fused projection + pre-coupling; C in {16, 32, 64, 128} (fp32) or {32, 64, 128} (bf16)
+bool proj_supported(int C, int dtype);
+int launch_proj(int lmax, int dtype, int C, const ProjArgs& a, const EaasCoef& cf, hipStream_t s);
 int launch_frames(int lmax, int64_t n, const float* r, float* Q, float* D, hipStream_t s);
 int launch_validate(int64_t N, int K, const int32_t* idx, const uint8_t* mask, int32_t* flag,
                     hipStream_t s);

@@ -5,7 +5,8 @@
 //              of every irrep row; rows are read and written as one coalesced
 //              vector access per lane.  In workspace mode it also copies the
 //              l = 0 row (the key) in front of h', so that a neighbour's K and
-//              V form one contiguous block for the stream below.
+//              V form one contiguous block for the stream below, and into the
+//              query rows.
 // k_aggregate  steps 2 and 3 (write-up section 3; gist.science summary 2.2):
 //              one wavefront per target, targets taken in a spatial schedule.
 //              The valid slots of the target's row are compacted into LDS
@@ -91,7 +92,10 @@ __global__ __launch_bounds__(256) void k_eaas(EaasArgs a, EaasCoef cf) {
     float x[S][V];
 #pragma unroll
     for (int s = 0; s < S; ++s) VecIO<T, V>::load(src + s * C + c0, x[s]);
-    if constexpr (WS) VecIO<T, V>::store(dst + c0, x[0]);
+    if constexpr (WS) {
+      VecIO<T, V>::store(dst + c0, x[0]);
+      VecIO<T, V>::store(static_cast<T*>(a.q_out) + atom * C + c0, x[0]);
+    }
     float y[S][V];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
 
   float q[V];
   if (act) {
-    VecIO<T, V>::load(ws + i * row + c0, q);
+    VecIO<T, V>::load(static_cast<const T*>(a.q) + i * C + c0, q);
   } else {
 #pragma unroll
     for (int v = 0; v < V; ++v) q[v] = 0.0f;

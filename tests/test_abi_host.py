@@ -72,15 +72,16 @@ def _r256(b):
 
 
 def _expected_ws(N, lmax, C, esize):
-    """Documented layout: rows | 256 B flag | order + cells (4N each) | cell counts | bbox partials."""
+    """Documented layout: rows | query rows | 256 B flag | order + cells (4N each) | cell counts |
+    bbox partials."""
     sched = 2 * _r256(4 * N) + _r256(4 * 2 ** 15) + _r256(256 * 6 * 4)
-    return _r256(N * ((lmax + 1) ** 2 + 1) * C * esize) + 256 + sched
+    return _r256(N * ((lmax + 1) ** 2 + 1) * C * esize) + _r256(N * C * esize) + 256 + sched
 
 
 def test_workspace_bytes():
     wb = lib.e2f_attn_workspace_bytes
     assert wb(32768, 2, 128, 0) == _expected_ws(32768, 2, 128, 4)
-    assert wb(32768, 2, 128, 0) - 32768 * 10 * 128 * 4 - 256 < 2 ** 20   # scratch is small
+    assert wb(32768, 2, 128, 0) - 32768 * 11 * 128 * 4 - 256 < 2 ** 20   # scratch is small
     assert wb(100000, 2, 128, 1) == _expected_ws(100000, 2, 128, 2)
     assert wb(3, 1, 5, 0) == _expected_ws(3, 1, 5, 4)          # 300 B of rows round up to 512
     assert wb(0, 2, 128, 0) == _expected_ws(0, 2, 128, 4)
@@ -225,3 +226,39 @@ def test_backward_argument_errors():
     assert _bwd(gh=fake(9)) == C["E2F_ERR_ALIAS"]             # grad_h over h
     assert _bwd(gp=fake(12)) == C["E2F_ERR_ALIAS"]            # grad_pos over grad_out
     assert _bwd(bws=fake(13)) == C["E2F_ERR_ALIAS"]           # scratch over grad_h
+
+
+def _pproj(**kw):
+    a = dict(stream=None, N=1000, lmax=2, C=128, dt=0, pos=fake(1), h=fake(2), wq=fake(20),
+             wk=fake(21), wv=fake(22), pw=None, ws=fake(4), ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.e2f_attn_precouple_proj(a["stream"], a["N"], a["lmax"], a["C"], a["dt"], a["pos"],
+                                       a["h"], a["wq"], a["wk"], a["wv"], a["pw"], a["ws"],
+                                       a["ws_bytes"])
+
+
+def _fproj(**kw):
+    a = dict(stream=None, N=1000, K=64, lmax=2, C=128, H=16, dt=0, pos=fake(1), h=fake(9),
+             wq=fake(20), wk=fake(21), wv=fake(22), idx=fake(2), mask=fake(3), scale=0.0, pw=None,
+             ws=fake(4), ws_bytes=1 << 30, out=fake(8), msg=None, lse=None, flags=0)
+    a.update(kw)
+    return lib.e2f_attn_forward_proj(a["stream"], a["N"], a["K"], a["lmax"], a["C"], a["H"],
+                                     a["dt"], a["pos"], a["h"], a["wq"], a["wk"], a["wv"],
+                                     a["idx"], a["mask"], a["scale"], a["pw"], a["ws"],
+                                     a["ws_bytes"], a["out"], a["msg"], a["lse"], a["flags"])
+
+
+@pytest.mark.parametrize("fn", [_pproj, _fproj])
+def test_projection_argument_errors(fn):
+    assert fn(N=0, pos=None, h=None) == C["E2F_OK"]
+    assert fn(wq=None) == C["E2F_ERR_NULL"]
+    assert fn(wk=None) == C["E2F_ERR_NULL"]
+    assert fn(wv=None) == C["E2F_ERR_NULL"]
+    assert fn(wv=ctypes.c_void_p(BASE + 22 * 64 * MB + 4)) == C["E2F_ERR_ALIGN"]
+    assert fn(ws_bytes=100) == C["E2F_ERR_WORKSPACE"]
+    assert fn(wk=fake(4)) == C["E2F_ERR_ALIAS"]                  # weights inside the workspace
+    assert fn(dt=7) == C["E2F_ERR_DTYPE"]
+    assert fn(lmax=3) == C["E2F_ERR_SHAPE"]
+    # MFMA tiles: C in {16, 32, 64, 128} for fp32, {32, 64, 128} for bf16
+    assert fn(C=96, **({"H": 12} if fn is _fproj else {})) == C["E2F_ERR_UNSUPPORTED"]
+    assert fn(C=16, dt=1, **({"H": 2} if fn is _fproj else {})) == C["E2F_ERR_UNSUPPORTED"]

@@ -218,6 +218,9 @@ def test_aggregate_with_given_values(e2f, dev):
     ws_np[:, 0, :] = cfg.h[:, 0, :]
     ws = torch.zeros(e2f.attn_workspace_bytes(N, s.lmax, C), dtype=torch.uint8, device=dev)
     ws[: ws_np.nbytes].copy_(T(ws_np.view(np.uint8).reshape(-1), dev))
+    q_np = np.ascontiguousarray(cfg.h[:, 0, :], dtype=np.float32)   # query rows after the k/v rows
+    qoff = (ws_np.nbytes + 255) // 256 * 256
+    ws[qoff: qoff + q_np.nbytes].copy_(T(q_np.view(np.uint8).reshape(-1), dev))
     out, msg = e2f.attn_aggregate(T(cfg.pos, dev), T(cfg.idx, dev), T(cfg.mask, dev), ws, s.H,
                                   s.lmax, C, torch.float32, return_msg=True)
     m = msg.cpu().numpy()
