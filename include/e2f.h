@@ -242,6 +242,50 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
                       void* bwd_workspace, size_t bwd_ws_bytes, uint32_t flags);
 
 /*
+ * Padded neighbour lists, built on the GPU: the list that the attention
+ * streams (write-up section 3.2: padded slots plus a mask, masked slots
+ * skipped; section 5.1: the edge cutoff).  The pages leave the list itself
+ * open; this is the definition the library implements:
+ *   - the neighbours of atom i are the atoms j != i with d2_ij < cutoff^2,
+ *     where d2_ij = (dx*dx + dy*dy) + dz*dz with (dx, dy, dz) = pos_i - pos_j,
+ *     all in float64 from the float32 positions, every operation rounded
+ *     once (no fused multiply-add), cutoff^2 = cutoff * cutoff in float64
+ *     (a strict cutoff; open boundaries: no periodic images);
+ *   - row i lists them by increasing (d2_ij, j) -- nearest first, equal
+ *     distances by atom index -- and keeps the first K: slots [0, k_i) hold
+ *     them with mask 1, k_i = min(K, count); slots [k_i, K) hold index -1
+ *     and mask 0.
+ * The rows are therefore unique (bit-reproducible), whatever order the
+ * builder meets the candidates in.
+ *
+ * e2f_neighbour_workspace_bytes -- scratch bytes for N atoms (cell grid,
+ * grouped atoms and their positions: about 24 N bytes plus the cell
+ * table); 0 when N < 0 or N > 2^30.
+ */
+size_t e2f_neighbour_workspace_bytes(int64_t N);
+
+/*
+ * e2f_neighbour_list -- build the rows above with a cell list: cells no
+ * smaller than the cutoff, numbered in Morton order; atoms grouped by cell;
+ * one wavefront per target scans the 27 cells around its own.
+ *   cutoff     > 0, finite (angstrom, like the positions); E2F_ERR_SHAPE
+ *              otherwise
+ *   pos        [N, 3] fp32 device array
+ *   nbr_idx    [N, K] int32 (written)
+ *   nbr_mask   [N, K] uint8 (written)
+ *   n_within   [N] int32 or NULL: the count before truncation to K
+ *   order      [N] int32 or NULL: every atom once, grouped by cell in
+ *              Morton order of the cells (a spatially coherent ordering;
+ *              the order within a cell is unspecified)
+ *   workspace  device scratch of e2f_neighbour_workspace_bytes(N)
+ * K ranges over 1..1984 (E2F_ERR_SHAPE below, E2F_ERR_UNSUPPORTED above);
+ * N over 0..2^30.  Outputs may not overlap each other, pos or the workspace.
+ */
+int e2f_neighbour_list(hipStream_t stream, int64_t N, int K, double cutoff, const float* pos,
+                       int32_t* nbr_idx, uint8_t* nbr_mask, int32_t* n_within, int32_t* order,
+                       void* workspace, size_t ws_bytes);
+
+/*
  * e2f_frames -- test hook: the alignment rotation Q (Q r_hat = z_hat, write-up
  * section 2.1) and the Wigner-D blocks D^l(Q), l = 0..lmax, exactly as the
  * kernels build them.

@@ -19,7 +19,8 @@ from typing import Optional
 __all__ = [
     "E2FError", "lib", "status_string", "path_count", "eaas_couple", "attn_workspace_bytes",
     "attn_precouple", "attn_aggregate", "attn_forward", "attn_backward",
-    "attn_backward_workspace_bytes", "frames", "F32", "BF16",
+    "attn_backward_workspace_bytes", "neighbour_workspace_bytes", "neighbour_list", "frames",
+    "F32", "BF16",
     "VALIDATE_INDICES", "TARGETS_IN_ORDER",
 ]
 
@@ -60,6 +61,9 @@ SIGNATURES = {
     "e2f_attn_backward_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32]),
     "e2f_attn_backward": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                  _f32, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _u32]),
+    "e2f_neighbour_workspace_bytes": (_sz, [_i64]),
+    "e2f_neighbour_list": (_i32, [_vp, _i64, _i32, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _sz]),
     "e2f_frames": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp]),
 }
 
@@ -363,6 +367,38 @@ def attn_backward(pos, h, nbr_idx, nbr_mask, heads: int, ws, msg, lse, grad_out,
                                  TARGETS_IN_ORDER if targets_in_order else 0),
            "e2f_attn_backward")
     return grad_h, grad_pos
+
+
+def neighbour_workspace_bytes(N: int) -> int:
+    return int(lib.e2f_neighbour_workspace_bytes(N))
+
+
+def neighbour_list(pos, cutoff: float, K: int, return_n_within: bool = False,
+                   return_order: bool = False, ws=None):
+    """Padded neighbour rows (nbr_idx [N,K] int32, nbr_mask [N,K] uint8) built on the GPU.
+
+    Row i lists the atoms j != i closer than ``cutoff`` by increasing (distance, j),
+    the first K of them; see e2f_neighbour_list in include/e2f.h.  Also returns
+    n_within [N] int32 (the count before truncation) and/or order [N] int32 (atoms
+    grouped by cell in Morton order) when asked.
+    """
+    torch = _torch()
+    _dev(pos, "pos", torch.float32)
+    N = pos.shape[0]
+    if pos.shape != (N, 3):
+        raise ValueError("pos must be [N, 3]")
+    dev = pos.device
+    idx = torch.empty((N, K), dtype=torch.int32, device=dev)
+    mask = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    nw = torch.empty(N, dtype=torch.int32, device=dev) if return_n_within else None
+    order = torch.empty(N, dtype=torch.int32, device=dev) if return_order else None
+    if ws is None:
+        ws = torch.empty(max(neighbour_workspace_bytes(N), 1), dtype=torch.uint8, device=dev)
+    _dev(ws, "ws")
+    _check(lib.e2f_neighbour_list(_stream(pos), N, K, float(cutoff), _ptr(pos), _ptr(idx),
+                                  _ptr(mask), _ptr(nw), _ptr(order), _ptr(ws),
+                                  ws.numel() * ws.element_size()), "e2f_neighbour_list")
+    return (idx, mask) + tuple(t for t in (nw, order) if t is not None)
 
 
 def frames(r, lmax: int = 2):

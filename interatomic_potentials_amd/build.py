@@ -36,6 +36,7 @@ SOURCES = [
     ("e2f_kernels.hip", True),
     ("e2f_backward.hip", True),
     ("e2f_project.hip", True),
+    ("e2f_neighbours.hip", True),
     ("e2f_host.cpp", False),
 ]
 

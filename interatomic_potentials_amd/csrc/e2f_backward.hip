@@ -590,12 +590,21 @@ int bwd_l(int V, const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
 
 }  // namespace
 
+int launch_scan_exclusive(int64_t n, int32_t* a, int32_t* tile_sums, int32_t* cur,
+                          hipStream_t s) {
+  const int ntiles = (int)((n + kScanTile - 1) / kScanTile);
+  hipLaunchKernelGGL(k_scan_tiles, dim3((unsigned)ntiles), dim3(1024), 0, s, n, a, tile_sums);
+  hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(1024), 0, s, n, ntiles, tile_sums, a);
+  hipLaunchKernelGGL(k_scan_fix, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, a,
+                     tile_sums, cur);
+  return last_err();
+}
+
 int launch_reverse_list(int64_t N, int K, const int32_t* idx, const uint8_t* mask,
                         const int32_t* sched, int32_t* off, int32_t* cur, int32_t* tile_sums,
                         int32_t* entries, hipStream_t s) {
   (void)hipGetLastError();
   const unsigned gn = (unsigned)((N + 255) / 256);
-  const int ntiles = (int)((N + kScanTile - 1) / kScanTile);
   // targets per workgroup: as many whole rows as fit kRevSlots (rows longer than
   // that are split over several workgroups by the slot range below)
   const int per = K <= kRevSlots ? kRevSlots / K : 1;
@@ -604,9 +613,8 @@ int launch_reverse_list(int64_t N, int K, const int32_t* idx, const uint8_t* mas
   hipLaunchKernelGGL(k_fill_i32, dim3(gn), dim3(256), 0, s, N, off, 0);
   hipLaunchKernelGGL(k_rev_pass<false>, dim3(gr), dim3(256), 0, s, N, K, per, idx, mask, sched,
                      off, (int32_t*)nullptr);
-  hipLaunchKernelGGL(k_scan_tiles, dim3((unsigned)ntiles), dim3(1024), 0, s, N, off, tile_sums);
-  hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(1024), 0, s, N, ntiles, tile_sums, off);
-  hipLaunchKernelGGL(k_scan_fix, dim3(gn), dim3(256), 0, s, N, off, tile_sums, cur);
+  const int st = launch_scan_exclusive(N, off, tile_sums, cur, s);
+  if (st != 0) return st;
   hipLaunchKernelGGL(k_rev_pass<true>, dim3(gr), dim3(256), 0, s, N, K, per, idx, mask, sched,
                      cur, entries);
   return last_err();

@@ -183,6 +183,39 @@ BwdLayout bwd_layout(int64_t N, int K, int lmax, int C, int H) {
   return L;
 }
 
+// neighbour-list builder workspace: [bbox partials][grid][cell per atom][cell starts]
+// [fill cursors][scan tile sums][atoms grouped by cell][their positions, float4];
+// every part 256-byte aligned.  The cell grid has at most 2^bits cells per axis,
+// with 2^(3 bits) about the atom count (at least 2 per axis, at most 2^kNlMaxBits).
+constexpr int64_t kNlMaxAtoms = (int64_t)1 << 30;
+struct NlLayout {
+  int bits;
+  size_t partial, grid, cell, starts, cursor, tiles, sorted_idx, sorted_pos, total;
+};
+
+NlLayout nl_layout(int64_t N) {
+  NlLayout L;
+  L.bits = 1;
+  while (L.bits < e2f::kNlMaxBits && ((int64_t)1 << (3 * L.bits)) < N) ++L.bits;
+  const size_t cells = (size_t)1 << (3 * L.bits);
+  size_t p = 0;
+  auto take = [&p](size_t bytes) {
+    const size_t at = p;
+    p += round256(bytes);
+    return at;
+  };
+  L.partial = take((size_t)e2f::kBboxBlocks * 6 * 4);
+  L.grid = take(256);
+  L.cell = take((size_t)N * 4);
+  L.starts = take((cells + 1) * 4);
+  L.cursor = take(cells * 4);
+  L.tiles = take((size_t)e2f::kScanTile * 4);
+  L.sorted_idx = take((size_t)N * 4);
+  L.sorted_pos = take((size_t)N * 16);
+  L.total = p;
+  return L;
+}
+
 e2f::SchedScratch sched_scratch(void* ws, int64_t N, int lmax, int C, int dt) {
   char* p = static_cast<char*>(ws) + ws_body_bytes(N, lmax, C, dt) + 256;
   e2f::SchedScratch sc;
@@ -609,6 +642,56 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
   a.scale_log2e = (float)(sc * 1.4426950408889634);
   const EaasCoef cf = make_coef(lmax, path_w);
   return hip_status(e2f::launch_backward(lmax, V, a, cf, stream));
+}
+
+size_t e2f_neighbour_workspace_bytes(int64_t N) {
+  if (N < 0 || N > kNlMaxAtoms) return 0;
+  return nl_layout(N).total;
+}
+
+int e2f_neighbour_list(hipStream_t stream, int64_t N, int K, double cutoff, const float* pos,
+                       int32_t* nbr_idx, uint8_t* nbr_mask, int32_t* n_within, int32_t* order,
+                       void* workspace, size_t ws_bytes) {
+  if (N < 0 || K < 1 || !(cutoff > 0.0) || !isfinite(cutoff)) return E2F_ERR_SHAPE;
+  if (N > kNlMaxAtoms || K > e2f::kNlMaxK) return E2F_ERR_UNSUPPORTED;
+  if (N == 0) return E2F_OK;
+  if (!pos || !nbr_idx || !nbr_mask || !workspace) return E2F_ERR_NULL;
+  if (!aligned(pos, 4) || !aligned(nbr_idx, 4) || !aligned(workspace, 16) ||
+      (n_within && !aligned(n_within, 4)) || (order && !aligned(order, 4)))
+    return E2F_ERR_ALIGN;
+  const NlLayout L = nl_layout(N);
+  if (ws_bytes < L.total) return E2F_ERR_WORKSPACE;
+  const Range outs[5] = {{nbr_idx, (size_t)N * K * 4},
+                         {nbr_mask, (size_t)N * K},
+                         {n_within, (size_t)N * 4},
+                         {order, (size_t)N * 4},
+                         {workspace, L.total}};
+  const Range in = {pos, (size_t)N * 12};
+  for (int a = 0; a < 5; ++a) {
+    if (overlap(outs[a], in)) return E2F_ERR_ALIAS;
+    for (int b = a + 1; b < 5; ++b)
+      if (overlap(outs[a], outs[b])) return E2F_ERR_ALIAS;
+  }
+  char* w = static_cast<char*>(workspace);
+  e2f::NlArgs a;
+  a.pos = pos;
+  a.N = N;
+  a.K = K;
+  a.rc = cutoff;
+  a.bmax = L.bits;
+  a.idx = nbr_idx;
+  a.mask = nbr_mask;
+  a.n_within = n_within;
+  a.order = order;
+  a.partial = reinterpret_cast<float*>(w + L.partial);
+  a.grid = w + L.grid;
+  a.cell = reinterpret_cast<int32_t*>(w + L.cell);
+  a.starts = reinterpret_cast<int32_t*>(w + L.starts);
+  a.cursor = reinterpret_cast<int32_t*>(w + L.cursor);
+  a.tile_sums = reinterpret_cast<int32_t*>(w + L.tiles);
+  a.sorted_idx = reinterpret_cast<int32_t*>(w + L.sorted_idx);
+  a.sorted_pos = reinterpret_cast<float*>(w + L.sorted_pos);
+  return hip_status(e2f::launch_neighbours(a, stream));
 }
 
 int e2f_frames(hipStream_t stream, int64_t n, int lmax, const float* r, float* Q, float* D) {

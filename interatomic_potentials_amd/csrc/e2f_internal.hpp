@@ -122,6 +122,36 @@ int launch_reverse_list(int64_t N, int K, const int32_t* idx, const uint8_t* mas
 constexpr int kRevMaxK = 2048;      // longest neighbour row the reverse-list build takes
 int launch_backward(int lmax, int V, const BwdArgs& a, const EaasCoef& cf, hipStream_t s);
 constexpr int kScanTile = 4096;     // elements per block of the generic scan
+// exclusive scan of a[0, n) in place (n <= kScanTile^2), a[n] = total, cur = copy of the
+// scanned values; tile_sums holds kScanTile ints.  Returns the first launch error since the
+// caller last cleared them.
+int launch_scan_exclusive(int64_t n, int32_t* a, int32_t* tile_sums, int32_t* cur,
+                          hipStream_t s);
+
+// padded neighbour lists (cell list) and the Morton order of the atoms
+constexpr int kNlMaxBits = 7;        // Morton bits per axis of the cell grid, at most
+constexpr int kNlMaxK = 1984;        // longest row the builder keeps
+struct NlArgs {
+  const float* pos;        // [N, 3]
+  int64_t N;
+  int K;
+  double rc;               // cutoff (strict)
+  int bmax;                // Morton bits per axis allowed by the workspace
+  int32_t* idx;            // [N, K] out
+  uint8_t* mask;           // [N, K] out
+  int32_t* n_within;       // [N] out or nullptr
+  int32_t* order;          // [N] out or nullptr: atoms grouped by cell, Morton order
+  // workspace parts
+  float* partial;          // [kBboxBlocks, 6]
+  void* grid;              // 256 bytes
+  int32_t* cell;           // [N]
+  int32_t* starts;         // [2^(3 bmax) + 1] counts, then exclusive starts
+  int32_t* cursor;         // [2^(3 bmax)]
+  int32_t* tile_sums;      // [kScanTile]
+  int32_t* sorted_idx;     // [N]
+  float* sorted_pos;       // [N, 4]
+};
+int launch_neighbours(const NlArgs& a, hipStream_t s);
 constexpr int kRevTile = 1024;      // reverse-list entries sorted per pass
 
 }  // namespace e2f

@@ -262,3 +262,54 @@ def test_projection_argument_errors(fn):
     # MFMA tiles: C in {16, 32, 64, 128} for fp32, {32, 64, 128} for bf16
     assert fn(C=96, **({"H": 12} if fn is _fproj else {})) == C["E2F_ERR_UNSUPPORTED"]
     assert fn(C=16, dt=1, **({"H": 2} if fn is _fproj else {})) == C["E2F_ERR_UNSUPPORTED"]
+
+
+def _nl(**kw):
+    a = dict(stream=None, N=1000, K=64, rc=5.0, pos=fake(1), idx=fake(2), mask=fake(3), nw=None,
+             order=None, ws=fake(4), ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.e2f_neighbour_list(a["stream"], a["N"], a["K"], a["rc"], a["pos"], a["idx"],
+                                  a["mask"], a["nw"], a["order"], a["ws"], a["ws_bytes"])
+
+
+def _expected_nl_ws(N):
+    """Documented layout: bbox partials | grid | cell per atom | cell starts | cursors |
+    scan tile sums | grouped atoms | their positions (float4); 2^(3 b) >= N cells, 1 <= b <= 7."""
+    b = 1
+    while b < 7 and 2 ** (3 * b) < N:
+        b += 1
+    cells = 2 ** (3 * b)
+    return (_r256(256 * 6 * 4) + 256 + _r256(4 * N) + _r256(4 * (cells + 1)) + _r256(4 * cells)
+            + _r256(4 * 4096) + _r256(4 * N) + _r256(16 * N))
+
+
+def test_neighbour_workspace_bytes():
+    wb = lib.e2f_neighbour_workspace_bytes
+    for N in (0, 1, 9, 64, 648, 32768, 100000, 3_000_000):
+        assert wb(N) == _expected_nl_ws(N), N
+    assert wb(-1) == 0
+    assert wb(2 ** 30 + 1) == 0
+
+
+def test_neighbour_list_argument_errors():
+    assert _nl(N=-1) == C["E2F_ERR_SHAPE"]
+    assert _nl(K=0) == C["E2F_ERR_SHAPE"]
+    assert _nl(rc=0.0) == C["E2F_ERR_SHAPE"]
+    assert _nl(rc=-1.0) == C["E2F_ERR_SHAPE"]
+    assert _nl(rc=float("inf")) == C["E2F_ERR_SHAPE"]
+    assert _nl(rc=float("nan")) == C["E2F_ERR_SHAPE"]
+    assert _nl(K=1985) == C["E2F_ERR_UNSUPPORTED"]
+    assert _nl(N=2 ** 30 + 1) == C["E2F_ERR_UNSUPPORTED"]
+    assert _nl(N=0, pos=None, idx=None, mask=None, ws=None) == C["E2F_OK"]
+    assert _nl(pos=None) == C["E2F_ERR_NULL"]
+    assert _nl(idx=None) == C["E2F_ERR_NULL"]
+    assert _nl(mask=None) == C["E2F_ERR_NULL"]
+    assert _nl(ws=None) == C["E2F_ERR_NULL"]
+    assert _nl(pos=ctypes.c_void_p(BASE + 64 * MB + 2)) == C["E2F_ERR_ALIGN"]
+    assert _nl(ws=ctypes.c_void_p(BASE + 4 * 64 * MB + 4)) == C["E2F_ERR_ALIGN"]
+    assert _nl(nw=ctypes.c_void_p(BASE + 5 * 64 * MB + 2)) == C["E2F_ERR_ALIGN"]
+    assert _nl(ws_bytes=lib.e2f_neighbour_workspace_bytes(1000) - 1) == C["E2F_ERR_WORKSPACE"]
+    assert _nl(idx=fake(1)) == C["E2F_ERR_ALIAS"]
+    assert _nl(mask=ctypes.c_void_p(BASE + 2 * 64 * MB + 1000)) == C["E2F_ERR_ALIAS"]
+    assert _nl(nw=fake(4)) == C["E2F_ERR_ALIAS"]
+    assert _nl(order=fake(3)) == C["E2F_ERR_ALIAS"]
