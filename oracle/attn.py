@@ -32,6 +32,20 @@ mixing v_j[l] = h_j[l] W_V[l] (W_V [lmax+1, C, C]), the most general linear
 map of irrep features that commutes with rotations (Schur's lemma), applied
 before the pre-coupling: h'_j = v_j (x) R(r_j).
 
+Optional smooth envelope (``env_cutoff``).  The EquiformerV3 page (method
+details, attention) multiplies the softmax numerator and denominator by an
+envelope e(|r_ij|) of the pair distance so that the weights fade out smoothly
+at the cutoff; it prints no formula for e.  Reading: the weights become
+
+    alpha_ijh = e_ij exp(s_ijh) / sum_k e_ik exp(s_ikh),
+    e_ij = u(|r_i - r_j| / r_env),  u(x) = 1 - 21 x^5 + 35 x^6 - 15 x^7 (x < 1), 0 (x >= 1),
+
+the polynomial smooth cutoff with u(0) = 1 and u = u' = u'' = 0 at x = 1
+(so the weights, and forces derived from them, stay continuous as a
+neighbour crosses r_env).  A slot with e_ij = 0 contributes nothing; a row
+whose every valid slot has e = 0 gives m_i = 0 like an empty row.  The
+distance is taken in float64 from the float32 positions.
+
 This function materialises logits [E, H] and messages [E, S, C]: it is the
 edge-centric form the pages contrast the fused kernel with.
 """
@@ -62,13 +76,28 @@ def project(h: np.ndarray, w_q: np.ndarray, w_k: np.ndarray, w_v: np.ndarray):
     return q, k, v
 
 
+def envelope(x: np.ndarray) -> np.ndarray:
+    """u(x) = 1 - 21 x^5 + 35 x^6 - 15 x^7 for 0 <= x < 1, 0 for x >= 1 (reading in the header)."""
+    x = np.asarray(x, dtype=np.float64)
+    u = 1.0 - 21.0 * x ** 5 + 35.0 * x ** 6 - 15.0 * x ** 7
+    return np.where(x < 1.0, u, 0.0)
+
+
+def pair_distance(pos: np.ndarray, i: np.ndarray, j: np.ndarray) -> np.ndarray:
+    """|r_i - r_j| in float64 from the positions as given."""
+    p = np.asarray(pos, dtype=np.float64)
+    return np.linalg.norm(p[np.asarray(i)] - p[np.asarray(j)], axis=-1)
+
+
 def attention_weights(h: np.ndarray, nbr_idx: np.ndarray, nbr_mask: np.ndarray, heads: int,
                       scale: Optional[float] = None, targets: Optional[np.ndarray] = None,
-                      qk: Optional[tuple] = None):
+                      qk: Optional[tuple] = None, env: Optional[tuple] = None):
     """Edge list and softmax weights: (e_row, e_src, alpha [E, H]).
 
     e_row indexes the target list, e_src the source atom of each valid slot.
     ``qk`` = (q [N, C], k [N, C]) replaces the default q = k = h[:, l=0, :].
+    ``env`` = (pos [N, 3], r_env) multiplies each pair's exp(logit) by the
+    envelope of its distance, numerator and denominator alike.
     """
     h = np.asarray(h, dtype=np.float64)
     N, _, C = h.shape
@@ -100,19 +129,24 @@ def attention_weights(h: np.ndarray, nbr_idx: np.ndarray, nbr_mask: np.ndarray, 
     mx = np.full((T, heads), -np.inf)
     np.maximum.at(mx, e_row, logits)
     p = np.exp(logits - mx[e_row])
+    if env is not None:
+        pos, r_env = env
+        p = p * envelope(pair_distance(pos, tgt[e_row], e_src) / float(r_env))[:, None]
     z = np.zeros((T, heads))
     np.add.at(z, e_row, p)
-    return e_row, e_src, p / z[e_row]
+    zr = z[e_row]
+    return e_row, e_src, np.divide(p, zr, out=np.zeros_like(p), where=zr > 0)
 
 
 def attn_forward(pos: np.ndarray, h: np.ndarray, nbr_idx: np.ndarray, nbr_mask: np.ndarray,
                  heads: int, lmax: int, scale: Optional[float] = None,
                  path_w: Optional[np.ndarray] = None, targets: Optional[np.ndarray] = None,
                  return_msg: bool = False, chunk_edges: int = 1 << 16,
-                 proj: Optional[tuple] = None):
+                 proj: Optional[tuple] = None, env_cutoff: Optional[float] = None):
     """Output [T, S, C] for the given targets (all atoms if None); optionally also m [T, S, C].
 
-    ``proj`` = (W_Q, W_K, W_V) switches on the learned projections (see ``project``).
+    ``proj`` = (W_Q, W_K, W_V) switches on the learned projections (see ``project``);
+    ``env_cutoff`` = r_env switches on the smooth envelope (see ``envelope``).
     """
     pos = np.asarray(pos, dtype=np.float64)
     h = np.asarray(h, dtype=np.float64)
@@ -128,7 +162,8 @@ def attn_forward(pos: np.ndarray, h: np.ndarray, nbr_idx: np.ndarray, nbr_mask: 
     else:
         q, k, v = project(h, *proj)
         qk = (q, k)
-    e_row, e_src, alpha = attention_weights(h, nbr_idx, nbr_mask, heads, scale, tgt, qk)
+    env = None if env_cutoff is None else (pos, env_cutoff)
+    e_row, e_src, alpha = attention_weights(h, nbr_idx, nbr_mask, heads, scale, tgt, qk, env)
     E = e_src.shape[0]
 
     # step 1 on every source that some edge reads

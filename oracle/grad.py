@@ -51,9 +51,16 @@ def tp_dense_torch(x: torch.Tensor, r: torch.Tensor, lmax: int,
     return torch.cat(blocks, dim=1)
 
 
+def envelope_torch(x: torch.Tensor) -> torch.Tensor:
+    """``oracle.attn.envelope`` in torch: 1 - 21 x^5 + 35 x^6 - 15 x^7 below 1, else 0."""
+    u = 1.0 - 21.0 * x ** 5 + 35.0 * x ** 6 - 15.0 * x ** 7
+    return torch.where(x < 1.0, u, torch.zeros_like(u))
+
+
 def attn_forward_torch(pos: torch.Tensor, h: torch.Tensor, nbr_idx: np.ndarray, nbr_mask: np.ndarray,
                        heads: int, lmax: int, scale: Optional[float] = None,
-                       path_w: Optional[np.ndarray] = None) -> torch.Tensor:
+                       path_w: Optional[np.ndarray] = None,
+                       env_cutoff: Optional[float] = None) -> torch.Tensor:
     """The three steps of ``oracle.attn.attn_forward`` for all targets, in torch."""
     N, S, C = h.shape
     d = C // heads
@@ -71,8 +78,12 @@ def attn_forward_torch(pos: torch.Tensor, h: torch.Tensor, nbr_idx: np.ndarray, 
     np.maximum.at(mx_np, e_row, s.detach().numpy())
     mx = torch.from_numpy(np.where(np.isfinite(mx_np), mx_np, 0.0))  # stabiliser, no gradient
     p = torch.exp(s - mx[er])
+    if env_cutoff is not None:
+        dist = torch.linalg.vector_norm(pos[er] - pos[es], dim=-1)
+        p = p * envelope_torch(dist / float(env_cutoff))[:, None]
     z = torch.zeros((N, heads), dtype=h.dtype).index_add(0, er, p)
-    alpha = p / z[er]
+    zr = z[er]
+    alpha = p / torch.where(zr > 0, zr, torch.ones_like(zr))
     a = alpha.repeat_interleave(d, dim=1)                          # channel c -> head c // d
     msg = torch.zeros((N, S, C), dtype=h.dtype).index_add(0, er, a[:, None, :] * hp[es])
     return tp_dense_torch(msg, pos, lmax, path_w)                  # step 3
@@ -80,11 +91,11 @@ def attn_forward_torch(pos: torch.Tensor, h: torch.Tensor, nbr_idx: np.ndarray, 
 
 def attn_backward(pos: np.ndarray, h: np.ndarray, nbr_idx: np.ndarray, nbr_mask: np.ndarray,
                   heads: int, lmax: int, grad_out: np.ndarray, scale: Optional[float] = None,
-                  path_w: Optional[np.ndarray] = None):
+                  path_w: Optional[np.ndarray] = None, env_cutoff: Optional[float] = None):
     """(dL/dh [N,S,C], dL/dpos [N,3]) for L = <grad_out, out>, float64."""
     pt = torch.tensor(np.asarray(pos, dtype=np.float64), requires_grad=True)
     ht = torch.tensor(np.asarray(h, dtype=np.float64), requires_grad=True)
-    out = attn_forward_torch(pt, ht, nbr_idx, nbr_mask, heads, lmax, scale, path_w)
+    out = attn_forward_torch(pt, ht, nbr_idx, nbr_mask, heads, lmax, scale, path_w, env_cutoff)
     g = torch.from_numpy(np.asarray(grad_out, dtype=np.float64))
     dh, dpos = torch.autograd.grad((out * g).sum(), (ht, pt), allow_unused=True)
     if dpos is None:            # lmax = 0: the harmonics are constant, positions do not enter
