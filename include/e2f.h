@@ -170,6 +170,17 @@ int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int 
  *   nbr_mask  [N, K] uint8   any pattern; valid slots need not come first;
  *                            repeated indices count once per slot
  *   scale     logit scale; <= 0 selects 1 / sqrt(C / H)
+ *   env_cutoff  0: plain softmax.  r_env > 0 (finite): smooth distance
+ *             envelope (EquiformerV3 page, method details, attention: an
+ *             envelope of the pair distance multiplies the softmax numerator
+ *             and denominator); the weights become
+ *               e_ij exp(s_ijh) / sum_k e_ik exp(s_ikh),  e_ij = u(|pos_i - pos_j| / r_env),
+ *               u(x) = 1 - 21 x^5 + 35 x^6 - 15 x^7 = (1-x)^3 (1+3x+6x^2+10x^3+15x^4)
+ *             for x < 1 and 0 beyond (u, u' and u'' vanish at the cutoff).
+ *             Distances are taken in fp32.  A slot at or beyond r_env weighs
+ *             nothing; a target whose every slot does gives 0 like an empty
+ *             row; lse then includes ln e.  Negative, infinite or NaN:
+ *             E2F_ERR_SHAPE.
  *   workspace filled by e2f_attn_precouple (or _proj); its schedule scratch (and, under
  *             E2F_VALIDATE_INDICES, its flag) is rewritten here, hence not
  *             const.  Targets are visited in Morton order of their
@@ -186,22 +197,22 @@ int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int 
  */
 int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                        const float* pos, const int32_t* nbr_idx, const uint8_t* nbr_mask,
-                       float scale, const float* path_w, void* workspace, size_t ws_bytes,
-                       void* out, void* out_msg, float* lse, uint32_t flags);
+                       float scale, float env_cutoff, const float* path_w, void* workspace,
+                       size_t ws_bytes, void* out, void* out_msg, float* lse, uint32_t flags);
 
 /* e2f_attn_forward -- e2f_attn_precouple then e2f_attn_aggregate on one stream. */
 int e2f_attn_forward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                      const float* pos, const void* h, const int32_t* nbr_idx,
-                     const uint8_t* nbr_mask, float scale, const float* path_w,
-                     void* workspace, size_t ws_bytes, void* out, void* out_msg, float* lse,
-                     uint32_t flags);
+                     const uint8_t* nbr_mask, float scale, float env_cutoff,
+                     const float* path_w, void* workspace, size_t ws_bytes, void* out,
+                     void* out_msg, float* lse, uint32_t flags);
 
 /* e2f_attn_forward_proj -- e2f_attn_precouple_proj then e2f_attn_aggregate. */
 int e2f_attn_forward_proj(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                           const float* pos, const void* h, const void* w_q, const void* w_k,
                           const void* w_v, const int32_t* nbr_idx, const uint8_t* nbr_mask,
-                          float scale, const float* path_w, void* workspace, size_t ws_bytes,
-                          void* out, void* out_msg, float* lse, uint32_t flags);
+                          float scale, float env_cutoff, const float* path_w, void* workspace,
+                          size_t ws_bytes, void* out, void* out_msg, float* lse, uint32_t flags);
 
 /*
  * Backward pass (vector-Jacobian product) of the attention, for forces as
@@ -221,7 +232,9 @@ size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int 
 /*
  * e2f_attn_backward -- fp32 storage only (E2F_ERR_UNSUPPORTED for bf16, for
  * N above 2^24, K above 2048 or N K at or above 2^31).
- *   pos, h, nbr_idx, nbr_mask, scale, path_w: as given to the forward
+ *   pos, h, nbr_idx, nbr_mask, scale, env_cutoff, path_w: as given to the
+ *               forward (with an envelope, dL/dpos includes its derivative
+ *               through each pair distance)
  *   workspace   the forward's workspace after e2f_attn_precouple (read only;
  *               the layer without projections is differentiated)
  *   msg, lse    the forward's out_msg and lse outputs
@@ -236,10 +249,11 @@ size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int 
  */
 int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                       const float* pos, const void* h, const int32_t* nbr_idx,
-                      const uint8_t* nbr_mask, float scale, const float* path_w,
-                      const void* workspace, size_t ws_bytes, const void* msg, const float* lse,
-                      const void* grad_out, void* grad_h, float* grad_pos,
-                      void* bwd_workspace, size_t bwd_ws_bytes, uint32_t flags);
+                      const uint8_t* nbr_mask, float scale, float env_cutoff,
+                      const float* path_w, const void* workspace, size_t ws_bytes,
+                      const void* msg, const float* lse, const void* grad_out, void* grad_h,
+                      float* grad_pos, void* bwd_workspace, size_t bwd_ws_bytes,
+                      uint32_t flags);
 
 /*
  * Padded neighbour lists, built on the GPU: the list that the attention

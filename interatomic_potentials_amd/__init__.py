@@ -53,14 +53,16 @@ SIGNATURES = {
     "e2f_attn_precouple_proj": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _sz]),
     "e2f_attn_forward_proj": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
-                                     _vp, _vp, _vp, _f32, _vp, _vp, _sz, _vp, _vp, _vp, _u32]),
+                                     _vp, _vp, _vp, _f32, _f32, _vp, _vp, _sz, _vp, _vp, _vp,
+                                     _u32]),
     "e2f_attn_aggregate": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _f32,
-                                  _vp, _vp, _sz, _vp, _vp, _vp, _u32]),
+                                  _f32, _vp, _vp, _sz, _vp, _vp, _vp, _u32]),
     "e2f_attn_forward": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
-                                _f32, _vp, _vp, _sz, _vp, _vp, _vp, _u32]),
+                                _f32, _f32, _vp, _vp, _sz, _vp, _vp, _vp, _u32]),
     "e2f_attn_backward_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32]),
     "e2f_attn_backward": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
-                                 _f32, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _u32]),
+                                 _f32, _f32, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                 _u32]),
     "e2f_neighbour_workspace_bytes": (_sz, [_i64]),
     "e2f_neighbour_list": (_i32, [_vp, _i64, _i32, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _sz]),
@@ -263,8 +265,12 @@ def _results(out, msg, lse):
 def attn_aggregate(pos, nbr_idx, nbr_mask, ws, heads: int, lmax: int, C: int, dtype,
                    scale: Optional[float] = None, path_w=None, out=None,
                    return_msg: bool = False, validate: bool = False,
-                   targets_in_order: bool = False, return_lse: bool = False):
-    """Steps 2-3 from a filled workspace; returns out, or (out[, m][, lse]) when asked."""
+                   targets_in_order: bool = False, return_lse: bool = False,
+                   env_cutoff: Optional[float] = None):
+    """Steps 2-3 from a filled workspace; returns out, or (out[, m][, lse]) when asked.
+
+    ``env_cutoff`` = r_env switches on the smooth distance envelope of the weights.
+    """
     torch = _torch()
     _dev(pos, "pos", torch.float32)
     _dev(nbr_idx, "nbr_idx", torch.int32)
@@ -279,7 +285,8 @@ def attn_aggregate(pos, nbr_idx, nbr_mask, ws, heads: int, lmax: int, C: int, dt
     lse = torch.empty((N, heads), dtype=torch.float32, device=ws.device) if return_lse else None
     pw = _path_w(path_w, ws.device)
     _check(lib.e2f_attn_aggregate(_stream(ws), N, K, lmax, C, heads, _dtype_code(out), _ptr(pos),
-                                  _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0), _ptr(pw),
+                                  _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0),
+                                  float(env_cutoff or 0.0), _ptr(pw),
                                   _ptr(ws), ws.numel() * ws.element_size(), _ptr(out), _ptr(msg),
                                   _ptr(lse), _flags(validate, targets_in_order)),
            "e2f_attn_aggregate")
@@ -289,11 +296,12 @@ def attn_aggregate(pos, nbr_idx, nbr_mask, ws, heads: int, lmax: int, C: int, dt
 def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] = None,
                  path_w=None, ws=None, out=None, return_msg: bool = False,
                  validate: bool = False, targets_in_order: bool = False,
-                 return_lse: bool = False, proj=None):
+                 return_lse: bool = False, proj=None, env_cutoff: Optional[float] = None):
     """Full path (steps 1-3): pos [N,3] fp32, h [N,S,C], nbr_idx [N,K] int32, nbr_mask [N,K] uint8.
 
     Returns out, or (out[, m][, lse]) when return_msg / return_lse ask for them.
-    ``proj`` = (w_q, w_k, w_v) adds the learned projections (see attn_precouple).
+    ``proj`` = (w_q, w_k, w_v) adds the learned projections (see attn_precouple);
+    ``env_cutoff`` = r_env the smooth distance envelope of the weights.
     """
     torch = _torch()
     _dev(pos, "pos", torch.float32)
@@ -316,14 +324,16 @@ def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] =
     w = _proj_weights(proj, h, lmax)
     if w is None:
         _check(lib.e2f_attn_forward(_stream(h), N, K, lmax, C, heads, dt, _ptr(pos), _ptr(h),
-                                    _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0), _ptr(pw),
+                                    _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0),
+                                    float(env_cutoff or 0.0), _ptr(pw),
                                     _ptr(ws), ws.numel() * ws.element_size(), _ptr(out), _ptr(msg),
                                     _ptr(lse), _flags(validate, targets_in_order)),
                "e2f_attn_forward")
     else:
         _check(lib.e2f_attn_forward_proj(_stream(h), N, K, lmax, C, heads, dt, _ptr(pos), _ptr(h),
                                          _ptr(w[0]), _ptr(w[1]), _ptr(w[2]), _ptr(nbr_idx),
-                                         _ptr(nbr_mask), float(scale or 0.0), _ptr(pw), _ptr(ws),
+                                         _ptr(nbr_mask), float(scale or 0.0),
+                                         float(env_cutoff or 0.0), _ptr(pw), _ptr(ws),
                                          ws.numel() * ws.element_size(), _ptr(out), _ptr(msg),
                                          _ptr(lse), _flags(validate, targets_in_order)),
                "e2f_attn_forward_proj")
@@ -337,7 +347,7 @@ def attn_backward_workspace_bytes(N: int, K: int, lmax: int, C: int, H: int,
 
 def attn_backward(pos, h, nbr_idx, nbr_mask, heads: int, ws, msg, lse, grad_out,
                   scale: Optional[float] = None, path_w=None, targets_in_order: bool = False,
-                  bwd_ws=None, grad_h=None, grad_pos=None):
+                  bwd_ws=None, grad_h=None, grad_pos=None, env_cutoff: Optional[float] = None):
     """(dL/dh, dL/dpos) for L = <grad_out, out>; ws, msg, lse from the forward (fp32 only)."""
     torch = _torch()
     _dev(pos, "pos", torch.float32)
@@ -360,7 +370,8 @@ def attn_backward(pos, h, nbr_idx, nbr_mask, heads: int, ws, msg, lse, grad_out,
                 else _dev(grad_pos, "grad_pos", torch.float32))
     pw = _path_w(path_w, h.device)
     _check(lib.e2f_attn_backward(_stream(h), N, K, lmax, C, heads, F32, _ptr(pos), _ptr(h),
-                                 _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0), _ptr(pw),
+                                 _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0),
+                                 float(env_cutoff or 0.0), _ptr(pw),
                                  _ptr(ws), ws.numel() * ws.element_size(), _ptr(msg), _ptr(lse),
                                  _ptr(grad_out), _ptr(grad_h), _ptr(grad_pos), _ptr(bwd_ws),
                                  bwd_ws.numel() * bwd_ws.element_size(),

@@ -180,10 +180,12 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a, EaasCoef cf) {
 
 // -------------------------------------------------- target-centric dq
 
-template <int LMAX, int V, int U, int HL, bool BUF>
+template <int LMAX, int V, int U, int HL, bool BUF, bool ENV>
 __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
   constexpr int S = ncomp(LMAX);
   __shared__ int s_nb[kWavesPerBlock][kTile];
+  // envelope per sorted slot: log2 u, then d ln u / d r_i as a vector
+  __shared__ float4 s_env[kWavesPerBlock][ENV ? kTile : 1];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t i = scheduled_atom(a.sched, a.N, w);
@@ -211,6 +213,7 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
   float dq[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) dq[v] = 0.0f;
+  float gpos[3] = {0.0f, 0.0f, 0.0f};   // envelope part of dL/dr_i, this lane's head share
 
   const int32_t* irow = a.idx + i * K;
   const uint8_t* mrow = a.mask + i * K;
@@ -231,6 +234,16 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
       cnt += __popcll(b);
     }
     sort_list(nb, cnt, lane);
+    if constexpr (ENV) {
+      const float xi = a.pos[3 * i], yi = a.pos[3 * i + 1], zi = a.pos[3 * i + 2];
+      for (int e = lane; e < cnt; e += 64) {
+        const int j = nb[e];
+        const float dx = xi - a.pos[3 * j], dy = yi - a.pos[3 * j + 1], dz = zi - a.pos[3 * j + 2];
+        const EnvTerm et = envelope_term(dx, dy, dz, a.env_inv_rc);
+        s_env[w][e] = make_float4(et.log2u, et.dlog * dx, et.dlog * dy, et.dlog * dz);
+      }
+      wave_sync_b();
+    }
     for (int n0 = 0; n0 < cnt; n0 += P * U) {
       Raw<float, V> kv[U][S + 1];
       bool val[U];
@@ -262,10 +275,21 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
           for (int v = 0; v < V; ++v) dp = fmaf(dm[r][v], kv[u][r + 1].f[v], dp);
         qk = head_sum_b<HL>(qk, a.head_lanes);
         dp = head_sum_b<HL>(dp, a.head_lanes);
-        const float alpha = val[u] ? exp2_b(qk * a.scale_log2e - L2) : 0.0f;
-        const float ds = alpha * (dp - Dv) * a.scale;
+        float4 env = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if constexpr (ENV) env = s_env[w][val[u] ? n0 + u * P + sub : 0];
+        // a slot beyond the envelope weighs 0 (its target's lse may itself be -inf)
+        const float alpha =
+            (val[u] && env.x != -INFINITY) ? exp2_b(qk * a.scale_log2e + env.x - L2) : 0.0f;
+        const float dsn = alpha * (dp - Dv);   // gradient of this head's (natural) logit
+        const float ds = dsn * a.scale;
 #pragma unroll
         for (int v = 0; v < V; ++v) dq[v] = fmaf(ds, kv[u][0].f[v], dq[v]);
+        if constexpr (ENV) {
+          // ln u_ij enters every head's logit: d/dr_i sums dsn over the heads
+          gpos[0] = fmaf(dsn, env.y, gpos[0]);
+          gpos[1] = fmaf(dsn, env.z, gpos[1]);
+          gpos[2] = fmaf(dsn, env.w, gpos[2]);
+        }
       }
     }
     wave_sync_b();
@@ -274,15 +298,31 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
 #pragma unroll
     for (int v = 0; v < V; ++v) dq[v] += __shfl_xor(dq[v], o);
   }
+  if constexpr (ENV) {
+    // every head's value sits on head_lanes active lanes of each subgroup
+    const float wgt = act ? 1.0f / (float)a.head_lanes : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      float t = gpos[k] * wgt;
+      for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
+      gpos[k] = t;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k) a.grad_pos[3 * i + k] += gpos[k];  // prep wrote its part
+    }
+  }
   if (sub == 0 && act) st<V>(a.dq + i * C + c0, dq);
 }
 
 // ------------------------------------------ source-centric dh', dk, dh, dpos
 
-template <int LMAX, int V, int U, int HL, bool BUF>
+template <int LMAX, int V, int U, int HL, bool BUF, bool ENV>
 __global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf) {
   constexpr int S = ncomp(LMAX);
   __shared__ int s_nb[kWavesPerBlock][kRevTile];
+  // envelope per sorted target: log2 u, then d ln u / d r_target as a vector
+  __shared__ float4 s_env[kWavesPerBlock][ENV ? kRevTile : 1];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t j = scheduled_atom(a.sched, a.N, w);
@@ -313,12 +353,24 @@ __global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf) {
     for (int s = 0; s < S; ++s) dhp[s][v] = 0.0f;
   }
 
+  float gpos[3] = {0.0f, 0.0f, 0.0f};   // envelope part of dL/dr_j, this lane's head share
   const int beg = a.rev_off[j], end = a.rev_off[j + 1];
   int* nb = s_nb[w];
   for (int t0 = beg; t0 < end; t0 += kRevTile) {
     const int cnt = end - t0 < kRevTile ? end - t0 : kRevTile;
     for (int e = lane; e < cnt; e += 64) nb[e] = a.rev_idx[t0 + e];
     sort_list(nb, cnt, lane);
+    if constexpr (ENV) {
+      const float xj = a.pos[3 * j], yj = a.pos[3 * j + 1], zj = a.pos[3 * j + 2];
+      for (int e = lane; e < cnt; e += 64) {
+        const int ti = nb[e];
+        const float dx = a.pos[3 * ti] - xj, dy = a.pos[3 * ti + 1] - yj,
+                    dz = a.pos[3 * ti + 2] - zj;
+        const EnvTerm et = envelope_term(dx, dy, dz, a.env_inv_rc);
+        s_env[w][e] = make_float4(et.log2u, et.dlog * dx, et.dlog * dy, et.dlog * dz);
+      }
+      wave_sync_b();
+    }
     for (int n0 = 0; n0 < cnt; n0 += P * U) {
       Raw<float, V> qd[U][S + 1];
       float L2[U], Dv[U];
@@ -352,10 +404,20 @@ __global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf) {
           for (int v = 0; v < V; ++v) dp = fmaf(qd[u][r + 1].f[v], hp[r][v], dp);
         qk = head_sum_b<HL>(qk, a.head_lanes);
         dp = head_sum_b<HL>(dp, a.head_lanes);
-        const float alpha = val[u] ? exp2_b(qk * a.scale_log2e - L2[u]) : 0.0f;
-        const float ds = alpha * (dp - Dv[u]) * a.scale;
+        float4 env = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if constexpr (ENV) env = s_env[w][val[u] ? n0 + u * P + sub : 0];
+        const float alpha =
+            (val[u] && env.x != -INFINITY) ? exp2_b(qk * a.scale_log2e + env.x - L2[u]) : 0.0f;
+        const float dsn = alpha * (dp - Dv[u]);
+        const float ds = dsn * a.scale;
 #pragma unroll
         for (int v = 0; v < V; ++v) dk[v] = fmaf(ds, qd[u][0].f[v], dk[v]);
+        if constexpr (ENV) {
+          // d ln u_ij / d r_j = -(d ln u_ij / d r_i)
+          gpos[0] = fmaf(-dsn, env.y, gpos[0]);
+          gpos[1] = fmaf(-dsn, env.z, gpos[1]);
+          gpos[2] = fmaf(-dsn, env.w, gpos[2]);
+        }
 #pragma unroll
         for (int r = 0; r < S; ++r)
 #pragma unroll
@@ -370,6 +432,15 @@ __global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf) {
       dk[v] += __shfl_xor(dk[v], o);
 #pragma unroll
       for (int s = 0; s < S; ++s) dhp[s][v] += __shfl_xor(dhp[s][v], o);
+    }
+  }
+  if constexpr (ENV) {
+    const float wgt = act ? 1.0f / (float)a.head_lanes : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      float t = gpos[k] * wgt;
+      for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o);
+      gpos[k] = t;
     }
   }
   if (sub != 0) return;
@@ -413,7 +484,7 @@ __global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf) {
     float gp[3];
     frame_to_global(f, acc, gp);
 #pragma unroll
-    for (int kk = 0; kk < 3; ++kk) a.grad_pos[3 * j + kk] += gp[kk];  // prep wrote the step-3 part
+    for (int kk = 0; kk < 3; ++kk) a.grad_pos[3 * j + kk] += gp[kk] + gpos[kk];  // prep wrote the step-3 part
   }
 }
 
@@ -555,7 +626,7 @@ __global__ __launch_bounds__(256) void k_scan_fix(int64_t n, int32_t* a, const i
 
 int last_err() { return static_cast<int>(hipGetLastError()); }
 
-template <int L, int V, int HL>
+template <int L, int V, int HL, bool E>
 int bwd_go(const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
   constexpr int UQ = 4;  // neighbours per subgroup in flight, target pass
   constexpr int US = 2;  // targets per subgroup in flight, source pass (more live registers)
@@ -567,25 +638,30 @@ int bwd_go(const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
   const bool buf = a.N * (ncomp(L) + 1) * (int64_t)a.C * 4 < ((int64_t)1 << 32);
   hipLaunchKernelGGL((k_bwd_prep<L, V, HL>), grid_prep, dim3(256), 0, s, a, cf);
   if (buf) {
-    hipLaunchKernelGGL((k_bwd_q<L, V, UQ, HL, true>), grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, true>), grid, dim3(256), 0, s, a, cf);
+    hipLaunchKernelGGL((k_bwd_q<L, V, UQ, HL, true, E>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, true, E>), grid, dim3(256), 0, s, a, cf);
   } else {
-    hipLaunchKernelGGL((k_bwd_q<L, V, UQ, HL, false>), grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, false>), grid, dim3(256), 0, s, a, cf);
+    hipLaunchKernelGGL((k_bwd_q<L, V, UQ, HL, false, E>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, false, E>), grid, dim3(256), 0, s, a, cf);
   }
   return last_err();
 }
 
-template <int L>
-int bwd_l(int V, const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
-  if (V == 4 && a.head_lanes == 2) return bwd_go<L, 4, 2>(a, cf, s);
-  if (V == 4 && a.head_lanes == 1) return bwd_go<L, 4, 1>(a, cf, s);
+template <int L, bool E>
+int bwd_v(int V, const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
+  if (V == 4 && a.head_lanes == 2) return bwd_go<L, 4, 2, E>(a, cf, s);
+  if (V == 4 && a.head_lanes == 1) return bwd_go<L, 4, 1, E>(a, cf, s);
   switch (V) {
-    case 1: return bwd_go<L, 1, 0>(a, cf, s);
-    case 2: return bwd_go<L, 2, 0>(a, cf, s);
-    case 4: return bwd_go<L, 4, 0>(a, cf, s);
+    case 1: return bwd_go<L, 1, 0, E>(a, cf, s);
+    case 2: return bwd_go<L, 2, 0, E>(a, cf, s);
+    case 4: return bwd_go<L, 4, 0, E>(a, cf, s);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
+}
+
+template <int L>
+int bwd_l(int V, const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
+  return a.env_inv_rc > 0.0f ? bwd_v<L, true>(V, a, cf, s) : bwd_v<L, false>(V, a, cf, s);
 }
 
 }  // namespace

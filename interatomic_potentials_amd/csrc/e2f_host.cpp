@@ -236,6 +236,14 @@ int check_shape_common(int64_t n, int lmax, int C, int dt) {
   return E2F_OK;
 }
 
+// envelope cutoff: 0 = no envelope, else a positive finite radius
+bool bad_env(float env_cutoff) {
+  return !(env_cutoff == 0.0f || (env_cutoff > 0.0f && isfinite(env_cutoff)));
+}
+float env_inv(float env_cutoff) {
+  return env_cutoff > 0.0f ? (float)(1.0 / (double)env_cutoff) : 0.0f;
+}
+
 int check_attn_shape(int64_t N, int K, int lmax, int C, int H, int dt, uint32_t flags) {
   const int st = check_shape_common(N, lmax, C, dt);
   if (st != E2F_OK) return st;
@@ -264,8 +272,8 @@ int precouple_impl(hipStream_t stream, int64_t N, int lmax, int C, int dt, const
 
 int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dt,
                    const float* pos, const int32_t* idx, const uint8_t* mask, float scale,
-                   const float* path_w, void* ws, void* out, void* out_msg, float* lse,
-                   uint32_t flags) {
+                   float env_cutoff, const float* path_w, void* ws, void* out, void* out_msg,
+                   float* lse, uint32_t flags) {
   if (flags & E2F_VALIDATE_INDICES) {
     int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
                                                ws_body_bytes(N, lmax, C, dt));
@@ -306,6 +314,7 @@ int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
   a.sched = sched;
   a.lse = lse;
   a.heads = H;
+  a.env_inv_rc = env_inv(env_cutoff);
   const EaasCoef cf = make_coef(lmax, path_w);
   return hip_status(e2f::launch_aggregate(lmax, dt, V, a, cf, stream));
 }
@@ -392,10 +401,11 @@ int e2f_attn_precouple(hipStream_t stream, int64_t N, int lmax, int C, int dtype
 
 int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                        const float* pos, const int32_t* nbr_idx, const uint8_t* nbr_mask,
-                       float scale, const float* path_w, void* workspace, size_t ws_bytes,
-                       void* out, void* out_msg, float* lse, uint32_t flags) {
+                       float scale, float env_cutoff, const float* path_w, void* workspace,
+                       size_t ws_bytes, void* out, void* out_msg, float* lse, uint32_t flags) {
   int st = check_attn_shape(N, K, lmax, C, H, dtype, flags);
   if (st != E2F_OK) return st;
+  if (bad_env(env_cutoff)) return E2F_ERR_SHAPE;
   if (N == 0) return E2F_OK;
   if (!pos || !nbr_idx || !nbr_mask || !workspace || !out) return E2F_ERR_NULL;
   if (!aligned(pos, 4) || !aligned(nbr_idx, 4) || !aligned(workspace, 16) || !aligned(out, 16) ||
@@ -418,8 +428,8 @@ int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, in
   if (out_msg && overlap({out, ob}, {out_msg, ob})) return E2F_ERR_ALIAS;
   if (lse && (overlap({lse, lb}, {out, ob}) || (out_msg && overlap({lse, lb}, {out_msg, ob}))))
     return E2F_ERR_ALIAS;
-  return aggregate_impl(stream, N, K, lmax, C, H, dtype, pos, nbr_idx, nbr_mask, scale, path_w,
-                        workspace, out, out_msg, lse, flags);
+  return aggregate_impl(stream, N, K, lmax, C, H, dtype, pos, nbr_idx, nbr_mask, scale,
+                        env_cutoff, path_w, workspace, out, out_msg, lse, flags);
 }
 
 }  // extern "C"
@@ -460,10 +470,11 @@ int precouple_proj_impl(hipStream_t stream, int64_t N, int lmax, int C, int dt, 
 int forward_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                  const float* pos, const void* h, const void* w_q, const void* w_k,
                  const void* w_v, const int32_t* nbr_idx, const uint8_t* nbr_mask, float scale,
-                 const float* path_w, void* workspace, size_t ws_bytes, void* out, void* out_msg,
-                 float* lse, uint32_t flags, bool proj) {
+                 float env_cutoff, const float* path_w, void* workspace, size_t ws_bytes,
+                 void* out, void* out_msg, float* lse, uint32_t flags, bool proj) {
   int st = check_attn_shape(N, K, lmax, C, H, dtype, flags);
   if (st != E2F_OK) return st;
+  if (bad_env(env_cutoff)) return E2F_ERR_SHAPE;
   if (N == 0) return E2F_OK;
   if (!h) return E2F_ERR_NULL;
   if (!aligned(h, 16)) return E2F_ERR_ALIGN;
@@ -504,8 +515,8 @@ int forward_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, i
     st = precouple_impl(stream, N, lmax, C, dtype, pos, h, path_w, workspace, ws_bytes);
   }
   if (st != E2F_OK) return st;
-  return aggregate_impl(stream, N, K, lmax, C, H, dtype, pos, nbr_idx, nbr_mask, scale, path_w,
-                        workspace, out, out_msg, lse, flags);
+  return aggregate_impl(stream, N, K, lmax, C, H, dtype, pos, nbr_idx, nbr_mask, scale,
+                        env_cutoff, path_w, workspace, out, out_msg, lse, flags);
 }
 
 }  // namespace
@@ -514,20 +525,22 @@ extern "C" {
 
 int e2f_attn_forward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                      const float* pos, const void* h, const int32_t* nbr_idx,
-                     const uint8_t* nbr_mask, float scale, const float* path_w, void* workspace,
-                     size_t ws_bytes, void* out, void* out_msg, float* lse, uint32_t flags) {
+                     const uint8_t* nbr_mask, float scale, float env_cutoff,
+                     const float* path_w, void* workspace, size_t ws_bytes, void* out,
+                     void* out_msg, float* lse, uint32_t flags) {
   return forward_impl(stream, N, K, lmax, C, H, dtype, pos, h, nullptr, nullptr, nullptr,
-                      nbr_idx, nbr_mask, scale, path_w, workspace, ws_bytes, out, out_msg, lse,
-                      flags, false);
+                      nbr_idx, nbr_mask, scale, env_cutoff, path_w, workspace, ws_bytes, out,
+                      out_msg, lse, flags, false);
 }
 
 int e2f_attn_forward_proj(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                           const float* pos, const void* h, const void* w_q, const void* w_k,
                           const void* w_v, const int32_t* nbr_idx, const uint8_t* nbr_mask,
-                          float scale, const float* path_w, void* workspace, size_t ws_bytes,
-                          void* out, void* out_msg, float* lse, uint32_t flags) {
+                          float scale, float env_cutoff, const float* path_w, void* workspace,
+                          size_t ws_bytes, void* out, void* out_msg, float* lse, uint32_t flags) {
   return forward_impl(stream, N, K, lmax, C, H, dtype, pos, h, w_q, w_k, w_v, nbr_idx, nbr_mask,
-                      scale, path_w, workspace, ws_bytes, out, out_msg, lse, flags, true);
+                      scale, env_cutoff, path_w, workspace, ws_bytes, out, out_msg, lse, flags,
+                      true);
 }
 
 int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int dtype,
@@ -559,12 +572,14 @@ size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int 
 
 int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                       const float* pos, const void* h, const int32_t* nbr_idx,
-                      const uint8_t* nbr_mask, float scale, const float* path_w,
-                      const void* workspace, size_t ws_bytes, const void* msg, const float* lse,
-                      const void* grad_out, void* grad_h, float* grad_pos,
-                      void* bwd_workspace, size_t bwd_ws_bytes, uint32_t flags) {
+                      const uint8_t* nbr_mask, float scale, float env_cutoff,
+                      const float* path_w, const void* workspace, size_t ws_bytes,
+                      const void* msg, const float* lse, const void* grad_out, void* grad_h,
+                      float* grad_pos, void* bwd_workspace, size_t bwd_ws_bytes,
+                      uint32_t flags) {
   int st = check_attn_shape(N, K, lmax, C, H, dtype, flags);
   if (st != E2F_OK) return st;
+  if (bad_env(env_cutoff)) return E2F_ERR_SHAPE;
   if (flags & E2F_VALIDATE_INDICES) return E2F_ERR_SHAPE;  // not offered for the backward
   if (dtype != E2F_F32) return E2F_ERR_UNSUPPORTED;         // fp32 storage only
   if (N == 0) return E2F_OK;
@@ -640,6 +655,7 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
   const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)d);
   a.scale = (float)sc;
   a.scale_log2e = (float)(sc * 1.4426950408889634);
+  a.env_inv_rc = env_inv(env_cutoff);
   const EaasCoef cf = make_coef(lmax, path_w);
   return hip_status(e2f::launch_backward(lmax, V, a, cf, stream));
 }

@@ -59,6 +59,7 @@ struct AggArgs {
   const int32_t* sched;    // [N] processing order of the targets
   float* lse;              // [N, H] natural log-sum-exp of each target's logits, or nullptr
   int heads;               // H
+  float env_inv_rc;        // 1 / r_env of the distance envelope (kernels with the envelope only)
 };
 
 // Backward pass (vector-Jacobian product) arguments, fp32 storage.
@@ -87,6 +88,7 @@ struct BwdArgs {
   int head_lanes;
   float scale;
   float scale_log2e;
+  float env_inv_rc;        // 1 / r_env of the distance envelope, 0 = none
 };
 
 // Learned projections fused with the pre-coupling (storage type T for h and

@@ -113,10 +113,11 @@ __global__ __launch_bounds__(256) void k_eaas(EaasArgs a, EaasCoef cf) {
 
 // ------------------------------------------------------------------ K2
 
-template <int LMAX, int V, typename T, int U, int HL, bool BUF>
+template <int LMAX, int V, typename T, int U, int HL, bool BUF, bool ENV>
 __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
   constexpr int S = ncomp(LMAX);
   __shared__ int s_nb[kWavesPerBlock][kTile];
+  __shared__ float s_le[kWavesPerBlock][ENV ? kTile : 1];  // log2 envelope of each sorted slot
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   // Workgroups are dealt to the XCDs round-robin; give XCD x the x-th
@@ -201,6 +202,18 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
         wave_sync();
       }
     }
+    if constexpr (ENV) {
+      // log2 of the distance envelope per sorted slot; it joins the base-2 logit,
+      // so the slot's weight is e_ij exp(s_ij) in numerator and normaliser alike
+      // (-inf at or beyond the cutoff: weight 0)
+      const float xi = a.pos[3 * i], yi = a.pos[3 * i + 1], zi = a.pos[3 * i + 2];
+      for (int e = lane; e < cnt; e += 64) {
+        const int j = nb[e];
+        s_le[w][e] = envelope_term(xi - a.pos[3 * j], yi - a.pos[3 * j + 1],
+                                   zi - a.pos[3 * j + 2], a.env_inv_rc).log2u;
+      }
+      wave_sync();
+    }
 
     for (int n0 = 0; n0 < cnt; n0 += P * U) {
       // Past the end of the list a subgroup re-reads the tile's last valid
@@ -231,7 +244,9 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
 #pragma unroll
         for (int v = 0; v < V; ++v) dt = fmaf(q[v], kv[u][0].get(v), dt);
         dt = head_sum_t<HL>(dt, a.head_lanes);
-        s[u] = val[u] ? dt * a.scale_log2e : -INFINITY;
+        float le = 0.0f;
+        if constexpr (ENV) le = s_le[w][val[u] ? n0 + u * P + sub : 0];
+        s[u] = val[u] ? dt * a.scale_log2e + le : -INFINITY;
         mx = fmaxf(mx, s[u]);
       }
       // rescale only when some lane's running max moved (rare after the first blocks)
@@ -507,7 +522,7 @@ int eaas_go(int V, const EaasArgs& a, const EaasCoef& cf, hipStream_t s) {
   return last_error();
 }
 
-template <int L, typename T>
+template <int L, typename T, bool E>
 int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
   constexpr int U = 4;  // neighbours per subgroup in flight per iteration
   const int64_t blocks = (a.N + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -520,29 +535,29 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     // bf16, 8 channels per lane: one neighbour per subgroup per iteration
     if (V == 8 && buf && a.head_lanes == 1) {
-      hipLaunchKernelGGL((k_aggregate<L, 8, T, 1, 1, true>), grid, blk, 0, s, a, cf);
+      hipLaunchKernelGGL((k_aggregate<L, 8, T, 1, 1, true, E>), grid, blk, 0, s, a, cf);
       return last_error();
     }
     if (V == 8 && buf && a.head_lanes == 2) {
-      hipLaunchKernelGGL((k_aggregate<L, 8, T, 1, 2, true>), grid, blk, 0, s, a, cf);
+      hipLaunchKernelGGL((k_aggregate<L, 8, T, 1, 2, true, E>), grid, blk, 0, s, a, cf);
       return last_error();
     }
     if (V == 8) {
-      hipLaunchKernelGGL((k_aggregate<L, 8, T, 1, 0, false>), grid, blk, 0, s, a, cf);
+      hipLaunchKernelGGL((k_aggregate<L, 8, T, 1, 0, false, E>), grid, blk, 0, s, a, cf);
       return last_error();
     }
   }
   if (V == 4 && buf && a.head_lanes == 2) {
-    hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 2, true>), grid, blk, 0, s, a, cf);
+    hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 2, true, E>), grid, blk, 0, s, a, cf);
   } else if (V == 4 && buf && a.head_lanes == 1) {
-    hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 1, true>), grid, blk, 0, s, a, cf);
+    hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 1, true, E>), grid, blk, 0, s, a, cf);
   } else if (V == 4 && buf && a.head_lanes == 4) {
-    hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 4, true>), grid, blk, 0, s, a, cf);
+    hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 4, true, E>), grid, blk, 0, s, a, cf);
   } else {
     switch (V) {
-      case 1: hipLaunchKernelGGL((k_aggregate<L, 1, T, U, 0, false>), grid, blk, 0, s, a, cf); break;
-      case 2: hipLaunchKernelGGL((k_aggregate<L, 2, T, U, 0, false>), grid, blk, 0, s, a, cf); break;
-      case 4: hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 0, false>), grid, blk, 0, s, a, cf); break;
+      case 1: hipLaunchKernelGGL((k_aggregate<L, 1, T, U, 0, false, E>), grid, blk, 0, s, a, cf); break;
+      case 2: hipLaunchKernelGGL((k_aggregate<L, 2, T, U, 0, false, E>), grid, blk, 0, s, a, cf); break;
+      case 4: hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 0, false, E>), grid, blk, 0, s, a, cf); break;
       default: return static_cast<int>(hipErrorInvalidValue);
     }
   }
@@ -559,12 +574,12 @@ int eaas_l(int lmax, int V, bool ws, const EaasArgs& a, const EaasCoef& cf, hipS
   }
 }
 
-template <typename T>
+template <typename T, bool E>
 int agg_l(int lmax, int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
   switch (lmax) {
-    case 0: return agg_go<0, T>(V, a, cf, s);
-    case 1: return agg_go<1, T>(V, a, cf, s);
-    case 2: return agg_go<2, T>(V, a, cf, s);
+    case 0: return agg_go<0, T, E>(V, a, cf, s);
+    case 1: return agg_go<1, T, E>(V, a, cf, s);
+    case 2: return agg_go<2, T, E>(V, a, cf, s);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }
@@ -579,7 +594,11 @@ int launch_eaas(int lmax, int dtype, int V, bool to_workspace, const EaasArgs& a
 
 int launch_aggregate(int lmax, int dtype, int V, const AggArgs& a, const EaasCoef& cf,
                      hipStream_t s) {
-  return dtype == 0 ? agg_l<float>(lmax, V, a, cf, s) : agg_l<uint16_t>(lmax, V, a, cf, s);
+  if (a.env_inv_rc > 0.0f)
+    return dtype == 0 ? agg_l<float, true>(lmax, V, a, cf, s)
+                      : agg_l<uint16_t, true>(lmax, V, a, cf, s);
+  return dtype == 0 ? agg_l<float, false>(lmax, V, a, cf, s)
+                    : agg_l<uint16_t, false>(lmax, V, a, cf, s);
 }
 
 int launch_frames(int lmax, int64_t n, const float* r, float* Q, float* D, hipStream_t s) {

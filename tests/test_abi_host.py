@@ -92,22 +92,23 @@ def test_workspace_bytes():
 
 def _agg(**kw):
     a = dict(stream=None, N=1000, K=64, lmax=2, C=128, H=16, dt=0, pos=fake(1), idx=fake(2),
-             mask=fake(3), scale=0.0, pw=None, ws=fake(4), ws_bytes=1 << 30, out=fake(8),
-             msg=None, lse=None, flags=0)
+             mask=fake(3), scale=0.0, env=0.0, pw=None, ws=fake(4), ws_bytes=1 << 30,
+             out=fake(8), msg=None, lse=None, flags=0)
     a.update(kw)
     return lib.e2f_attn_aggregate(a["stream"], a["N"], a["K"], a["lmax"], a["C"], a["H"], a["dt"],
-                                  a["pos"], a["idx"], a["mask"], a["scale"], a["pw"], a["ws"],
-                                  a["ws_bytes"], a["out"], a["msg"], a["lse"], a["flags"])
+                                  a["pos"], a["idx"], a["mask"], a["scale"], a["env"], a["pw"],
+                                  a["ws"], a["ws_bytes"], a["out"], a["msg"], a["lse"], a["flags"])
 
 
 def _fwd(**kw):
     a = dict(stream=None, N=1000, K=64, lmax=2, C=128, H=16, dt=0, pos=fake(1), h=fake(9),
-             idx=fake(2), mask=fake(3), scale=0.0, pw=None, ws=fake(4), ws_bytes=1 << 30,
-             out=fake(8), msg=None, lse=None, flags=0)
+             idx=fake(2), mask=fake(3), scale=0.0, env=0.0, pw=None, ws=fake(4),
+             ws_bytes=1 << 30, out=fake(8), msg=None, lse=None, flags=0)
     a.update(kw)
     return lib.e2f_attn_forward(a["stream"], a["N"], a["K"], a["lmax"], a["C"], a["H"], a["dt"],
-                                a["pos"], a["h"], a["idx"], a["mask"], a["scale"], a["pw"],
-                                a["ws"], a["ws_bytes"], a["out"], a["msg"], a["lse"], a["flags"])
+                                a["pos"], a["h"], a["idx"], a["mask"], a["scale"], a["env"],
+                                a["pw"], a["ws"], a["ws_bytes"], a["out"], a["msg"], a["lse"],
+                                a["flags"])
 
 
 def _eaas(**kw):
@@ -199,12 +200,13 @@ def test_frames_errors():
 
 def _bwd(**kw):
     a = dict(stream=None, N=1000, K=64, lmax=2, C=128, H=16, dt=0, pos=fake(1), h=fake(9),
-             idx=fake(2), mask=fake(3), scale=0.0, pw=None, ws=fake(4), ws_bytes=1 << 30,
-             msg=fake(10), lse=fake(11), gout=fake(12), gh=fake(13), gp=fake(14), bws=fake(16),
-             bws_bytes=1 << 30, flags=0)
+             idx=fake(2), mask=fake(3), scale=0.0, env=0.0, pw=None, ws=fake(4),
+             ws_bytes=1 << 30, msg=fake(10), lse=fake(11), gout=fake(12), gh=fake(13),
+             gp=fake(14), bws=fake(16), bws_bytes=1 << 30, flags=0)
     a.update(kw)
     return lib.e2f_attn_backward(a["stream"], a["N"], a["K"], a["lmax"], a["C"], a["H"], a["dt"],
-                                 a["pos"], a["h"], a["idx"], a["mask"], a["scale"], a["pw"],
+                                 a["pos"], a["h"], a["idx"], a["mask"], a["scale"], a["env"],
+                                 a["pw"],
                                  a["ws"], a["ws_bytes"], a["msg"], a["lse"], a["gout"], a["gh"],
                                  a["gp"], a["bws"], a["bws_bytes"], a["flags"])
 
@@ -239,13 +241,21 @@ def _pproj(**kw):
 
 def _fproj(**kw):
     a = dict(stream=None, N=1000, K=64, lmax=2, C=128, H=16, dt=0, pos=fake(1), h=fake(9),
-             wq=fake(20), wk=fake(21), wv=fake(22), idx=fake(2), mask=fake(3), scale=0.0, pw=None,
-             ws=fake(4), ws_bytes=1 << 30, out=fake(8), msg=None, lse=None, flags=0)
+             wq=fake(20), wk=fake(21), wv=fake(22), idx=fake(2), mask=fake(3), scale=0.0, env=0.0,
+             pw=None, ws=fake(4), ws_bytes=1 << 30, out=fake(8), msg=None, lse=None, flags=0)
     a.update(kw)
     return lib.e2f_attn_forward_proj(a["stream"], a["N"], a["K"], a["lmax"], a["C"], a["H"],
                                      a["dt"], a["pos"], a["h"], a["wq"], a["wk"], a["wv"],
-                                     a["idx"], a["mask"], a["scale"], a["pw"], a["ws"],
+                                     a["idx"], a["mask"], a["scale"], a["env"], a["pw"], a["ws"],
                                      a["ws_bytes"], a["out"], a["msg"], a["lse"], a["flags"])
+
+
+@pytest.mark.parametrize("fn", [_agg, _fwd, _bwd, _fproj])
+def test_envelope_cutoff_errors(fn):
+    for bad in (-1.0, float("inf"), float("-inf"), float("nan")):
+        assert fn(env=bad) == C["E2F_ERR_SHAPE"], bad
+    assert fn(env=3.0, N=0, pos=None, h=None) == C["E2F_OK"]
+    assert fn(env=3.0, out=None, gh=None) == C["E2F_ERR_NULL"]   # a valid radius passes the check
 
 
 @pytest.mark.parametrize("fn", [_pproj, _fproj])

@@ -1,0 +1,199 @@
+"""GPU envelope-weighted softmax (``env_cutoff``) against the oracle.
+
+Forward: block-relative error of the message and the output (1e-4 fp32,
+2e-2 bf16 storage), slots beyond the envelope radius weigh nothing, rows with
+every slot beyond it are exactly zero, and the log-sum-exp includes ln e.
+Backward: dL/dh and dL/dpos (which now also flows through every pair distance)
+against the float64 autograd oracle, with the metrics of the plain backward.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from gen import make_config
+from oracle.attn import attn_forward as oracle_attn
+from oracle.attn import envelope
+from oracle.grad import attn_backward as oracle_backward
+from tests.helpers import TOL_BF16, TOL_F32, block_rel_err, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def e2f():
+    import interatomic_potentials_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return torch.device("cuda:0")
+
+
+def T(x, dev, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    return t if dtype is None else t.to(dtype)
+
+
+def random_graph(rng, pos, K, p=0.7):
+    """K random sources j != i per row, about p of them valid."""
+    N = pos.shape[0]
+    idx = rng.integers(0, N - 1, size=(N, K)).astype(np.int32)
+    idx += (idx >= np.arange(N)[:, None])           # skip i itself
+    mask = (rng.random((N, K)) < p).astype(np.uint8)
+    return idx, mask
+
+
+def pos_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    nr = np.linalg.norm(ref, axis=1)
+    den = np.maximum(nr, 1e-3 * nr.max() + 1e-300)
+    return float((np.linalg.norm(got - ref, axis=1) / den).max())
+
+
+@pytest.mark.parametrize("name,r_env", [("tiny", 5.0), ("water", 5.0), ("water", 3.2)])
+def test_small_configs_full(e2f, dev, name, r_env):
+    cfg = make_config(name)
+    s = cfg.spec
+    say(f"envelope {name}: r_env={r_env} (list cutoff {s.cutoff}) N={cfg.N} E={cfg.nl.n_edges}")
+    out, msg = e2f.attn_forward(T(cfg.pos, dev), T(cfg.h, dev), T(cfg.idx, dev), T(cfg.mask, dev),
+                                s.H, return_msg=True, env_cutoff=r_env)
+    ref, ref_msg = oracle_attn(cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, s.lmax, return_msg=True,
+                               env_cutoff=r_env, chunk_edges=4096)
+    assert block_rel_err(to_host(msg), ref_msg, s.lmax) <= TOL_F32
+    assert block_rel_err(to_host(out), ref, s.lmax) <= TOL_F32
+    plain = e2f.attn_forward(T(cfg.pos, dev), T(cfg.h, dev), T(cfg.idx, dev), T(cfg.mask, dev),
+                             s.H)
+    assert not torch.equal(plain, out)             # the envelope does change the weights
+
+
+@pytest.mark.parametrize("name", ["large", "scaleout"])
+def test_big_configs_sampled(e2f, dev, name):
+    cfg = make_config(name)
+    s = cfg.spec
+    say(f"envelope {name}: r_env={s.cutoff} dtype={s.dtype} (sampled targets)")
+    dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    out, msg = e2f.attn_forward(T(cfg.pos, dev), T(cfg.h, dev, dt), T(cfg.idx, dev),
+                                T(cfg.mask, dev), s.H, return_msg=True, env_cutoff=s.cutoff)
+    torch.cuda.synchronize()
+    tg = np.random.default_rng(8).choice(cfg.N, 80, replace=False)
+    tgt = torch.from_numpy(tg).to(dev)
+    ref, ref_msg = oracle_attn(cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, s.lmax, targets=tg,
+                               return_msg=True, env_cutoff=s.cutoff, chunk_edges=4096)
+    tol = TOL_BF16 if s.dtype == "bf16" else TOL_F32
+    assert block_rel_err(to_host(msg[tgt]), ref_msg, s.lmax) <= tol
+    assert block_rel_err(to_host(out[tgt]), ref, s.lmax) <= tol
+
+
+@pytest.mark.parametrize("lmax,C,H,K,dtype", [(0, 32, 4, 10, "f32"), (1, 16, 2, 33, "f32"),
+                                              (2, 64, 4, 300, "f32"), (2, 128, 16, 64, "f32"),
+                                              (2, 128, 16, 64, "bf16"), (1, 8, 8, 7, "f32")])
+def test_shapes_and_slots_beyond_the_radius(e2f, dev, lmax, C, H, K, dtype):
+    say(f"envelope shapes: lmax={lmax} C={C} H={H} K={K} {dtype}")
+    rng = np.random.default_rng(lmax * 100 + C + K)
+    N = 160
+    S = (lmax + 1) ** 2
+    pos = (rng.random((N, 3)) * 9).astype(np.float32)
+    h = rng.standard_normal((N, S, C)).astype(np.float32)
+    if dtype == "bf16":
+        h = torch.from_numpy(h).to(torch.bfloat16).to(torch.float32).numpy()
+    idx, mask = random_graph(rng, pos, K)
+    mask[5] = 0                                     # no valid slot
+    r_env = 4.0                                     # many listed sources lie beyond it
+    pos[11] = pos[idx[11]].mean(axis=0) + 500.0     # every source of target 11 is beyond r_env
+    d = np.linalg.norm(pos[:, None, :].astype(np.float64) - pos[idx].astype(np.float64), axis=-1)
+    assert ((d >= r_env) & (mask != 0)).any() and ((d < r_env) & (mask != 0)).any()
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out, msg, lse = e2f.attn_forward(T(pos, dev), T(h, dev, tdt), T(idx, dev), T(mask, dev), H,
+                                     return_msg=True, return_lse=True, env_cutoff=r_env)
+    ref, ref_msg = oracle_attn(pos, h, idx, mask, H, lmax, return_msg=True, env_cutoff=r_env)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    assert block_rel_err(to_host(msg), ref_msg, lmax) <= tol
+    assert block_rel_err(to_host(out), ref, lmax) <= tol
+    for t in (5, 11):
+        assert (out[t] == 0).all() and (msg[t] == 0).all()
+        assert torch.isinf(lse[t]).all() and (lse[t] < 0).all()
+    # log-sum-exp of the enveloped logits, rows with something inside the radius
+    hh = h.astype(np.float64)
+    dd = C // H
+    q = hh[:, 0, :].reshape(N, H, dd)
+    for i in (0, 1, 2, 40, 77):
+        sel = mask[i] != 0
+        js = idx[i][sel]
+        u = envelope(d[i][sel] / r_env)
+        if not (u > 0).any():
+            continue
+        logit = (q[i][None] * q[js]).sum(-1) / np.sqrt(dd)
+        mx = logit.max(0)
+        want = mx + np.log((u[:, None] * np.exp(logit - mx)).sum(0))
+        np.testing.assert_allclose(lse[i].cpu().numpy(), want, rtol=1e-5, atol=1e-5)
+
+
+def test_projections_with_envelope(e2f, dev):
+    from gen import proj_weights
+    cfg = make_config("water")
+    s = cfg.spec
+    say("envelope + learned projections: water")
+    w = proj_weights(s.lmax, s.C, 13, "f32")
+    out = e2f.attn_forward(T(cfg.pos, dev), T(cfg.h, dev), T(cfg.idx, dev), T(cfg.mask, dev), s.H,
+                           proj=tuple(T(x, dev) for x in w), env_cutoff=4.5)
+    ref = oracle_attn(cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, s.lmax, proj=w, env_cutoff=4.5,
+                      chunk_edges=4096)
+    assert block_rel_err(to_host(out), ref, s.lmax) <= TOL_F32
+
+
+def gpu_backward(e2f, dev, pos, h, idx, mask, H, g, r_env, **kw):
+    p, hh, ii, mm = T(pos, dev), T(h, dev), T(idx, dev), T(mask, dev)
+    lmax = int(round(h.shape[1] ** 0.5)) - 1
+    ws = e2f.attn_precouple(p, hh)
+    out, msg, lse = e2f.attn_aggregate(p, ii, mm, ws, H, lmax, h.shape[2], torch.float32,
+                                       return_msg=True, return_lse=True, env_cutoff=r_env)
+    gh, gp = e2f.attn_backward(p, hh, ii, mm, H, ws, msg, lse, T(g, dev), env_cutoff=r_env, **kw)
+    torch.cuda.synchronize()
+    return gh.cpu().numpy(), gp.cpu().numpy()
+
+
+@pytest.mark.parametrize("lmax,C,H,K", [(0, 16, 2, 12), (1, 16, 2, 20), (2, 32, 4, 24),
+                                        (2, 128, 16, 64), (2, 64, 4, 300)])
+def test_backward_with_envelope(e2f, dev, lmax, C, H, K):
+    say(f"envelope backward: lmax={lmax} C={C} H={H} K={K}")
+    rng = np.random.default_rng(lmax * 7 + C + K)
+    N = 80
+    S = (lmax + 1) ** 2
+    pos = (rng.random((N, 3)) * 7).astype(np.float32)
+    h = rng.standard_normal((N, S, C)).astype(np.float32)
+    idx, mask = random_graph(rng, pos, K, p=0.6)
+    mask[7] = 0
+    pos[13] += 100.0          # target 13 and source 13: every pair beyond r_env (lse = -inf)
+    g = rng.standard_normal((N, S, C)).astype(np.float32)
+    r_env = 5.0
+    gh, gp = gpu_backward(e2f, dev, pos, h, idx, mask, H, g, r_env)
+    rh, rp = oracle_backward(pos, h, idx, mask, H, lmax, g, env_cutoff=r_env)
+    assert block_rel_err(gh, rh, lmax) <= TOL_F32
+    assert pos_err(gp, rp) <= TOL_F32
+    # the envelope's own share of dL/dpos is not negligible here
+    _, rp0 = oracle_backward(pos, h, idx, mask, H, lmax, g)
+    assert pos_err(rp0, rp) > 1e-2
+
+
+def test_backward_with_envelope_water_and_determinism(e2f, dev):
+    cfg = make_config("water")
+    s = cfg.spec
+    say("envelope backward: water, twice and in index order")
+    g = np.random.default_rng(3).standard_normal(cfg.h.shape).astype(np.float32)
+    a = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g, 4.0)
+    rh, rp = oracle_backward(cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, s.lmax, g, env_cutoff=4.0)
+    assert block_rel_err(a[0], rh, s.lmax) <= TOL_F32
+    assert pos_err(a[1], rp) <= TOL_F32
+    b = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g, 4.0,
+                     targets_in_order=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
