@@ -299,6 +299,66 @@ def bench_proj(args, e2f, cfg, pos, h, idx, mask, ws, out, stream):
             "hbm_frac": hbm_frac, "weights": "seeded N(0, 1/C), proj_weights(seed=13)"}
 
 
+def _time(stream, steps, fn):
+    """Mean milliseconds of fn() over `steps` launches, HIP events on `stream`."""
+    import numpy as np
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
+        fn()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+
+def bench_neighbours(args, e2f, cfg, pos, stream):
+    """The GPU neighbour-list builder on the same positions, cutoff and K (not part of a step)."""
+    import numpy as np
+    import torch
+
+    s = cfg.spec
+    N, K = cfg.N, s.K
+    nws = torch.empty(e2f.neighbour_workspace_bytes(N), dtype=torch.uint8, device=pos.device)
+    for _ in range(args.warmup):
+        idx, mask = e2f.neighbour_list(pos, s.cutoff, K, ws=nws)
+    torch.cuda.synchronize()
+    same = bool(np.array_equal(idx.cpu().numpy(), cfg.idx)
+                and np.array_equal(mask.cpu().numpy(), cfg.mask))
+    ms = _time(stream, args.steps, lambda: e2f.neighbour_list(pos, s.cutoff, K, ws=nws))
+    # per target: its 27 cells' grouped positions and indices are read (mostly from cache);
+    # the algorithmic floor is reading the positions once and writing the rows
+    nbytes = N * (12 + 16 + 4 + 4) + N * K * 5
+    print(f"[bench] neighbour list: {ms:.3f} ms ({N / (ms * 1e-3) / 1e6:.1f} M atoms/s), rows equal "
+          f"to the generator's: {same}", file=sys.stderr, flush=True)
+    return {"kernel": "e2f_neighbour_list (cell list, Morton-ordered cells, one wave per target)",
+            "ms": ms, "atoms_per_s": N / (ms * 1e-3), "rows_equal_generator": same,
+            "output_bytes": N * K * 5, "min_bytes": nbytes,
+            "note": "builds the padded list the step consumes; not inside the timed step"}
+
+
+def bench_envelope(args, e2f, cfg, pos, h, idx, mask, ws, out, stream, k2_ms):
+    """The same step with the smooth distance envelope on the softmax weights (r_env = cutoff)."""
+    import torch
+    s = cfg.spec
+    tdt = h.dtype
+
+    def agg():
+        e2f.attn_aggregate(pos, idx, mask, ws, s.H, s.lmax, s.C, tdt, out=out,
+                           env_cutoff=s.cutoff)
+
+    e2f.attn_precouple(pos, h, ws)
+    for _ in range(args.warmup):
+        agg()
+    torch.cuda.synchronize()
+    ms = _time(stream, args.steps, agg)
+    print(f"[bench] envelope: aggregate {ms:.3f} ms (plain {k2_ms:.3f} ms)", file=sys.stderr,
+          flush=True)
+    return {"kernel": "k_aggregate with the distance envelope (r_env = list cutoff)",
+            "aggregate_ms": ms, "edges_per_s_aggregate": cfg.nl.n_edges / (ms * 1e-3),
+            "overhead_vs_plain": ms / k2_ms - 1.0}
+
+
 def bench_eaas(args, e2f, dev):
     """The EAAS tensor product on its own (e2f_eaas_couple over 2^20 vectors)."""
     import numpy as np
@@ -349,6 +409,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-proj", action="store_true",
                     help="skip the learned-projection variant (MFMA) timed after the main step")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the envelope variant and the neighbour-list build timed after it")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward pass (dL/dh, dL/dpos) of the same workload")
     ap.add_argument("--index-order-reference", action="store_true",
@@ -499,6 +561,10 @@ def main(argv=None):
     }
     if not args.no_proj:
         result["projected"] = bench_proj(args, e2f, cfg, pos, h, idx, mask, ws, out, stream)
+    if not args.no_extras:
+        result["envelope"] = bench_envelope(args, e2f, cfg, pos, h, idx, mask, ws, out, stream,
+                                            k2_ms)
+        result["neighbour_list"] = bench_neighbours(args, e2f, cfg, pos, stream)
     if args.backward:
         result["backward"] = bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream)
     if not args.no_cpu_baseline:
