@@ -113,6 +113,8 @@ __global__ __launch_bounds__(256) void k_eaas(EaasArgs a, EaasCoef cf) {
 
 // ------------------------------------------------------------------ K2
 
+constexpr float kSlack = 8.0f;   // lazy-rescale slack of the running max (base 2)
+
 template <int LMAX, int V, typename T, int U, int HL, bool BUF, bool ENV>
 __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
   constexpr int S = ncomp(LMAX);
@@ -249,8 +251,10 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
         s[u] = val[u] ? dt * a.scale_log2e + le : -INFINITY;
         mx = fmaxf(mx, s[u]);
       }
-      // rescale only when some lane's running max moved (rare after the first blocks)
-      if (__any(mx > mu)) {
+      // Lazy rescale: mu only has to bound the logits seen so far to within
+      // kSlack (base 2), so weights stay below 2^kSlack until the final
+      // normalisation; the state is rescaled only when a logit exceeds it by more
+      if (__any(mx > mu + kSlack)) {
         const float corr = exp2_fast(mu - mx);
         z *= corr;
 #pragma unroll
@@ -326,6 +330,324 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
   }
 #pragma unroll
   for (int r = 0; r < S; ++r) VecIO<T, V>::store(op + r * C, y[r]);
+}
+
+// ------------------------------------------------ K2, targets sharing rows
+//
+// The same three steps for T spatially adjacent targets per wavefront (fp32
+// storage, 4 channels per lane).  Their valid slots are merged into one
+// union of distinct sources; each union source's S + 1 rows are read once and
+// applied to every target that lists it (a source in c of a target's slots
+// weighs c exp(s), so repeated slots still count once each).  Adjacent targets share most of their neighbours, so the
+// rows read per target drop by the union's sharing factor.
+//
+// Subgroup g streams the union sources j with j mod P == g in increasing j,
+// and a target's state is touched only by sources it lists (a subgroup-uniform
+// branch), so every target's arithmetic -- which subgroup adds which source,
+// in which order -- depends on its own neighbour set alone: not on the other
+// targets sharing the wave, the schedule, or slot order.
+constexpr int kMtMaxK = 256;      // longest neighbour row this kernel takes
+
+constexpr int pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+// Two targets per wave, three union sources per subgroup in flight: measured
+// against three or four targets (more sharing, but more subgroups idling on
+// targets that do not list their source) and one or two sources in flight.
+constexpr int kMtTargets = 2;     // targets per wave
+constexpr int kMtInflight = 3;    // union sources per subgroup in flight
+
+template <int LMAX, int T, int U, int HL>
+__global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
+  constexpr int S = ncomp(LMAX);
+  constexpr int V = 4;
+  constexpr int EN = T * kMtMaxK;            // merged slots per wave, at most
+  constexpr int EN2 = pow2_ceil(EN);         // the sort pads the keys to a power of two
+  constexpr int CW = (T + 1) / 2;            // count words per union source (16 bits per target)
+  static_assert(T >= 1 && T <= 4, "two bits of target index in the merge key");
+  __shared__ uint32_t s_key[kWavesPerBlock][EN2];     // merge keys, sorted
+  __shared__ int32_t s_uj[kWavesPerBlock][EN];        // union sources, bucket by bucket
+  __shared__ uint32_t s_cnt[kWavesPerBlock][CW][EN];  // per union source: slot counts per target
+  __shared__ int32_t s_bk[kWavesPerBlock][2][64];     // per bucket: union sources, then start
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
+  const int64_t blk = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int64_t slot0 = (blk * kWavesPerBlock + w) * T;
+  if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
+  const int64_t N = a.N;
+  const int K = a.K;
+  const int C = a.C;
+  int64_t tg[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t sl = slot0 + t;
+    int64_t i = -1;
+    if (sl < N) i = a.sched ? (int64_t)a.sched[sl] : sl;
+    tg[t] = (i >= 0 && i < N) ? i : -1;
+  }
+  const int lg = a.lane_log;
+  const int lgp = 6 - lg;                    // log2 of the subgroups per wave
+  const int P = 1 << lgp;
+  const int sub = lane >> lg;
+  const int c0 = (lane & ((1 << lg) - 1)) * V;
+  const bool act = c0 < C;
+  const int c0_load = act ? c0 : 0;
+  const int64_t row = (int64_t)(S + 1) * C;
+  const uint32_t row_bytes = (uint32_t)(row * 4);
+  const uint32_t cbytes = (uint32_t)C * 4u;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(a.ws, (uint32_t)(N * row * 4));
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t* key = s_key[w];
+  int32_t* uj = s_uj[w];
+  int32_t* bcnt = s_bk[w][0];
+  int32_t* bstart = s_bk[w][1];
+  // merge key: bucket j mod P in the top lgp bits, then j / P, then the target
+  // (j < 2^30), so the sorted keys list each bucket's sources in increasing j
+  auto make_key = [&](uint32_t j, uint32_t t) -> uint32_t {
+    const uint32_t hi = lgp ? (j & (uint32_t)(P - 1)) << (32 - lgp) : 0u;
+    return hi | ((j >> lgp) << 2) | t;
+  };
+  auto key_source = [&](uint32_t k) -> int32_t {
+    const uint32_t b = lgp ? k >> (32 - lgp) : 0u;
+    const uint32_t q = (k & (lgp ? (~0u >> lgp) : ~0u)) >> 2;
+    return (int32_t)((q << lgp) | b);
+  };
+
+  // 1. merge the targets' valid slots
+  int cnt = 0;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (tg[t] < 0) continue;
+    const int32_t* irow = a.idx + tg[t] * K;
+    const uint8_t* mrow = a.mask + tg[t] * K;
+    for (int u = 0; u < K; u += 64) {
+      const int sl = u + lane;
+      bool ok = false;
+      int j = 0;
+      if (sl < K && mrow[sl] != 0) {
+        j = irow[sl];
+        ok = j >= 0 && (int64_t)j < N;
+      }
+      const uint64_t b = __ballot(ok);
+      if (ok) key[cnt + __popcll(b & below)] = make_key((uint32_t)j, (uint32_t)t);
+      cnt += __popcll(b);
+    }
+  }
+  bcnt[lane] = 0;
+  // 2. sort the keys (bitonic network in LDS, one wave)
+  {
+    int n2 = 1;
+    while (n2 < cnt) n2 <<= 1;
+    for (int e = cnt + lane; e < n2; e += 64) key[e] = 0xffffffffu;
+    wave_sync();
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int e = lane; e < (n2 >> 1); e += 64) {
+          const int lo = ((e & ~(jj - 1)) << 1) | (e & (jj - 1));
+          const uint32_t x = key[lo], y = key[lo + jj];
+          if ((x > y) == ((lo & k) == 0)) {
+            key[lo] = y;
+            key[lo + jj] = x;
+          }
+        }
+        wave_sync();
+      }
+    }
+  }
+  // 3. the union: one entry per distinct source (bucket by bucket), per-target
+  //    slot counts, and each bucket's size
+  int nu = 0;
+  for (int e0 = 0; e0 < cnt; e0 += 64) {
+    const int e = e0 + lane;
+    const bool in = e < cnt;
+    const uint32_t kk = in ? key[e] : 0u;
+    const bool head = in && (e == 0 || (key[e - 1] >> 2) != (kk >> 2));
+    const uint64_t b = __ballot(head);
+    if (head) {
+      const int u = nu + __popcll(b & below);
+      const int32_t j = key_source(kk);
+      uj[u] = j;
+#pragma unroll
+      for (int c = 0; c < CW; ++c) s_cnt[w][c][u] = 0u;
+      atomicAdd(&bcnt[j & (P - 1)], 1);
+    }
+    nu += __popcll(b);
+  }
+  wave_sync();
+  {
+    int run = 0;  // heads before this chunk
+    for (int e0 = 0; e0 < cnt; e0 += 64) {
+      const int e = e0 + lane;
+      const bool in = e < cnt;
+      const uint32_t kk = in ? key[e] : 0u;
+      const bool head = in && (e == 0 || (key[e - 1] >> 2) != (kk >> 2));
+      const uint64_t b = __ballot(head);
+      if (in) {
+        const int u = run + __popcll(b & (below | (1ull << lane))) - 1;
+        const int t = (int)(kk & 3u);
+        atomicAdd(&s_cnt[w][t >> 1][u], 1u << (16 * (t & 1)));
+      }
+      run += __popcll(b);
+    }
+  }
+  // bucket starts: buckets follow each other in the sorted union
+  if (lane == 0) {
+    int acc0 = 0;
+    for (int g = 0; g < P; ++g) {
+      bstart[g] = acc0;
+      acc0 += bcnt[g];
+    }
+  }
+  wave_sync();
+  const int my_cnt = bcnt[sub];
+  const int my_start = bstart[sub];
+  int maxlen = my_cnt;
+  for (int o = 1; o < 64; o <<= 1) maxlen = max(maxlen, __shfl_xor(maxlen, o));
+
+  // 4. stream the union once for all targets
+  float q[T][V];
+  float mu[T], z[T];
+  float acc[T][S][V];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (act && tg[t] >= 0) {
+      VecIO<float, V>::load(static_cast<const float*>(a.q) + tg[t] * C + c0, q[t]);
+    } else {
+#pragma unroll
+      for (int v = 0; v < V; ++v) q[t][v] = 0.0f;
+    }
+    mu[t] = -1e30f;
+    z[t] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < S; ++r)
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[t][r][v] = 0.0f;
+  }
+#pragma unroll 1
+  for (int it = 0; it < maxlen; it += U) {
+    Raw<float, V> kv[U][S + 1];
+    uint32_t cw[U][CW];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool val = it + u < my_cnt;
+      // a subgroup past the end of its bucket re-reads some valid source and adds nothing
+      const int nn = val ? my_start + it + u : (my_cnt > 0 ? my_start + my_cnt - 1 : 0);
+      const int jn = uj[nn];
+      const uint32_t voff = (uint32_t)jn * row_bytes + (uint32_t)c0_load * 4u;
+#pragma unroll
+      for (int r = 0; r <= S; ++r)
+        buffer_load_raw<float, V>(rsrc, voff, (uint32_t)r * cbytes, kv[u][r]);
+#pragma unroll
+      for (int c = 0; c < CW; ++c) cw[u][c] = val ? s_cnt[w][c][nn] : 0u;
+    }
+    // keep every source's loads in flight before the first use
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint32_t m = (cw[u][t >> 1] >> (16 * (t & 1))) & 0xffffu;
+        if (m != 0u) {   // uniform within the subgroup: targets that do not list j are untouched
+          float dt = 0.0f;
+#pragma unroll
+          for (int v = 0; v < V; ++v) dt = fmaf(q[t][v], kv[u][0].get(v), dt);
+          dt = head_sum_t<HL>(dt, a.head_lanes);
+          const float sc = dt * a.scale_log2e;
+          // lazy rescale, as in the single-target kernel, but decided per lane
+          // (per head and subgroup): whether the other subgroup happens to be
+          // updating this target must not move this subgroup's reference point
+          const bool need = sc > mu[t] + kSlack;
+          if (__any(need)) {
+            const float mx = need ? sc : mu[t];
+            const float corr = exp2_fast(mu[t] - mx);   // exactly 1 where not needed
+            z[t] *= corr;
+#pragma unroll
+            for (int r = 0; r < S; ++r)
+#pragma unroll
+              for (int v = 0; v < V; ++v) acc[t][r][v] *= corr;
+            mu[t] = mx;
+          }
+          // c slots of the same source weigh c times
+          const float p = exp2_fast(sc - mu[t]) * (float)m;
+          z[t] += p;
+#pragma unroll
+          for (int r = 0; r < S; ++r)
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+              acc[t][r][v] = fmaf(p, kv[u][r + 1].get(v), acc[t][r][v]);
+        }
+      }
+    }
+  }
+
+  // 5. merge the subgroups' partial states, per target, in a fixed order
+  for (int o = 1 << lg; o < 64; o <<= 1) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float mo = __shfl_xor(mu[t], o);
+      const float zo = __shfl_xor(z[t], o);
+      const float mx = fmaxf(mu[t], mo);
+      const float ca = exp2_fast(mu[t] - mx);
+      const float cb = exp2_fast(mo - mx);
+      z[t] = z[t] * ca + zo * cb;
+#pragma unroll
+      for (int r = 0; r < S; ++r) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+          acc[t][r][v] = acc[t][r][v] * ca + __shfl_xor(acc[t][r][v], o) * cb;
+        // a row's exchanges at a time: all of them in flight would need as many
+        // registers again as the accumulators
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mu[t] = mx;
+    }
+  }
+
+  // 6. per target: normalise, target-side EAAS, store.  Subgroup 0 finalises
+  //    every target: its merged state always took the same operand order (it is
+  //    the lower partner at every step), whereas the other subgroups' copies
+  //    differ from it in the last bit.
+  if (!act || sub != 0) return;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t i = tg[t];
+    if (i < 0) continue;
+    if (a.lse != nullptr && (lane & (a.head_lanes - 1)) == 0) {
+      const int d = C / a.heads;
+      a.lse[i * a.heads + c0 / d] =
+          z[t] > 0.0f ? (mu[t] + log2f(z[t])) * 0.6931471805599453f : -INFINITY;
+    }
+    const float inv = z[t] > 0.0f ? 1.0f / z[t] : 0.0f;
+    float m[S][V];
+#pragma unroll
+    for (int r = 0; r < S; ++r)
+#pragma unroll
+      for (int v = 0; v < V; ++v) m[r][v] = acc[t][r][v] * inv;
+    if (a.out_msg != nullptr) {
+      float* mp = static_cast<float*>(a.out_msg) + i * (int64_t)S * C + c0;
+#pragma unroll
+      for (int r = 0; r < S; ++r) VecIO<float, V>::store(mp + r * C, m[r]);
+    }
+    const Frame f = make_frame(a.pos[3 * i], a.pos[3 * i + 1], a.pos[3 * i + 2]);
+    const Dy2 d = make_dy2(f);
+    const Reindex<LMAX> R = make_reindex<LMAX>(cf, f);
+    float* op = static_cast<float*>(a.out) + i * (int64_t)S * C + c0;
+    float y[S][V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float xv[S], yv[S];
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2) xv[s2] = m[s2][v];
+      eaas_channel<LMAX>(xv, yv, f, d, R);
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2) y[s2][v] = yv[s2];
+    }
+#pragma unroll
+    for (int r = 0; r < S; ++r) VecIO<float, V>::store(op + r * C, y[r]);
+  }
 }
 
 // ------------------------------------------------------------ helpers
@@ -544,6 +866,23 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
     }
     if (V == 8) {
       hipLaunchKernelGGL((k_aggregate<L, 8, T, 1, 0, false, E>), grid, blk, 0, s, a, cf);
+      return last_error();
+    }
+  }
+  if constexpr (sizeof(T) == 4 && !E) {
+    // fp32, 4 channels per lane, rows of at most kMtMaxK slots: several targets
+    // per wave share every row they read
+    if (V == 4 && buf && a.K <= kMtMaxK && a.N < ((int64_t)1 << 30) &&
+        (a.head_lanes == 1 || a.head_lanes == 2 || a.head_lanes == 4)) {
+      constexpr int TM = kMtTargets;
+      constexpr int UM = kMtInflight;
+      const int64_t mblocks = (a.N + kWavesPerBlock * TM - 1) / (kWavesPerBlock * TM);
+      const dim3 mgrid((unsigned)((mblocks + kXcds - 1) / kXcds * kXcds));
+      switch (a.head_lanes) {
+        case 1: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 1>), mgrid, blk, 0, s, a, cf); break;
+        case 2: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 2>), mgrid, blk, 0, s, a, cf); break;
+        default: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 4>), mgrid, blk, 0, s, a, cf); break;
+      }
       return last_error();
     }
   }

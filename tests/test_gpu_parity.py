@@ -372,3 +372,31 @@ def test_unsupported_head_layout_is_reported(e2f, dev):
                          torch.zeros((4, 2), dtype=torch.int32, device=dev),
                          torch.zeros((4, 2), dtype=torch.uint8, device=dev), 8)
     assert ei.value.name == "E2F_ERR_UNSUPPORTED"
+
+
+def test_targets_sharing_a_wave_stay_independent(e2f, dev):
+    """Several targets share each row they read; a row only changes the targets that list it.
+
+    Visiting targets in index order groups consecutive atoms; a non-finite source listed by
+    one target must leave its neighbours in the group bit-identical to a run without it.
+    """
+    cfg = make_config("water")
+    s = cfg.spec
+    say("shared rows: a NaN source listed by one target only")
+    N = cfg.N
+    h = np.concatenate([cfg.h, np.full((1,) + cfg.h.shape[1:], np.nan, np.float32)])
+    pos = np.concatenate([cfg.pos, cfg.pos[1:2] + 0.5])
+    idx = np.concatenate([cfg.idx, np.zeros((1, s.K), np.int32)])
+    mask = np.concatenate([cfg.mask, np.zeros((1, s.K), np.uint8)])
+    free = int(np.argmin(mask[1]))
+    assert mask[1, free] == 0
+    idx_nan, mask_nan = idx.copy(), mask.copy()
+    idx_nan[1, free] = N                             # only target 1 lists the NaN atom
+    mask_nan[1, free] = 1
+    run = lambda i, m: e2f.attn_forward(T(pos, dev), T(h, dev), T(i, dev), T(m, dev), s.H,
+                                        targets_in_order=True).cpu()  # noqa: E731
+    with_nan = run(idx_nan, mask_nan)
+    without = run(idx, mask)
+    others = np.setdiff1d(np.arange(N + 1), [1])
+    assert torch.isnan(with_nan[1]).any()
+    assert torch.equal(with_nan[others], without[others])
