@@ -338,7 +338,9 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
 // storage, 4 channels per lane).  Their valid slots are merged into one
 // union of distinct sources; each union source's S + 1 rows are read once and
 // applied to every target that lists it (a source in c of a target's slots
-// weighs c exp(s), so repeated slots still count once each).  Adjacent targets share most of their neighbours, so the
+// weighs c exp(s), so repeated slots still count once each).  With the distance
+// envelope, each (target, source) pair's log2 u is tabulated in LDS while the
+// slots are counted and joins that pair's logit.  Adjacent targets share most of their neighbours, so the
 // rows read per target drop by the union's sharing factor.
 //
 // Subgroup g streams the union sources j with j mod P == g in increasing j,
@@ -359,7 +361,7 @@ constexpr int pow2_ceil(int x) {
 constexpr int kMtTargets = 2;     // targets per wave
 constexpr int kMtInflight = 3;    // union sources per subgroup in flight
 
-template <int LMAX, int T, int U, int HL>
+template <int LMAX, int T, int U, int HL, bool ENV>
 __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
   constexpr int S = ncomp(LMAX);
   constexpr int V = 4;
@@ -371,6 +373,8 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
   __shared__ int32_t s_uj[kWavesPerBlock][EN];        // union sources, bucket by bucket
   __shared__ uint32_t s_cnt[kWavesPerBlock][CW][EN];  // per union source: slot counts per target
   __shared__ int32_t s_bk[kWavesPerBlock][2][64];     // per bucket: union sources, then start
+  // log2 of the distance envelope per (target, union source), with the envelope
+  __shared__ float s_le[kWavesPerBlock][ENV ? T : 1][ENV ? EN : 1];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
@@ -489,6 +493,17 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
         const int u = run + __popcll(b & (below | (1ull << lane))) - 1;
         const int t = (int)(kk & 3u);
         atomicAdd(&s_cnt[w][t >> 1][u], 1u << (16 * (t & 1)));
+        if constexpr (ENV) {
+          // the pair's envelope (a repeated slot writes the same value again)
+          int64_t ti = tg[0];
+#pragma unroll
+          for (int tt = 1; tt < T; ++tt)
+            if (t == tt) ti = tg[tt];
+          const int32_t j = key_source(kk);
+          s_le[w][t][u] = envelope_term(a.pos[3 * ti] - a.pos[3 * j],
+                                        a.pos[3 * ti + 1] - a.pos[3 * j + 1],
+                                        a.pos[3 * ti + 2] - a.pos[3 * j + 2], a.env_inv_rc).log2u;
+        }
       }
       run += __popcll(b);
     }
@@ -555,7 +570,12 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
 #pragma unroll
           for (int v = 0; v < V; ++v) dt = fmaf(q[t][v], kv[u][0].get(v), dt);
           dt = head_sum_t<HL>(dt, a.head_lanes);
-          const float sc = dt * a.scale_log2e;
+          float sc = dt * a.scale_log2e;
+          if constexpr (ENV) {
+            // log2 of the envelope joins the base-2 logit (-inf beyond the cutoff: weight 0)
+            const int n = my_start + it + u;
+            sc += s_le[w][t][n];
+          }
           // lazy rescale, as in the single-target kernel, but decided per lane
           // (per head and subgroup): whether the other subgroup happens to be
           // updating this target must not move this subgroup's reference point
@@ -869,7 +889,7 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
       return last_error();
     }
   }
-  if constexpr (sizeof(T) == 4 && !E) {
+  if constexpr (sizeof(T) == 4) {
     // fp32, 4 channels per lane, rows of at most kMtMaxK slots: several targets
     // per wave share every row they read
     if (V == 4 && buf && a.K <= kMtMaxK && a.N < ((int64_t)1 << 30) &&
@@ -879,9 +899,9 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
       const int64_t mblocks = (a.N + kWavesPerBlock * TM - 1) / (kWavesPerBlock * TM);
       const dim3 mgrid((unsigned)((mblocks + kXcds - 1) / kXcds * kXcds));
       switch (a.head_lanes) {
-        case 1: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 1>), mgrid, blk, 0, s, a, cf); break;
-        case 2: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 2>), mgrid, blk, 0, s, a, cf); break;
-        default: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 4>), mgrid, blk, 0, s, a, cf); break;
+        case 1: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 1, E>), mgrid, blk, 0, s, a, cf); break;
+        case 2: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 2, E>), mgrid, blk, 0, s, a, cf); break;
+        default: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 4, E>), mgrid, blk, 0, s, a, cf); break;
       }
       return last_error();
     }
