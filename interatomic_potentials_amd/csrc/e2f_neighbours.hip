@@ -21,7 +21,8 @@
 //     candidate loop reads them contiguously;
 //  5. one wavefront per target, targets in the grouped order (neighbouring
 //     waves share cells in cache): the 27 cells around the target's cell are
-//     read 64 candidates at a time; accepted (d2, j) pairs are compacted into
+//     flattened into one stream of candidates, read 64 at a time (the next 64
+//     in flight while the current ones are tested); accepted (d2, j) pairs are compacted into
 //     LDS with a ballot; when the LDS batch is full, and at the end, the kept
 //     pairs and the batch are sorted by (d2, j) with a bitonic network and the
 //     first K are kept.  The result does not depend on the order of atoms
@@ -43,6 +44,7 @@ struct NlGrid {
 };
 
 constexpr int kNlWaves = 4;   // targets per workgroup
+constexpr int kNlAhead = 3;   // candidate batches in flight per wave
 
 __device__ inline uint32_t spread3(uint32_t v) {  // bits b -> 3b
   v &= 0x3ffu;
@@ -190,7 +192,8 @@ __device__ inline bool pair_less(uint64_t da, int32_t ja, uint64_t db, int32_t j
   return da < db || (da == db && ja < jb);
 }
 
-// sort kd/kj[0, cnt) ascending by (d2, j): one wave, bitonic, LDS
+// sort kd/kj[0, cnt) ascending by (d2, j): one wave, bitonic, LDS; each lane
+// takes compare-exchange pairs (lo, lo + jj) directly, so no lane idles
 __device__ inline void sort_pairs(uint64_t* kd, int32_t* kj, int cnt, int lane) {
   int n2 = 1;
   while (n2 < cnt) n2 <<= 1;
@@ -200,17 +203,16 @@ __device__ inline void sort_pairs(uint64_t* kd, int32_t* kj, int cnt, int lane) 
   }
   nl_wave_sync();
   for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int e = lane; e < n2; e += 64) {
-        const int o = e ^ j;
-        if (o > e) {
-          const uint64_t da = kd[e], db = kd[o];
-          const int32_t ja = kj[e], jb = kj[o];
-          const bool up = (e & k) == 0;
-          if (up ? pair_less(db, jb, da, ja) : pair_less(da, ja, db, jb)) {
-            kd[e] = db; kd[o] = da;
-            kj[e] = jb; kj[o] = ja;
-          }
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int e = lane; e < (n2 >> 1); e += 64) {
+        const int lo = ((e & ~(jj - 1)) << 1) | (e & (jj - 1));
+        const int hi = lo + jj;
+        const uint64_t da = kd[lo], db = kd[hi];
+        const int32_t ja = kj[lo], jb = kj[hi];
+        const bool up = (lo & k) == 0;
+        if (up ? pair_less(db, jb, da, ja) : pair_less(da, ja, db, jb)) {
+          kd[lo] = db; kd[hi] = da;
+          kj[lo] = jb; kj[hi] = ja;
         }
       }
       nl_wave_sync();
@@ -242,46 +244,91 @@ __global__ __launch_bounds__(kNlWaves * 64) void k_nl_build(NlArgs a, const NlGr
   int kept = 0;     // sorted pairs at [0, kept)
   int nb = 0;       // unsorted batch at [kept, kept + nb)
   int total = 0;    // all accepted
-  for (int dz = -1; dz <= 1; ++dz) {
-    const int z = cz + dz;
-    if (z < 0 || z >= g.dims[2]) continue;
-    for (int dy = -1; dy <= 1; ++dy) {
-      const int y = cy + dy;
-      if (y < 0 || y >= g.dims[1]) continue;
-      for (int dx = -1; dx <= 1; ++dx) {
-        const int x = cx + dx;
-        if (x < 0 || x >= g.dims[0]) continue;
-        const int32_t c = morton(x, y, z);
-        const int32_t beg = a.starts[c], end = a.starts[c + 1];
-        for (int32_t b0 = beg; b0 < end; b0 += 64) {
-          const int32_t p = b0 + lane;
-          bool ok = false;
-          double d2 = 0.0;
-          int32_t j = 0;
-          if (p < end) {
-            const float4 q = reinterpret_cast<const float4*>(a.sorted_pos)[p];
-            j = a.sorted_idx[p];
-            const double ex = xi - (double)q.x, ey = yi - (double)q.y, ez = zi - (double)q.z;
-            d2 = (ex * ex + ey * ey) + ez * ez;
-            ok = j != i && d2 < rc2;
-          }
-          const uint64_t bal = __ballot(ok);
-          const int add = __popcll(bal);
-          if (add == 0) continue;
-          if (kept + nb + add > LCAP) {   // make room: keep the K nearest so far
-            sort_pairs(kd, kj, kept + nb, lane);
-            kept = kept + nb < K ? kept + nb : K;
-            nb = 0;
-          }
-          if (ok) {
-            const int at = kept + nb + __popcll(bal & ((1ull << lane) - 1ull));
-            kd[at] = (uint64_t)__double_as_longlong(d2);
-            kj[at] = j;
-          }
-          nb += add;
-          total += add;
-          nl_wave_sync();
+
+  // The 27 surrounding cells' ranges, flattened into one candidate stream: lane
+  // c < 27 holds cell c's start and its offset in the stream, so every batch of
+  // 64 candidates is full whatever the cell sizes.
+  int cbeg = 0, clen = 0;
+  if (lane < 27) {
+    const int x = cx + lane % 3 - 1, y = cy + (lane / 3) % 3 - 1, z = cz + lane / 9 - 1;
+    if (x >= 0 && x < g.dims[0] && y >= 0 && y < g.dims[1] && z >= 0 && z < g.dims[2]) {
+      const int32_t c = morton(x, y, z);
+      cbeg = a.starts[c];
+      clen = a.starts[c + 1] - cbeg;
+    }
+  }
+  int coff = clen;   // inclusive scan over the 27 lanes, then exclusive
+  for (int o = 1; o < 32; o <<= 1) {
+    const int v = __shfl_up(coff, o);
+    if (lane >= o) coff += v;
+  }
+  const int ncand = __builtin_amdgcn_readfirstlane(__shfl(coff, 26));   // wave-uniform
+  coff -= clen;
+  // candidate e of the stream: its cell is the last c < 27 with offset <= e.
+  // Every lane shuffles at every step (a lane that skips a shuffle does not
+  // provide its own value to the others), so the source lane is clamped and
+  // only the comparison is conditional.
+  auto locate = [&](int e) -> int32_t {
+    int c = 0;
+#pragma unroll
+    for (int k = 16; k > 0; k >>= 1) {
+      const int t = c + k;
+      const int ot = __shfl(coff, t < 27 ? t : 26);
+      if (t < 27 && ot <= e) c = t;
+    }
+    return __shfl(cbeg, c) + (e - __shfl(coff, c));
+  };
+  // kNlAhead batches of loads in flight.  The loop is unrolled by kNlAhead so
+  // that each register slot is tested and refilled in place (copying a slot
+  // whose load is still in flight would wait for it).  locate() shuffles, so
+  // every lane calls it.
+  float4 qr[kNlAhead];
+  int32_t jr[kNlAhead];
+  auto fetch = [&](int B, float4& q, int32_t& j) {
+    const int e = B + lane;
+    const int32_t pidx = locate(e < ncand ? e : 0);
+    if (e < ncand) {
+      q = reinterpret_cast<const float4*>(a.sorted_pos)[pidx];
+      j = a.sorted_idx[pidx];
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < kNlAhead; ++d) {
+    qr[d] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    jr[d] = -1;
+    if (64 * d < ncand) fetch(64 * d, qr[d], jr[d]);
+  }
+  for (int b0 = 0; b0 < ncand; b0 += 64 * kNlAhead) {
+#pragma unroll
+    for (int d = 0; d < kNlAhead; ++d) {
+      const int B = b0 + 64 * d;
+      if (B >= ncand) break;
+      const float4 q = qr[d];
+      const int32_t j = jr[d];
+      if (B + 64 * kNlAhead < ncand) fetch(B + 64 * kNlAhead, qr[d], jr[d]);
+      bool ok = false;
+      double d2 = 0.0;
+      if (B + lane < ncand) {
+        const double ex = xi - (double)q.x, ey = yi - (double)q.y, ez = zi - (double)q.z;
+        d2 = (ex * ex + ey * ey) + ez * ez;
+        ok = j != i && d2 < rc2;
+      }
+      const uint64_t bal = __ballot(ok);
+      const int add = __popcll(bal);
+      if (add != 0) {
+        if (kept + nb + add > LCAP) {   // make room: keep the K nearest so far
+          sort_pairs(kd, kj, kept + nb, lane);
+          kept = kept + nb < K ? kept + nb : K;
+          nb = 0;
         }
+        if (ok) {
+          const int at = kept + nb + __popcll(bal & ((1ull << lane) - 1ull));
+          kd[at] = (uint64_t)__double_as_longlong(d2);
+          kj[at] = j;
+        }
+        nb += add;
+        total += add;
+        nl_wave_sync();
       }
     }
   }
