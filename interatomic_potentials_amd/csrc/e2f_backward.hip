@@ -315,6 +315,172 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
   if (sub == 0 && act) st<V>(a.dq + i * C + c0, dq);
 }
 
+// ------------------------------- target-centric dq, targets sharing rows
+//
+// k_bwd_q for two spatially adjacent targets per wavefront (fp32, 4 channels
+// per lane, rows of at most kShareMaxK slots), built like the forward's shared
+// aggregate: the targets' sources form one union (share_union), subgroup g
+// streams the sources with j mod P == g in increasing j, each source's rows
+// are read once and applied to every target that lists it (c slots weigh c
+// times), and a target's state is touched only by its own sources, so its
+// arithmetic depends on its own neighbour set alone.
+constexpr int kBqTargets = 2;    // targets per wave
+constexpr int kBqInflight = 2;   // union sources per subgroup in flight
+
+template <int LMAX, int T, int U, int HL, bool ENV>
+__global__ __launch_bounds__(256) void k_bwd_q_mt(BwdArgs a) {
+  constexpr int S = ncomp(LMAX);
+  constexpr int V = 4;
+  constexpr int EN = ShareLds<T>::EN;
+  constexpr int CW = ShareLds<T>::CW;
+  __shared__ ShareLds<T> s_un[kWavesPerBlock];
+  // envelope per (target, union source): log2 u, then d ln u / d r_target as a vector
+  __shared__ float4 s_env[kWavesPerBlock][ENV ? T : 1][ENV ? EN : 1];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
+  const int64_t blk = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int64_t slot0 = (blk * kWavesPerBlock + w) * T;
+  if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
+  const int64_t N = a.N;
+  const int C = a.C;
+  int64_t tg[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t sl = slot0 + t;
+    int64_t i = -1;
+    if (sl < N) i = a.sched ? (int64_t)a.sched[sl] : sl;
+    tg[t] = (i >= 0 && i < N) ? i : -1;
+  }
+  const int lg = a.lane_log;
+  const int lgp = 6 - lg;
+  const int sub = lane >> lg;
+  const int c0 = (lane & ((1 << lg) - 1)) * V;
+  const bool act = c0 < C;
+  const int cl = act ? c0 : 0;
+  const int64_t row = (int64_t)(S + 1) * C;
+  const int head = cl / (C / a.heads);
+  const uint32_t row_bytes = (uint32_t)(row * 4);
+  const uint32_t cbytes = (uint32_t)C * 4u;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(a.ws, (uint32_t)(N * row * 4));
+  ShareLds<T>& un = s_un[w];
+
+  (void)share_union<T>(un, a.idx, a.mask, N, a.K, tg, lgp, lane,
+                       [&](int t, int u, int32_t j) {
+                         if constexpr (ENV) {
+                           int64_t ti = tg[0];
+#pragma unroll
+                           for (int tt = 1; tt < T; ++tt)
+                             if (t == tt) ti = tg[tt];
+                           const float dx = a.pos[3 * ti] - a.pos[3 * j];
+                           const float dy = a.pos[3 * ti + 1] - a.pos[3 * j + 1];
+                           const float dz = a.pos[3 * ti + 2] - a.pos[3 * j + 2];
+                           const EnvTerm et = envelope_term(dx, dy, dz, a.env_inv_rc);
+                           s_env[w][t][u] = make_float4(et.log2u, et.dlog * dx, et.dlog * dy,
+                                                        et.dlog * dz);
+                         }
+                       });
+  const int my_cnt = un.bcnt[sub];
+  const int my_start = un.bstart[sub];
+  int maxlen = my_cnt;
+  for (int o = 1; o < 64; o <<= 1) maxlen = max(maxlen, __shfl_xor(maxlen, o));
+
+  // per-target state: q, dm (from the prep pass), lse (base 2), D, dq, envelope dpos
+  float q[T][V], dm[T][S][V], L2[T], Dv[T], dq[T][V], gpos[T][3];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t i = tg[t] >= 0 ? tg[t] : 0;
+    ld<V>(a.brows + i * row + cl, q[t]);
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2) ld<V>(a.brows + i * row + (s2 + 1) * C + cl, dm[t][s2]);
+    L2[t] = a.lse[i * a.heads + head] * 1.4426950408889634f;
+    Dv[t] = a.dh[i * a.heads + head];
+#pragma unroll
+    for (int v = 0; v < V; ++v) dq[t][v] = 0.0f;
+    gpos[t][0] = gpos[t][1] = gpos[t][2] = 0.0f;
+  }
+#pragma unroll 1
+  for (int it = 0; it < maxlen; it += U) {
+    Raw<float, V> kv[U][S + 1];
+    uint32_t cw[U][CW];
+    int nidx[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool val = it + u < my_cnt;
+      // a subgroup past the end of its bucket re-reads some valid source and adds nothing
+      const int nn = val ? my_start + it + u : (my_cnt > 0 ? my_start + my_cnt - 1 : 0);
+      nidx[u] = nn;
+      const uint32_t voff = (uint32_t)un.uj[nn] * row_bytes + (uint32_t)cl * 4u;
+#pragma unroll
+      for (int r = 0; r <= S; ++r)
+        buffer_load_raw<float, V>(rsrc, voff, (uint32_t)r * cbytes, kv[u][r]);
+#pragma unroll
+      for (int c = 0; c < CW; ++c) cw[u][c] = val ? un.cnt[c][nn] : 0u;
+    }
+    // keep every source's loads in flight before the first use
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint32_t m = share_count<CW>(cw[u], t);
+        if (m != 0u) {   // uniform within the subgroup
+          float qk = 0.0f, dp = 0.0f;
+#pragma unroll
+          for (int v = 0; v < V; ++v) qk = fmaf(q[t][v], kv[u][0].f[v], qk);
+#pragma unroll
+          for (int r = 0; r < S; ++r)
+#pragma unroll
+            for (int v = 0; v < V; ++v) dp = fmaf(dm[t][r][v], kv[u][r + 1].f[v], dp);
+          qk = head_sum_b<HL>(qk, a.head_lanes);
+          dp = head_sum_b<HL>(dp, a.head_lanes);
+          float4 env = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          if constexpr (ENV) env = s_env[w][t][nidx[u]];
+          // c slots of the source count c times; a pair beyond the envelope weighs 0
+          const float alpha = env.x != -INFINITY
+                                  ? exp2_b(qk * a.scale_log2e + env.x - L2[t]) * (float)m
+                                  : 0.0f;
+          const float dsn = alpha * (dp - Dv[t]);
+          const float ds = dsn * a.scale;
+#pragma unroll
+          for (int v = 0; v < V; ++v) dq[t][v] = fmaf(ds, kv[u][0].f[v], dq[t][v]);
+          if constexpr (ENV) {
+            gpos[t][0] = fmaf(dsn, env.y, gpos[t][0]);
+            gpos[t][1] = fmaf(dsn, env.z, gpos[t][1]);
+            gpos[t][2] = fmaf(dsn, env.w, gpos[t][2]);
+          }
+        }
+      }
+    }
+  }
+  // sum the subgroups (additions of two terms commute exactly)
+  for (int o = 1 << lg; o < 64; o <<= 1) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int v = 0; v < V; ++v) dq[t][v] += __shfl_xor(dq[t][v], o);
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t i = tg[t];
+    if constexpr (ENV) {
+      // every head's value sits on head_lanes active lanes of each subgroup
+      const float wgt = act ? 1.0f / (float)a.head_lanes : 0.0f;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        float v = gpos[t][k] * wgt;
+        for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+        gpos[t][k] = v;
+      }
+      if (i >= 0 && lane == 0) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) a.grad_pos[3 * i + k] += gpos[t][k];  // prep wrote its part
+      }
+    }
+    if (i >= 0 && sub == 0 && act) st<V>(a.dq + i * C + c0, dq[t]);
+  }
+}
+
 // ------------------------------------------ source-centric dh', dk, dh, dpos
 
 template <int LMAX, int V, int U, int HL, bool BUF, bool ENV>
@@ -637,6 +803,17 @@ int bwd_go(const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
   // 32-bit buffer offsets when the row arrays fit 4 GiB
   const bool buf = a.N * (ncomp(L) + 1) * (int64_t)a.C * 4 < ((int64_t)1 << 32);
   hipLaunchKernelGGL((k_bwd_prep<L, V, HL>), grid_prep, dim3(256), 0, s, a, cf);
+  if constexpr (V == 4 && HL > 0) {
+    // rows of at most kShareMaxK slots: two targets per wave share every row they read
+    if (buf && a.K <= kShareMaxK && a.N < ((int64_t)1 << 30)) {
+      const int64_t qb = (a.N + kWavesPerBlock * kBqTargets - 1) / (kWavesPerBlock * kBqTargets);
+      const dim3 qgrid((unsigned)((qb + kXcds - 1) / kXcds * kXcds));
+      hipLaunchKernelGGL((k_bwd_q_mt<L, kBqTargets, kBqInflight, HL, E>), qgrid, dim3(256), 0, s,
+                         a);
+      hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, true, E>), grid, dim3(256), 0, s, a, cf);
+      return last_err();
+    }
+  }
   if (buf) {
     hipLaunchKernelGGL((k_bwd_q<L, V, UQ, HL, true, E>), grid, dim3(256), 0, s, a);
     hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, true, E>), grid, dim3(256), 0, s, a, cf);

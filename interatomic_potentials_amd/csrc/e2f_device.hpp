@@ -562,4 +562,156 @@ __device__ inline EnvTerm envelope_term(float dx, float dy, float dz, float inv_
   return e;
 }
 
+// ------------------------------------------------------------------------
+// Union of several targets' neighbour lists, for kernels in which the targets
+// of one wavefront share every source row they read.  The valid slots of the
+// T targets (rows of at most kShareMaxK slots) are merged into 32-bit keys
+// (bucket j mod P in the top lgp bits, then j / P, then the target), sorted
+// with a bitonic network in LDS, and turned into the union of distinct sources,
+// bucket by bucket and in increasing j within a bucket, with each source's
+// slot count per target (16 bits per target) and each bucket's size and start.
+// Subgroup g of the wave then streams bucket g.  hook(t, u, j) runs once per
+// valid slot after the counts are cleared (e.g. to tabulate per-pair data).
+constexpr int kShareMaxK = 256;
+
+constexpr int pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+template <int T>
+struct ShareLds {
+  static constexpr int EN = T * kShareMaxK;   // merged slots, at most
+  static constexpr int EN2 = pow2_ceil(EN);   // the sort pads to a power of two
+  static constexpr int CW = (T + 1) / 2;      // count words per source
+  uint32_t key[EN2];                          // merge keys, sorted
+  int32_t uj[EN];                             // union sources, bucket by bucket
+  uint32_t cnt[CW][EN];                       // slot counts per target, 16 bits each
+  int32_t bcnt[64];                           // per bucket: union sources
+  int32_t bstart[64];                         // per bucket: first union entry
+};
+
+__device__ inline void share_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ inline uint32_t share_key(uint32_t j, uint32_t t, int lgp) {
+  const uint32_t hi = lgp ? (j & ((1u << lgp) - 1u)) << (32 - lgp) : 0u;
+  return hi | ((j >> lgp) << 2) | t;
+}
+
+__device__ inline int32_t share_key_source(uint32_t k, int lgp) {
+  const uint32_t b = lgp ? k >> (32 - lgp) : 0u;
+  const uint32_t q = (k & (lgp ? (~0u >> lgp) : ~0u)) >> 2;
+  return (int32_t)((q << lgp) | b);
+}
+
+// Build the union for targets tg[0..T) (-1 = none); sources j need j < 2^30.
+// Returns the number of union sources.  Ends with a wave-wide LDS sync.
+template <int T, typename Hook>
+__device__ inline int share_union(ShareLds<T>& L, const int32_t* idx, const uint8_t* mask,
+                                  int64_t N, int K, const int64_t (&tg)[T], int lgp, int lane,
+                                  Hook hook) {
+  static_assert(T >= 1 && T <= 4, "two bits of target index in the merge key");
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int P = 1 << lgp;
+  // merge the targets' valid slots
+  int cnt = 0;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (tg[t] < 0) continue;
+    const int32_t* irow = idx + tg[t] * K;
+    const uint8_t* mrow = mask + tg[t] * K;
+    for (int u = 0; u < K; u += 64) {
+      const int sl = u + lane;
+      bool ok = false;
+      int j = 0;
+      if (sl < K && mrow[sl] != 0) {
+        j = irow[sl];
+        ok = j >= 0 && (int64_t)j < N;
+      }
+      const uint64_t b = __ballot(ok);
+      if (ok) L.key[cnt + __popcll(b & below)] = share_key((uint32_t)j, (uint32_t)t, lgp);
+      cnt += __popcll(b);
+    }
+  }
+  L.bcnt[lane] = 0;
+  // sort the keys
+  {
+    int n2 = 1;
+    while (n2 < cnt) n2 <<= 1;
+    for (int e = cnt + lane; e < n2; e += 64) L.key[e] = 0xffffffffu;
+    share_wave_sync();
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int e = lane; e < (n2 >> 1); e += 64) {
+          const int lo = ((e & ~(jj - 1)) << 1) | (e & (jj - 1));
+          const uint32_t x = L.key[lo], y = L.key[lo + jj];
+          if ((x > y) == ((lo & k) == 0)) {
+            L.key[lo] = y;
+            L.key[lo + jj] = x;
+          }
+        }
+        share_wave_sync();
+      }
+    }
+  }
+  // the union: one entry per distinct source, bucket sizes
+  int nu = 0;
+  for (int e0 = 0; e0 < cnt; e0 += 64) {
+    const int e = e0 + lane;
+    const bool in = e < cnt;
+    const uint32_t kk = in ? L.key[e] : 0u;
+    const bool head = in && (e == 0 || (L.key[e - 1] >> 2) != (kk >> 2));
+    const uint64_t b = __ballot(head);
+    if (head) {
+      const int u = nu + __popcll(b & below);
+      const int32_t j = share_key_source(kk, lgp);
+      L.uj[u] = j;
+#pragma unroll
+      for (int c = 0; c < ShareLds<T>::CW; ++c) L.cnt[c][u] = 0u;
+      atomicAdd(&L.bcnt[j & (P - 1)], 1);
+    }
+    nu += __popcll(b);
+  }
+  share_wave_sync();
+  // slot counts per (source, target)
+  {
+    int run = 0;  // heads before this chunk
+    for (int e0 = 0; e0 < cnt; e0 += 64) {
+      const int e = e0 + lane;
+      const bool in = e < cnt;
+      const uint32_t kk = in ? L.key[e] : 0u;
+      const bool head = in && (e == 0 || (L.key[e - 1] >> 2) != (kk >> 2));
+      const uint64_t b = __ballot(head);
+      if (in) {
+        const int u = run + __popcll(b & (below | (1ull << lane))) - 1;
+        const int t = (int)(kk & 3u);
+        atomicAdd(&L.cnt[t >> 1][u], 1u << (16 * (t & 1)));
+        hook(t, u, share_key_source(kk, lgp));
+      }
+      run += __popcll(b);
+    }
+  }
+  // bucket starts: buckets follow each other in the sorted union
+  if (lane == 0) {
+    int acc0 = 0;
+    for (int g = 0; g < P; ++g) {
+      L.bstart[g] = acc0;
+      acc0 += L.bcnt[g];
+    }
+  }
+  share_wave_sync();
+  return nu;
+}
+
+// slot count of target t in the packed count words of one union source
+template <int CW>
+__device__ inline uint32_t share_count(const uint32_t (&cw)[CW], int t) {
+  return (cw[t >> 1] >> (16 * (t & 1))) & 0xffffu;
+}
+
 }  // namespace e2f

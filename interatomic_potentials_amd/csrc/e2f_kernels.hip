@@ -348,13 +348,7 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
 // branch), so every target's arithmetic -- which subgroup adds which source,
 // in which order -- depends on its own neighbour set alone: not on the other
 // targets sharing the wave, the schedule, or slot order.
-constexpr int kMtMaxK = 256;      // longest neighbour row this kernel takes
-
-constexpr int pow2_ceil(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
-}
+constexpr int kMtMaxK = kShareMaxK;   // longest neighbour row this kernel takes
 // Two targets per wave, three union sources per subgroup in flight: measured
 // against three or four targets (more sharing, but more subgroups idling on
 // targets that do not list their source) and one or two sources in flight.
@@ -365,14 +359,9 @@ template <int LMAX, int T, int U, int HL, bool ENV>
 __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
   constexpr int S = ncomp(LMAX);
   constexpr int V = 4;
-  constexpr int EN = T * kMtMaxK;            // merged slots per wave, at most
-  constexpr int EN2 = pow2_ceil(EN);         // the sort pads the keys to a power of two
-  constexpr int CW = (T + 1) / 2;            // count words per union source (16 bits per target)
-  static_assert(T >= 1 && T <= 4, "two bits of target index in the merge key");
-  __shared__ uint32_t s_key[kWavesPerBlock][EN2];     // merge keys, sorted
-  __shared__ int32_t s_uj[kWavesPerBlock][EN];        // union sources, bucket by bucket
-  __shared__ uint32_t s_cnt[kWavesPerBlock][CW][EN];  // per union source: slot counts per target
-  __shared__ int32_t s_bk[kWavesPerBlock][2][64];     // per bucket: union sources, then start
+  constexpr int EN = ShareLds<T>::EN;
+  constexpr int CW = ShareLds<T>::CW;
+  __shared__ ShareLds<T> s_un[kWavesPerBlock];
   // log2 of the distance envelope per (target, union source), with the envelope
   __shared__ float s_le[kWavesPerBlock][ENV ? T : 1][ENV ? EN : 1];
   const int lane = threadIdx.x & 63;
@@ -382,7 +371,6 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
   const int64_t slot0 = (blk * kWavesPerBlock + w) * T;
   if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
   const int64_t N = a.N;
-  const int K = a.K;
   const int C = a.C;
   int64_t tg[T];
 #pragma unroll
@@ -394,7 +382,6 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
   }
   const int lg = a.lane_log;
   const int lgp = 6 - lg;                    // log2 of the subgroups per wave
-  const int P = 1 << lgp;
   const int sub = lane >> lg;
   const int c0 = (lane & ((1 << lg) - 1)) * V;
   const bool act = c0 < C;
@@ -403,122 +390,26 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
   const uint32_t row_bytes = (uint32_t)(row * 4);
   const uint32_t cbytes = (uint32_t)C * 4u;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(a.ws, (uint32_t)(N * row * 4));
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint32_t* key = s_key[w];
-  int32_t* uj = s_uj[w];
-  int32_t* bcnt = s_bk[w][0];
-  int32_t* bstart = s_bk[w][1];
-  // merge key: bucket j mod P in the top lgp bits, then j / P, then the target
-  // (j < 2^30), so the sorted keys list each bucket's sources in increasing j
-  auto make_key = [&](uint32_t j, uint32_t t) -> uint32_t {
-    const uint32_t hi = lgp ? (j & (uint32_t)(P - 1)) << (32 - lgp) : 0u;
-    return hi | ((j >> lgp) << 2) | t;
-  };
-  auto key_source = [&](uint32_t k) -> int32_t {
-    const uint32_t b = lgp ? k >> (32 - lgp) : 0u;
-    const uint32_t q = (k & (lgp ? (~0u >> lgp) : ~0u)) >> 2;
-    return (int32_t)((q << lgp) | b);
-  };
+  ShareLds<T>& un = s_un[w];
+  const int32_t* uj = un.uj;
 
-  // 1. merge the targets' valid slots
-  int cnt = 0;
+  // 1-3. the union of the targets' sources, bucket by bucket, with slot counts
+  (void)share_union<T>(un, a.idx, a.mask, N, a.K, tg, lgp, lane,
+                       [&](int t, int u, int32_t j) {
+                         if constexpr (ENV) {
+                           // the pair's envelope (a repeated slot writes the same value again)
+                           int64_t ti = tg[0];
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    if (tg[t] < 0) continue;
-    const int32_t* irow = a.idx + tg[t] * K;
-    const uint8_t* mrow = a.mask + tg[t] * K;
-    for (int u = 0; u < K; u += 64) {
-      const int sl = u + lane;
-      bool ok = false;
-      int j = 0;
-      if (sl < K && mrow[sl] != 0) {
-        j = irow[sl];
-        ok = j >= 0 && (int64_t)j < N;
-      }
-      const uint64_t b = __ballot(ok);
-      if (ok) key[cnt + __popcll(b & below)] = make_key((uint32_t)j, (uint32_t)t);
-      cnt += __popcll(b);
-    }
-  }
-  bcnt[lane] = 0;
-  // 2. sort the keys (bitonic network in LDS, one wave)
-  {
-    int n2 = 1;
-    while (n2 < cnt) n2 <<= 1;
-    for (int e = cnt + lane; e < n2; e += 64) key[e] = 0xffffffffu;
-    wave_sync();
-    for (int k = 2; k <= n2; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int e = lane; e < (n2 >> 1); e += 64) {
-          const int lo = ((e & ~(jj - 1)) << 1) | (e & (jj - 1));
-          const uint32_t x = key[lo], y = key[lo + jj];
-          if ((x > y) == ((lo & k) == 0)) {
-            key[lo] = y;
-            key[lo + jj] = x;
-          }
-        }
-        wave_sync();
-      }
-    }
-  }
-  // 3. the union: one entry per distinct source (bucket by bucket), per-target
-  //    slot counts, and each bucket's size
-  int nu = 0;
-  for (int e0 = 0; e0 < cnt; e0 += 64) {
-    const int e = e0 + lane;
-    const bool in = e < cnt;
-    const uint32_t kk = in ? key[e] : 0u;
-    const bool head = in && (e == 0 || (key[e - 1] >> 2) != (kk >> 2));
-    const uint64_t b = __ballot(head);
-    if (head) {
-      const int u = nu + __popcll(b & below);
-      const int32_t j = key_source(kk);
-      uj[u] = j;
-#pragma unroll
-      for (int c = 0; c < CW; ++c) s_cnt[w][c][u] = 0u;
-      atomicAdd(&bcnt[j & (P - 1)], 1);
-    }
-    nu += __popcll(b);
-  }
-  wave_sync();
-  {
-    int run = 0;  // heads before this chunk
-    for (int e0 = 0; e0 < cnt; e0 += 64) {
-      const int e = e0 + lane;
-      const bool in = e < cnt;
-      const uint32_t kk = in ? key[e] : 0u;
-      const bool head = in && (e == 0 || (key[e - 1] >> 2) != (kk >> 2));
-      const uint64_t b = __ballot(head);
-      if (in) {
-        const int u = run + __popcll(b & (below | (1ull << lane))) - 1;
-        const int t = (int)(kk & 3u);
-        atomicAdd(&s_cnt[w][t >> 1][u], 1u << (16 * (t & 1)));
-        if constexpr (ENV) {
-          // the pair's envelope (a repeated slot writes the same value again)
-          int64_t ti = tg[0];
-#pragma unroll
-          for (int tt = 1; tt < T; ++tt)
-            if (t == tt) ti = tg[tt];
-          const int32_t j = key_source(kk);
-          s_le[w][t][u] = envelope_term(a.pos[3 * ti] - a.pos[3 * j],
-                                        a.pos[3 * ti + 1] - a.pos[3 * j + 1],
-                                        a.pos[3 * ti + 2] - a.pos[3 * j + 2], a.env_inv_rc).log2u;
-        }
-      }
-      run += __popcll(b);
-    }
-  }
-  // bucket starts: buckets follow each other in the sorted union
-  if (lane == 0) {
-    int acc0 = 0;
-    for (int g = 0; g < P; ++g) {
-      bstart[g] = acc0;
-      acc0 += bcnt[g];
-    }
-  }
-  wave_sync();
-  const int my_cnt = bcnt[sub];
-  const int my_start = bstart[sub];
+                           for (int tt = 1; tt < T; ++tt)
+                             if (t == tt) ti = tg[tt];
+                           s_le[w][t][u] = envelope_term(a.pos[3 * ti] - a.pos[3 * j],
+                                                         a.pos[3 * ti + 1] - a.pos[3 * j + 1],
+                                                         a.pos[3 * ti + 2] - a.pos[3 * j + 2],
+                                                         a.env_inv_rc).log2u;
+                         }
+                       });
+  const int my_cnt = un.bcnt[sub];
+  const int my_start = un.bstart[sub];
   int maxlen = my_cnt;
   for (int o = 1; o < 64; o <<= 1) maxlen = max(maxlen, __shfl_xor(maxlen, o));
 
@@ -556,7 +447,7 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
       for (int r = 0; r <= S; ++r)
         buffer_load_raw<float, V>(rsrc, voff, (uint32_t)r * cbytes, kv[u][r]);
 #pragma unroll
-      for (int c = 0; c < CW; ++c) cw[u][c] = val ? s_cnt[w][c][nn] : 0u;
+      for (int c = 0; c < CW; ++c) cw[u][c] = val ? un.cnt[c][nn] : 0u;
     }
     // keep every source's loads in flight before the first use
     __builtin_amdgcn_sched_barrier(0);
@@ -564,7 +455,7 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const uint32_t m = (cw[u][t >> 1] >> (16 * (t & 1))) & 0xffffu;
+        const uint32_t m = share_count<CW>(cw[u], t);
         if (m != 0u) {   // uniform within the subgroup: targets that do not list j are untouched
           float dt = 0.0f;
 #pragma unroll
