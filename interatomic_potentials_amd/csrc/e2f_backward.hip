@@ -12,10 +12,14 @@
 // with a_ij recomputed from the forward's saved log-sum-exp, as in the
 // recompute scheme of FlashAttention-2, so no per-edge tensor is stored.
 //
-// k_bwd_prep  per atom: dm, D, the step-3 part of dpos
-// k_bwd_q     per target, streaming its sorted neighbours: dq
-// k_bwd_src   per source, streaming the targets that list it (reverse list,
-//             sorted): dh', dk, then dh and the step-1 part of dpos
+// k_bwd_prep    per atom: dm, D, the step-3 part of dpos
+// k_bwd_q       per target, streaming its sorted neighbours: dq
+// k_bwd_q_mt    the same for two targets a wave, reading the union of their
+//               rows once
+// k_bwd_src     per source, streaming the targets that list it (reverse list,
+//               sorted): dh', dk, then dh and the step-1 part of dpos
+// k_bwd_src_mt  the same for two sources a wave over the union of their
+//               reverse lists (sources listed at most kSrcShareMaxL times)
 // The reverse list is a CSR built with a count, a scan and a fill (atomics
 // aggregated in LDS per group of spatially adjacent targets); the per-source
 // sort makes the summation order independent of the fill order for sources
@@ -334,8 +338,10 @@ __global__ __launch_bounds__(256) void k_bwd_q_mt(BwdArgs a) {
   constexpr int EN = ShareLds<T>::EN;
   constexpr int CW = ShareLds<T>::CW;
   __shared__ ShareLds<T> s_un[kWavesPerBlock];
-  // envelope per (target, union source): log2 u, then d ln u / d r_target as a vector
-  __shared__ float4 s_env[kWavesPerBlock][ENV ? T : 1][ENV ? EN : 1];
+  // envelope per (target, union source): log2 u and the radial d ln u (the
+  // direction comes from the source's position, gathered with its row), 8 bytes
+  // a pair so that two blocks fit a CU
+  __shared__ float2 s_env[kWavesPerBlock][ENV ? T : 1][ENV ? EN : 1];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
@@ -365,7 +371,7 @@ __global__ __launch_bounds__(256) void k_bwd_q_mt(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(a.ws, (uint32_t)(N * row * 4));
   ShareLds<T>& un = s_un[w];
 
-  (void)share_union<T>(un, a.idx, a.mask, N, a.K, tg, lgp, lane,
+  (void)share_union_rows<T>(un, a.idx, a.mask, N, a.K, tg, lgp, lane,
                        [&](int t, int u, int32_t j) {
                          if constexpr (ENV) {
                            int64_t ti = tg[0];
@@ -376,8 +382,7 @@ __global__ __launch_bounds__(256) void k_bwd_q_mt(BwdArgs a) {
                            const float dy = a.pos[3 * ti + 1] - a.pos[3 * j + 1];
                            const float dz = a.pos[3 * ti + 2] - a.pos[3 * j + 2];
                            const EnvTerm et = envelope_term(dx, dy, dz, a.env_inv_rc);
-                           s_env[w][t][u] = make_float4(et.log2u, et.dlog * dx, et.dlog * dy,
-                                                        et.dlog * dz);
+                           s_env[w][t][u] = make_float2(et.log2u, et.dlog);
                          }
                        });
   const int my_cnt = un.bcnt[sub];
@@ -386,10 +391,15 @@ __global__ __launch_bounds__(256) void k_bwd_q_mt(BwdArgs a) {
   for (int o = 1; o < 64; o <<= 1) maxlen = max(maxlen, __shfl_xor(maxlen, o));
 
   // per-target state: q, dm (from the prep pass), lse (base 2), D, dq, envelope dpos
-  float q[T][V], dm[T][S][V], L2[T], Dv[T], dq[T][V], gpos[T][3];
+  float q[T][V], dm[T][S][V], L2[T], Dv[T], dq[T][V], gpos[T][3], pt[ENV ? T : 1][3];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int64_t i = tg[t] >= 0 ? tg[t] : 0;
+    if constexpr (ENV) {
+      pt[t][0] = a.pos[3 * i];
+      pt[t][1] = a.pos[3 * i + 1];
+      pt[t][2] = a.pos[3 * i + 2];
+    }
     ld<V>(a.brows + i * row + cl, q[t]);
 #pragma unroll
     for (int s2 = 0; s2 < S; ++s2) ld<V>(a.brows + i * row + (s2 + 1) * C + cl, dm[t][s2]);
@@ -404,13 +414,20 @@ __global__ __launch_bounds__(256) void k_bwd_q_mt(BwdArgs a) {
     Raw<float, V> kv[U][S + 1];
     uint32_t cw[U][CW];
     int nidx[U];
+    float pj[ENV ? U : 1][3];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool val = it + u < my_cnt;
       // a subgroup past the end of its bucket re-reads some valid source and adds nothing
       const int nn = val ? my_start + it + u : (my_cnt > 0 ? my_start + my_cnt - 1 : 0);
       nidx[u] = nn;
-      const uint32_t voff = (uint32_t)un.uj[nn] * row_bytes + (uint32_t)cl * 4u;
+      const int64_t jn = un.uj[nn];
+      const uint32_t voff = (uint32_t)jn * row_bytes + (uint32_t)cl * 4u;
+      if constexpr (ENV) {
+        pj[u][0] = a.pos[3 * jn];
+        pj[u][1] = a.pos[3 * jn + 1];
+        pj[u][2] = a.pos[3 * jn + 2];
+      }
 #pragma unroll
       for (int r = 0; r <= S; ++r)
         buffer_load_raw<float, V>(rsrc, voff, (uint32_t)r * cbytes, kv[u][r]);
@@ -434,7 +451,7 @@ __global__ __launch_bounds__(256) void k_bwd_q_mt(BwdArgs a) {
             for (int v = 0; v < V; ++v) dp = fmaf(dm[t][r][v], kv[u][r + 1].f[v], dp);
           qk = head_sum_b<HL>(qk, a.head_lanes);
           dp = head_sum_b<HL>(dp, a.head_lanes);
-          float4 env = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          float2 env = make_float2(0.0f, 0.0f);
           if constexpr (ENV) env = s_env[w][t][nidx[u]];
           // c slots of the source count c times; a pair beyond the envelope weighs 0
           const float alpha = env.x != -INFINITY
@@ -445,9 +462,10 @@ __global__ __launch_bounds__(256) void k_bwd_q_mt(BwdArgs a) {
 #pragma unroll
           for (int v = 0; v < V; ++v) dq[t][v] = fmaf(ds, kv[u][0].f[v], dq[t][v]);
           if constexpr (ENV) {
-            gpos[t][0] = fmaf(dsn, env.y, gpos[t][0]);
-            gpos[t][1] = fmaf(dsn, env.z, gpos[t][1]);
-            gpos[t][2] = fmaf(dsn, env.w, gpos[t][2]);
+            // d ln u / d r_target along r_target - r_source
+            gpos[t][0] = fmaf(dsn, env.y * (pt[t][0] - pj[u][0]), gpos[t][0]);
+            gpos[t][1] = fmaf(dsn, env.y * (pt[t][1] - pj[u][1]), gpos[t][1]);
+            gpos[t][2] = fmaf(dsn, env.y * (pt[t][2] - pj[u][2]), gpos[t][2]);
           }
         }
       }
@@ -483,8 +501,64 @@ __global__ __launch_bounds__(256) void k_bwd_q_mt(BwdArgs a) {
 
 // ------------------------------------------ source-centric dh', dk, dh, dpos
 
+// dh_j and the step-1 part of dpos_j from the summed dh'_j, dk_j and envelope
+// dpos of source j; run by the lanes of one subgroup (2^lg lanes, V channels each).
+template <int LMAX, int V>
+__device__ __forceinline__ void src_finish(const BwdArgs& a, const EaasCoef& cf, int64_t j,
+                                           const float (&gdk)[V],
+                                           const float (&gdhp)[ncomp(LMAX)][V],
+                                           const float (&genv)[3], int lg, int gl, bool act,
+                                           int cl, int c0) {
+  constexpr int S = ncomp(LMAX);
+  const int C = a.C;
+  const Frame f = make_frame(a.pos[3 * j], a.pos[3 * j + 1], a.pos[3 * j + 2]);
+  const Dy2 d = make_dy2(f);
+  const Reindex<LMAX> R = make_reindex<LMAX>(cf, f);
+  Reindex<LMAX> Rrad, Rhat;
+  make_grad_reindex<LMAX>(cf, f, Rrad, Rhat);
+  const int64_t base = j * (int64_t)S * C;
+  float hj[S][V], dqj[V], gh[S][V];
+#pragma unroll
+  for (int s2 = 0; s2 < S; ++s2) ld<V>(a.h + base + s2 * C + cl, hj[s2]);
+  ld<V>(a.dq + j * C + cl, dqj);
+  float acc[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float gv[S], xv[S], out[S];
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2) {
+      gv[s2] = gdhp[s2][v];
+      xv[s2] = hj[s2][v];
+    }
+    eaas_channel_t<LMAX>(gv, out, f, d, R);  // gv is rotated in place
+    out[0] += dqj[v] + gdk[v];
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2) gh[s2][v] = out[s2];
+    rotate_in<LMAX>(xv, f, d);
+    pos_grad_channel<LMAX>(xv, gv, Rrad, Rhat, acc);
+  }
+  if (!act) acc[0] = acc[1] = acc[2] = 0.0f;
+  // within the subgroup, whose lanes are all active here
+  for (int o = 1; o < (1 << lg); o <<= 1) {
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) acc[kk] += __shfl_xor(acc[kk], o);
+  }
+  if (act) {
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2) st<V>(a.grad_h + base + s2 * C + c0, gh[s2]);
+  }
+  if (gl == 0) {
+    float gp[3];
+    frame_to_global(f, acc, gp);
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) a.grad_pos[3 * j + kk] += gp[kk] + genv[kk];  // prep wrote the step-3 part
+  }
+}
+
+// skip_le >= 0: sources listed by at most skip_le targets are left out (another
+// kernel has done them).
 template <int LMAX, int V, int U, int HL, bool BUF, bool ENV>
-__global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf) {
+__global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf, int skip_le) {
   constexpr int S = ncomp(LMAX);
   __shared__ int s_nb[kWavesPerBlock][kRevTile];
   // envelope per sorted target: log2 u, then d ln u / d r_target as a vector
@@ -493,6 +567,7 @@ __global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf) {
   const int w = threadIdx.x >> 6;
   const int64_t j = scheduled_atom(a.sched, a.N, w);
   if (j < 0) return;
+  if (skip_le >= 0 && a.rev_off[j + 1] - a.rev_off[j] <= skip_le) return;
   const int lg = a.lane_log;
   const int P = 64 >> lg;
   const int sub = lane >> lg;
@@ -610,48 +685,210 @@ __global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf) {
     }
   }
   if (sub != 0) return;
+  src_finish<LMAX, V>(a, cf, j, dk, dhp, gpos, lg, gl, act, cl, c0);
+}
 
-  const Frame f = make_frame(a.pos[3 * j], a.pos[3 * j + 1], a.pos[3 * j + 2]);
-  const Dy2 d = make_dy2(f);
-  const Reindex<LMAX> R = make_reindex<LMAX>(cf, f);
-  Reindex<LMAX> Rrad, Rhat;
-  make_grad_reindex<LMAX>(cf, f, Rrad, Rhat);
-  const int64_t base = j * (int64_t)S * C;
-  float hj[S][V], dqj[V], gh[S][V];
+// ------------------------------ source pass, two sources per wave sharing rows
+//
+// The same sums as k_bwd_src for T sources of adjacent schedule slots (the
+// schedule orders atoms along a space-filling curve, so neighbouring sources
+// are listed by mostly the same targets).  Their reverse-list segments are
+// merged into one union of targets, each with its slot count per source; the
+// subgroups of the wave split the union into buckets, so each union target's
+// row (q, dm) is read once for all T sources.  A target listing a source c
+// times counts c times.  A source listed by more than kSrcShareMaxL targets is
+// left to k_bwd_src, so which kernel handles a source, and its summation order
+// (its own sorted segment, bucket by bucket), depend on its own segment alone.
+// The sources' h' sits in LDS (read once per union target and source), which
+// leaves registers for two union targets in flight at two waves a SIMD.  (The
+// envelope variant stays with k_bwd_src: its per-pair table would leave LDS for
+// one block a CU.)
+constexpr int kBsSources = 2;                 // sources per wave
+constexpr int kBsInflight = 2;                // union targets per subgroup in flight
+constexpr int kSrcShareMaxL = 384;            // longest reverse-list segment shared
+
+// Four channels a lane; needs at least T subgroups (lane_log <= 5).
+template <int LMAX, int T, int U, int HL>
+__global__ __launch_bounds__(256) void k_bwd_src_mt(BwdArgs a, EaasCoef cf) {
+  constexpr int S = ncomp(LMAX);
+  constexpr int V = 4;
+  using Lds = ShareLds<T, kSrcShareMaxL>;
+  constexpr int EN = Lds::EN;
+  constexpr int CW = Lds::CW;
+  __shared__ Lds s_un[kWavesPerBlock];
+  // h' of the wave's sources, one float4 per (source, component, lane of a subgroup)
+  __shared__ float4 s_hp[kWavesPerBlock][T][S][32];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
+  const int64_t blk = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int64_t slot0 = (blk * kWavesPerBlock + w) * T;
+  if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
+  const int64_t N = a.N;
+  const int C = a.C;
+  int64_t jo[T];
+  int beg[T], len[T];
+  bool any = false;
 #pragma unroll
-  for (int s = 0; s < S; ++s) ld<V>(a.h + base + s * C + cl, hj[s]);
-  ld<V>(a.dq + j * C + cl, dqj);
-  float acc[3] = {0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < T; ++t) {
+    const int64_t sl = slot0 + t;
+    int64_t j = -1;
+    if (sl < N) j = a.sched ? (int64_t)a.sched[sl] : sl;
+    beg[t] = 0;
+    len[t] = 0;
+    if (j >= 0 && j < N) {
+      beg[t] = a.rev_off[j];
+      len[t] = a.rev_off[j + 1] - beg[t];
+      if (len[t] > kSrcShareMaxL) {  // k_bwd_src's
+        j = -1;
+        len[t] = 0;
+      }
+    } else {
+      j = -1;
+    }
+    jo[t] = j;
+    any |= j >= 0;
+  }
+  if (!any) return;
+  const int lg = a.lane_log;
+  const int lgp = 6 - lg;
+  const int sub = lane >> lg;
+  const int gl = lane & ((1 << lg) - 1);
+  const int c0 = gl * V;
+  const bool act = c0 < C;
+  const int cl = act ? c0 : 0;
+  const int64_t row = (int64_t)(S + 1) * C;
+  const int head = cl / (C / a.heads);
+  const uint32_t row_bytes = (uint32_t)(row * 4);
+  const uint32_t cbytes = (uint32_t)C * 4u;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(a.brows, (uint32_t)(N * row * 4));
+  Lds& un = s_un[w];
+
+  (void)share_union<T, kSrcShareMaxL>(
+      un, len,
+      [&](int t, int sl) -> int {
+        int b = beg[0];
+#pragma unroll
+        for (int tt = 1; tt < T; ++tt)
+          if (t == tt) b = beg[tt];
+        return a.rev_idx[b + sl];
+      },
+      lgp, lane, [](int, int, int32_t) {});
+  const int my_cnt = un.bcnt[sub];
+  const int my_start = un.bstart[sub];
+  int maxlen = my_cnt;
+  for (int o = 1; o < 64; o <<= 1) maxlen = max(maxlen, __shfl_xor(maxlen, o));
+
+  // per-source state: k (registers), h' (LDS), dk, dh'
+  float k[T][V], dk[T][V], dhp[T][S][V];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t j = jo[t] >= 0 ? jo[t] : 0;
+    ld<V>(a.ws + j * row + cl, k[t]);
+    if (sub == 0) {  // 2^lg <= 32 lanes
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2)
+        s_hp[w][t][s2][gl] = *reinterpret_cast<const float4*>(a.ws + j * row + (s2 + 1) * C + cl);
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      dk[t][v] = 0.0f;
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2) dhp[t][s2][v] = 0.0f;
+    }
+  }
+  wave_sync_b();
+#pragma unroll 1
+  for (int it = 0; it < maxlen; it += U) {
+    Raw<float, V> qd[U][S + 1];
+    uint32_t cw[U][CW];
+    int nidx[U];
+    float L2[U], Dv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool val = it + u < my_cnt;
+      // a subgroup past the end of its bucket re-reads some valid target and adds nothing
+      const int nn = val ? my_start + it + u : (my_cnt > 0 ? my_start + my_cnt - 1 : 0);
+      nidx[u] = nn;
+      const int64_t ti = un.uj[nn];
+      const uint32_t voff = (uint32_t)ti * row_bytes + (uint32_t)cl * 4u;
+#pragma unroll
+      for (int r = 0; r <= S; ++r)
+        buffer_load_raw<float, V>(rsrc, voff, (uint32_t)r * cbytes, qd[u][r]);
+      L2[u] = a.lse[ti * a.heads + head] * 1.4426950408889634f;
+      Dv[u] = a.dh[ti * a.heads + head];
+#pragma unroll
+      for (int c = 0; c < CW; ++c) cw[u][c] = val ? un.cnt[c][nn] : 0u;
+    }
+    // keep every target's loads in flight before the first use
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const uint32_t m = share_count<CW>(cw[u], t);
+        if (m != 0u) {   // uniform within the subgroup
+          float qk = 0.0f, dp = 0.0f;
+#pragma unroll
+          for (int v = 0; v < V; ++v) qk = fmaf(qd[u][0].f[v], k[t][v], qk);
+#pragma unroll
+          for (int r = 0; r < S; ++r) {
+            const float4 x = s_hp[w][t][r][gl];
+            dp = fmaf(qd[u][r + 1].f[0], x.x, dp);
+            dp = fmaf(qd[u][r + 1].f[1], x.y, dp);
+            dp = fmaf(qd[u][r + 1].f[2], x.z, dp);
+            dp = fmaf(qd[u][r + 1].f[3], x.w, dp);
+          }
+          qk = head_sum_b<HL>(qk, HL);
+          dp = head_sum_b<HL>(dp, HL);
+          // c slots count c times
+          const float alpha = exp2_b(qk * a.scale_log2e - L2[u]) * (float)m;
+          const float ds = alpha * (dp - Dv[u]) * a.scale;
+#pragma unroll
+          for (int v = 0; v < V; ++v) dk[t][v] = fmaf(ds, qd[u][0].f[v], dk[t][v]);
+#pragma unroll
+          for (int r = 0; r < S; ++r)
+#pragma unroll
+            for (int v = 0; v < V; ++v) dhp[t][r][v] = fmaf(alpha, qd[u][r + 1].f[v], dhp[t][r][v]);
+        }
+      }
+    }
+  }
+  // sum the subgroups (additions of two terms commute exactly)
+  for (int o = 1 << lg; o < 64; o <<= 1) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        dk[t][v] += __shfl_xor(dk[t][v], o);
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2) dhp[t][s2][v] += __shfl_xor(dhp[t][s2][v], o);
+      }
+  }
+  // subgroup t finishes source t
+  if (sub >= T) return;
+  int64_t j = jo[0];
+  float gdk[V], gdhp[S][V];
+  const float genv[3] = {0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    float gv[S], xv[S], out[S];
+    gdk[v] = dk[0][v];
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      gv[s] = dhp[s][v];
-      xv[s] = hj[s][v];
+    for (int s2 = 0; s2 < S; ++s2) gdhp[s2][v] = dhp[0][s2][v];
+  }
+#pragma unroll
+  for (int t = 1; t < T; ++t) {
+    if (sub == t) {
+      j = jo[t];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        gdk[v] = dk[t][v];
+#pragma unroll
+        for (int s2 = 0; s2 < S; ++s2) gdhp[s2][v] = dhp[t][s2][v];
+      }
     }
-    eaas_channel_t<LMAX>(gv, out, f, d, R);  // gv is rotated in place
-    out[0] += dqj[v] + dk[v];
-#pragma unroll
-    for (int s = 0; s < S; ++s) gh[s][v] = out[s];
-    rotate_in<LMAX>(xv, f, d);
-    pos_grad_channel<LMAX>(xv, gv, Rrad, Rhat, acc);
   }
-  if (!act) acc[0] = acc[1] = acc[2] = 0.0f;
-  for (int o = 1; o < (1 << lg); o <<= 1) {
-#pragma unroll
-    for (int kk = 0; kk < 3; ++kk) acc[kk] += __shfl_xor(acc[kk], o);
-  }
-  if (act) {
-#pragma unroll
-    for (int s = 0; s < S; ++s) st<V>(a.grad_h + base + s * C + c0, gh[s]);
-  }
-  if (gl == 0) {
-    float gp[3];
-    frame_to_global(f, acc, gp);
-#pragma unroll
-    for (int kk = 0; kk < 3; ++kk) a.grad_pos[3 * j + kk] += gp[kk] + gpos[kk];  // prep wrote the step-3 part
-  }
+  if (j >= 0) src_finish<LMAX, V>(a, cf, j, gdk, gdhp, genv, lg, gl, act, cl, c0);
 }
 
 // -------------------------------------------------------- reverse list
@@ -804,22 +1041,37 @@ int bwd_go(const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
   const bool buf = a.N * (ncomp(L) + 1) * (int64_t)a.C * 4 < ((int64_t)1 << 32);
   hipLaunchKernelGGL((k_bwd_prep<L, V, HL>), grid_prep, dim3(256), 0, s, a, cf);
   if constexpr (V == 4 && HL > 0) {
-    // rows of at most kShareMaxK slots: two targets per wave share every row they read
-    if (buf && a.K <= kShareMaxK && a.N < ((int64_t)1 << 30)) {
-      const int64_t qb = (a.N + kWavesPerBlock * kBqTargets - 1) / (kWavesPerBlock * kBqTargets);
-      const dim3 qgrid((unsigned)((qb + kXcds - 1) / kXcds * kXcds));
-      hipLaunchKernelGGL((k_bwd_q_mt<L, kBqTargets, kBqInflight, HL, E>), qgrid, dim3(256), 0, s,
-                         a);
-      hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, true, E>), grid, dim3(256), 0, s, a, cf);
+    // several atoms per wave sharing every row they read: the target pass for rows
+    // of at most kShareMaxK slots, the source pass when each source gets a subgroup
+    if (buf && a.N < ((int64_t)1 << 30)) {
+      if (a.K <= kShareMaxK) {
+        const int64_t qb = (a.N + kWavesPerBlock * kBqTargets - 1) / (kWavesPerBlock * kBqTargets);
+        const dim3 qgrid((unsigned)((qb + kXcds - 1) / kXcds * kXcds));
+        hipLaunchKernelGGL((k_bwd_q_mt<L, kBqTargets, kBqInflight, HL, E>), qgrid, dim3(256), 0,
+                           s, a);
+      } else {
+        hipLaunchKernelGGL((k_bwd_q<L, V, UQ, HL, true, E>), grid, dim3(256), 0, s, a);
+      }
+      if (!E && (64 >> a.lane_log) >= kBsSources) {
+        const int64_t sb = (a.N + kWavesPerBlock * kBsSources - 1) / (kWavesPerBlock * kBsSources);
+        const dim3 sgrid((unsigned)((sb + kXcds - 1) / kXcds * kXcds));
+        hipLaunchKernelGGL((k_bwd_src_mt<L, kBsSources, kBsInflight, HL>), sgrid, dim3(256), 0, s,
+                           a, cf);
+        // sources listed by more targets than the shared union holds
+        hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, true, E>), grid, dim3(256), 0, s, a, cf,
+                           kSrcShareMaxL);
+      } else {
+        hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, true, E>), grid, dim3(256), 0, s, a, cf, -1);
+      }
       return last_err();
     }
   }
   if (buf) {
     hipLaunchKernelGGL((k_bwd_q<L, V, UQ, HL, true, E>), grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, true, E>), grid, dim3(256), 0, s, a, cf);
+    hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, true, E>), grid, dim3(256), 0, s, a, cf, -1);
   } else {
     hipLaunchKernelGGL((k_bwd_q<L, V, UQ, HL, false, E>), grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, false, E>), grid, dim3(256), 0, s, a, cf);
+    hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, false, E>), grid, dim3(256), 0, s, a, cf, -1);
   }
   return last_err();
 }

@@ -565,7 +565,8 @@ __device__ inline EnvTerm envelope_term(float dx, float dy, float dz, float inv_
 // ------------------------------------------------------------------------
 // Union of several targets' neighbour lists, for kernels in which the targets
 // of one wavefront share every source row they read.  The valid slots of the
-// T targets (rows of at most kShareMaxK slots) are merged into 32-bit keys
+// T lists (of at most MAXL slots each, kShareMaxK by default) are merged into
+// 32-bit keys
 // (bucket j mod P in the top lgp bits, then j / P, then the target), sorted
 // with a bitonic network in LDS, and turned into the union of distinct sources,
 // bucket by bucket and in increasing j within a bucket, with each source's
@@ -580,9 +581,9 @@ constexpr int pow2_ceil(int x) {
   return p;
 }
 
-template <int T>
+template <int T, int MAXL = kShareMaxK>
 struct ShareLds {
-  static constexpr int EN = T * kShareMaxK;   // merged slots, at most
+  static constexpr int EN = T * MAXL;         // merged slots, at most
   static constexpr int EN2 = pow2_ceil(EN);   // the sort pads to a power of two
   static constexpr int CW = (T + 1) / 2;      // count words per source
   uint32_t key[EN2];                          // merge keys, sorted
@@ -609,30 +610,24 @@ __device__ inline int32_t share_key_source(uint32_t k, int lgp) {
   return (int32_t)((q << lgp) | b);
 }
 
-// Build the union for targets tg[0..T) (-1 = none); sources j need j < 2^30.
-// Returns the number of union sources.  Ends with a wave-wide LDS sync.
-template <int T, typename Hook>
-__device__ inline int share_union(ShareLds<T>& L, const int32_t* idx, const uint8_t* mask,
-                                  int64_t N, int K, const int64_t (&tg)[T], int lgp, int lane,
-                                  Hook hook) {
+// Build the union of T lists: list t has len[t] <= MAXL slots and
+// slot(t, sl) returns the source of its slot sl, or -1 for an empty slot;
+// sources need j < 2^30.  Returns the number of union sources.  Ends with a
+// wave-wide LDS sync.
+template <int T, int MAXL, typename Slot, typename Hook>
+__device__ inline int share_union(ShareLds<T, MAXL>& L, const int (&len)[T], Slot slot, int lgp,
+                                  int lane, Hook hook) {
   static_assert(T >= 1 && T <= 4, "two bits of target index in the merge key");
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int P = 1 << lgp;
-  // merge the targets' valid slots
+  // merge the lists' valid slots
   int cnt = 0;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    if (tg[t] < 0) continue;
-    const int32_t* irow = idx + tg[t] * K;
-    const uint8_t* mrow = mask + tg[t] * K;
-    for (int u = 0; u < K; u += 64) {
+    for (int u = 0; u < len[t]; u += 64) {
       const int sl = u + lane;
-      bool ok = false;
-      int j = 0;
-      if (sl < K && mrow[sl] != 0) {
-        j = irow[sl];
-        ok = j >= 0 && (int64_t)j < N;
-      }
+      const int j = sl < len[t] ? slot(t, sl) : -1;
+      const bool ok = j >= 0;
       const uint64_t b = __ballot(ok);
       if (ok) L.key[cnt + __popcll(b & below)] = share_key((uint32_t)j, (uint32_t)t, lgp);
       cnt += __popcll(b);
@@ -672,7 +667,7 @@ __device__ inline int share_union(ShareLds<T>& L, const int32_t* idx, const uint
       const int32_t j = share_key_source(kk, lgp);
       L.uj[u] = j;
 #pragma unroll
-      for (int c = 0; c < ShareLds<T>::CW; ++c) L.cnt[c][u] = 0u;
+      for (int c = 0; c < ShareLds<T, MAXL>::CW; ++c) L.cnt[c][u] = 0u;
       atomicAdd(&L.bcnt[j & (P - 1)], 1);
     }
     nu += __popcll(b);
@@ -706,6 +701,28 @@ __device__ inline int share_union(ShareLds<T>& L, const int32_t* idx, const uint
   }
   share_wave_sync();
   return nu;
+}
+
+// The union of T targets' padded neighbour rows (idx + mask, K slots each; an
+// index outside [0, N) at a valid slot is skipped like a masked slot).
+template <int T, typename Hook>
+__device__ inline int share_union_rows(ShareLds<T>& L, const int32_t* idx, const uint8_t* mask,
+                                       int64_t N, int K, const int64_t (&tg)[T], int lgp,
+                                       int lane, Hook hook) {
+  int len[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) len[t] = tg[t] >= 0 ? K : 0;
+  return share_union<T, kShareMaxK>(L, len,
+                        [&](int t, int sl) -> int {
+                          int64_t i = tg[0];
+#pragma unroll
+                          for (int tt = 1; tt < T; ++tt)
+                            if (t == tt) i = tg[tt];
+                          if (mask[i * K + sl] == 0) return -1;
+                          const int j = idx[i * K + sl];
+                          return (j >= 0 && (int64_t)j < N) ? j : -1;
+                        },
+                        lgp, lane, hook);
 }
 
 // slot count of target t in the packed count words of one union source

@@ -394,7 +394,7 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
   const int32_t* uj = un.uj;
 
   // 1-3. the union of the targets' sources, bucket by bucket, with slot counts
-  (void)share_union<T>(un, a.idx, a.mask, N, a.K, tg, lgp, lane,
+  (void)share_union_rows<T>(un, a.idx, a.mask, N, a.K, tg, lgp, lane,
                        [&](int t, int u, int32_t j) {
                          if constexpr (ENV) {
                            // the pair's envelope (a repeated slot writes the same value again)

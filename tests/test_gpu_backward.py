@@ -134,3 +134,41 @@ def test_backward_deterministic_and_linear(e2f, dev):
     assert np.all(z[0] == 0) and np.all(z[1] == 0)
     two = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, 2 * g)
     assert np.array_equal(two[0], 2 * a[0]) and np.array_equal(two[1], 2 * a[1])
+
+
+@pytest.mark.parametrize("lmax,C,H,r_env", [(2, 128, 16, None), (1, 32, 8, None),
+                                            (2, 128, 16, 6.0)])
+def test_backward_sources_listed_many_times(e2f, dev, lmax, C, H, r_env):
+    """Sources whose reverse lists are long (over 384 slots) beside short ones.
+
+    Source 0 fills three slots of every row (480 listings), source 1 two (320),
+    the rest are random; run in schedule order and in index order (other wave
+    pairings), both results bit-identical and within tolerance of the oracle.
+    """
+    say(f"backward long reverse lists: lmax={lmax} C={C} H={H} r_env={r_env}")
+    rng = np.random.default_rng(lmax * 13 + C)
+    N, K = 160, 256
+    S = (lmax + 1) ** 2
+    pos = (rng.standard_normal((N, 3)) * 2).astype(np.float32)
+    h = rng.standard_normal((N, S, C)).astype(np.float32)
+    idx = rng.integers(2, N, size=(N, K)).astype(np.int32)
+    mask = (rng.random((N, K)) < 0.5).astype(np.uint8)
+    idx[:, :5] = [0, 0, 0, 1, 1]
+    mask[:, :5] = 1
+    mask[9] = 0                                          # a target with no valid slot
+    g = rng.standard_normal((N, S, C)).astype(np.float32)
+    kw = {} if r_env is None else {"env_cutoff": r_env}
+    p, hh, ii, mm = T(pos, dev), T(h, dev), T(idx, dev), T(mask, dev)
+    ws = e2f.attn_precouple(p, hh)
+    _, msg, lse = e2f.attn_aggregate(p, ii, mm, ws, H, lmax, C, torch.float32, return_msg=True,
+                                     return_lse=True, **kw)
+    res = []
+    for order in (False, True):
+        gh, gp = e2f.attn_backward(p, hh, ii, mm, H, ws, msg, lse, T(g, dev),
+                                   targets_in_order=order, **kw)
+        torch.cuda.synchronize()
+        res.append((gh.cpu().numpy(), gp.cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+    rh, rp = oracle_backward(pos, h, idx, mask, H, lmax, g, **kw)
+    assert block_rel_err(res[0][0], rh, lmax) <= TOL_F32
+    assert pos_err(res[0][1], rp) <= TOL_F32
