@@ -113,9 +113,17 @@ def _counter_means(path):
     acc = collections.defaultdict(list)
     with open(path) as f:
         for row in csv.DictReader(f):
-            name = row["Kernel_Name"]
-            short = name.split("<")[0].replace("void ", "").strip()
-            acc[(short, row["Counter_Name"])].append(float(row["Counter_Value"]))
+            # the kernel with its template arguments, without its parameter list
+            name = row["Kernel_Name"].replace("void ", "").replace("(anonymous namespace)::", "")
+            name = name.strip()
+            depth, cut = 0, len(name)
+            for n, ch in enumerate(name):
+                depth += ch == "<"
+                depth -= ch == ">"
+                if ch == "(" and depth == 0:
+                    cut = n
+                    break
+            acc[(name[:cut].strip(), row["Counter_Name"])].append(float(row["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
 
 
@@ -140,7 +148,7 @@ def summarize_profile(pmc_dir, workload, out_path):
     lines = [f"# rocprofv3 summary: {w} workload ({WORKLOADS[w]})", "",
              f"kernel source hash: {kernel_source_hash()}", "",
              "Commands (run from the repository root on the GPU box; TMPDIR=/tmp):", "```"]
-    extra = " --backward" if w == "large" else ""
+    extra = ""
     bench_cmd = ("python -u bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline"
                  "{x}").format(w=w, x=extra)
     lines += [f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/pmc/trace_{w} "
@@ -198,14 +206,16 @@ def aggregate_kernel(spec):
 
 def committed_traffic(workload, kernel="e2f::k_aggregate"):
     """Calibrated HBM bytes per launch from the committed summary, if the kernel is unchanged."""
-    path = os.path.join(ROOT, "profiles", f"k_aggregate_{workload}.md")
+    base = "k_eaas" if workload == "eaas" else "k_aggregate"
+    path = os.path.join(ROOT, "profiles", f"{base}_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     if f"kernel source hash: {kernel_source_hash()}" not in text:
         return None
     import re
-    m = re.search(r"<!-- traffic %s (\d+) -->" % re.escape(kernel), text)
+    # the plain (no envelope) instance: its last template argument is false
+    m = re.search(r"<!-- traffic %s<[^>]*, false> (\d+) -->" % re.escape(kernel), text)
     return float(m.group(1)) if m else None
 
 
@@ -218,28 +228,34 @@ def bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream):
     N, K, S, C, H, E = cfg.N, s.K, cfg.S, s.C, s.H, cfg.nl.n_edges
     if h.dtype != torch.float32:
         return {"skipped": "backward is fp32-only"}
-    out, msg, lse = e2f.attn_aggregate(pos, idx, mask, ws, H, s.lmax, C, torch.float32, out=out,
-                                       return_msg=True, return_lse=True)
     g = torch.randn_like(out)
     bws = torch.empty(e2f.attn_backward_workspace_bytes(N, K, s.lmax, C, H), dtype=torch.uint8,
                       device=h.device)
     gh = torch.empty_like(h)
     gp = torch.empty_like(pos)
 
-    def run():
-        e2f.attn_backward(pos, h, idx, mask, H, ws, msg, lse, g, bwd_ws=bws, grad_h=gh,
-                          grad_pos=gp)
+    def timed(env_cutoff):
+        _, msg, lse = e2f.attn_aggregate(pos, idx, mask, ws, H, s.lmax, C, torch.float32,
+                                         out=out, return_msg=True, return_lse=True,
+                                         env_cutoff=env_cutoff)
 
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for e in ev:
-        e[0].record(stream)
-        run()
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        def run():
+            e2f.attn_backward(pos, h, idx, mask, H, ws, msg, lse, g, bwd_ws=bws, grad_h=gh,
+                              grad_pos=gp, env_cutoff=env_cutoff)
+
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in ev:
+            e[0].record(stream)
+            run()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+    ms = timed(None)
+    env_ms = timed(float(s.cutoff))      # the envelope-weighted softmax, radius = list cutoff
     row = (S + 1) * C * 4
     # prep reads G, m, h row 0 and writes q + dm rows; each stream reads one row block per edge
     # (k + h' for the target pass; q + dm plus lse and D for the source pass) and per atom
@@ -248,11 +264,11 @@ def bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream):
     b_q = E * row + N * (K * 5 + row + C * 4 + 2 * H * 4)
     b_src = E * (row + 2 * 4) + N * (row + S * C * 4 + S * C * 4 + C * 4 + 12 + 12)
     total = b_prep + b_q + b_src
-    print(f"[bench] backward: {ms:.3f} ms, {total / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic",
-          file=sys.stderr, flush=True)
+    print(f"[bench] backward: {ms:.3f} ms, {total / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic; "
+          f"with the envelope {env_ms:.3f} ms", file=sys.stderr, flush=True)
     return {"ms": ms, "edges_per_s": E / (ms * 1e-3), "algorithmic_bytes": total,
             "algorithmic_GBps": total / (ms * 1e-3) / 1e9,
-            "bytes_per_edge": 2 * row + 8}
+            "bytes_per_edge": 2 * row + 8, "envelope_ms": env_ms}
 
 
 # published dense peaks of MI355X (TFLOP/s) for the matrix-core dtypes used here
@@ -402,7 +418,8 @@ def bench_eaas(args, e2f, dev):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded generator)",
         "config": {"workload": WORKLOADS["eaas"], "vectors": B, "lmax": 2, "channels": C},
         "roofline": {"kernel": "k_eaas", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": committed_traffic("eaas", "e2f::k_eaas"),
                      "algorithmic_bytes_per_launch": B * per_vec, "bytes_per_vector": per_vec},
     }
     print(json.dumps(result), flush=True)
@@ -420,8 +437,8 @@ def main(argv=None):
                     help="skip the learned-projection variant (MFMA) timed after the main step")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the envelope variant and the neighbour-list build timed after it")
-    ap.add_argument("--backward", action="store_true",
-                    help="also time the backward pass (dL/dh, dL/dpos) of the same workload")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward pass (dL/dh, dL/dpos) timed after the forward")
     ap.add_argument("--index-order-reference", action="store_true",
                     help="also time the aggregate visiting targets in index order (no schedule)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
@@ -531,6 +548,7 @@ def main(argv=None):
           f"({k1_bytes / (k1_ms * 1e-3) / 1e9:.0f} GB/s), aggregate {k2_ms:.3f} ms "
           f"(min {k2_ms_min:.3f}) = {k2_gbs:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
 
+    traffic = committed_traffic(args.workload, aggregate_kernel(s))
     result = {
         "metric": "edges/s + achieved HBM GB/s, fused on-the-fly attention, N=32768 K=256",
         "value": E / (ms_step * 1e-3),
@@ -563,7 +581,10 @@ def main(argv=None):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": k2_gbs / HBM_PEAK_GBS,
-            "traffic": committed_traffic(args.workload, aggregate_kernel(s)),
+            "traffic": traffic,
+            # calibrated HBM/fabric bytes of the committed profile over this run's duration
+            "traffic_GBps": traffic / (k2_ms * 1e-3) / 1e9 if traffic else None,
+            "traffic_frac": traffic / (k2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS if traffic else None,
             "algorithmic_bytes_per_launch": k2_bytes,
             "bytes_per_edge": per_edge,
             "bytes_per_target": per_target,
@@ -577,7 +598,7 @@ def main(argv=None):
         result["envelope"] = bench_envelope(args, e2f, cfg, pos, h, idx, mask, ws, out, stream,
                                             k2_ms)
         result["neighbour_list"] = bench_neighbours(args, e2f, cfg, pos, stream)
-    if args.backward:
+    if not args.no_backward:
         result["backward"] = bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
