@@ -56,7 +56,8 @@ def gpu_backward(e2f, dev, pos, h, idx, mask, H, g, **kw):
 
 
 @pytest.mark.parametrize("lmax,C,H,K", [(0, 16, 2, 12), (1, 16, 2, 20), (2, 32, 4, 24),
-                                        (2, 128, 16, 64), (2, 64, 4, 300), (1, 8, 8, 10)])
+                                        (2, 128, 16, 64), (2, 64, 4, 300), (1, 8, 8, 10),
+                                        (2, 128, 16, 300)])
 def test_backward_random_graphs(e2f, dev, lmax, C, H, K):
     say(f"backward random graph: lmax={lmax} C={C} H={H} K={K}")
     rng = np.random.default_rng(lmax * 31 + C + K)
