@@ -610,6 +610,44 @@ __device__ inline int32_t share_key_source(uint32_t k, int lgp) {
   return (int32_t)((q << lgp) | b);
 }
 
+// Bitonic sort of 64·R keys, R a lane in registers (element lane·R + r): the
+// stages of stride below R compare within a lane, the others across lanes
+// through a shuffle, so no stage waits on LDS.
+template <int R>
+__device__ inline void share_sort_regs(uint32_t* key, int lane) {
+  uint32_t k[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) k[r] = key[lane * R + r];
+#pragma unroll
+  for (int kk = 2; kk <= 64 * R; kk <<= 1) {
+#pragma unroll
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      if (jj >= R) {
+        const int dl = jj / R;                       // partner lane: lane ^ dl
+        const bool up = ((lane * R) & kk) == 0;      // ascending run
+        const bool keep_min = ((lane & dl) == 0) == up;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t p = (uint32_t)__shfl_xor((int)k[r], dl);
+          k[r] = keep_min ? min(k[r], p) : max(k[r], p);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r & jj) continue;
+          const int r2 = r + jj;
+          const bool up = ((lane * R + r) & kk) == 0;
+          const uint32_t lo = min(k[r], k[r2]), hi = max(k[r], k[r2]);
+          k[r] = up ? lo : hi;
+          k[r2] = up ? hi : lo;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) key[lane * R + r] = k[r];
+}
+
 // Build the union of T lists: list t has len[t] <= MAXL slots and
 // slot(t, sl) returns the source of its slot sl, or -1 for an empty slot;
 // sources need j < 2^30.  Returns the number of union sources.  Ends with a
@@ -634,25 +672,24 @@ __device__ inline int share_union(ShareLds<T, MAXL>& L, const int (&len)[T], Slo
     }
   }
   L.bcnt[lane] = 0;
-  // sort the keys
+  // sort the keys, padded with the largest key to 256, 512 or 1024 (4, 8 or 16 a lane)
   {
-    int n2 = 1;
+    constexpr int EN2 = ShareLds<T, MAXL>::EN2;
+    static_assert(EN2 >= 256 && EN2 <= 1024, "union sizes the sort handles");
+    int n2 = 256;
     while (n2 < cnt) n2 <<= 1;
     for (int e = cnt + lane; e < n2; e += 64) L.key[e] = 0xffffffffu;
     share_wave_sync();
-    for (int k = 2; k <= n2; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int e = lane; e < (n2 >> 1); e += 64) {
-          const int lo = ((e & ~(jj - 1)) << 1) | (e & (jj - 1));
-          const uint32_t x = L.key[lo], y = L.key[lo + jj];
-          if ((x > y) == ((lo & k) == 0)) {
-            L.key[lo] = y;
-            L.key[lo + jj] = x;
-          }
-        }
-        share_wave_sync();
+    if (n2 == 256) {
+      share_sort_regs<4>(L.key, lane);
+    } else if constexpr (EN2 >= 512) {
+      if (n2 == 512) {
+        share_sort_regs<8>(L.key, lane);
+      } else if constexpr (EN2 >= 1024) {
+        share_sort_regs<16>(L.key, lane);
       }
     }
+    share_wave_sync();
   }
   // the union: one entry per distinct source, bucket sizes
   int nu = 0;
