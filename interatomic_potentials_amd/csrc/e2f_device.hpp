@@ -658,19 +658,27 @@ __device__ inline int share_union(ShareLds<T, MAXL>& L, const int (&len)[T], Slo
   static_assert(T >= 1 && T <= 4, "two bits of target index in the merge key");
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int P = 1 << lgp;
-  // merge the lists' valid slots
+  // merge the lists' valid slots; every chunk's loads are issued before the first is used
+  constexpr int NS = (MAXL + 63) / 64;   // 64-slot chunks a list
+  int jv[T][NS];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+      const int sl = c * 64 + lane;
+      jv[t][c] = sl < len[t] ? slot(t, sl) : -1;
+    }
   int cnt = 0;
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    for (int u = 0; u < len[t]; u += 64) {
-      const int sl = u + lane;
-      const int j = sl < len[t] ? slot(t, sl) : -1;
-      const bool ok = j >= 0;
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+      if (c * 64 >= len[t]) break;   // uniform
+      const bool ok = jv[t][c] >= 0;
       const uint64_t b = __ballot(ok);
-      if (ok) L.key[cnt + __popcll(b & below)] = share_key((uint32_t)j, (uint32_t)t, lgp);
+      if (ok) L.key[cnt + __popcll(b & below)] = share_key((uint32_t)jv[t][c], (uint32_t)t, lgp);
       cnt += __popcll(b);
     }
-  }
   L.bcnt[lane] = 0;
   // sort the keys, padded with the largest key to 256, 512 or 1024 (4, 8 or 16 a lane)
   {
@@ -755,9 +763,10 @@ __device__ inline int share_union_rows(ShareLds<T>& L, const int32_t* idx, const
 #pragma unroll
                           for (int tt = 1; tt < T; ++tt)
                             if (t == tt) i = tg[tt];
-                          if (mask[i * K + sl] == 0) return -1;
+                          // both loads independent of each other
+                          const uint8_t m = mask[i * K + sl];
                           const int j = idx[i * K + sl];
-                          return (j >= 0 && (int64_t)j < N) ? j : -1;
+                          return (m != 0 && j >= 0 && (int64_t)j < N) ? j : -1;
                         },
                         lgp, lane, hook);
 }
