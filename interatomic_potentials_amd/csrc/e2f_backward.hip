@@ -76,25 +76,10 @@ __device__ inline void st(float* p, const float* o) {
   VecIO<float, V>::store(p, o);
 }
 
-// bitonic sort of nb[0..cnt) ascending (one wave, LDS), padding to a power of two
+// ascending sort of nb[0..cnt) by one wave (cnt <= MAXN)
+template <int MAXN>
 __device__ inline void sort_list(int* nb, int cnt, int lane) {
-  int n2 = 1;
-  while (n2 < cnt) n2 <<= 1;
-  for (int e = cnt + lane; e < n2; e += 64) nb[e] = 0x7fffffff;
-  wave_sync_b();
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int e = lane; e < (n2 >> 1); e += 64) {
-        const int lo = ((e & ~(jj - 1)) << 1) | (e & (jj - 1));
-        const int x = nb[lo], y = nb[lo + jj];
-        if ((x > y) == ((lo & k) == 0)) {
-          nb[lo] = y;
-          nb[lo + jj] = x;
-        }
-      }
-      wave_sync_b();
-    }
-  }
+  wave_sort<MAXN>(reinterpret_cast<uint32_t*>(nb), cnt, lane, 0x7fffffffu);
 }
 
 // the target or source handled by this wave (Morton schedule, XCD-aware order)
@@ -224,20 +209,30 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int* nb = s_nb[w];
   for (int t0 = 0; t0 < K; t0 += kTile) {
-    int cnt = 0;
-    for (int u = 0; u < kTile && t0 + u < K; u += 64) {
-      const int slot = t0 + u + lane;
-      bool ok = false;
-      int j = 0;
-      if (slot < K && mrow[slot] != 0) {
-        j = irow[slot];
-        ok = j >= 0 && (int64_t)j < N;
+    // (every chunk's index and mask loads issued before the first ballot)
+    constexpr int NC = kTile / 64;
+    int jv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int slot = t0 + c * 64 + lane;
+      int j = -1;
+      if (slot < K) {
+        const uint8_t m = mrow[slot];
+        const int jj = irow[slot];
+        j = (m != 0 && jj >= 0 && (int64_t)jj < N) ? jj : -1;
       }
+      jv[c] = j;
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (t0 + c * 64 >= K) break;   // uniform
+      const bool ok = jv[c] >= 0;
       const uint64_t b = __ballot(ok);
-      if (ok) nb[cnt + __popcll(b & below)] = j;
+      if (ok) nb[cnt + __popcll(b & below)] = jv[c];
       cnt += __popcll(b);
     }
-    sort_list(nb, cnt, lane);
+    sort_list<kTile>(nb, cnt, lane);
     if constexpr (ENV) {
       const float xi = a.pos[3 * i], yi = a.pos[3 * i + 1], zi = a.pos[3 * i + 2];
       for (int e = lane; e < cnt; e += 64) {
@@ -600,7 +595,7 @@ __global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf, int ski
   for (int t0 = beg; t0 < end; t0 += kRevTile) {
     const int cnt = end - t0 < kRevTile ? end - t0 : kRevTile;
     for (int e = lane; e < cnt; e += 64) nb[e] = a.rev_idx[t0 + e];
-    sort_list(nb, cnt, lane);
+    sort_list<kRevTile>(nb, cnt, lane);
     if constexpr (ENV) {
       const float xj = a.pos[3 * j], yj = a.pos[3 * j + 1], zj = a.pos[3 * j + 2];
       for (int e = lane; e < cnt; e += 64) {

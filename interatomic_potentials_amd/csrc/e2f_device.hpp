@@ -648,6 +648,30 @@ __device__ inline void share_sort_regs(uint32_t* key, int lane) {
   for (int r = 0; r < R; ++r) key[lane * R + r] = k[r];
 }
 
+// Ascending sort of key[0..cnt) by one wave (cnt <= MAXN, MAXN a power of two
+// in [64, 1024]): padded with `pad`, which sorts after every key, to a power of
+// two of at least 64, then sorted in registers.  Ends with a wave-wide LDS sync.
+template <int MAXN>
+__device__ inline void wave_sort(uint32_t* key, int cnt, int lane, uint32_t pad) {
+  static_assert(MAXN >= 64 && MAXN <= 1024 && (MAXN & (MAXN - 1)) == 0, "sort sizes");
+  int n2 = 64;
+  while (n2 < cnt) n2 <<= 1;
+  for (int e = cnt + lane; e < n2; e += 64) key[e] = pad;
+  share_wave_sync();
+  if (n2 == 64) {
+    share_sort_regs<1>(key, lane);
+  } else if (n2 == 128) {
+    if constexpr (MAXN >= 128) share_sort_regs<2>(key, lane);
+  } else if (n2 == 256) {
+    if constexpr (MAXN >= 256) share_sort_regs<4>(key, lane);
+  } else if (n2 == 512) {
+    if constexpr (MAXN >= 512) share_sort_regs<8>(key, lane);
+  } else {
+    if constexpr (MAXN >= 1024) share_sort_regs<16>(key, lane);
+  }
+  share_wave_sync();
+}
+
 // Build the union of T lists: list t has len[t] <= MAXL slots and
 // slot(t, sl) returns the source of its slot sl, or -1 for an empty slot;
 // sources need j < 2^30.  Returns the number of union sources.  Ends with a
@@ -680,25 +704,8 @@ __device__ inline int share_union(ShareLds<T, MAXL>& L, const int (&len)[T], Slo
       cnt += __popcll(b);
     }
   L.bcnt[lane] = 0;
-  // sort the keys, padded with the largest key to 256, 512 or 1024 (4, 8 or 16 a lane)
-  {
-    constexpr int EN2 = ShareLds<T, MAXL>::EN2;
-    static_assert(EN2 >= 256 && EN2 <= 1024, "union sizes the sort handles");
-    int n2 = 256;
-    while (n2 < cnt) n2 <<= 1;
-    for (int e = cnt + lane; e < n2; e += 64) L.key[e] = 0xffffffffu;
-    share_wave_sync();
-    if (n2 == 256) {
-      share_sort_regs<4>(L.key, lane);
-    } else if constexpr (EN2 >= 512) {
-      if (n2 == 512) {
-        share_sort_regs<8>(L.key, lane);
-      } else if constexpr (EN2 >= 1024) {
-        share_sort_regs<16>(L.key, lane);
-      }
-    }
-    share_wave_sync();
-  }
+  // sort the keys (the largest key pads)
+  wave_sort<ShareLds<T, MAXL>::EN2>(L.key, cnt, lane, 0xffffffffu);
   // the union: one entry per distinct source, bucket sizes
   int nu = 0;
   for (int e0 = 0; e0 < cnt; e0 += 64) {

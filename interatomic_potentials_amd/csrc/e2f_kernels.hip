@@ -170,40 +170,34 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
   int* nb = s_nb[w];
   for (int t0 = 0; t0 < K; t0 += kTile) {
     // compact this tile's valid slots (mask = 1 and index in range) into LDS
-    int cnt = 0;
-    for (int u = 0; u < kTile && t0 + u < K; u += 64) {
-      const int slot = t0 + u + lane;
-      bool ok = false;
-      int j = 0;
-      if (slot < K && mrow[slot] != 0) {
-        j = irow[slot];
-        ok = j >= 0 && (int64_t)j < N;
+    // (every chunk's index and mask loads issued before the first ballot)
+    constexpr int NC = kTile / 64;
+    int jv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int slot = t0 + c * 64 + lane;
+      int j = -1;
+      if (slot < K) {
+        const uint8_t m = mrow[slot];
+        const int jj = irow[slot];
+        j = (m != 0 && jj >= 0 && (int64_t)jj < N) ? jj : -1;
       }
+      jv[c] = j;
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (t0 + c * 64 >= K) break;   // uniform
+      const bool ok = jv[c] >= 0;
       const uint64_t b = __ballot(ok);
-      if (ok) nb[cnt + __popcll(b & below)] = j;
+      if (ok) nb[cnt + __popcll(b & below)] = jv[c];
       cnt += __popcll(b);
     }
-    // Sort the tile's neighbours by atom index (bitonic network in LDS).  All
+    // Sort the tile's neighbours by atom index (bitonic, in registers).  All
     // waves then sweep shared neighbours in the same order, so rows fetched
     // by one target are still in L2 when nearby targets ask for them; and the
     // visiting order, hence the rounding, no longer depends on slot order.
-    int n2 = 1;
-    while (n2 < cnt) n2 <<= 1;
-    for (int e = cnt + lane; e < n2; e += 64) nb[e] = 0x7fffffff;
-    wave_sync();
-    for (int k = 2; k <= n2; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int e = lane; e < (n2 >> 1); e += 64) {
-          const int lo = ((e & ~(jj - 1)) << 1) | (e & (jj - 1));
-          const int x = nb[lo], y = nb[lo + jj];
-          if ((x > y) == ((lo & k) == 0)) {
-            nb[lo] = y;
-            nb[lo + jj] = x;
-          }
-        }
-        wave_sync();
-      }
-    }
+    wave_sort<kTile>(reinterpret_cast<uint32_t*>(nb), cnt, lane, 0x7fffffffu);
     if constexpr (ENV) {
       // log2 of the distance envelope per sorted slot; it joins the base-2 logit,
       // so the slot's weight is e_ij exp(s_ij) in numerator and normaliser alike
