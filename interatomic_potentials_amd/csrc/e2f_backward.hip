@@ -962,54 +962,40 @@ __global__ __launch_bounds__(256) void k_rev_pass(int64_t N, int K, int per, con
 
 // exclusive scan, pass 1: each 1024-thread block scans kScanTile elements in place
 __global__ __launch_bounds__(1024) void k_scan_tiles(int64_t n, int32_t* a, int32_t* tile_sums) {
-  __shared__ int32_t part[1024];
+  __shared__ int32_t part[16];
   const int t = threadIdx.x;
   const int64_t e0 = (int64_t)blockIdx.x * kScanTile + 4 * t;
   int32_t v[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) v[k] = e0 + k < n ? a[e0 + k] : 0;
   const int32_t sum = v[0] + v[1] + v[2] + v[3];
-  part[t] = sum;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int32_t add = t >= o ? part[t - o] : 0;
-    __syncthreads();
-    part[t] += add;
-    __syncthreads();
-  }
-  int32_t run = part[t] - sum;
+  int32_t total;
+  int32_t run = block_exclusive_scan_1024(sum, part, &total);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if (e0 + k < n) a[e0 + k] = run;
     run += v[k];
   }
-  if (t == 1023) tile_sums[blockIdx.x] = part[1023];
+  if (t == 1023) tile_sums[blockIdx.x] = total;
 }
 
 // pass 2: one block scans the tile totals (at most kScanTile of them); a[n] = total
 __global__ __launch_bounds__(1024) void k_scan_top(int64_t n, int ntiles, int32_t* tile_sums,
                                                    int32_t* a) {
-  __shared__ int32_t part[1024];
+  __shared__ int32_t part[16];
   const int t = threadIdx.x;
   int32_t v[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) v[k] = 4 * t + k < ntiles ? tile_sums[4 * t + k] : 0;
   const int32_t sum = v[0] + v[1] + v[2] + v[3];
-  part[t] = sum;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int32_t add = t >= o ? part[t - o] : 0;
-    __syncthreads();
-    part[t] += add;
-    __syncthreads();
-  }
-  int32_t run = part[t] - sum;
+  int32_t total;
+  int32_t run = block_exclusive_scan_1024(sum, part, &total);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if (4 * t + k < ntiles) tile_sums[4 * t + k] = run;
     run += v[k];
   }
-  if (t == 1023) a[n] = part[1023];
+  if (t == 1023) a[n] = total;
 }
 
 // pass 3: add the tile offsets; keep a copy as the fill cursors

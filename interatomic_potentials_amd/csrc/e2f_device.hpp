@@ -562,6 +562,29 @@ __device__ inline EnvTerm envelope_term(float dx, float dy, float dz, float inv_
   return e;
 }
 
+// Exclusive prefix of v over the 1024 threads of a workgroup, in thread order,
+// and the workgroup's total: a shuffle scan within each wave, then the 16 wave
+// totals through `part` (16 ints of LDS).  One workgroup barrier; call once.
+__device__ inline int32_t block_exclusive_scan_1024(int32_t v, int32_t* part, int32_t* total) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  int32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t up = __shfl_up(inc, o);
+    if (lane >= o) inc += up;
+  }
+  if (lane == 63) part[wv] = inc;
+  __syncthreads();
+  int32_t before = 0, all = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    before += k < wv ? part[k] : 0;
+    all += part[k];
+  }
+  *total = all;
+  return before + inc - v;
+}
+
 // ------------------------------------------------------------------------
 // Union of several targets' neighbour lists, for kernels in which the targets
 // of one wavefront share every source row they read.  The valid slots of the

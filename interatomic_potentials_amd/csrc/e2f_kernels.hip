@@ -687,7 +687,7 @@ __global__ __launch_bounds__(256) void k_sched_count(int64_t N, const float* pos
 // workgroup, 32 consecutive counts per thread moved as 128-bit accesses
 __global__ __launch_bounds__(1024) void k_sched_scan(int32_t* counts) {
   static_assert(kSchedCells == 1024 * 32, "32 counts per thread");
-  __shared__ int32_t part[1024];
+  __shared__ int32_t part[16];
   const int t = threadIdx.x;
   int4* p = reinterpret_cast<int4*>(counts) + t * 8;
   int4 v[8];
@@ -696,15 +696,8 @@ __global__ __launch_bounds__(1024) void k_sched_scan(int32_t* counts) {
   int32_t sum = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) sum += v[k].x + v[k].y + v[k].z + v[k].w;
-  part[t] = sum;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan of the per-thread sums
-    const int32_t add = t >= o ? part[t - o] : 0;
-    __syncthreads();
-    part[t] += add;
-    __syncthreads();
-  }
-  int32_t run = part[t] - sum;
+  int32_t total;
+  int32_t run = block_exclusive_scan_1024(sum, part, &total);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     int4 o;
