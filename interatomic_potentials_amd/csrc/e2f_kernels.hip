@@ -115,7 +115,9 @@ __global__ __launch_bounds__(256) void k_eaas(EaasArgs a, EaasCoef cf) {
 
 constexpr float kSlack = 8.0f;   // lazy-rescale slack of the running max (base 2)
 
-template <int LMAX, int V, typename T, int U, int HL, bool BUF, bool ENV>
+// SPLIT: V == 2 P (two channels of each lane per subgroup in the epilogue),
+// chosen by the launcher from the lane layout.
+template <int LMAX, int V, typename T, int U, int HL, bool BUF, bool ENV, bool SPLIT = false>
 __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
   constexpr int S = ncomp(LMAX);
   __shared__ int s_nb[kWavesPerBlock][kTile];
@@ -276,22 +278,70 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
     wave_sync();  // every read of s_nb is done before the next tile rewrites it
   }
 
-  // merge the subgroups' partial softmax states (same channels, other neighbours)
+  // merge the subgroups' partial softmax states (same channels, other
+  // neighbours).  Each step rounds both products and then adds them, which
+  // commutes, so both partners, and in the end every subgroup, hold the same bits.
   for (int o = 1 << lg; o < 64; o <<= 1) {
     const float mo = __shfl_xor(mu, o);
     const float zo = __shfl_xor(z, o);
     const float mx = fmaxf(mu, mo);
     const float ca = exp2_fast(mu - mx);
     const float cb = exp2_fast(mo - mx);
-    z = z * ca + zo * cb;
+    z = __fadd_rn(__fmul_rn(z, ca), __fmul_rn(zo, cb));
 #pragma unroll
     for (int r = 0; r < S; ++r)
 #pragma unroll
-      for (int v = 0; v < V; ++v) acc[r][v] = acc[r][v] * ca + __shfl_xor(acc[r][v], o) * cb;
+      for (int v = 0; v < V; ++v)
+        acc[r][v] = __fadd_rn(__fmul_rn(acc[r][v], ca), __fmul_rn(__shfl_xor(acc[r][v], o), cb));
     mu = mx;
   }
 
-  if (sub != 0 || !act) return;
+  if (!act) return;
+  if constexpr (SPLIT) {
+    // every subgroup finishes two of each lane's V channels: channels 2 sub, 2 sub + 1
+    // (the same instructions on all lanes; the pair is picked out with selects)
+    if (sub == 0 && a.lse != nullptr && (lane & (a.head_lanes - 1)) == 0) {
+      const int d = a.C / a.heads;
+      a.lse[i * a.heads + c0 / d] =
+          z > 0.0f ? (mu + log2f(z)) * 0.6931471805599453f : -INFINITY;
+    }
+    const float inv = z > 0.0f ? 1.0f / z : 0.0f;
+    float m2[S][2];
+#pragma unroll
+    for (int r = 0; r < S; ++r)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        float x = acc[r][k];
+#pragma unroll
+        for (int g = 1; g < V / 2; ++g)
+          if (sub == g) x = acc[r][2 * g + k];
+        m2[r][k] = x * inv;
+      }
+    const int cs = c0 + 2 * sub;
+    if (a.out_msg != nullptr) {
+      T* mp = static_cast<T*>(a.out_msg) + i * (int64_t)S * C + cs;
+#pragma unroll
+      for (int r = 0; r < S; ++r) VecIO<T, 2>::store(mp + r * C, m2[r]);
+    }
+    const Frame f = make_frame(a.pos[3 * i], a.pos[3 * i + 1], a.pos[3 * i + 2]);
+    const Dy2 d = make_dy2(f);
+    const Reindex<LMAX> R = make_reindex<LMAX>(cf, f);
+    T* op = static_cast<T*>(a.out) + i * (int64_t)S * C + cs;
+    float y[S][2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      float xv[S], yv[S];
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2) xv[s2] = m2[s2][k];
+      eaas_channel<LMAX>(xv, yv, f, d, R);
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2) y[s2][k] = yv[s2];
+    }
+#pragma unroll
+    for (int r = 0; r < S; ++r) VecIO<T, 2>::store(op + r * C, y[r]);
+    return;
+  }
+  if (sub != 0) return;
   if (a.lse != nullptr && (lane & (a.head_lanes - 1)) == 0) {
     // natural log-sum-exp of this head's logits (base-2 running state times ln 2)
     const int d = a.C / a.heads;
@@ -742,6 +792,16 @@ int eaas_go(int V, const EaasArgs& a, const EaasCoef& cf, hipStream_t s) {
   return last_error();
 }
 
+// The single-target kernel, with the split epilogue when each lane's V channels
+// are twice the subgroups (P = 64 >> lane_log)
+template <int L, int V, typename T, int U, int HL, bool BUF, bool E>
+void launch_single(const AggArgs& a, const EaasCoef& cf, dim3 grid, dim3 blk, hipStream_t s) {
+  if (V == 2 * (64 >> a.lane_log))
+    hipLaunchKernelGGL((k_aggregate<L, V, T, U, HL, BUF, E, true>), grid, blk, 0, s, a, cf);
+  else
+    hipLaunchKernelGGL((k_aggregate<L, V, T, U, HL, BUF, E, false>), grid, blk, 0, s, a, cf);
+}
+
 template <int L, typename T, bool E>
 int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
   constexpr int U = 4;  // neighbours per subgroup in flight per iteration
@@ -755,11 +815,11 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     // bf16, 8 channels per lane: one neighbour per subgroup per iteration
     if (V == 8 && buf && a.head_lanes == 1) {
-      hipLaunchKernelGGL((k_aggregate<L, 8, T, 1, 1, true, E>), grid, blk, 0, s, a, cf);
+      launch_single<L, 8, T, 1, 1, true, E>(a, cf, grid, blk, s);
       return last_error();
     }
     if (V == 8 && buf && a.head_lanes == 2) {
-      hipLaunchKernelGGL((k_aggregate<L, 8, T, 1, 2, true, E>), grid, blk, 0, s, a, cf);
+      launch_single<L, 8, T, 1, 2, true, E>(a, cf, grid, blk, s);
       return last_error();
     }
     if (V == 8) {
@@ -785,11 +845,11 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
     }
   }
   if (V == 4 && buf && a.head_lanes == 2) {
-    hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 2, true, E>), grid, blk, 0, s, a, cf);
+    launch_single<L, 4, T, U, 2, true, E>(a, cf, grid, blk, s);
   } else if (V == 4 && buf && a.head_lanes == 1) {
-    hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 1, true, E>), grid, blk, 0, s, a, cf);
+    launch_single<L, 4, T, U, 1, true, E>(a, cf, grid, blk, s);
   } else if (V == 4 && buf && a.head_lanes == 4) {
-    hipLaunchKernelGGL((k_aggregate<L, 4, T, U, 4, true, E>), grid, blk, 0, s, a, cf);
+    launch_single<L, 4, T, U, 4, true, E>(a, cf, grid, blk, s);
   } else {
     switch (V) {
       case 1: hipLaunchKernelGGL((k_aggregate<L, 1, T, U, 0, false, E>), grid, blk, 0, s, a, cf); break;
