@@ -282,17 +282,17 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
   // neighbours).  Each step rounds both products and then adds them, which
   // commutes, so both partners, and in the end every subgroup, hold the same bits.
   for (int o = 1 << lg; o < 64; o <<= 1) {
+#pragma clang fp contract(off)   // a*b + c*d as two products and a sum: no fused multiply-add
     const float mo = __shfl_xor(mu, o);
     const float zo = __shfl_xor(z, o);
     const float mx = fmaxf(mu, mo);
     const float ca = exp2_fast(mu - mx);
     const float cb = exp2_fast(mo - mx);
-    z = __fadd_rn(__fmul_rn(z, ca), __fmul_rn(zo, cb));
+    z = z * ca + zo * cb;
 #pragma unroll
     for (int r = 0; r < S; ++r)
 #pragma unroll
-      for (int v = 0; v < V; ++v)
-        acc[r][v] = __fadd_rn(__fmul_rn(acc[r][v], ca), __fmul_rn(__shfl_xor(acc[r][v], o), cb));
+      for (int v = 0; v < V; ++v) acc[r][v] = acc[r][v] * ca + __shfl_xor(acc[r][v], o) * cb;
     mu = mx;
   }
 
@@ -538,8 +538,11 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
     }
   }
 
-  // 5. merge the subgroups' partial states, per target, in a fixed order
+  // 5. merge the subgroups' partial states, per target.  Each step rounds both
+  //    products and then adds them, which commutes, so both partners, and in
+  //    the end every subgroup, hold the same bits.
   for (int o = 1 << lg; o < 64; o <<= 1) {
+#pragma clang fp contract(off)   // a*b + c*d as two products and a sum: no fused multiply-add
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float mo = __shfl_xor(mu[t], o);
@@ -561,26 +564,51 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
     }
   }
 
-  // 6. per target: normalise, target-side EAAS, store.  Subgroup 0 finalises
-  //    every target: its merged state always took the same operand order (it is
-  //    the lower partner at every step), whereas the other subgroups' copies
-  //    differ from it in the last bit.
-  if (!act || sub != 0) return;
+  // 6. per target: normalise, target-side EAAS, store.  The merged states are
+  //    the same in every subgroup, so subgroup t finishes target t (the same
+  //    instructions on all lanes, the target picked out with selects); with
+  //    fewer subgroups than targets, subgroup 0 finishes them one by one.
+  if (!act) return;
+  const bool split = (64 >> lg) >= T;
+  if (split && sub >= T) return;
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int64_t i = tg[t];
-    if (i < 0) continue;
-    if (a.lse != nullptr && (lane & (a.head_lanes - 1)) == 0) {
-      const int d = C / a.heads;
-      a.lse[i * a.heads + c0 / d] =
-          z[t] > 0.0f ? (mu[t] + log2f(z[t])) * 0.6931471805599453f : -INFINITY;
-    }
-    const float inv = z[t] > 0.0f ? 1.0f / z[t] : 0.0f;
+  for (int tt = 0; tt < T; ++tt) {
+    if (split && tt > 0) break;
+    // this lane's target: tt, or its subgroup's one
+    int64_t i = tg[tt];
+    float zt = z[tt], mut = mu[tt];
     float m[S][V];
 #pragma unroll
     for (int r = 0; r < S; ++r)
 #pragma unroll
-      for (int v = 0; v < V; ++v) m[r][v] = acc[t][r][v] * inv;
+      for (int v = 0; v < V; ++v) m[r][v] = acc[tt][r][v];
+    if (split) {
+#pragma unroll
+      for (int t = 1; t < T; ++t) {
+        if (sub == t) {
+          i = tg[t];
+          zt = z[t];
+          mut = mu[t];
+#pragma unroll
+          for (int r = 0; r < S; ++r)
+#pragma unroll
+            for (int v = 0; v < V; ++v) m[r][v] = acc[t][r][v];
+        }
+      }
+    } else if (sub != 0) {
+      return;
+    }
+    if (i < 0) continue;   // uniform within the subgroup
+    if (a.lse != nullptr && (lane & (a.head_lanes - 1)) == 0) {
+      const int d = C / a.heads;
+      a.lse[i * a.heads + c0 / d] =
+          zt > 0.0f ? (mut + log2f(zt)) * 0.6931471805599453f : -INFINITY;
+    }
+    const float inv = zt > 0.0f ? 1.0f / zt : 0.0f;
+#pragma unroll
+    for (int r = 0; r < S; ++r)
+#pragma unroll
+      for (int v = 0; v < V; ++v) m[r][v] *= inv;
     if (a.out_msg != nullptr) {
       float* mp = static_cast<float*>(a.out_msg) + i * (int64_t)S * C + c0;
 #pragma unroll
