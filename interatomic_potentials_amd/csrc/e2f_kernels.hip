@@ -40,6 +40,95 @@ __device__ inline float dpp(float x) {
 // from `hl` with uniform branches.  DPP within a 16-lane row.
 __device__ inline float head_sum(float x, int hl);
 
+// The values of x on the two lanes of the pair (lane, lane ^ o), the lower
+// lane's first, on both lanes: o = 16 and 32 by a cross-row swap (VALU, no
+// LDS), other o by a shuffle.
+template <int O>
+__device__ inline void pair_lohi(float x, int o, int lane, float& lo, float& hi) {
+  if constexpr (O == 32) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                     false, false);
+    lo = __uint_as_float(sw[0]);   // lanes 0-31's value, on every lane
+    hi = __uint_as_float(sw[1]);   // lanes 32-63's value
+  } else if constexpr (O == 16) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                     false, false);
+    lo = __uint_as_float(sw[0]);   // the even 16-lane row's value
+    hi = __uint_as_float(sw[1]);   // the odd row's value
+  } else {
+    const float p = __shfl_xor(x, o);
+    const bool upper = (lane & o) != 0;
+    lo = upper ? p : x;
+    hi = upper ? x : p;
+  }
+}
+
+// One step of merging the online-softmax states (mu, z, acc) of the lane pairs
+// (lane, lane ^ o): both lanes evaluate lo c_lo + hi c_hi from the same
+// operands, so both end with the same bits.
+template <int O, int S, int V>
+__device__ inline void merge_state(float& mu, float& z, float (&acc)[S][V], int o, int lane) {
+  float mlo, mhi, zlo, zhi;
+  pair_lohi<O>(mu, o, lane, mlo, mhi);
+  pair_lohi<O>(z, o, lane, zlo, zhi);
+  const float mx = fmaxf(mlo, mhi);
+  const float clo = exp2_fast(mlo - mx);
+  const float chi = exp2_fast(mhi - mx);
+  z = zlo * clo + zhi * chi;
+#pragma unroll
+  for (int r = 0; r < S; ++r)
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float alo, ahi;
+      pair_lohi<O>(acc[r][v], o, lane, alo, ahi);
+      acc[r][v] = alo * clo + ahi * chi;
+    }
+  mu = mx;
+}
+
+// One halving step of a reduce-scatter of online-softmax states across the lane
+// pairs (lane, lane ^ O), O = 16 or 32: of the 2W channels in `in`, the lower
+// lane of each pair keeps channels [0, W) and the upper lane [W, 2W), merged,
+// in `out`.  One swap hands each lane both copies of the channel it keeps, the
+// lower lane's first, so both lanes merge from the same operands.
+template <int O, int S, int W>
+__device__ inline void merge_halve(float& mu, float& z, const float (&in)[S][2 * W],
+                                   float (&out)[S][W], int lane) {
+  float mlo, mhi, zlo, zhi;
+  pair_lohi<O>(mu, O, lane, mlo, mhi);
+  pair_lohi<O>(z, O, lane, zlo, zhi);
+  const float mx = fmaxf(mlo, mhi);
+  const float clo = exp2_fast(mlo - mx);
+  const float chi = exp2_fast(mhi - mx);
+  z = zlo * clo + zhi * chi;
+  mu = mx;
+#pragma unroll
+  for (int r = 0; r < S; ++r)
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      const uint32_t a = __float_as_uint(in[r][k]), b = __float_as_uint(in[r][k + W]);
+      float lo, hi;
+      if constexpr (O == 32) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+        lo = __uint_as_float(sw[0]);
+        hi = __uint_as_float(sw[1]);
+      } else {
+        static_assert(O == 16, "cross-row swaps");
+        const auto sw = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+        lo = __uint_as_float(sw[0]);
+        hi = __uint_as_float(sw[1]);
+      }
+      out[r][k] = lo * clo + hi * chi;
+    }
+}
+
+template <int S, int V>
+__device__ inline void merge_step(float& mu, float& z, float (&acc)[S][V], int o, int lane) {
+  if (o == 32) merge_state<32>(mu, z, acc, o, lane);
+  else if (o == 16) merge_state<16>(mu, z, acc, o, lane);
+  else merge_state<0>(mu, z, acc, o, lane);
+}
+
 template <int HL>
 __device__ inline float head_sum_t(float x, int hl) {
   if constexpr (HL == 0) {
@@ -278,45 +367,30 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
     wave_sync();  // every read of s_nb is done before the next tile rewrites it
   }
 
-  // merge the subgroups' partial softmax states (same channels, other
-  // neighbours).  Each step rounds both products and then adds them, which
-  // commutes, so both partners, and in the end every subgroup, hold the same bits.
-  for (int o = 1 << lg; o < 64; o <<= 1) {
-#pragma clang fp contract(off)   // a*b + c*d as two products and a sum: no fused multiply-add
-    const float mo = __shfl_xor(mu, o);
-    const float zo = __shfl_xor(z, o);
-    const float mx = fmaxf(mu, mo);
-    const float ca = exp2_fast(mu - mx);
-    const float cb = exp2_fast(mo - mx);
-    z = z * ca + zo * cb;
-#pragma unroll
-    for (int r = 0; r < S; ++r)
-#pragma unroll
-      for (int v = 0; v < V; ++v) acc[r][v] = acc[r][v] * ca + __shfl_xor(acc[r][v], o) * cb;
-    mu = mx;
-  }
-
-  if (!act) return;
   if constexpr (SPLIT) {
-    // every subgroup finishes two of each lane's V channels: channels 2 sub, 2 sub + 1
-    // (the same instructions on all lanes; the pair is picked out with selects)
+    // reduce-scatter of the subgroups' partial softmax states (same channels,
+    // other neighbours), largest lane distance first, so that subgroup g ends
+    // with channels 2g and 2g + 1 of each lane's V, merged; it finishes them.
+    static_assert(V == 4 || V == 8, "two or four subgroups");
+    float m2[S][2];
+    if constexpr (V == 8) {
+      float h[S][4];
+      merge_halve<32>(mu, z, acc, h, lane);
+      merge_halve<16>(mu, z, h, m2, lane);
+    } else {
+      merge_halve<32>(mu, z, acc, m2, lane);
+    }
+    if (!act) return;
     if (sub == 0 && a.lse != nullptr && (lane & (a.head_lanes - 1)) == 0) {
       const int d = a.C / a.heads;
       a.lse[i * a.heads + c0 / d] =
           z > 0.0f ? (mu + log2f(z)) * 0.6931471805599453f : -INFINITY;
     }
     const float inv = z > 0.0f ? 1.0f / z : 0.0f;
-    float m2[S][2];
 #pragma unroll
     for (int r = 0; r < S; ++r)
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        float x = acc[r][k];
-#pragma unroll
-        for (int g = 1; g < V / 2; ++g)
-          if (sub == g) x = acc[r][2 * g + k];
-        m2[r][k] = x * inv;
-      }
+      for (int k = 0; k < 2; ++k) m2[r][k] *= inv;
     const int cs = c0 + 2 * sub;
     if (a.out_msg != nullptr) {
       T* mp = static_cast<T*>(a.out_msg) + i * (int64_t)S * C + cs;
@@ -341,7 +415,10 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
     for (int r = 0; r < S; ++r) VecIO<T, 2>::store(op + r * C, y[r]);
     return;
   }
-  if (sub != 0) return;
+  // merge the subgroups' partial softmax states; every subgroup ends with the
+  // same bits, and subgroup 0 finishes
+  for (int o = 1 << lg; o < 64; o <<= 1) merge_step(mu, z, acc, o, lane);
+  if (sub != 0 || !act) return;
   if (a.lse != nullptr && (lane & (a.head_lanes - 1)) == 0) {
     // natural log-sum-exp of this head's logits (base-2 running state times ln 2)
     const int d = a.C / a.heads;
@@ -538,30 +615,11 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
     }
   }
 
-  // 5. merge the subgroups' partial states, per target.  Each step rounds both
-  //    products and then adds them, which commutes, so both partners, and in
-  //    the end every subgroup, hold the same bits.
+  // 5. merge the subgroups' partial states, per target; every subgroup ends
+  //    with the same bits
   for (int o = 1 << lg; o < 64; o <<= 1) {
-#pragma clang fp contract(off)   // a*b + c*d as two products and a sum: no fused multiply-add
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float mo = __shfl_xor(mu[t], o);
-      const float zo = __shfl_xor(z[t], o);
-      const float mx = fmaxf(mu[t], mo);
-      const float ca = exp2_fast(mu[t] - mx);
-      const float cb = exp2_fast(mo - mx);
-      z[t] = z[t] * ca + zo * cb;
-#pragma unroll
-      for (int r = 0; r < S; ++r) {
-#pragma unroll
-        for (int v = 0; v < V; ++v)
-          acc[t][r][v] = acc[t][r][v] * ca + __shfl_xor(acc[t][r][v], o) * cb;
-        // a row's exchanges at a time: all of them in flight would need as many
-        // registers again as the accumulators
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      mu[t] = mx;
-    }
+    for (int t = 0; t < T; ++t) merge_step(mu[t], z[t], acc[t], o, lane);
   }
 
   // 6. per target: normalise, target-side EAAS, store.  The merged states are
