@@ -615,48 +615,8 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
     }
   }
 
-  // 5. merge the subgroups' partial states, per target; every subgroup ends
-  //    with the same bits
-  for (int o = 1 << lg; o < 64; o <<= 1) {
-#pragma unroll
-    for (int t = 0; t < T; ++t) merge_step(mu[t], z[t], acc[t], o, lane);
-  }
-
-  // 6. per target: normalise, target-side EAAS, store.  The merged states are
-  //    the same in every subgroup, so subgroup t finishes target t (the same
-  //    instructions on all lanes, the target picked out with selects); with
-  //    fewer subgroups than targets, subgroup 0 finishes them one by one.
-  if (!act) return;
-  const bool split = (64 >> lg) >= T;
-  if (split && sub >= T) return;
-#pragma unroll
-  for (int tt = 0; tt < T; ++tt) {
-    if (split && tt > 0) break;
-    // this lane's target: tt, or its subgroup's one
-    int64_t i = tg[tt];
-    float zt = z[tt], mut = mu[tt];
-    float m[S][V];
-#pragma unroll
-    for (int r = 0; r < S; ++r)
-#pragma unroll
-      for (int v = 0; v < V; ++v) m[r][v] = acc[tt][r][v];
-    if (split) {
-#pragma unroll
-      for (int t = 1; t < T; ++t) {
-        if (sub == t) {
-          i = tg[t];
-          zt = z[t];
-          mut = mu[t];
-#pragma unroll
-          for (int r = 0; r < S; ++r)
-#pragma unroll
-            for (int v = 0; v < V; ++v) m[r][v] = acc[t][r][v];
-        }
-      }
-    } else if (sub != 0) {
-      return;
-    }
-    if (i < 0) continue;   // uniform within the subgroup
+  // 6. per target: normalise, target-side EAAS, store (the lanes of one subgroup)
+  auto finish = [&](int64_t i, float (&m)[S][V], float zt, float mut) {
     if (a.lse != nullptr && (lane & (a.head_lanes - 1)) == 0) {
       const int d = C / a.heads;
       a.lse[i * a.heads + c0 / d] =
@@ -688,6 +648,81 @@ __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
     }
 #pragma unroll
     for (int r = 0; r < S; ++r) VecIO<float, V>::store(op + r * C, y[r]);
+  };
+
+  // 5. merge the subgroups' partial states per target
+  if (T == 2 && lg == 5) {
+    // two subgroups, two targets: a reduce-scatter.  One swap of target 0's and
+    // target 1's value hands the lower half both copies of target 0's, and the
+    // upper half both copies of target 1's, the lower lane's first; subgroup t
+    // finishes target t.
+    float clo[T], chi[T], zm[T], mm[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float mlo, mhi, zlo, zhi;
+      pair_lohi<32>(mu[t], 32, lane, mlo, mhi);
+      pair_lohi<32>(z[t], 32, lane, zlo, zhi);
+      mm[t] = fmaxf(mlo, mhi);
+      clo[t] = exp2_fast(mlo - mm[t]);
+      chi[t] = exp2_fast(mhi - mm[t]);
+      zm[t] = zlo * clo[t] + zhi * chi[t];
+    }
+    const bool up = sub != 0;
+    const float cl = up ? clo[T - 1] : clo[0], ch = up ? chi[T - 1] : chi[0];
+    float m[S][V];
+#pragma unroll
+    for (int r = 0; r < S; ++r)
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0][r][v]),
+                                                         __float_as_uint(acc[T - 1][r][v]),
+                                                         false, false);
+        m[r][v] = __uint_as_float(sw[0]) * cl + __uint_as_float(sw[1]) * ch;
+      }
+    const int64_t i = up ? tg[T - 1] : tg[0];
+    if (!act || i < 0) return;
+    finish(i, m, up ? zm[T - 1] : zm[0], up ? mm[T - 1] : mm[0]);
+    return;
+  }
+  // otherwise an all-reduce: every subgroup ends with the same bits; subgroup t
+  // finishes target t (with fewer subgroups than targets, subgroup 0 finishes
+  // them one by one)
+  for (int o = 1 << lg; o < 64; o <<= 1) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) merge_step(mu[t], z[t], acc[t], o, lane);
+  }
+  if (!act) return;
+  const bool split = (64 >> lg) >= T;
+  if (split && sub >= T) return;
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) {
+    if (split && tt > 0) break;
+    // this lane's target: tt, or its subgroup's one
+    int64_t i = tg[tt];
+    float zt = z[tt], mut = mu[tt];
+    float m[S][V];
+#pragma unroll
+    for (int r = 0; r < S; ++r)
+#pragma unroll
+      for (int v = 0; v < V; ++v) m[r][v] = acc[tt][r][v];
+    if (split) {
+#pragma unroll
+      for (int t = 1; t < T; ++t) {
+        if (sub == t) {
+          i = tg[t];
+          zt = z[t];
+          mut = mu[t];
+#pragma unroll
+          for (int r = 0; r < S; ++r)
+#pragma unroll
+            for (int v = 0; v < V; ++v) m[r][v] = acc[t][r][v];
+        }
+      }
+    } else if (sub != 0) {
+      return;
+    }
+    if (i < 0) continue;   // uniform within the subgroup
+    finish(i, m, zt, mut);
   }
 }
 
