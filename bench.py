@@ -214,9 +214,12 @@ def committed_traffic(workload, kernel="e2f::k_aggregate"):
     if f"kernel source hash: {kernel_source_hash()}" not in text:
         return None
     import re
-    # the plain (no envelope) instance: its last template argument is false
-    m = re.search(r"<!-- traffic %s<[^>]*, false> (\d+) -->" % re.escape(kernel), text)
-    return float(m.group(1)) if m else None
+    # the plain instance: the envelope flag (the workspace flag of k_eaas) is false
+    flag = {"e2f::k_aggregate": 6, "e2f::k_aggregate_mt": 4, "e2f::k_eaas": 3}[kernel]
+    for args, val in re.findall(r"<!-- traffic %s<([^>]*)> (\d+) -->" % re.escape(kernel), text):
+        if [x.strip() for x in args.split(",")][flag] == "false":
+            return float(val)
+    return None
 
 
 def bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream):

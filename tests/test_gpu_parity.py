@@ -176,7 +176,8 @@ def test_attention_big_configs_sampled(e2f, dev, name):
 
 
 @pytest.mark.parametrize("lmax,C,H,K", [(0, 32, 4, 10), (1, 16, 2, 32), (2, 64, 4, 300),
-                                        (2, 128, 16, 64), (1, 8, 8, 7), (2, 256, 8, 40)])
+                                        (2, 128, 16, 64), (1, 8, 8, 7), (2, 256, 8, 40),
+                                        (2, 128, 16, 300), (2, 96, 12, 300)])
 def test_attention_shapes_vs_oracle(e2f, dev, lmax, C, H, K):
     """Ragged sizes: K not a multiple of 64, K above one LDS tile, d = 1, 16, 32."""
     say(f"attention shapes: lmax={lmax} C={C} H={H} K={K}")
@@ -344,7 +345,8 @@ def test_schedule_covers_every_target_bit_exact(e2f, dev, name):
 
 
 @pytest.mark.parametrize("lmax,C,H,K", [(2, 128, 16, 64), (2, 128, 8, 40), (1, 64, 16, 30),
-                                        (2, 8, 8, 20), (2, 512, 64, 16), (0, 16, 2, 300)])
+                                        (2, 8, 8, 20), (2, 512, 64, 16), (0, 16, 2, 300),
+                                        (1, 128, 8, 300)])
 def test_attention_bf16_shapes_vs_oracle(e2f, dev, lmax, C, H, K):
     """bf16 storage over every lane mapping: 8, 4 and 1 channels per lane, 1 or 2 lanes per head."""
     say(f"attention bf16 shapes: lmax={lmax} C={C} H={H} K={K}")
