@@ -190,6 +190,29 @@ def summarize_profile(pmc_dir, workload, out_path):
         lines.append(f"| `{k}` | {fb:.0f} | {wb:.0f} | {th:.4g} | {tm:.4g} | "
                      f"{th / max(th + tm, 1):.3f} | {traffic:.6g} |")
         lines.append(f"<!-- traffic {k} {traffic:.0f} -->")
+    mfma_path = os.path.join(pmc_dir, f"mfma_{w}", "run_counter_collection.csv")
+    if os.path.exists(mfma_path):
+        mf, nm = _counter_means(mfma_path)
+        lines += ["", "## MFMA counters of the learned projections (`k_proj_eaas`)", "",
+                  "```",
+                  f"rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                  f"SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d "
+                  f"gpurun_out/pmc/mfma_{w} -o run -- {bench_cmd} --no-extras --no-backward",
+                  "```", "",
+                  "- MOPS count 512 flops each; the projections' algorithmic count is "
+                  "2 (S + 2) C^2 flops per atom.",
+                  "- busy share = SQ_VALU_MFMA_BUSY_CYCLES (summed over 1024 SIMDs) / "
+                  "(1024 x GRBM_GUI_ACTIVE / 8), GRBM_GUI_ACTIVE being summed over the 8 XCDs.", "",
+                  "| kernel | dispatches | MFMA flops per dispatch | busy share |",
+                  "|---|---|---|---|"]
+        for k in sorted({k for (k, c) in mf if "k_proj_eaas" in k}):
+            flops = 512.0 * (mf.get((k, "SQ_INSTS_VALU_MFMA_MOPS_F32"), 0.0)
+                             + mf.get((k, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), 0.0))
+            busy = mf.get((k, "SQ_VALU_MFMA_BUSY_CYCLES"), 0.0)
+            active = mf.get((k, "GRBM_GUI_ACTIVE"), 0.0)
+            share = busy / (1024.0 * active / 8.0) if active > 0 else float("nan")
+            lines.append(f"| `{k}` | {nm.get((k, 'GRBM_GUI_ACTIVE'), 0)} | {flops:.4g} | "
+                         f"{share:.2f} |")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(out_path)
