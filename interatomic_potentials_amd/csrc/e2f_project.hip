@@ -133,19 +133,31 @@ __global__ __launch_bounds__(C / 16 * 64) void k_proj_eaas(ProjArgs a, EaasCoef 
   T* ws = static_cast<T*>(a.ws);
   T* qo = static_cast<T*>(a.q_out);
   const int64_t ntiles = (a.n + TA - 1) / TA;
+  // A tile's rows are loaded into registers one tile ahead: issued after the
+  // previous tile's products (when their accumulators are free), they arrive
+  // during its EAAS and stores.  Not at fp32 with C = 128, whose weight slices
+  // leave no registers for it: there the loads are issued at the tile's start.
+  // The buffer range ends at the tile's last atom, so reads past it (a partial
+  // last tile) return zeros without a branch.
+  constexpr bool AHEAD = !(sizeof(T) == 4 && C >= 128);
+  v4u buf[PER];
+  auto fetch = [&](int64_t t) {
+    const int64_t b0 = t * TA;
+    const int nb = (int)(a.n - b0 < TA ? a.n - b0 : TA);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(h + b0 * (int64_t)(S * C), (uint32_t)(nb * CPA * 16));
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+      buf[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + p * NT) * 16, 0, 0);
+  };
+  if (AHEAD && (int64_t)blockIdx.x < ntiles) fetch(blockIdx.x);
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int64_t a0 = tile * TA;
     const int na = (int)(a.n - a0 < TA ? a.n - a0 : TA);
 
-    // 1. stage the tile's rows; the buffer range ends at the tile's last atom,
-    //    so reads past it (a partial last tile) return zeros without a branch
+    // 1. stage the tile's rows in LDS
     {
-      const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(h + a0 * (int64_t)(S * C), (uint32_t)(na * CPA * 16));
-      v4u buf[PER];
-#pragma unroll
-      for (int p = 0; p < PER; ++p)
-        buf[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + p * NT) * 16, 0, 0);
+      if (!AHEAD) fetch(tile);
 #pragma unroll
       for (int p = 0; p < PER; ++p) {
         const int q = tid + p * NT;
@@ -188,6 +200,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_proj_eaas(ProjArgs a, EaasCoef 
 #pragma unroll
       for (int s = 0; s < S; ++s) sv[i * PV + s * C + c0 + col] = acc[s][r];
     }
+    if (AHEAD && tile + gridDim.x < ntiles) fetch(tile + gridDim.x);
     __syncthreads();
 
     // 4. EAAS per (atom, channel); stores coalesced along the channels
