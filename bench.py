@@ -609,7 +609,7 @@ def main(argv=None):
                        "aggregate_index_order_reference": k2_unsched_ms},
         "roofline": {
             "kernel": (aggregate_kernel(s).split("::")[1]
-                       + (" (steps 2-3, two targets per wave sharing the rows they read)"
+                       + (" (steps 2-3, three targets per wave sharing the rows they read)"
                           if aggregate_kernel(s).endswith("_mt") else " (steps 2-3)")
                        + ", timed with its target-schedule kernels"),
             "bound": "hbm",

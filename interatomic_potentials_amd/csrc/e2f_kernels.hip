@@ -470,11 +470,12 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
 // in which order -- depends on its own neighbour set alone: not on the other
 // targets sharing the wave, the schedule, or slot order.
 constexpr int kMtMaxK = kShareMaxK;   // longest neighbour row this kernel takes
-// Two targets per wave, three union sources per subgroup in flight: measured
-// against three or four targets (more sharing, but more subgroups idling on
-// targets that do not list their source) and one or two sources in flight.
-constexpr int kMtTargets = 2;     // targets per wave
-constexpr int kMtInflight = 3;    // union sources per subgroup in flight
+// Three targets per wave, two union sources per subgroup in flight: measured
+// against two targets with three in flight (the union of two rows is a larger
+// share of their lengths, and more rows go through the vector-memory path) and
+// three targets with three in flight (registers for one wave a SIMD only).
+constexpr int kMtTargets = 3;     // targets per wave
+constexpr int kMtInflight = 2;    // union sources per subgroup in flight
 
 template <int LMAX, int T, int U, int HL, bool ENV>
 __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
