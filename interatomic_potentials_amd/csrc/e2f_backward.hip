@@ -316,15 +316,19 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
 
 // ------------------------------- target-centric dq, targets sharing rows
 //
-// k_bwd_q for two spatially adjacent targets per wavefront (fp32, 4 channels
+// k_bwd_q for T spatially adjacent targets per wavefront (fp32, 4 channels
 // per lane, rows of at most kShareMaxK slots), built like the forward's shared
 // aggregate: the targets' sources form one union (share_union), subgroup g
 // streams the sources with j mod P == g in increasing j, each source's rows
 // are read once and applied to every target that lists it (c slots weigh c
 // times), and a target's state is touched only by its own sources, so its
 // arithmetic depends on its own neighbour set alone.
-constexpr int kBqTargets = 2;    // targets per wave
-constexpr int kBqInflight = 2;   // union sources per subgroup in flight
+// Three targets a wave (the smaller union beat two by 4% of the backward);
+// with the envelope two, whose per-pair table would otherwise leave LDS for
+// one block a CU.
+constexpr int kBqTargets = 3;      // targets per wave
+constexpr int kBqTargetsEnv = 2;   // targets per wave, envelope variant
+constexpr int kBqInflight = 2;     // union sources per subgroup in flight
 
 template <int LMAX, int T, int U, int HL, bool ENV>
 __global__ __launch_bounds__(256) void k_bwd_q_mt(BwdArgs a) {
@@ -1026,9 +1030,10 @@ int bwd_go(const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
     // of at most kShareMaxK slots, the source pass when each source gets a subgroup
     if (buf && a.N < ((int64_t)1 << 30)) {
       if (a.K <= kShareMaxK) {
-        const int64_t qb = (a.N + kWavesPerBlock * kBqTargets - 1) / (kWavesPerBlock * kBqTargets);
+        constexpr int TQ = E ? kBqTargetsEnv : kBqTargets;
+        const int64_t qb = (a.N + kWavesPerBlock * TQ - 1) / (kWavesPerBlock * TQ);
         const dim3 qgrid((unsigned)((qb + kXcds - 1) / kXcds * kXcds));
-        hipLaunchKernelGGL((k_bwd_q_mt<L, kBqTargets, kBqInflight, HL, E>), qgrid, dim3(256), 0,
+        hipLaunchKernelGGL((k_bwd_q_mt<L, TQ, kBqInflight, HL, E>), qgrid, dim3(256), 0,
                            s, a);
       } else {
         hipLaunchKernelGGL((k_bwd_q<L, V, UQ, HL, true, E>), grid, dim3(256), 0, s, a);
