@@ -476,6 +476,10 @@ constexpr int kMtMaxK = kShareMaxK;   // longest neighbour row this kernel takes
 // three targets with three in flight (registers for one wave a SIMD only).
 constexpr int kMtTargets = 3;     // targets per wave
 constexpr int kMtInflight = 2;    // union sources per subgroup in flight
+// With the envelope, two targets and three in flight: a third target's log2 u
+// table would leave LDS for one block a CU.
+constexpr int kMtTargetsEnv = 2;
+constexpr int kMtInflightEnv = 3;
 
 template <int LMAX, int T, int U, int HL, bool ENV>
 __global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
@@ -954,8 +958,8 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
     // per wave share every row they read
     if (V == 4 && buf && a.K <= kMtMaxK && a.N < ((int64_t)1 << 30) &&
         (a.head_lanes == 1 || a.head_lanes == 2 || a.head_lanes == 4)) {
-      constexpr int TM = kMtTargets;
-      constexpr int UM = kMtInflight;
+      constexpr int TM = E ? kMtTargetsEnv : kMtTargets;
+      constexpr int UM = E ? kMtInflightEnv : kMtInflight;
       const int64_t mblocks = (a.N + kWavesPerBlock * TM - 1) / (kWavesPerBlock * TM);
       const dim3 mgrid((unsigned)((mblocks + kXcds - 1) / kXcds * kXcds));
       switch (a.head_lanes) {
