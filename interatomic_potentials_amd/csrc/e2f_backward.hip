@@ -934,20 +934,30 @@ __global__ __launch_bounds__(256) void k_rev_pass(int64_t N, int K, int per, con
   }
   __syncthreads();
   const int64_t g0 = (int64_t)blockIdx.x * per;
-  int hs[8], rk[8], tg[8];
+  // every slot's target, then every slot's index and mask, are loaded before
+  // the first insert, so the loads overlap instead of queueing behind the atomics
+  int tg[8], jv[8], hs[8], rk[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = t + 256 * u;
+    const int64_t slot_t = g0 + e / K;
+    tg[u] = -1;
+    if (e < per * K && slot_t < N) tg[u] = sched ? sched[slot_t] : (int)slot_t;
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    jv[u] = -1;
+    if (tg[u] >= 0) {
+      const int64_t sl = (int64_t)tg[u] * K + (t + 256 * u) % K;
+      const uint8_t m = mask[sl];
+      const int32_t j = idx[sl];
+      jv[u] = (m != 0 && j >= 0 && (int64_t)j < N) ? j : -1;
+    }
+  }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     hs[u] = -1;
-    const int e = t + 256 * u;
-    const int64_t slot_t = g0 + e / K;
-    if (e >= per * K || slot_t >= N) continue;
-    const int64_t i = sched ? (int64_t)sched[slot_t] : slot_t;
-    const int64_t sl = i * K + e % K;
-    if (mask[sl] == 0) continue;
-    const int32_t j = idx[sl];
-    if (j < 0 || (int64_t)j >= N) continue;
-    hs[u] = rev_hash_insert(keys, vals, j, &rk[u]);
-    tg[u] = (int)i;
+    if (jv[u] >= 0) hs[u] = rev_hash_insert(keys, vals, jv[u], &rk[u]);
   }
   __syncthreads();
   for (int e = t; e < kRevHash; e += 256) {
