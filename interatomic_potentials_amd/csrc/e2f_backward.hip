@@ -904,11 +904,16 @@ __global__ __launch_bounds__(256) void k_fill_i32(int64_t n, int32_t* p, int32_t
 // per distinct source per workgroup.  The fill also returns each slot's rank
 // within its source and workgroup, so one atomic per source reserves the
 // workgroup's block of entries.
-constexpr int kRevSlots = 2048;   // slots per workgroup (8 per thread)
-constexpr int kRevHash = 4096;    // hash table entries (load factor <= 1/2)
+// 8 slots a thread (8 targets of K = 256 a workgroup); 16 measured slower: the
+// larger hash tables cost more than the global atomics they save.
+constexpr int kRevPerThread = 8;                // slots per thread
+constexpr int kRevSlots = 256 * kRevPerThread;  // slots per workgroup
+constexpr int kRevHash = 2 * kRevSlots;         // hash table entries (load factor <= 1/2)
+constexpr int kRevHashBits = kRevHash == 4096 ? 12 : (kRevHash == 8192 ? 13 : 14);
+static_assert((1 << kRevHashBits) == kRevHash, "hash size");
 
 __device__ inline int rev_hash_insert(int* keys, int* vals, int j, int* rank) {
-  unsigned hh = ((unsigned)j * 2654435761u) >> (32 - 12);
+  unsigned hh = ((unsigned)j * 2654435761u) >> (32 - kRevHashBits);
   while (true) {
     const int k = atomicCAS(&keys[hh], -1, j);
     if (k == -1 || k == j) {
@@ -923,7 +928,6 @@ template <bool FILL>
 __global__ __launch_bounds__(256) void k_rev_pass(int64_t N, int K, int per, const int32_t* idx,
                                                   const uint8_t* mask, const int32_t* sched,
                                                   int32_t* cnt_or_cur, int32_t* entries) {
-  static_assert(kRevSlots == 256 * 8, "8 slots per thread");
   __shared__ int keys[kRevHash];
   __shared__ int vals[kRevHash];
   __shared__ int base[FILL ? kRevHash : 1];
@@ -936,16 +940,17 @@ __global__ __launch_bounds__(256) void k_rev_pass(int64_t N, int K, int per, con
   const int64_t g0 = (int64_t)blockIdx.x * per;
   // every slot's target, then every slot's index and mask, are loaded before
   // the first insert, so the loads overlap instead of queueing behind the atomics
-  int tg[8], jv[8], hs[8], rk[8];
+  constexpr int PT = kRevPerThread;
+  int tg[PT], jv[PT], hs[PT], rk[PT];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < PT; ++u) {
     const int e = t + 256 * u;
     const int64_t slot_t = g0 + e / K;
     tg[u] = -1;
     if (e < per * K && slot_t < N) tg[u] = sched ? sched[slot_t] : (int)slot_t;
   }
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < PT; ++u) {
     jv[u] = -1;
     if (tg[u] >= 0) {
       const int64_t sl = (int64_t)tg[u] * K + (t + 256 * u) % K;
@@ -955,7 +960,7 @@ __global__ __launch_bounds__(256) void k_rev_pass(int64_t N, int K, int per, con
     }
   }
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < PT; ++u) {
     hs[u] = -1;
     if (jv[u] >= 0) hs[u] = rev_hash_insert(keys, vals, jv[u], &rk[u]);
   }
@@ -969,7 +974,7 @@ __global__ __launch_bounds__(256) void k_rev_pass(int64_t N, int K, int per, con
   if constexpr (FILL) {
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < PT; ++u)
       if (hs[u] >= 0) entries[base[hs[u]] + rk[u]] = tg[u];
   }
 }
