@@ -185,7 +185,7 @@ int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int 
  *             E2F_VALIDATE_INDICES, its flag) is rewritten here, hence not
  *             const.  Targets are visited in Morton order of their
  *             positions (built on the GPU each call unless
- *             E2F_TARGETS_IN_ORDER), each XCD taking one contiguous
+ *             E2F_TARGETS_IN_ORDER or N <= 2048), each XCD taking one contiguous
  *             stretch, so that waves sharing an L2 share neighbours; the
  *             visiting order never changes any target's result.
  *   out       [N, S, C] T    out_i; exactly 0 for a target with no valid slot
@@ -242,7 +242,8 @@ size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int 
  *   grad_h      [N, S, C] fp32  dL/dh (written)
  *   grad_pos    [N, 3] fp32     dL/dpos (written)
  *   bwd_workspace, bwd_ws_bytes  scratch of e2f_attn_backward_workspace_bytes
- *   flags       0 or E2F_TARGETS_IN_ORDER
+ *   flags       0 or E2F_TARGETS_IN_ORDER (index order; also taken for
+ *               N <= 2048)
  * The result does not depend on the order of a target's slots, nor on the
  * order in which the reverse list is filled for sources listed by at most
  * 1024 targets (each source's list is sorted before it is summed).

@@ -142,6 +142,10 @@ void* ws_query_rows(void* ws, int64_t N, int lmax, int C, int dt) {
   return static_cast<char*>(ws) + ws_rows_bytes(N, lmax, C, dt);
 }
 
+// Up to this many atoms every gathered row stays in cache whatever the visiting
+// order, and the four schedule launches would cost more than they save.
+constexpr int64_t kSchedMinAtoms = 2048;
+
 // Morton bits per axis of the target schedule: about one cell per atom, at most 2^15 cells
 int sched_bits(int64_t N) {
   int bits = 1;
@@ -290,7 +294,7 @@ int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
   const int V = attn_width(C, H, dt);
   const int d = C / H;
   const int32_t* sched = nullptr;
-  if (!(flags & E2F_TARGETS_IN_ORDER)) {
+  if (!(flags & E2F_TARGETS_IN_ORDER) && N > kSchedMinAtoms) {
     const e2f::SchedScratch sc = sched_scratch(ws, N, lmax, C, dt);
     const int st = hip_status(e2f::launch_schedule(N, pos, sc, stream));
     if (st != E2F_OK) return st;
@@ -630,7 +634,7 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
   a.rev_off = off;
   a.rev_idx = entries;
   a.sched = nullptr;
-  if (!(flags & E2F_TARGETS_IN_ORDER)) {
+  if (!(flags & E2F_TARGETS_IN_ORDER) && N > kSchedMinAtoms) {
     e2f::SchedScratch sc;
     sc.bits = sched_bits(N);
     sc.sched = reinterpret_cast<int32_t*>(b + L.sched);
