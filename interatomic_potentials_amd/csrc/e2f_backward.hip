@@ -326,26 +326,30 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
 // Three targets a wave (the smaller union beat two by 4% of the backward);
 // with the envelope two, whose per-pair table would otherwise leave LDS for
 // one block a CU.
+// One wave a workgroup for the shared passes: the waves share nothing, and a
+// workgroup's LDS is freed only when its last wave ends (backward 2.62 -> 2.51
+// ms at Large against four waves).
+constexpr int kBwWaves = 1;   // waves per workgroup of the shared passes
 constexpr int kBqTargets = 3;      // targets per wave
 constexpr int kBqTargetsEnv = 2;   // targets per wave, envelope variant
 constexpr int kBqInflight = 2;     // union sources per subgroup in flight
 
 template <int LMAX, int T, int U, int HL, bool ENV>
-__global__ __launch_bounds__(256) void k_bwd_q_mt(BwdArgs a) {
+__global__ __launch_bounds__(64 * kBwWaves) void k_bwd_q_mt(BwdArgs a) {
   constexpr int S = ncomp(LMAX);
   constexpr int V = 4;
   constexpr int EN = ShareLds<T>::EN;
   constexpr int CW = ShareLds<T>::CW;
-  __shared__ ShareLds<T> s_un[kWavesPerBlock];
+  __shared__ ShareLds<T> s_un[kBwWaves];
   // envelope per (target, union source): log2 u and the radial d ln u (the
   // direction comes from the source's position, gathered with its row), 8 bytes
   // a pair so that two blocks fit a CU
-  __shared__ float2 s_env[kWavesPerBlock][ENV ? T : 1][ENV ? EN : 1];
+  __shared__ float2 s_env[kBwWaves][ENV ? T : 1][ENV ? EN : 1];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
   const int64_t blk = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int64_t slot0 = (blk * kWavesPerBlock + w) * T;
+  const int64_t slot0 = (blk * kBwWaves + w) * T;
   if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
   const int64_t N = a.N;
   const int C = a.C;
@@ -708,20 +712,20 @@ constexpr int kSrcShareMaxL = 384;            // longest reverse-list segment sh
 
 // Four channels a lane; needs at least T subgroups (lane_log <= 5).
 template <int LMAX, int T, int U, int HL>
-__global__ __launch_bounds__(256) void k_bwd_src_mt(BwdArgs a, EaasCoef cf) {
+__global__ __launch_bounds__(64 * kBwWaves) void k_bwd_src_mt(BwdArgs a, EaasCoef cf) {
   constexpr int S = ncomp(LMAX);
   constexpr int V = 4;
   using Lds = ShareLds<T, kSrcShareMaxL>;
   constexpr int EN = Lds::EN;
   constexpr int CW = Lds::CW;
-  __shared__ Lds s_un[kWavesPerBlock];
+  __shared__ Lds s_un[kBwWaves];
   // h' of the wave's sources, one float4 per (source, component, lane of a subgroup)
-  __shared__ float4 s_hp[kWavesPerBlock][T][S][32];
+  __shared__ float4 s_hp[kBwWaves][T][S][32];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
   const int64_t blk = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int64_t slot0 = (blk * kWavesPerBlock + w) * T;
+  const int64_t slot0 = (blk * kBwWaves + w) * T;
   if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
   const int64_t N = a.N;
   const int C = a.C;
@@ -1046,18 +1050,18 @@ int bwd_go(const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
     if (buf && a.N < ((int64_t)1 << 30)) {
       if (a.K <= kShareMaxK) {
         constexpr int TQ = E ? kBqTargetsEnv : kBqTargets;
-        const int64_t qb = (a.N + kWavesPerBlock * TQ - 1) / (kWavesPerBlock * TQ);
+        const int64_t qb = (a.N + kBwWaves * TQ - 1) / (kBwWaves * TQ);
         const dim3 qgrid((unsigned)((qb + kXcds - 1) / kXcds * kXcds));
-        hipLaunchKernelGGL((k_bwd_q_mt<L, TQ, kBqInflight, HL, E>), qgrid, dim3(256), 0,
-                           s, a);
+        hipLaunchKernelGGL((k_bwd_q_mt<L, TQ, kBqInflight, HL, E>), qgrid, dim3(64 * kBwWaves),
+                           0, s, a);
       } else {
         hipLaunchKernelGGL((k_bwd_q<L, V, UQ, HL, true, E>), grid, dim3(256), 0, s, a);
       }
       if (!E && (64 >> a.lane_log) >= kBsSources) {
-        const int64_t sb = (a.N + kWavesPerBlock * kBsSources - 1) / (kWavesPerBlock * kBsSources);
+        const int64_t sb = (a.N + kBwWaves * kBsSources - 1) / (kBwWaves * kBsSources);
         const dim3 sgrid((unsigned)((sb + kXcds - 1) / kXcds * kXcds));
-        hipLaunchKernelGGL((k_bwd_src_mt<L, kBsSources, kBsInflight, HL>), sgrid, dim3(256), 0, s,
-                           a, cf);
+        hipLaunchKernelGGL((k_bwd_src_mt<L, kBsSources, kBsInflight, HL>), sgrid,
+                           dim3(64 * kBwWaves), 0, s, a, cf);
         // sources listed by more targets than the shared union holds
         hipLaunchKernelGGL((k_bwd_src<L, V, US, HL, true, E>), grid, dim3(256), 0, s, a, cf,
                            kSrcShareMaxL);

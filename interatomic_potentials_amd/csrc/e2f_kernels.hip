@@ -204,13 +204,16 @@ __global__ __launch_bounds__(256) void k_eaas(EaasArgs a, EaasCoef cf) {
 
 constexpr float kSlack = 8.0f;   // lazy-rescale slack of the running max (base 2)
 
+// Four waves a workgroup (one measured the same at Scale-out: short, even work).
+constexpr int kAggWaves = 4;   // waves per workgroup
+
 // SPLIT: V == 2 P (two channels of each lane per subgroup in the epilogue),
 // chosen by the launcher from the lane layout.
 template <int LMAX, int V, typename T, int U, int HL, bool BUF, bool ENV, bool SPLIT = false>
-__global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
+__global__ __launch_bounds__(64 * kAggWaves) void k_aggregate(AggArgs a, EaasCoef cf) {
   constexpr int S = ncomp(LMAX);
-  __shared__ int s_nb[kWavesPerBlock][kTile];
-  __shared__ float s_le[kWavesPerBlock][ENV ? kTile : 1];  // log2 envelope of each sorted slot
+  __shared__ int s_nb[kAggWaves][kTile];
+  __shared__ float s_le[kAggWaves][ENV ? kTile : 1];  // log2 envelope of each sorted slot
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   // Workgroups are dealt to the XCDs round-robin; give XCD x the x-th
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(256) void k_aggregate(AggArgs a, EaasCoef cf) {
   // on neighbouring targets (the grid is a multiple of kXcds).
   const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
   const int64_t blk = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int64_t slot = blk * kWavesPerBlock + w;
+  const int64_t slot = blk * kAggWaves + w;
   if (slot >= a.N) return;  // whole wave: no workgroup barrier below
   const int64_t i = a.sched ? (int64_t)a.sched[slot] : slot;
   if (i < 0 || i >= a.N) return;
@@ -481,20 +484,25 @@ constexpr int kMtInflight = 2;    // union sources per subgroup in flight
 constexpr int kMtTargetsEnv = 2;
 constexpr int kMtInflightEnv = 3;
 
+// One wave a workgroup: the waves share nothing, and a workgroup's LDS and slot
+// are freed only when its last wave ends, so with four waves the early ones
+// idled (one: 0.93 ms at Large against 0.98 with four).
+constexpr int kMtWaves = 1;   // waves per workgroup
+
 template <int LMAX, int T, int U, int HL, bool ENV>
-__global__ __launch_bounds__(256) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
+__global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
   constexpr int S = ncomp(LMAX);
   constexpr int V = 4;
   constexpr int EN = ShareLds<T>::EN;
   constexpr int CW = ShareLds<T>::CW;
-  __shared__ ShareLds<T> s_un[kWavesPerBlock];
+  __shared__ ShareLds<T> s_un[kMtWaves];
   // log2 of the distance envelope per (target, union source), with the envelope
-  __shared__ float s_le[kWavesPerBlock][ENV ? T : 1][ENV ? EN : 1];
+  __shared__ float s_le[kMtWaves][ENV ? T : 1][ENV ? EN : 1];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
   const int64_t blk = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int64_t slot0 = (blk * kWavesPerBlock + w) * T;
+  const int64_t slot0 = (blk * kMtWaves + w) * T;
   if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
   const int64_t N = a.N;
   const int C = a.C;
@@ -931,9 +939,9 @@ void launch_single(const AggArgs& a, const EaasCoef& cf, dim3 grid, dim3 blk, hi
 template <int L, typename T, bool E>
 int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
   constexpr int U = 4;  // neighbours per subgroup in flight per iteration
-  const int64_t blocks = (a.N + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t blocks = (a.N + kAggWaves - 1) / kAggWaves;
   const dim3 grid((unsigned)((blocks + kXcds - 1) / kXcds * kXcds));
-  const dim3 blk(256);
+  const dim3 blk(64 * kAggWaves);
   // 4 channels per lane with 1, 2 or 4 lanes per head and a workspace under
   // 4 GiB take the specialised buffer-load kernels; anything else the general one
   const bool buf = (int64_t)a.N * (ncomp(L) + 1) * a.C * (int64_t)sizeof(T) < ((int64_t)1 << 32);
@@ -960,12 +968,13 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
         (a.head_lanes == 1 || a.head_lanes == 2 || a.head_lanes == 4)) {
       constexpr int TM = E ? kMtTargetsEnv : kMtTargets;
       constexpr int UM = E ? kMtInflightEnv : kMtInflight;
-      const int64_t mblocks = (a.N + kWavesPerBlock * TM - 1) / (kWavesPerBlock * TM);
+      const int64_t mblocks = (a.N + kMtWaves * TM - 1) / (kMtWaves * TM);
       const dim3 mgrid((unsigned)((mblocks + kXcds - 1) / kXcds * kXcds));
+      const dim3 mblk(64 * kMtWaves);
       switch (a.head_lanes) {
-        case 1: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 1, E>), mgrid, blk, 0, s, a, cf); break;
-        case 2: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 2, E>), mgrid, blk, 0, s, a, cf); break;
-        default: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 4, E>), mgrid, blk, 0, s, a, cf); break;
+        case 1: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 1, E>), mgrid, mblk, 0, s, a, cf); break;
+        case 2: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 2, E>), mgrid, mblk, 0, s, a, cf); break;
+        default: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 4, E>), mgrid, mblk, 0, s, a, cf); break;
       }
       return last_error();
     }
