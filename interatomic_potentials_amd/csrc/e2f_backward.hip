@@ -14,8 +14,8 @@
 //
 // k_bwd_prep    per atom: dm, D, the step-3 part of dpos
 // k_bwd_q       per target, streaming its sorted neighbours: dq
-// k_bwd_q_mt    the same for two targets a wave, reading the union of their
-//               rows once
+// k_bwd_q_mt    the same for three targets a wave (two with the envelope),
+//               reading the union of their rows once
 // k_bwd_src     per source, streaming the targets that list it (reverse list,
 //               sorted): dh', dk, then dh and the step-1 part of dpos
 // k_bwd_src_mt  the same for two sources a wave over the union of their

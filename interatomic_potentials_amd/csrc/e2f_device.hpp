@@ -589,10 +589,9 @@ __device__ inline int32_t block_exclusive_scan_1024(int32_t v, int32_t* part, in
 // Union of several targets' neighbour lists, for kernels in which the targets
 // of one wavefront share every source row they read.  The valid slots of the
 // T lists (of at most MAXL slots each, kShareMaxK by default) are merged into
-// 32-bit keys
-// (bucket j mod P in the top lgp bits, then j / P, then the target), sorted
-// with a bitonic network in LDS, and turned into the union of distinct sources,
-// bucket by bucket and in increasing j within a bucket, with each source's
+// 32-bit keys (bucket j mod P in the top lgp bits, then j / P, then the target),
+// sorted in registers (wave_sort), and turned into the union of distinct
+// sources, bucket by bucket and in increasing j within a bucket, with each source's
 // slot count per target (16 bits per target) and each bucket's size and start.
 // Subgroup g of the wave then streams bucket g.  hook(t, u, j) runs once per
 // valid slot after the counts are cleared (e.g. to tabulate per-pair data).

@@ -9,7 +9,7 @@ namespace e2f {
 
 constexpr int kMaxLmax = 2;
 constexpr int kMaxPaths = 15;       // triangle-allowed (li, lf, lo) with all <= 2
-constexpr int kWavesPerBlock = 4;   // 256-thread workgroups, one wave per target
+constexpr int kWavesPerBlock = 4;   // 256-thread workgroups of the one-target-a-wave kernels
 constexpr int kTile = 256;          // neighbour slots compacted per pass
 constexpr int kXcds = 8;            // gfx950 (MI350 series): 8 XCDs, workgroups dealt round-robin
 constexpr int kBboxBlocks = 256;    // partial bounding boxes reduced by the schedule builder

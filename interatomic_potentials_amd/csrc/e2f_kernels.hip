@@ -464,8 +464,9 @@ __global__ __launch_bounds__(64 * kAggWaves) void k_aggregate(AggArgs a, EaasCoe
 // applied to every target that lists it (a source in c of a target's slots
 // weighs c exp(s), so repeated slots still count once each).  With the distance
 // envelope, each (target, source) pair's log2 u is tabulated in LDS while the
-// slots are counted and joins that pair's logit.  Adjacent targets share most of their neighbours, so the
-// rows read per target drop by the union's sharing factor.
+// slots are counted and joins that pair's logit.  Adjacent targets share most
+// of their neighbours, so the rows read per target drop by the union's sharing
+// factor.
 //
 // Subgroup g streams the union sources j with j mod P == g in increasing j,
 // and a target's state is touched only by sources it lists (a subgroup-uniform
