@@ -98,11 +98,16 @@ KERNEL_SOURCES = ["interatomic_potentials_amd/csrc/e2f_kernels.hip",
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code: comments and whitespace do not count."""
     import hashlib
+    import re
     hsh = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            hsh.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                  # line comments
+        hsh.update(" ".join(text.split()).encode())
     return hsh.hexdigest()[:16]
 
 
