@@ -869,28 +869,30 @@ __global__ __launch_bounds__(256) void k_sched_count(int64_t N, const float* pos
 }
 
 // exclusive scan of counts[0..kSchedCells) in place: one 1024-thread
-// workgroup, 32 consecutive counts per thread moved as 128-bit accesses
+// workgroup, eight tiles of 4096 counts with a running carry, each tile moved
+// as one coalesced 16-byte access a thread
 __global__ __launch_bounds__(1024) void k_sched_scan(int32_t* counts) {
-  static_assert(kSchedCells == 1024 * 32, "32 counts per thread");
+  static_assert(kSchedCells == 8 * 4096, "eight tiles of 4096 counts");
   __shared__ int32_t part[16];
   const int t = threadIdx.x;
-  int4* p = reinterpret_cast<int4*>(counts) + t * 8;
+  int4* p = reinterpret_cast<int4*>(counts);
   int4 v[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) v[k] = p[k];
-  int32_t sum = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) sum += v[k].x + v[k].y + v[k].z + v[k].w;
-  int32_t total;
-  int32_t run = block_exclusive_scan_1024(sum, part, &total);
+  for (int k = 0; k < 8; ++k) v[k] = p[k * 1024 + t];
+  int32_t carry = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
+    const int32_t sum = v[k].x + v[k].y + v[k].z + v[k].w;
+    int32_t total;
+    int32_t run = carry + block_exclusive_scan_1024(sum, part, &total);
     int4 o;
     o.x = run; run += v[k].x;
     o.y = run; run += v[k].y;
     o.z = run; run += v[k].z;
-    o.w = run; run += v[k].w;
-    p[k] = o;
+    o.w = run;
+    p[k * 1024 + t] = o;
+    carry += total;
+    __syncthreads();   // part is rewritten by the next tile's scan
   }
 }
 
