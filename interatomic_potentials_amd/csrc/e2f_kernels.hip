@@ -477,13 +477,10 @@ constexpr int kMtMaxK = kShareMaxK;   // longest neighbour row this kernel takes
 // Three targets per wave, two union sources per subgroup in flight: measured
 // against two targets with three in flight (the union of two rows is a larger
 // share of their lengths, and more rows go through the vector-memory path) and
-// three targets with three in flight (registers for one wave a SIMD only).
+// three targets with three in flight (registers for one wave a SIMD only).  The
+// envelope variant takes the same (its log2 u table fits at one wave a workgroup).
 constexpr int kMtTargets = 3;     // targets per wave
 constexpr int kMtInflight = 2;    // union sources per subgroup in flight
-// With the envelope, two targets and three in flight: a third target's log2 u
-// table would leave LDS for one block a CU.
-constexpr int kMtTargetsEnv = 2;
-constexpr int kMtInflightEnv = 3;
 
 // One wave a workgroup: the waves share nothing, and a workgroup's LDS and slot
 // are freed only when its last wave ends, so with four waves the early ones
@@ -969,8 +966,8 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
     // per wave share every row they read
     if (V == 4 && buf && a.K <= kMtMaxK && a.N < ((int64_t)1 << 30) &&
         (a.head_lanes == 1 || a.head_lanes == 2 || a.head_lanes == 4)) {
-      constexpr int TM = E ? kMtTargetsEnv : kMtTargets;
-      constexpr int UM = E ? kMtInflightEnv : kMtInflight;
+      constexpr int TM = kMtTargets;
+      constexpr int UM = kMtInflight;
       const int64_t mblocks = (a.N + kMtWaves * TM - 1) / (kMtWaves * TM);
       const dim3 mgrid((unsigned)((mblocks + kXcds - 1) / kXcds * kXcds));
       const dim3 mblk(64 * kMtWaves);
