@@ -716,7 +716,6 @@ __global__ __launch_bounds__(64 * kBwWaves) void k_bwd_src_mt(BwdArgs a, EaasCoe
   constexpr int S = ncomp(LMAX);
   constexpr int V = 4;
   using Lds = ShareLds<T, kSrcShareMaxL>;
-  constexpr int EN = Lds::EN;
   constexpr int CW = Lds::CW;
   __shared__ Lds s_un[kBwWaves];
   // h' of the wave's sources, one float4 per (source, component, lane of a subgroup)
