@@ -96,7 +96,8 @@ def test_big_configs_sampled(e2f, dev, name):
 
 @pytest.mark.parametrize("lmax,C,H,K,dtype", [(0, 32, 4, 10, "f32"), (1, 16, 2, 33, "f32"),
                                               (2, 64, 4, 300, "f32"), (2, 128, 16, 64, "f32"),
-                                              (2, 128, 16, 64, "bf16"), (1, 8, 8, 7, "f32")])
+                                              (2, 128, 16, 64, "bf16"), (1, 8, 8, 7, "f32"),
+                                              (2, 128, 16, 200, "bf16")])
 def test_shapes_and_slots_beyond_the_radius(e2f, dev, lmax, C, H, K, dtype):
     say(f"envelope shapes: lmax={lmax} C={C} H={H} K={K} {dtype}")
     rng = np.random.default_rng(lmax * 100 + C + K)

@@ -328,13 +328,14 @@ def test_empty_and_single_atom(e2f, dev):
     assert (out == 0).all()
 
 
-@pytest.mark.parametrize("name", ["water", "large"])
+@pytest.mark.parametrize("name", ["water", "large", "scaleout"])
 def test_schedule_covers_every_target_bit_exact(e2f, dev, name):
     """The Morton schedule only reorders work: same bits as index order, every target written."""
     cfg = make_config(name)
     s = cfg.spec
     say(f"schedule vs index order on {name}")
-    pos, h = T(cfg.pos, dev), T(cfg.h, dev)
+    dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    pos, h = T(cfg.pos, dev), T(cfg.h, dev, dt)
     idx, mask = T(cfg.idx, dev), T(cfg.mask, dev)
     a = torch.full_like(h, float("nan"))
     b = torch.full_like(h, float("nan"))
@@ -346,9 +347,12 @@ def test_schedule_covers_every_target_bit_exact(e2f, dev, name):
 
 @pytest.mark.parametrize("lmax,C,H,K", [(2, 128, 16, 64), (2, 128, 8, 40), (1, 64, 16, 30),
                                         (2, 8, 8, 20), (2, 512, 64, 16), (0, 16, 2, 300),
-                                        (1, 128, 8, 300)])
+                                        (1, 128, 8, 300), (2, 128, 16, 200), (2, 96, 12, 100),
+                                        (2, 64, 4, 64)])
 def test_attention_bf16_shapes_vs_oracle(e2f, dev, lmax, C, H, K):
-    """bf16 storage over every lane mapping: 8, 4 and 1 channels per lane, 1 or 2 lanes per head."""
+    """bf16 storage over every lane mapping: several targets a wave sharing rows (rows of up
+    to 64 and up to 256 slots, 1, 2 or 4 lanes per head, idle lanes at C = 96), and one
+    target a wave at 8, 4 and 1 channels per lane."""
     say(f"attention bf16 shapes: lmax={lmax} C={C} H={H} K={K}")
     rng = np.random.default_rng(7000 + lmax * 100 + C + K)
     N = 120
