@@ -218,9 +218,55 @@ def summarize_profile(pmc_dir, workload, out_path):
             share = busy / (1024.0 * active / 8.0) if active > 0 else float("nan")
             lines.append(f"| `{k}` | {nm.get((k, 'GRBM_GUI_ACTIVE'), 0)} | {flops:.4g} | "
                          f"{share:.2f} |")
+    if os.path.exists(os.path.join(pmc_dir, "trace_default", "run_kernel_trace.csv")) and \
+            os.path.exists(os.path.join(pmc_dir, "default.json")) and w == "large":
+        lines += _default_trace_section(pmc_dir)
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(out_path)
+
+
+def _default_trace_section(pmc_dir):
+    """The timed steps of the default command under --kernel-trace, beside the bench's own
+    HIP-event timing of the same steps in the same run."""
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(pmc_dir, "trace_default",
+                                                 "run_kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    with open(os.path.join(pmc_dir, "default.json")) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    warmup, steps = line["warmup"], line["steps"]
+    # the plain (no envelope) instance of the shared-row aggregate
+    is_plain = lambda n: "k_aggregate_mt<" in n and n.split(">(")[0].endswith("false")
+    plain = next((r["Kernel_Name"].split("(")[0].replace("void ", "") for r in rows
+                  if is_plain(r["Kernel_Name"])), "k_aggregate_mt")
+    kern, span, sched_start = [], [], None
+    for r in rows:
+        name = r["Kernel_Name"]
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        if "k_sched_" in name and sched_start is None:
+            sched_start = t0
+        elif is_plain(name):
+            kern.append((t1 - t0) * 1e-6)
+            span.append((t1 - (sched_start if sched_start is not None else t0)) * 1e-6)
+            sched_start = None
+        elif "k_eaas" in name or "k_proj_eaas" in name:
+            sched_start = None
+    timed_k = kern[warmup:warmup + steps]
+    timed_s = span[warmup:warmup + steps]
+    mean = lambda v: sum(v) / max(len(v), 1)
+    return ["", "## The default command under the kernel trace", "", "```",
+            "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/pmc/trace_default "
+            "-o run -- python -u bench.py > gpurun_out/pmc/default.json", "```", "",
+            f"The bench's own timing of its {steps} timed steps in this run (HIP events around "
+            f"the aggregate call, schedule kernels included): "
+            f"{line['kernels_ms']['aggregate']:.4f} ms.", "",
+            f"- `{plain}` dispatches {warmup + 1}-{warmup + steps} (the timed steps, after "
+            f"{warmup} warm-up steps): mean {mean(timed_k):.4f} ms, "
+            f"min {min(timed_k):.4f}, max {max(timed_k):.4f}",
+            f"- the same steps from the first schedule kernel's start to the aggregate's end: "
+            f"mean {mean(timed_s):.4f} ms",
+            f"- all {len(kern)} dispatches of `{plain}` in the run: mean {mean(kern):.4f} ms"]
 
 
 def aggregate_kernel(spec):
