@@ -140,6 +140,7 @@ def summarize_profile(pmc_dir, workload, out_path):
     """
     import csv
     w = workload
+    d = os.path.relpath(pmc_dir, ROOT) if os.path.isabs(pmc_dir) else pmc_dir   # as the runs named it
     stats = list(csv.DictReader(open(os.path.join(pmc_dir, f"trace_{w}", "run_kernel_stats.csv"))))
     fetch, nf = _counter_means(os.path.join(pmc_dir, f"fetch_{w}", "run_counter_collection.csv"))
     write, _ = _counter_means(os.path.join(pmc_dir, f"write_{w}", "run_counter_collection.csv"))
@@ -152,23 +153,23 @@ def summarize_profile(pmc_dir, workload, out_path):
     kw = copy_bytes / (cw[("__amd_rocclr_copyBuffer", "WRITE_SIZE")] * 1024)
     lines = [f"# rocprofv3 summary: {w} workload ({WORKLOADS[w]})", "",
              f"kernel source hash: {kernel_source_hash()}", "",
-             "Commands (run from the repository root on the GPU box; TMPDIR=/tmp):", "```"]
+             "Commands (run from the repository root on an MI355X, TMPDIR=/tmp):", "```"]
     extra = ""
     bench_cmd = ("python -u bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline"
                  "{x}").format(w=w, x=extra)
-    lines += [f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/pmc/trace_{w} "
+    lines += [f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_{w} "
               f"-o run -- {bench_cmd}",
-              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/fetch_{w} -o run "
+              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch_{w} -o run "
               f"-- {bench_cmd}",
-              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/write_{w} -o run "
+              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write_{w} -o run "
               f"-- {bench_cmd}",
               f"rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv -d "
-              f"gpurun_out/pmc/hit_{w} -o run -- {bench_cmd}",
-              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc/fetch_copy -o run "
+              f"{d}/hit_{w} -o run -- {bench_cmd}",
+              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch_copy -o run "
               f"-- python -u bench.py --calib-copy-mib {CALIB_COPY_MIB} --steps 3",
-              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc/write_copy -o run "
+              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write_copy -o run "
               f"-- python -u bench.py --calib-copy-mib {CALIB_COPY_MIB} --steps 3",
-              f"python bench.py --summarize-profile gpurun_out/pmc --workload {w}", "```", "",
+              f"python bench.py --summarize-profile {d} --workload {w}", "```", "",
               "## Kernel trace (--kernel-trace --stats)", "",
               "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in stats:
@@ -192,9 +193,10 @@ def summarize_profile(pmc_dir, workload, out_path):
         th = hit.get((k, "TCC_HIT_sum"), 0.0)
         tm = hit.get((k, "TCC_MISS_sum"), 0.0)
         traffic = fb * 1024 * kf + wb * 1024 * kw
-        lines.append(f"| `{k}` | {fb:.0f} | {wb:.0f} | {th:.4g} | {tm:.4g} | "
+        kn = k if len(k) <= 200 else k.split("<")[0].strip() + "<...>"
+        lines.append(f"| `{kn}` | {fb:.0f} | {wb:.0f} | {th:.4g} | {tm:.4g} | "
                      f"{th / max(th + tm, 1):.3f} | {traffic:.6g} |")
-        lines.append(f"<!-- traffic {k} {traffic:.0f} -->")
+        lines.append(f"<!-- traffic {kn} {traffic:.0f} -->")
     mfma_path = os.path.join(pmc_dir, f"mfma_{w}", "run_counter_collection.csv")
     if os.path.exists(mfma_path):
         mf, nm = _counter_means(mfma_path)
@@ -202,7 +204,7 @@ def summarize_profile(pmc_dir, workload, out_path):
                   "```",
                   f"rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16 "
                   f"SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d "
-                  f"gpurun_out/pmc/mfma_{w} -o run -- {bench_cmd} --no-extras --no-backward",
+                  f"{d}/mfma_{w} -o run -- {bench_cmd} --no-extras --no-backward",
                   "```", "",
                   "- MOPS count 512 flops each; the projections' algorithmic count is "
                   "2 (S + 2) C^2 flops per atom.",
@@ -220,13 +222,13 @@ def summarize_profile(pmc_dir, workload, out_path):
                          f"{share:.2f} |")
     if os.path.exists(os.path.join(pmc_dir, "trace_default", "run_kernel_trace.csv")) and \
             os.path.exists(os.path.join(pmc_dir, "default.json")) and w == "large":
-        lines += _default_trace_section(pmc_dir)
+        lines += _default_trace_section(pmc_dir, d)
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(out_path)
 
 
-def _default_trace_section(pmc_dir):
+def _default_trace_section(pmc_dir, d):
     """The timed steps of the default command under --kernel-trace, beside the bench's own
     HIP-event timing of the same steps in the same run."""
     import csv
@@ -256,8 +258,8 @@ def _default_trace_section(pmc_dir):
     timed_s = span[warmup:warmup + steps]
     mean = lambda v: sum(v) / max(len(v), 1)
     return ["", "## The default command under the kernel trace", "", "```",
-            "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/pmc/trace_default "
-            "-o run -- python -u bench.py > gpurun_out/pmc/default.json", "```", "",
+            f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_default "
+            f"-o run -- python -u bench.py > {d}/default.json", "```", "",
             f"The bench's own timing of its {steps} timed steps in this run (HIP events around "
             f"the aggregate call, schedule kernels included): "
             f"{line['kernels_ms']['aggregate']:.4f} ms.", "",
