@@ -77,9 +77,16 @@ def project(h: np.ndarray, w_q: np.ndarray, w_k: np.ndarray, w_v: np.ndarray):
 
 
 def envelope(x: np.ndarray) -> np.ndarray:
-    """u(x) = 1 - 21 x^5 + 35 x^6 - 15 x^7 for 0 <= x < 1, 0 for x >= 1 (reading in the header)."""
+    """u(x) = 1 - 21 x^5 + 35 x^6 - 15 x^7 for 0 <= x < 1, 0 for x >= 1 (reading in the header).
+
+    Evaluated as (1 - x)^3 (1 + 3x + 6x^2 + 10x^3 + 15x^4), the same polynomial.  Its
+    factors are positive on [0, 1), so u keeps its relative precision up to the cutoff;
+    the expanded sum cancels there (within 1e-5 of x = 1 no digit of it is left in
+    float64), and weights and gradients of pairs near the cutoff are relative to u.
+    """
     x = np.asarray(x, dtype=np.float64)
-    u = 1.0 - 21.0 * x ** 5 + 35.0 * x ** 6 - 15.0 * x ** 7
+    y = 1.0 - x
+    u = y ** 3 * (1.0 + x * (3.0 + x * (6.0 + x * (10.0 + 15.0 * x))))
     return np.where(x < 1.0, u, 0.0)
 
 

@@ -52,8 +52,10 @@ def tp_dense_torch(x: torch.Tensor, r: torch.Tensor, lmax: int,
 
 
 def envelope_torch(x: torch.Tensor) -> torch.Tensor:
-    """``oracle.attn.envelope`` in torch: 1 - 21 x^5 + 35 x^6 - 15 x^7 below 1, else 0."""
-    u = 1.0 - 21.0 * x ** 5 + 35.0 * x ** 6 - 15.0 * x ** 7
+    """``oracle.attn.envelope`` in torch: 1 - 21 x^5 + 35 x^6 - 15 x^7 below 1, else 0,
+    in the same factored form (1 - x)^3 (1 + 3x + 6x^2 + 10x^3 + 15x^4)."""
+    y = 1.0 - x
+    u = y ** 3 * (1.0 + x * (3.0 + x * (6.0 + x * (10.0 + 15.0 * x))))
     return torch.where(x < 1.0, u, torch.zeros_like(u))
 
 

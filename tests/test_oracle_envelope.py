@@ -29,6 +29,20 @@ def test_envelope_is_the_integral_of_its_derivative():
     assert np.all(envelope([1.0, 1.5, 7.0]) == 0.0)
 
 
+def test_envelope_keeps_its_relative_precision_up_to_the_cutoff():
+    """Against the defining polynomial 1 - 21 x^5 + 35 x^6 - 15 x^7 evaluated exactly (rational
+    arithmetic on each float x): relative error at float64 rounding level, right up to x -> 1,
+    where the pair weights and their gradients are relative to u."""
+    from fractions import Fraction
+    xs = [1.0 - 10.0 ** -k for k in range(1, 12)] + [0.0, 0.25, 0.5, 0.75, 0.9999999999]
+    xs += list(np.random.default_rng(3).random(20))
+    for x in xs:
+        f = Fraction(x)
+        exact = 1 - 21 * f ** 5 + 35 * f ** 6 - 15 * f ** 7
+        got = float(envelope(x))
+        assert abs(Fraction(got) - exact) <= Fraction(1, 10 ** 13) * abs(exact), x
+
+
 def test_envelope_is_smooth_and_monotone_at_the_cutoff():
     x = np.linspace(0.0, 1.0, 2001)
     u = envelope(x)

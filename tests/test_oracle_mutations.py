@@ -124,7 +124,11 @@ MUTATIONS = [
     (attn, "hp_src = tp_dense(v[src], pos[src], lmax, path_w)",
      "hp_src = tp_dense(v[src], -pos[src], lmax, path_w)",
      "step 1 with the reversed source direction"),
-    (attn, "- 15.0 * x ** 7", "- 14.0 * x ** 7", "a wrong envelope coefficient"),
+    (attn, "(10.0 + 15.0 * x)", "(10.0 + 14.0 * x)", "a wrong envelope coefficient"),
+    (attn, "u = y ** 3 * (", "u = y ** 2 * (", "the envelope's zero at the cutoff one order short"),
+    (attn, "u = y ** 3 * (1.0 + x * (3.0 + x * (6.0 + x * (10.0 + 15.0 * x))))",
+     "u = 1.0 - 21.0 * x ** 5 + 35.0 * x ** 6 - 15.0 * x ** 7",
+     "the envelope summed expanded, cancelling near the cutoff"),
     (attn, "e_src = idx[e_row, e_slot].astype(np.int64)",
      "e_src = idx[e_row, np.maximum(e_slot - 1, 0)].astype(np.int64)",
      "slot index off by one"),
