@@ -237,8 +237,9 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
       const float xi = a.pos[3 * i], yi = a.pos[3 * i + 1], zi = a.pos[3 * i + 2];
       for (int e = lane; e < cnt; e += 64) {
         const int j = nb[e];
-        const float dx = xi - a.pos[3 * j], dy = yi - a.pos[3 * j + 1], dz = zi - a.pos[3 * j + 2];
-        const EnvTerm et = envelope_term(dx, dy, dz, a.env_inv_rc);
+        const float xj = a.pos[3 * j], yj = a.pos[3 * j + 1], zj = a.pos[3 * j + 2];
+        const float dx = xi - xj, dy = yi - yj, dz = zi - zj;
+        const EnvTerm et = envelope_term(xi, yi, zi, xj, yj, zj, a.env_rc);
         s_env[w][e] = make_float4(et.log2u, et.dlog * dx, et.dlog * dy, et.dlog * dz);
       }
       wave_sync_b();
@@ -381,10 +382,10 @@ __global__ __launch_bounds__(64 * kBwWaves) void k_bwd_q_mt(BwdArgs a) {
 #pragma unroll
                            for (int tt = 1; tt < T; ++tt)
                              if (t == tt) ti = tg[tt];
-                           const float dx = a.pos[3 * ti] - a.pos[3 * j];
-                           const float dy = a.pos[3 * ti + 1] - a.pos[3 * j + 1];
-                           const float dz = a.pos[3 * ti + 2] - a.pos[3 * j + 2];
-                           const EnvTerm et = envelope_term(dx, dy, dz, a.env_inv_rc);
+                           const EnvTerm et =
+                               envelope_term(a.pos[3 * ti], a.pos[3 * ti + 1], a.pos[3 * ti + 2],
+                                             a.pos[3 * j], a.pos[3 * j + 1], a.pos[3 * j + 2],
+                                             a.env_rc);
                            s_env[w][t][u] = make_float2(et.log2u, et.dlog);
                          }
                        });
@@ -608,9 +609,9 @@ __global__ __launch_bounds__(256) void k_bwd_src(BwdArgs a, EaasCoef cf, int ski
       const float xj = a.pos[3 * j], yj = a.pos[3 * j + 1], zj = a.pos[3 * j + 2];
       for (int e = lane; e < cnt; e += 64) {
         const int ti = nb[e];
-        const float dx = a.pos[3 * ti] - xj, dy = a.pos[3 * ti + 1] - yj,
-                    dz = a.pos[3 * ti + 2] - zj;
-        const EnvTerm et = envelope_term(dx, dy, dz, a.env_inv_rc);
+        const float xi = a.pos[3 * ti], yi = a.pos[3 * ti + 1], zi = a.pos[3 * ti + 2];
+        const float dx = xi - xj, dy = yi - yj, dz = zi - zj;
+        const EnvTerm et = envelope_term(xi, yi, zi, xj, yj, zj, a.env_rc);
         s_env[w][e] = make_float4(et.log2u, et.dlog * dx, et.dlog * dy, et.dlog * dz);
       }
       wave_sync_b();

@@ -319,6 +319,7 @@ int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
   a.lse = lse;
   a.heads = H;
   a.env_inv_rc = env_inv(env_cutoff);
+  a.env_rc = env_cutoff > 0.0f ? env_cutoff : 0.0f;
   const EaasCoef cf = make_coef(lmax, path_w);
   return hip_status(e2f::launch_aggregate(lmax, dt, V, a, cf, stream));
 }
@@ -660,6 +661,7 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
   a.scale = (float)sc;
   a.scale_log2e = (float)(sc * 1.4426950408889634);
   a.env_inv_rc = env_inv(env_cutoff);
+  a.env_rc = env_cutoff > 0.0f ? env_cutoff : 0.0f;
   const EaasCoef cf = make_coef(lmax, path_w);
   return hip_status(e2f::launch_backward(lmax, V, a, cf, stream));
 }

@@ -60,6 +60,7 @@ struct AggArgs {
   float* lse;              // [N, H] natural log-sum-exp of each target's logits, or nullptr
   int heads;               // H
   float env_inv_rc;        // 1 / r_env of the distance envelope (kernels with the envelope only)
+  float env_rc;            // r_env itself
 };
 
 // Backward pass (vector-Jacobian product) arguments, fp32 storage.
@@ -89,6 +90,7 @@ struct BwdArgs {
   float scale;
   float scale_log2e;
   float env_inv_rc;        // 1 / r_env of the distance envelope, 0 = none
+  float env_rc;            // r_env itself
 };
 
 // Learned projections fused with the pre-coupling (storage type T for h and

@@ -299,8 +299,8 @@ __global__ __launch_bounds__(64 * kAggWaves) void k_aggregate(AggArgs a, EaasCoe
       const float xi = a.pos[3 * i], yi = a.pos[3 * i + 1], zi = a.pos[3 * i + 2];
       for (int e = lane; e < cnt; e += 64) {
         const int j = nb[e];
-        s_le[w][e] = envelope_term(xi - a.pos[3 * j], yi - a.pos[3 * j + 1],
-                                   zi - a.pos[3 * j + 2], a.env_inv_rc).log2u;
+        s_le[w][e] = envelope_term(xi, yi, zi, a.pos[3 * j], a.pos[3 * j + 1], a.pos[3 * j + 2],
+                                   a.env_rc).log2u;
       }
       wave_sync();
     }
@@ -534,10 +534,10 @@ __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasC
 #pragma unroll
                            for (int tt = 1; tt < T; ++tt)
                              if (t == tt) ti = tg[tt];
-                           s_le[w][t][u] = envelope_term(a.pos[3 * ti] - a.pos[3 * j],
-                                                         a.pos[3 * ti + 1] - a.pos[3 * j + 1],
-                                                         a.pos[3 * ti + 2] - a.pos[3 * j + 2],
-                                                         a.env_inv_rc).log2u;
+                           s_le[w][t][u] =
+                               envelope_term(a.pos[3 * ti], a.pos[3 * ti + 1], a.pos[3 * ti + 2],
+                                             a.pos[3 * j], a.pos[3 * j + 1], a.pos[3 * j + 2],
+                                             a.env_rc).log2u;
                          }
                        });
   const int my_cnt = un.bcnt[sub];

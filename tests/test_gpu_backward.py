@@ -45,12 +45,14 @@ def pos_err(got, ref):
     return float((np.linalg.norm(got - ref, axis=1) / den).max())
 
 
-def gpu_backward(e2f, dev, pos, h, idx, mask, H, g, **kw):
+def gpu_backward(e2f, dev, pos, h, idx, mask, H, g, env_cutoff=None, **kw):
     p, hh, ii, mm = T(pos, dev), T(h, dev), T(idx, dev), T(mask, dev)
     ws = e2f.attn_precouple(p, hh)
     out, msg, lse = e2f.attn_aggregate(p, ii, mm, ws, H, int(round(h.shape[1] ** 0.5)) - 1,
-                                       h.shape[2], torch.float32, return_msg=True, return_lse=True)
-    gh, gp = e2f.attn_backward(p, hh, ii, mm, H, ws, msg, lse, T(g, dev), **kw)
+                                       h.shape[2], torch.float32, return_msg=True, return_lse=True,
+                                       env_cutoff=env_cutoff)
+    gh, gp = e2f.attn_backward(p, hh, ii, mm, H, ws, msg, lse, T(g, dev), env_cutoff=env_cutoff,
+                               **kw)
     torch.cuda.synchronize()
     return gh.cpu().numpy(), gp.cpu().numpy(), lse
 
@@ -100,19 +102,22 @@ def test_backward_small_configs(e2f, dev, name):
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=1e-5)
 
 
-def test_backward_large_sampled(e2f, dev):
-    """Large workload: the upstream gradient lives on a few targets, so the oracle needs only their edges."""
+@pytest.mark.parametrize("envelope", [False, True])
+def test_backward_large_sampled(e2f, dev, envelope):
+    """Large workload: the upstream gradient lives on a few targets, so the oracle needs only their
+    edges; plain, and with the envelope at the list's cutoff (the two backward lines the bench times)."""
     cfg = make_config("large")
     s = cfg.spec
+    r_env = float(np.float32(s.cutoff)) if envelope else None   # as the library receives it
     rng = np.random.default_rng(9)
     tg = rng.choice(cfg.N, 24, replace=False)
     g = np.zeros(cfg.h.shape, np.float32)
     g[tg] = rng.standard_normal((tg.size,) + cfg.h.shape[1:]).astype(np.float32)
-    say(f"backward large, gradient on {tg.size} targets")
-    gh, gp, _ = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g)
+    say(f"backward large, gradient on {tg.size} targets, envelope {r_env}")
+    gh, gp, _ = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g, env_cutoff=r_env)
     mask_t = np.zeros_like(cfg.mask)
     mask_t[tg] = cfg.mask[tg]
-    rh, rp = oracle_backward(cfg.pos, cfg.h, cfg.idx, mask_t, s.H, s.lmax, g)
+    rh, rp = oracle_backward(cfg.pos, cfg.h, cfg.idx, mask_t, s.H, s.lmax, g, env_cutoff=r_env)
     touched = np.unique(np.concatenate([tg, cfg.idx[tg][cfg.mask[tg] != 0]]))
     assert block_rel_err(gh[touched], rh[touched], s.lmax) <= TOL_F32
     assert pos_err(gp[touched], rp[touched]) <= TOL_F32

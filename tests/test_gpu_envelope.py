@@ -62,6 +62,7 @@ def pos_err(got, ref):
 
 @pytest.mark.parametrize("name,r_env", [("tiny", 5.0), ("water", 5.0), ("water", 3.2)])
 def test_small_configs_full(e2f, dev, name, r_env):
+    r_env = float(np.float32(r_env))   # the cutoff as the library receives it
     cfg = make_config(name)
     s = cfg.spec
     say(f"envelope {name}: r_env={r_env} (list cutoff {s.cutoff}) N={cfg.N} E={cfg.nl.n_edges}")
@@ -80,15 +81,16 @@ def test_small_configs_full(e2f, dev, name, r_env):
 def test_big_configs_sampled(e2f, dev, name):
     cfg = make_config(name)
     s = cfg.spec
-    say(f"envelope {name}: r_env={s.cutoff} dtype={s.dtype} (sampled targets)")
+    r_env = float(np.float32(s.cutoff))   # the cutoff as the library receives it
+    say(f"envelope {name}: r_env={r_env} dtype={s.dtype} (sampled targets)")
     dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
     out, msg = e2f.attn_forward(T(cfg.pos, dev), T(cfg.h, dev, dt), T(cfg.idx, dev),
-                                T(cfg.mask, dev), s.H, return_msg=True, env_cutoff=s.cutoff)
+                                T(cfg.mask, dev), s.H, return_msg=True, env_cutoff=r_env)
     torch.cuda.synchronize()
     tg = np.random.default_rng(8).choice(cfg.N, 80, replace=False)
     tgt = torch.from_numpy(tg).to(dev)
     ref, ref_msg = oracle_attn(cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, s.lmax, targets=tg,
-                               return_msg=True, env_cutoff=s.cutoff, chunk_edges=4096)
+                               return_msg=True, env_cutoff=r_env, chunk_edges=4096)
     tol = TOL_BF16 if s.dtype == "bf16" else TOL_F32
     assert block_rel_err(to_host(msg[tgt]), ref_msg, s.lmax) <= tol
     assert block_rel_err(to_host(out[tgt]), ref, s.lmax) <= tol
