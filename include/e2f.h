@@ -177,9 +177,9 @@ int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int 
  *               e_ij exp(s_ijh) / sum_k e_ik exp(s_ikh),  e_ij = u(|pos_i - pos_j| / r_env),
  *               u(x) = 1 - 21 x^5 + 35 x^6 - 15 x^7 = (1-x)^3 (1+3x+6x^2+10x^3+15x^4)
  *             for x < 1 and 0 beyond (u, u' and u'' vanish at the cutoff).
- *             The pair distance and 1 - x are taken in fp64 from the fp32
- *             positions (1 - x is ill-conditioned near the cutoff), the rest
- *             of u in fp32.  A slot at or beyond r_env weighs
+ *             The squared distance and r_env^2 - d^2 are taken in fp64 from
+ *             the fp32 positions (1 - x is ill-conditioned near the cutoff),
+ *             the rest of u in fp32.  A slot at or beyond r_env weighs
  *             nothing; a target whose every slot does gives 0 like an empty
  *             row; lse then includes ln e.  Negative, infinite or NaN:
  *             E2F_ERR_SHAPE.

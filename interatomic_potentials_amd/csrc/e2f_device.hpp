@@ -539,35 +539,38 @@ struct VecIO<uint16_t, V> {
 // 0 beyond, evaluated in its factored form (1 - x)^3 (1 + 3x + 6x^2 + 10x^3 +
 // 15x^4), whose factors are all positive.  1 - x itself is ill-conditioned near
 // the cutoff: from an fp32 distance its relative error grows as 2^-24 / (1 - x),
-// and the cube triples it (3e-3 in u at 1 - x = 1e-4).  So the distance and
-// 1 - x = (r_env - d) / r_env are taken in float64, where the difference of two
-// fp32 coordinates is exact; the rest is fp32.
+// and the cube triples it (3e-3 in u at 1 - x = 1e-4).  So the squared distance
+// and r_env^2 - d^2 are taken in float64, where the difference of two fp32
+// coordinates is exact; the rest is fp32.
 struct EnvTerm {
   float log2u;   // log2 u(x); -inf at or beyond the cutoff
   float dlog;    // (d ln u / d r_i) = dlog * (r_i - r_j); 0 at or beyond the cutoff
 };
 
-// pi = r_i, pj = r_j (fp32 positions as given), rc = r_env
+// pi = r_i, pj = r_j (fp32 positions as given), rc = r_env.  d^2 and r_env^2 - d^2
+// in float64 (exact differences, no cancellation left in 1 - x = (r_env^2 - d^2) /
+// (r_env (r_env + d))); the denominator, x and the polynomial in fp32.
 __device__ inline EnvTerm envelope_term(float xi, float yi, float zi, float xj, float yj, float zj,
                                         float rc) {
   const double dx = (double)xi - (double)xj;
   const double dy = (double)yi - (double)yj;
   const double dz = (double)zi - (double)zj;
-  const double d = sqrt(fma(dx, dx, fma(dy, dy, dz * dz)));
-  const double rcd = (double)rc;
+  const double d2 = fma(dx, dx, fma(dy, dy, dz * dz));
+  const double rc2 = (double)rc * (double)rc;
   EnvTerm e;
-  if (!(d < rcd)) {
+  if (!(d2 < rc2)) {
     e.log2u = -INFINITY;
     e.dlog = 0.0f;
     return e;
   }
-  const float y = (float)((rcd - d) / rcd);
-  const float x = (float)(d / rcd);
+  const float d = sqrtf((float)d2);
+  const float inv_rc = 1.0f / rc;
+  const float y = (float)(rc2 - d2) / (rc * (rc + d));
+  const float x = d * inv_rc;
   const float q = fmaf(x, fmaf(x, fmaf(x, fmaf(x, 15.0f, 10.0f), 6.0f), 3.0f), 1.0f);
   e.log2u = __log2f(y * y * y * q);
   // u'(x) = -105 x^4 (1 - x)^2, so d ln u / dd = -105 x^4 / ((1 - x) q) / r_env and
   // the gradient along r_i - r_j divides by d = x r_env once more
-  const float inv_rc = 1.0f / rc;
   e.dlog = -105.0f * x * x * x / (y * q) * (inv_rc * inv_rc);
   return e;
 }
