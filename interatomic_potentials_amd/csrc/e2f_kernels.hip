@@ -568,6 +568,7 @@ __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasC
   for (int it = 0; it < maxlen; it += U) {
     Raw<float, V> kv[U][S + 1];
     uint32_t cw[U][CW];
+    float le[U][ENV ? T : 1];   // log2 of the envelope per (source, target), read with the rows
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool val = it + u < my_cnt;
@@ -580,6 +581,10 @@ __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasC
         buffer_load_raw<float, V>(rsrc, voff, (uint32_t)r * cbytes, kv[u][r]);
 #pragma unroll
       for (int c = 0; c < CW; ++c) cw[u][c] = val ? un.cnt[c][nn] : 0u;
+      if constexpr (ENV) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) le[u][t] = s_le[w][t][nn];
+      }
     }
     // keep every source's loads in flight before the first use
     __builtin_amdgcn_sched_barrier(0);
@@ -594,11 +599,8 @@ __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasC
           for (int v = 0; v < V; ++v) dt = fmaf(q[t][v], kv[u][0].get(v), dt);
           dt = head_sum_t<HL>(dt, a.head_lanes);
           float sc = dt * a.scale_log2e;
-          if constexpr (ENV) {
-            // log2 of the envelope joins the base-2 logit (-inf beyond the cutoff: weight 0)
-            const int n = my_start + it + u;
-            sc += s_le[w][t][n];
-          }
+          // log2 of the envelope joins the base-2 logit (-inf beyond the cutoff: weight 0)
+          if constexpr (ENV) sc += le[u][t];
           // lazy rescale, as in the single-target kernel, but decided per lane
           // (per head and subgroup): whether the other subgroup happens to be
           // updating this target must not move this subgroup's reference point
