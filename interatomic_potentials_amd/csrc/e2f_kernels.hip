@@ -564,6 +564,14 @@ __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasC
 #pragma unroll
       for (int v = 0; v < V; ++v) acc[t][r][v] = 0.0f;
   }
+  // union entry of the subgroup's k-th source; past the end of its bucket a
+  // subgroup re-reads some valid source and adds nothing
+  auto entry = [&](int k) {
+    return k < my_cnt ? my_start + k : (my_cnt > 0 ? my_start + my_cnt - 1 : 0);
+  };
+  int jcur[U];   // the sources of the coming iteration, read one iteration ahead
+#pragma unroll
+  for (int u = 0; u < U; ++u) jcur[u] = uj[entry(u)];
 #pragma unroll 1
   for (int it = 0; it < maxlen; it += U) {
     Raw<float, V> kv[U][S + 1];
@@ -572,10 +580,8 @@ __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasC
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool val = it + u < my_cnt;
-      // a subgroup past the end of its bucket re-reads some valid source and adds nothing
-      const int nn = val ? my_start + it + u : (my_cnt > 0 ? my_start + my_cnt - 1 : 0);
-      const int jn = uj[nn];
-      const uint32_t voff = (uint32_t)jn * row_bytes + (uint32_t)c0_load * 4u;
+      const int nn = entry(it + u);
+      const uint32_t voff = (uint32_t)jcur[u] * row_bytes + (uint32_t)c0_load * 4u;
 #pragma unroll
       for (int r = 0; r <= S; ++r)
         buffer_load_raw<float, V>(rsrc, voff, (uint32_t)r * cbytes, kv[u][r]);
@@ -586,6 +592,9 @@ __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasC
         for (int t = 0; t < T; ++t) le[u][t] = s_le[w][t][nn];
       }
     }
+    // the next iteration's sources, while these rows are in flight
+#pragma unroll
+    for (int u = 0; u < U; ++u) jcur[u] = uj[entry(it + U + u)];
     // keep every source's loads in flight before the first use
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
