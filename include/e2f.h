@@ -27,8 +27,9 @@
  * ---------------------------------------
  * - Buffers are device memory owned by the caller (path_w excepted: it is a
  *   small host array folded into the kernel arguments); the library
- *   allocates nothing and keeps no mutable global state (reentrant,
- *   thread-safe).
+ *   allocates nothing and keeps no mutable global state beyond a
+ *   mutex-guarded count of the HIP runtimes mapped (E2F_ERR_RUNTIME);
+ *   entry points are reentrant and thread-safe.
  * - Layouts are dense row-major with channels innermost:
  *     positions   float  [n, 3]          (always fp32, angstrom, as given)
  *     features    T      [n, S, C]       S = (lmax + 1)^2, T per `dtype`
@@ -82,6 +83,10 @@ typedef enum e2f_dtype {
 #define E2F_ERR_HIP (-7)         /* the HIP runtime reported an error at launch */
 #define E2F_ERR_INDEX (-8)       /* a valid slot holds an index outside [0, N) (validation only) */
 #define E2F_ERR_UNSUPPORTED (-9) /* channel / head layout outside the kernels' lane mapping */
+#define E2F_ERR_RUNTIME (-10)    /* two HIP runtimes are mapped into the process (e.g. this
+                                    library's libamdhip64.so.7 and a framework's own copy):
+                                    pointers and streams of one are invalid in the other; every
+                                    entry point that launches returns this before touching HIP */
 
 /* flags of the attention entry points (any other bit: E2F_ERR_SHAPE) */
 #define E2F_VALIDATE_INDICES 1u  /* check every valid slot's index before running; synchronises */

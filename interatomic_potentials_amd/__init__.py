@@ -35,7 +35,7 @@ TARGETS_IN_ORDER = 2
 _STATUS = {
     0: "E2F_OK", -1: "E2F_ERR_NULL", -2: "E2F_ERR_SHAPE", -3: "E2F_ERR_DTYPE",
     -4: "E2F_ERR_ALIGN", -5: "E2F_ERR_WORKSPACE", -6: "E2F_ERR_ALIAS", -7: "E2F_ERR_HIP",
-    -8: "E2F_ERR_INDEX", -9: "E2F_ERR_UNSUPPORTED",
+    -8: "E2F_ERR_INDEX", -9: "E2F_ERR_UNSUPPORTED", -10: "E2F_ERR_RUNTIME",
 }
 STATUS_CODES = {v: k for k, v in _STATUS.items()}
 
@@ -70,17 +70,49 @@ SIGNATURES = {
 }
 
 
+def hip_runtimes_mapped(maps_text: Optional[str] = None) -> list:
+    """Distinct HIP runtime files (libamdhip64*) mapped into this process.
+
+    Read from /proc/self/maps (or the given text in that format); files are
+    compared after resolving symbolic links.
+    """
+    if maps_text is None:
+        with open("/proc/self/maps") as f:
+            maps_text = f.read()
+    found = set()
+    for line in maps_text.splitlines():
+        parts = line.split(None, 5)
+        if len(parts) == 6:
+            path = parts[5].strip()
+            if os.path.basename(path).startswith("libamdhip64"):
+                found.add(os.path.realpath(path) if os.path.exists(path) else path)
+    return sorted(found)
+
+
+def _check_one_runtime(maps_text: Optional[str] = None) -> None:
+    found = hip_runtimes_mapped(maps_text)
+    if len(found) > 1:
+        raise ImportError(
+            "two HIP runtimes are mapped into this process (" + ", ".join(found) + "): "
+            "libe2f.so was loaded before torch.  Device pointers and streams of one runtime are "
+            "invalid in the other; import torch (or this package) before loading libe2f.so by "
+            "hand, in a fresh process.")
+
+
 def _load():
     # torch first: its wheel ships its own HIP runtime (requested as
     # libamdhip64.so), while libe2f.so asks for libamdhip64.so.7.  Loading
     # torch first makes the library bind to that same runtime, so the streams
     # and device pointers torch hands over are valid in it.  Loaded the other
-    # way round, the process would hold two HIP runtimes.
+    # way round, the process would hold two HIP runtimes: refuse that.
+    _check_one_runtime()
     import torch  # noqa: F401
+    _check_one_runtime()
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python interatomic_potentials_amd/build.py` (no fallback exists)")
     so = ctypes.CDLL(LIB_PATH)
+    _check_one_runtime()
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(so, name)
         fn.restype = res
@@ -147,6 +179,23 @@ def _dev(t, name: str, dtype=None):
     return t
 
 
+def _shape(t, name: str, shape) -> None:
+    """Raise ValueError unless tensor t (if given) has exactly this shape.
+
+    The C ABI receives bare pointers, so this is the one place where a buffer
+    too small for the sizes passed alongside it can be caught.
+    """
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+
+
+def _same_device(**tensors) -> None:
+    devs = {n: t.device for n, t in tensors.items() if t is not None}
+    if len(set(devs.values())) > 1:
+        raise ValueError("tensors live on different devices: "
+                         + ", ".join(f"{n} on {d}" for n, d in devs.items()))
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -185,20 +234,40 @@ def _path_w(path_w, device=None):
 
 
 # ------------------------------------------------------------ entry points
+#
+# Every entry point checks shapes first (ValueError), then that the tensors are
+# contiguous GPU tensors of the right dtype on one device, and only then calls
+# the library, so a mismatched buffer never reaches a kernel.
+
+def _dims(h, name="h"):
+    if h.dim() != 3:
+        raise ValueError(f"{name} must be [N, S, C], got {list(h.shape)}")
+    return tuple(h.shape)
+
+
+def _nbr_dims(nbr_idx, nbr_mask, N):
+    if nbr_idx.dim() != 2:
+        raise ValueError(f"nbr_idx must be [N, K], got {list(nbr_idx.shape)}")
+    K = nbr_idx.shape[1]
+    _shape(nbr_idx, "nbr_idx", (N, K))
+    _shape(nbr_mask, "nbr_mask", (N, K))
+    return K
+
 
 def eaas_couple(r, h, path_w=None, out=None):
     """h (x) R(r) through EAAS: r [n,3] fp32, h [n,S,C] fp32|bf16 -> [n,S,C]."""
     torch = _torch()
+    n, S, C = _dims(h)
+    lmax = _lmax_of(S)
+    _shape(r, "r", (n, 3))
+    _shape(out, "out", (n, S, C))
     _dev(r, "r", torch.float32)
     _dev(h, "h")
-    n, S, C = h.shape
-    lmax = _lmax_of(S)
-    if r.shape != (n, 3):
-        raise ValueError("r must be [n, 3]")
-    pw = _path_w(path_w, h.device)
     if out is None:
         out = torch.empty_like(h)
     _dev(out, "out", h.dtype)
+    _same_device(r=r, h=h, out=out)
+    pw = _path_w(path_w, h.device)
     _check(lib.e2f_eaas_couple(_stream(h), n, lmax, C, _dtype_code(h), _ptr(r), _ptr(h), _ptr(pw),
                                _ptr(out)), "e2f_eaas_couple")
     return out
@@ -214,18 +283,29 @@ def _new_workspace(N, lmax, C, dt, device):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
+def _proj_shapes(proj, C, lmax):
+    """Shape check of (w_q, w_k, w_v): [C, C], [C, C], [lmax + 1, C, C]."""
+    if proj is None:
+        return
+    w_q, w_k, w_v = proj
+    for t, name, shape in ((w_q, "w_q", (C, C)), (w_k, "w_k", (C, C)),
+                           (w_v, "w_v", (lmax + 1, C, C))):
+        _shape(t, name, shape)
+
+
 def _proj_weights(proj, h, lmax):
     """(w_q, w_k, w_v) as device tensors of h's dtype: [C, C], [C, C], [lmax + 1, C, C]."""
     if proj is None:
         return None
-    w_q, w_k, w_v = proj
-    C = h.shape[2]
-    for t, name, shape in ((w_q, "w_q", (C, C)), (w_k, "w_k", (C, C)),
-                           (w_v, "w_v", (lmax + 1, C, C))):
+    _proj_shapes(proj, h.shape[2], lmax)
+    for t, name in zip(proj, ("w_q", "w_k", "w_v")):
         _dev(t, name, h.dtype)
-        if tuple(t.shape) != shape:
-            raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
-    return w_q, w_k, w_v
+        _same_device(h=h, **{name: t})
+    return tuple(proj)
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
 
 
 def attn_precouple(pos, h, ws=None, path_w=None, proj=None):
@@ -235,24 +315,27 @@ def attn_precouple(pos, h, ws=None, path_w=None, proj=None):
     k = h[l=0] w_k, v[l] = h[l] w_v[l] before the coupling) on the matrix cores.
     """
     torch = _torch()
+    N, S, C = _dims(h)
+    lmax = _lmax_of(S)
+    _shape(pos, "pos", (N, 3))
+    _proj_shapes(proj, C, lmax)
     _dev(pos, "pos", torch.float32)
     _dev(h, "h")
-    N, S, C = h.shape
-    lmax = _lmax_of(S)
     dt = _dtype_code(h)
     if ws is None:
         ws = _new_workspace(N, lmax, C, dt, h.device)
     _dev(ws, "ws")
+    _same_device(pos=pos, h=h, ws=ws)
     pw = _path_w(path_w, h.device)
     w = _proj_weights(proj, h, lmax)
     if w is None:
         _check(lib.e2f_attn_precouple(_stream(h), N, lmax, C, dt, _ptr(pos), _ptr(h), _ptr(pw),
-                                      _ptr(ws), ws.numel() * ws.element_size()),
+                                      _ptr(ws), _nbytes(ws)),
                "e2f_attn_precouple")
     else:
         _check(lib.e2f_attn_precouple_proj(_stream(h), N, lmax, C, dt, _ptr(pos), _ptr(h),
                                            _ptr(w[0]), _ptr(w[1]), _ptr(w[2]), _ptr(pw), _ptr(ws),
-                                           ws.numel() * ws.element_size()),
+                                           _nbytes(ws)),
                "e2f_attn_precouple_proj")
     return ws
 
@@ -272,22 +355,28 @@ def attn_aggregate(pos, nbr_idx, nbr_mask, ws, heads: int, lmax: int, C: int, dt
     ``env_cutoff`` = r_env switches on the smooth distance envelope of the weights.
     """
     torch = _torch()
+    if nbr_idx.dim() != 2:
+        raise ValueError(f"nbr_idx must be [N, K], got {list(nbr_idx.shape)}")
+    N = nbr_idx.shape[0]
+    K = _nbr_dims(nbr_idx, nbr_mask, N)
+    S = (lmax + 1) ** 2
+    _shape(pos, "pos", (N, 3))
+    _shape(out, "out", (N, S, C))
     _dev(pos, "pos", torch.float32)
     _dev(nbr_idx, "nbr_idx", torch.int32)
     _dev(nbr_mask, "nbr_mask", torch.uint8)
     _dev(ws, "ws")
-    N, K = nbr_idx.shape
-    S = (lmax + 1) ** 2
     if out is None:
         out = torch.empty((N, S, C), dtype=dtype, device=ws.device)
     _dev(out, "out", dtype)
+    _same_device(pos=pos, nbr_idx=nbr_idx, nbr_mask=nbr_mask, ws=ws, out=out)
     msg = torch.empty_like(out) if return_msg else None
     lse = torch.empty((N, heads), dtype=torch.float32, device=ws.device) if return_lse else None
     pw = _path_w(path_w, ws.device)
     _check(lib.e2f_attn_aggregate(_stream(ws), N, K, lmax, C, heads, _dtype_code(out), _ptr(pos),
                                   _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0),
                                   float(env_cutoff or 0.0), _ptr(pw),
-                                  _ptr(ws), ws.numel() * ws.element_size(), _ptr(out), _ptr(msg),
+                                  _ptr(ws), _nbytes(ws), _ptr(out), _ptr(msg),
                                   _ptr(lse), _flags(validate, targets_in_order)),
            "e2f_attn_aggregate")
     return _results(out, msg, lse)
@@ -304,13 +393,16 @@ def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] =
     ``env_cutoff`` = r_env the smooth distance envelope of the weights.
     """
     torch = _torch()
+    N, S, C = _dims(h)
+    lmax = _lmax_of(S)
+    K = _nbr_dims(nbr_idx, nbr_mask, N)
+    _shape(pos, "pos", (N, 3))
+    _shape(out, "out", (N, S, C))
+    _proj_shapes(proj, C, lmax)
     _dev(pos, "pos", torch.float32)
     _dev(h, "h")
     _dev(nbr_idx, "nbr_idx", torch.int32)
     _dev(nbr_mask, "nbr_mask", torch.uint8)
-    N, S, C = h.shape
-    K = nbr_idx.shape[1]
-    lmax = _lmax_of(S)
     dt = _dtype_code(h)
     if ws is None:
         ws = _new_workspace(N, lmax, C, dt, h.device)
@@ -318,6 +410,7 @@ def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] =
     if out is None:
         out = torch.empty_like(h)
     _dev(out, "out", h.dtype)
+    _same_device(pos=pos, h=h, nbr_idx=nbr_idx, nbr_mask=nbr_mask, ws=ws, out=out)
     msg = torch.empty_like(h) if return_msg else None
     lse = torch.empty((N, heads), dtype=torch.float32, device=h.device) if return_lse else None
     pw = _path_w(path_w, h.device)
@@ -326,7 +419,7 @@ def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] =
         _check(lib.e2f_attn_forward(_stream(h), N, K, lmax, C, heads, dt, _ptr(pos), _ptr(h),
                                     _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0),
                                     float(env_cutoff or 0.0), _ptr(pw),
-                                    _ptr(ws), ws.numel() * ws.element_size(), _ptr(out), _ptr(msg),
+                                    _ptr(ws), _nbytes(ws), _ptr(out), _ptr(msg),
                                     _ptr(lse), _flags(validate, targets_in_order)),
                "e2f_attn_forward")
     else:
@@ -334,7 +427,7 @@ def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] =
                                          _ptr(w[0]), _ptr(w[1]), _ptr(w[2]), _ptr(nbr_idx),
                                          _ptr(nbr_mask), float(scale or 0.0),
                                          float(env_cutoff or 0.0), _ptr(pw), _ptr(ws),
-                                         ws.numel() * ws.element_size(), _ptr(out), _ptr(msg),
+                                         _nbytes(ws), _ptr(out), _ptr(msg),
                                          _ptr(lse), _flags(validate, targets_in_order)),
                "e2f_attn_forward_proj")
     return _results(out, msg, lse)
@@ -348,33 +441,41 @@ def attn_backward_workspace_bytes(N: int, K: int, lmax: int, C: int, H: int,
 def attn_backward(pos, h, nbr_idx, nbr_mask, heads: int, ws, msg, lse, grad_out,
                   scale: Optional[float] = None, path_w=None, targets_in_order: bool = False,
                   bwd_ws=None, grad_h=None, grad_pos=None, env_cutoff: Optional[float] = None):
-    """(dL/dh, dL/dpos) for L = <grad_out, out>; ws, msg, lse from the forward (fp32 only)."""
+    """(dL/dh, dL/dpos) for L = <grad_out, out>; ws, msg, lse from the forward."""
     torch = _torch()
+    N, S, C = _dims(h)
+    lmax = _lmax_of(S)
+    K = _nbr_dims(nbr_idx, nbr_mask, N)
+    _shape(pos, "pos", (N, 3))
+    for t, name in ((msg, "msg"), (grad_out, "grad_out"), (grad_h, "grad_h")):
+        _shape(t, name, (N, S, C))
+    _shape(lse, "lse", (N, heads))
+    _shape(grad_pos, "grad_pos", (N, 3))
     _dev(pos, "pos", torch.float32)
-    _dev(h, "h", torch.float32)
+    _dev(h, "h")
+    dt = _dtype_code(h)
     _dev(nbr_idx, "nbr_idx", torch.int32)
     _dev(nbr_mask, "nbr_mask", torch.uint8)
     _dev(ws, "ws")
-    _dev(msg, "msg", torch.float32)
+    _dev(msg, "msg", h.dtype)
     _dev(lse, "lse", torch.float32)
-    _dev(grad_out, "grad_out", torch.float32)
-    N, S, C = h.shape
-    K = nbr_idx.shape[1]
-    lmax = _lmax_of(S)
+    _dev(grad_out, "grad_out", h.dtype)
     if bwd_ws is None:
-        nbytes = attn_backward_workspace_bytes(N, K, lmax, C, heads, F32)
+        nbytes = attn_backward_workspace_bytes(N, K, lmax, C, heads, dt)
         bwd_ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=h.device)
     _dev(bwd_ws, "bwd_ws")
-    grad_h = torch.empty_like(h) if grad_h is None else _dev(grad_h, "grad_h", torch.float32)
+    grad_h = torch.empty_like(h) if grad_h is None else _dev(grad_h, "grad_h", h.dtype)
     grad_pos = (torch.empty_like(pos) if grad_pos is None
                 else _dev(grad_pos, "grad_pos", torch.float32))
+    _same_device(pos=pos, h=h, nbr_idx=nbr_idx, nbr_mask=nbr_mask, ws=ws, msg=msg, lse=lse,
+                 grad_out=grad_out, bwd_ws=bwd_ws, grad_h=grad_h, grad_pos=grad_pos)
     pw = _path_w(path_w, h.device)
-    _check(lib.e2f_attn_backward(_stream(h), N, K, lmax, C, heads, F32, _ptr(pos), _ptr(h),
+    _check(lib.e2f_attn_backward(_stream(h), N, K, lmax, C, heads, dt, _ptr(pos), _ptr(h),
                                  _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0),
                                  float(env_cutoff or 0.0), _ptr(pw),
-                                 _ptr(ws), ws.numel() * ws.element_size(), _ptr(msg), _ptr(lse),
+                                 _ptr(ws), _nbytes(ws), _ptr(msg), _ptr(lse),
                                  _ptr(grad_out), _ptr(grad_h), _ptr(grad_pos), _ptr(bwd_ws),
-                                 bwd_ws.numel() * bwd_ws.element_size(),
+                                 _nbytes(bwd_ws),
                                  TARGETS_IN_ORDER if targets_in_order else 0),
            "e2f_attn_backward")
     return grad_h, grad_pos
@@ -394,10 +495,10 @@ def neighbour_list(pos, cutoff: float, K: int, return_n_within: bool = False,
     grouped by cell in Morton order) when asked.
     """
     torch = _torch()
+    if pos.dim() != 2 or pos.shape[1] != 3:
+        raise ValueError(f"pos must be [N, 3], got {list(pos.shape)}")
     _dev(pos, "pos", torch.float32)
     N = pos.shape[0]
-    if pos.shape != (N, 3):
-        raise ValueError("pos must be [N, 3]")
     dev = pos.device
     idx = torch.empty((N, K), dtype=torch.int32, device=dev)
     mask = torch.empty((N, K), dtype=torch.uint8, device=dev)
@@ -406,15 +507,18 @@ def neighbour_list(pos, cutoff: float, K: int, return_n_within: bool = False,
     if ws is None:
         ws = torch.empty(max(neighbour_workspace_bytes(N), 1), dtype=torch.uint8, device=dev)
     _dev(ws, "ws")
+    _same_device(pos=pos, ws=ws)
     _check(lib.e2f_neighbour_list(_stream(pos), N, K, float(cutoff), _ptr(pos), _ptr(idx),
                                   _ptr(mask), _ptr(nw), _ptr(order), _ptr(ws),
-                                  ws.numel() * ws.element_size()), "e2f_neighbour_list")
+                                  _nbytes(ws)), "e2f_neighbour_list")
     return (idx, mask) + tuple(t for t in (nw, order) if t is not None)
 
 
 def frames(r, lmax: int = 2):
     """Alignment rotations Q [n,9] and Wigner-D blocks D [n,35] as the kernels build them."""
     torch = _torch()
+    if r.dim() != 2 or r.shape[1] != 3:
+        raise ValueError(f"r must be [n, 3], got {list(r.shape)}")
     _dev(r, "r", torch.float32)
     n = r.shape[0]
     Q = torch.zeros((n, 9), dtype=torch.float32, device=r.device)

@@ -5,9 +5,12 @@
 // formula for Clebsch-Gordan coefficients (Condon-Shortley phase), evaluated
 // here in double precision; the write-up (stapisi.com, section 2.2) states
 // the reindex rule, and section 5.2 warns that the CG normalisation matters.
+#include <link.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+
+#include <mutex>
 
 #include <hip/hip_runtime_api.h>
 
@@ -23,6 +26,60 @@ int hip_status(int err) {
   if (err == 0) return E2F_OK;
   g_last_hip_error = err;
   return E2F_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- runtime
+// A process that maps two HIP runtimes (e.g. this library's libamdhip64.so.7
+// loaded before a Python framework that ships its own copy) hands this library
+// streams and device pointers that belong to the other runtime; launches then
+// fail or crash.  Every entry point that would touch HIP first counts the
+// runtimes mapped; the loader's add/remove counters make the recount rare.
+struct RuntimeScan {
+  unsigned long long adds, subs;  // loader counters at the last full scan
+  bool valid;                     // a scan has been made
+  int runtimes;                   // HIP runtime objects found then
+  bool early;                     // set by the callback when the counters are unchanged
+};
+std::mutex g_rt_mutex;
+RuntimeScan g_rt = {0, 0, false, 0, false};
+
+int runtime_scan_cb(struct dl_phdr_info* info, size_t, void* data) {
+  RuntimeScan* sc = static_cast<RuntimeScan*>(data);
+  if (sc->valid && info->dlpi_adds == sc->adds && info->dlpi_subs == sc->subs) {
+    sc->early = true;   // nothing loaded or unloaded since the last scan
+    return 1;
+  }
+  if (sc->valid) sc->valid = false;   // first object of a full scan
+  sc->adds = info->dlpi_adds;
+  sc->subs = info->dlpi_subs;
+  const char* name = info->dlpi_name ? info->dlpi_name : "";
+  const char* base = strrchr(name, '/');
+  base = base ? base + 1 : name;
+  if (strncmp(base, "libamdhip64", 11) == 0) ++sc->runtimes;
+  return 0;
+}
+
+// E2F_OK when at most one HIP runtime is mapped, E2F_ERR_RUNTIME otherwise
+int check_runtime() {
+  RuntimeScan sc;
+  {
+    std::lock_guard<std::mutex> lk(g_rt_mutex);
+    sc = g_rt;
+  }
+  sc.early = false;
+  const bool had = sc.valid;
+  const int before = sc.runtimes;
+  sc.runtimes = 0;
+  dl_iterate_phdr(runtime_scan_cb, &sc);
+  if (sc.early) {
+    sc.runtimes = before;
+    sc.valid = had;
+  } else {
+    sc.valid = true;
+    std::lock_guard<std::mutex> lk(g_rt_mutex);
+    g_rt = sc;
+  }
+  return sc.runtimes > 1 ? E2F_ERR_RUNTIME : E2F_OK;
 }
 
 using e2f::EaasCoef;
@@ -340,6 +397,7 @@ const char* e2f_status_string(int status) {
     case E2F_ERR_HIP: return "E2F_ERR_HIP";
     case E2F_ERR_INDEX: return "E2F_ERR_INDEX";
     case E2F_ERR_UNSUPPORTED: return "E2F_ERR_UNSUPPORTED";
+    case E2F_ERR_RUNTIME: return "E2F_ERR_RUNTIME";
     default: return "E2F_ERR_UNKNOWN";
   }
 }
@@ -357,6 +415,7 @@ int e2f_path_count(int lmax) {
 
 int e2f_eaas_couple(hipStream_t stream, int64_t n, int lmax, int C, int dtype, const float* r,
                     const void* h_in, const float* path_w, void* h_out) {
+  if (const int rt = check_runtime()) return rt;
   int st = check_shape_common(n, lmax, C, dtype);
   if (st != E2F_OK) return st;
   if (n == 0) return E2F_OK;
@@ -389,6 +448,7 @@ size_t e2f_attn_workspace_bytes(int64_t N, int lmax, int C, int dtype) {
 int e2f_attn_precouple(hipStream_t stream, int64_t N, int lmax, int C, int dtype,
                        const float* pos, const void* h, const float* path_w, void* workspace,
                        size_t ws_bytes) {
+  if (const int rt = check_runtime()) return rt;
   int st = check_shape_common(N, lmax, C, dtype);
   if (st != E2F_OK) return st;
   if (N == 0) return E2F_OK;
@@ -408,6 +468,7 @@ int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, in
                        const float* pos, const int32_t* nbr_idx, const uint8_t* nbr_mask,
                        float scale, float env_cutoff, const float* path_w, void* workspace,
                        size_t ws_bytes, void* out, void* out_msg, float* lse, uint32_t flags) {
+  if (const int rt = check_runtime()) return rt;
   int st = check_attn_shape(N, K, lmax, C, H, dtype, flags);
   if (st != E2F_OK) return st;
   if (bad_env(env_cutoff)) return E2F_ERR_SHAPE;
@@ -477,6 +538,7 @@ int forward_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, i
                  const void* w_v, const int32_t* nbr_idx, const uint8_t* nbr_mask, float scale,
                  float env_cutoff, const float* path_w, void* workspace, size_t ws_bytes,
                  void* out, void* out_msg, float* lse, uint32_t flags, bool proj) {
+  if (const int rt = check_runtime()) return rt;
   int st = check_attn_shape(N, K, lmax, C, H, dtype, flags);
   if (st != E2F_OK) return st;
   if (bad_env(env_cutoff)) return E2F_ERR_SHAPE;
@@ -552,6 +614,7 @@ int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int 
                             const float* pos, const void* h, const void* w_q, const void* w_k,
                             const void* w_v, const float* path_w, void* workspace,
                             size_t ws_bytes) {
+  if (const int rt = check_runtime()) return rt;
   int st = check_shape_common(N, lmax, C, dtype);
   if (st != E2F_OK) return st;
   if (N == 0) return E2F_OK;
@@ -582,6 +645,7 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
                       const void* msg, const float* lse, const void* grad_out, void* grad_h,
                       float* grad_pos, void* bwd_workspace, size_t bwd_ws_bytes,
                       uint32_t flags) {
+  if (const int rt = check_runtime()) return rt;
   int st = check_attn_shape(N, K, lmax, C, H, dtype, flags);
   if (st != E2F_OK) return st;
   if (bad_env(env_cutoff)) return E2F_ERR_SHAPE;
@@ -674,6 +738,7 @@ size_t e2f_neighbour_workspace_bytes(int64_t N) {
 int e2f_neighbour_list(hipStream_t stream, int64_t N, int K, double cutoff, const float* pos,
                        int32_t* nbr_idx, uint8_t* nbr_mask, int32_t* n_within, int32_t* order,
                        void* workspace, size_t ws_bytes) {
+  if (const int rt = check_runtime()) return rt;
   if (N < 0 || K < 1 || !(cutoff > 0.0) || !isfinite(cutoff)) return E2F_ERR_SHAPE;
   if (N > kNlMaxAtoms || K > e2f::kNlMaxK) return E2F_ERR_UNSUPPORTED;
   if (N == 0) return E2F_OK;
@@ -717,6 +782,7 @@ int e2f_neighbour_list(hipStream_t stream, int64_t N, int K, double cutoff, cons
 }
 
 int e2f_frames(hipStream_t stream, int64_t n, int lmax, const float* r, float* Q, float* D) {
+  if (const int rt = check_runtime()) return rt;
   if (n < 0 || lmax < 0 || lmax > e2f::kMaxLmax) return E2F_ERR_SHAPE;
   if (n == 0) return E2F_OK;
   if (!r || !Q || !D) return E2F_ERR_NULL;

@@ -323,3 +323,115 @@ def test_neighbour_list_argument_errors():
     assert _nl(mask=ctypes.c_void_p(BASE + 2 * 64 * MB + 1000)) == C["E2F_ERR_ALIAS"]
     assert _nl(nw=fake(4)) == C["E2F_ERR_ALIAS"]
     assert _nl(order=fake(3)) == C["E2F_ERR_ALIAS"]
+
+
+# ------------------------------------------------ two HIP runtimes in one process
+
+def test_runtime_scan_of_maps_text():
+    maps = "\n".join([
+        "7f00-7f01 r-xp 00000000 00:00 1 /opt/rocm-7.2.0/lib/libamdhip64.so.7.2.70200",
+        "7f01-7f02 r--p 00001000 00:00 1 /opt/rocm-7.2.0/lib/libamdhip64.so.7.2.70200",
+        "7f02-7f03 r-xp 00000000 00:00 2 /site/torch/lib/libamdhip64.so",
+        "7f03-7f04 rw-p 00000000 00:00 0 ",
+        "7f04-7f05 r-xp 00000000 00:00 3 /usr/lib/libc.so.6",
+    ])
+    assert len(e2f.hip_runtimes_mapped(maps)) == 2
+    with pytest.raises(ImportError, match="two HIP runtimes"):
+        e2f._check_one_runtime(maps)
+    one = "\n".join(maps.splitlines()[:2])
+    assert len(e2f.hip_runtimes_mapped(one)) == 1
+    e2f._check_one_runtime(one)
+    # this test process loaded torch first, so only one runtime is mapped
+    assert len(e2f.hip_runtimes_mapped()) <= 1
+
+
+def test_library_loaded_before_torch_refuses_to_run():
+    """libe2f.so loaded by hand before torch maps two HIP runtimes: every launching entry point
+    returns E2F_ERR_RUNTIME before touching HIP, and importing the binding raises ImportError.
+    CPU only: no HIP call is made in the child process."""
+    import sys
+    code = f"""
+import ctypes, sys
+sys.path.insert(0, {ROOT!r})
+so = ctypes.CDLL({e2f.LIB_PATH!r})
+import torch
+f = so.e2f_eaas_couple
+f.restype = ctypes.c_int
+f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+print("rc", f(None, 1, 2, 128, 0, None, None, None, None))
+g = so.e2f_frames
+g.restype = ctypes.c_int
+g.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+              ctypes.c_void_p]
+print("rc", g(None, 1, 2, None, None, None))
+try:
+    import interatomic_potentials_amd
+    print("imported")
+except ImportError as e:
+    print("ImportError", "two HIP runtimes" in str(e))
+"""
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         timeout=300, env={**os.environ, "HIP_VISIBLE_DEVICES": ""})
+    lines = res.stdout.split("\n")
+    assert f"rc {C['E2F_ERR_RUNTIME']}" in lines, res.stdout + res.stderr
+    assert lines.count(f"rc {C['E2F_ERR_RUNTIME']}") == 2, res.stdout + res.stderr
+    assert "ImportError True" in lines, res.stdout + res.stderr
+
+
+# ------------------------------------------------ shape checks of the binding
+
+def _cpu_inputs(N=6, K=4, lmax=1, C=16, H=2):
+    import torch
+    S = (lmax + 1) ** 2
+    return dict(pos=torch.zeros(N, 3), h=torch.zeros(N, S, C),
+                idx=torch.zeros(N, K, dtype=torch.int32), mask=torch.zeros(N, K, dtype=torch.uint8),
+                ws=torch.zeros(1024, dtype=torch.uint8), N=N, K=K, lmax=lmax, C=C, H=H, S=S)
+
+
+def test_binding_rejects_mismatched_shapes_before_any_launch():
+    """Every size the library trusts is checked in Python first (ValueError), so a buffer too
+    small for the sizes passed beside it never reaches a kernel.  CPU tensors: a shape error is
+    reported before the device check, so nothing here touches the library."""
+    import torch
+    a = _cpu_inputs()
+    N, K, S, C, H = a["N"], a["K"], a["S"], a["C"], a["H"]
+    pos, h, idx, mask, ws = a["pos"], a["h"], a["idx"], a["mask"], a["ws"]
+    bad = [
+        (lambda: e2f.attn_forward(pos[:-1], h, idx, mask, H), "pos"),
+        (lambda: e2f.attn_forward(pos, h, idx[:-1], mask[:-1], H), "nbr_idx"),
+        (lambda: e2f.attn_forward(pos, h, idx, mask[:, :-1], H), "nbr_mask"),
+        (lambda: e2f.attn_forward(pos, h, idx, mask, H, out=torch.zeros(N, S, C + 1)), "out"),
+        (lambda: e2f.attn_forward(pos, h[:, :3], idx, mask, H), "square"),
+        (lambda: e2f.attn_aggregate(pos[:-1], idx, mask, ws, H, 1, C, torch.float32), "pos"),
+        (lambda: e2f.attn_aggregate(pos, idx, mask[:-1], ws, H, 1, C, torch.float32), "nbr_mask"),
+        (lambda: e2f.attn_aggregate(pos, idx, mask, ws, H, 1, C, torch.float32,
+                                    out=torch.zeros(N, S + 1, C)), "out"),
+        (lambda: e2f.attn_precouple(pos[:, :2], h), "pos"),
+        (lambda: e2f.eaas_couple(pos[:-1], h), "r"),
+        (lambda: e2f.eaas_couple(pos, h, out=torch.zeros(N, S, C // 2)), "out"),
+        (lambda: e2f.attn_precouple(pos, h, proj=(torch.zeros(C, C), torch.zeros(C, C + 1),
+                                                  torch.zeros(2, C, C))), "w_k"),
+        (lambda: e2f.frames(pos[:, :2]), "r"),
+        (lambda: e2f.neighbour_list(pos[:, :2], 1.0, 4), "pos"),
+    ]
+    g = torch.zeros(N, S, C)
+    lse = torch.zeros(N, H)
+    bwd = dict(msg=g, lse=lse, grad_out=g)
+    bad += [
+        (lambda: e2f.attn_backward(pos, h, idx, mask, H, ws, g[:-1], lse, g), "msg"),
+        (lambda: e2f.attn_backward(pos, h, idx, mask, H, ws, g, lse[:, :-1], g), "lse"),
+        (lambda: e2f.attn_backward(pos, h, idx, mask, H, ws, g, lse, g[:, :, :-1]), "grad_out"),
+        (lambda: e2f.attn_backward(pos, h, idx, mask, H, ws, **bwd,
+                                   grad_h=torch.zeros(N, S, C + 4)), "grad_h"),
+        (lambda: e2f.attn_backward(pos, h, idx, mask, H, ws, **bwd,
+                                   grad_pos=torch.zeros(N + 1, 3)), "grad_pos"),
+        (lambda: e2f.attn_backward(pos[:-1], h, idx, mask, H, ws, **bwd), "pos"),
+        (lambda: e2f.attn_backward(pos, h, idx[:, :-1], mask, H, ws, **bwd), "nbr_mask"),
+    ]
+    for fn, what in bad:
+        with pytest.raises(ValueError, match=what):
+            fn()
+    # matching shapes on the CPU stop at the device check instead
+    with pytest.raises(ValueError, match="GPU"):
+        e2f.attn_forward(pos, h, idx, mask, H)
