@@ -7,9 +7,13 @@ e2f_attn_precouple + e2f_attn_aggregate, exactly what e2f_attn_forward runs.
 Inputs are synthetic (seeded generator), resident in HBM before timing.
 
 Prints one JSON line.  ``value`` is valid edges per second for the whole
-step; ``roofline`` reports the dominant kernel (the aggregate) against
-MI355X's 8 TB/s HBM peak using its algorithmic bytes; ``cpu_baseline`` times
-the CPU oracle on a bounded sample of the same workload.
+step (warm, back-to-back steps); ``cold`` gives medians of steps that each
+follow a 1 GiB eviction write.  ``roofline`` reports the step's kernels
+against MI355X's 8 TB/s HBM peak with their counter-measured L2-to-fabric
+bytes (committed rocprofv3 summary under profiles/) over this run's kernel
+time, next to the method's algorithmic bytes and the cache reuse between
+them; ``cpu_baseline`` times the CPU oracle on the host's cores on a bounded
+sample of the same workload.
 """
 
 from __future__ import annotations
@@ -25,6 +29,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# fp32 vector rate of MI355X, packed math counted (the library is built without packed fp32,
+# so plain FMA issue tops out at half of it)
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 CALIB_COPY_MIB = 1024
 
 WORKLOADS = {
@@ -39,14 +46,6 @@ WORKLOADS = {
             "all 15 paths of lmax=2, fp32",
 }
 
-# Per-CU vector-memory path of gfx950: one 64-lane 16-byte-per-lane load per
-# 16 cycles through the texture addresser / data return units, i.e. 64 B/clk
-# per CU; 256 CUs at 2.4 GHz.  The aggregate kernel's counters show these
-# units >90% busy, so this is the ceiling it runs against once the gathered
-# rows hit in L2.
-VMEM_PATH_PEAK_GBS = 64 * 256 * 2.4
-
-
 
 def algorithmic_bytes(N, K, E, S, C, b):
     """Bytes the method must move (each neighbour's k and h' rows once per edge; no edge tensors)."""
@@ -57,44 +56,151 @@ def algorithmic_bytes(N, K, E, S, C, b):
     return k1, k2, per_edge, per_target
 
 
-def cpu_baseline(cfg, budget_s=15.0, seed=0):
-    """Time the CPU oracle (single-threaded numpy, fp64) on a bounded target sample."""
+def _cpu_model():
+    """The host CPU's model name (as lscpu reports it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Worker processes of the CPU baseline.  The box gives one GPU a share of 16 host
+# cores, whatever the machine's core count: the pool never exceeds that.
+CPU_POOL_MAX = 16
+
+
+def _cpu_load(data_dir):
+    """The workload's arrays, saved by the parent; features widened to float64 once."""
+    import numpy as np
+    d = {k: np.load(os.path.join(data_dir, k + ".npy"), mmap_mode="r")
+         for k in ("pos", "h", "idx", "mask")}
+    meta = json.load(open(os.path.join(data_dir, "meta.json")))
+    return (np.asarray(d["pos"], dtype=np.float64), np.asarray(d["h"], dtype=np.float64),
+            d["idx"], d["mask"], meta)
+
+
+def _cpu_run(pos, h, idx, mask, meta, targets, t_stop, chunk):
+    """Oracle forward over `targets` in chunks until the wall clock passes t_stop.
+
+    Returns (targets done, edges done, seconds)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle.attn import attn_forward as oracle_forward
 
-    s = cfg.spec
-    rng = np.random.default_rng(seed)
-    order = rng.permutation(cfg.N)
-    n_t, done_t, done_e, elapsed = 16, 0, 0, 0.0
+    done_t = done_e = 0
+    t0 = time.perf_counter()
     with threadpool_limits(limits=1):
-        while elapsed < budget_s and done_t < cfg.N:
-            tg = np.sort(order[done_t:done_t + n_t])
-            t0 = time.perf_counter()
-            oracle_forward(cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, s.lmax, targets=tg,
+        while done_t < len(targets) and time.time() < t_stop:
+            tg = np.sort(targets[done_t:done_t + chunk])
+            oracle_forward(pos, h, idx, mask, meta["H"], meta["lmax"], targets=tg,
                            chunk_edges=4096)
-            elapsed += time.perf_counter() - t0
-            done_e += int(cfg.mask[tg].sum())
+            done_e += int(np.asarray(mask[tg]).sum())
             done_t += tg.size
-            n_t = min(n_t * 2, 1024)
+    return done_t, done_e, time.perf_counter() - t0
+
+
+def _cpu_worker(data_dir, rank, n, t_start, budget_s, queue):
+    """One pool process: load, wait for the common start, run the oracle for budget_s."""
+    import numpy as np
+    pos, h, idx, mask, meta = _cpu_load(data_dir)
+    targets = np.random.default_rng(1000 + rank).permutation(meta["N"])
+    while time.time() < t_start:
+        time.sleep(0.01)
+    w0 = time.time()
+    done_t, done_e, secs = _cpu_run(pos, h, idx, mask, meta, targets, t_start + budget_s, 256)
+    queue.put((rank, done_t, done_e, w0, time.time()))
+
+
+def cpu_baseline_child(data_dir, budget_s):
+    """Time the CPU oracle: one core for a third of the budget, then a pool of n processes
+    (n = the cores this process may run on, at most CPU_POOL_MAX), one BLAS thread each."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    pos, h, idx, mask, meta = _cpu_load(data_dir)
+    # one core
+    targets = np.random.default_rng(999).permutation(meta["N"])
+    one_t, one_e, one_s = _cpu_run(pos, h, idx, mask, meta, targets,
+                                   time.time() + budget_s / 3.0, 256)
+    del pos, h
+    # n cores: every worker loads first, all start together, each runs for the same time
+    n = max(1, min(len(os.sched_getaffinity(0)), CPU_POOL_MAX))
+    ctx = mp.get_context("spawn")
+    q = ctx.Queue()
+    t_start = time.time() + 8.0 + 0.5 * n
+    pool_s = 2.0 * budget_s / 3.0
+    procs = [ctx.Process(target=_cpu_worker, args=(data_dir, r, n, t_start, pool_s, q))
+             for r in range(n)]
+    for p in procs:
+        p.start()
+    res = [q.get(timeout=600) for _ in procs]
+    for p in procs:
+        p.join(timeout=60)
+    t_all = sum(r[1] for r in res)
+    e_all = sum(r[2] for r in res)
+    wall = max(r[4] for r in res) - min(r[3] for r in res)
+    late = max(r[3] for r in res) - t_start
     return {
-        "value": done_e / elapsed,
-        "unit": "edges/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"{done_t} random targets of the {cfg.N}-atom workload ({done_e} edges), "
-                  f"{elapsed:.1f} s, fp64 numpy with every edge materialised, BLAS limited to 1 "
-                  "thread",
-        "atoms_per_s": done_t / elapsed,
+        "value": e_all / wall, "unit": "edges/s", "cores": n, "kind": "oracle",
+        "sample": (f"random targets of the {meta['N']}-atom workload, drawn per process: {n} "
+                   f"processes (one BLAS thread each) ran the oracle for {wall:.1f} s wall and "
+                   f"evaluated {t_all} targets ({e_all} edges) in chunks of 256; fp64 numpy "
+                   f"with every edge materialised; input generation and neighbour lists untimed"),
+        "atoms_per_s": t_all / wall,
+        "cpu_model": _cpu_model(),
+        "single_core": {"edges_per_s": one_e / one_s, "atoms_per_s": one_t / one_s,
+                        "targets": one_t, "edges": one_e, "seconds": one_s},
+        "parallel_efficiency": (e_all / wall) / (n * one_e / one_s),
+        "worker_start_spread_s": late,
     }
 
 
+def cpu_baseline(cfg, budget_s=15.0):
+    """The CPU oracle on the host, in a child process that never touches the GPU.
+
+    The workload's arrays go to a temporary directory; the child times one core and then a
+    pool of processes over random targets of the same workload (input generation and the
+    neighbour list are not timed)."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    import numpy as np
+
+    d = tempfile.mkdtemp(prefix="e2f_cpu_")
+    try:
+        np.save(os.path.join(d, "pos.npy"), cfg.pos)
+        np.save(os.path.join(d, "h.npy"), cfg.h)
+        np.save(os.path.join(d, "idx.npy"), cfg.idx)
+        np.save(os.path.join(d, "mask.npy"), cfg.mask)
+        with open(os.path.join(d, "meta.json"), "w") as f:
+            json.dump({"N": int(cfg.N), "H": int(cfg.spec.H), "lmax": int(cfg.spec.lmax)}, f)
+        res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-dir", d,
+                              "--cpu-budget", str(budget_s)], capture_output=True, text=True,
+                             timeout=900)
+        if res.returncode != 0:
+            return {"error": f"CPU baseline child exited {res.returncode}: {res.stderr[-500:]}"}
+        return json.loads(res.stdout.strip().splitlines()[-1])
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+
+
+# Sources of the kernels a forward step and the EAAS workload launch: the committed counters of
+# a workload stay valid while these are unchanged (the backward, projection and neighbour-list
+# files do not touch those kernels).
 KERNEL_SOURCES = ["interatomic_potentials_amd/csrc/e2f_kernels.hip",
-                  "interatomic_potentials_amd/csrc/e2f_backward.hip",
-                  "interatomic_potentials_amd/csrc/e2f_project.hip",
+                  "interatomic_potentials_amd/csrc/e2f_aggregate_wg.hip",
+                  "interatomic_potentials_amd/csrc/e2f_dense.hip",
                   "interatomic_potentials_amd/csrc/e2f_device.hpp",
                   "interatomic_potentials_amd/csrc/e2f_internal.hpp"]
+
+N_CU, N_XCD, N_SIMD = 256, 8, 1024   # MI355X
 
 
 def kernel_source_hash():
@@ -111,6 +217,19 @@ def kernel_source_hash():
     return hsh.hexdigest()[:16]
 
 
+def _kernel_key(name):
+    """A kernel's name with its template arguments, without its parameter list."""
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "").strip()
+    depth, cut = 0, len(name)
+    for n, ch in enumerate(name):
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            cut = n
+            break
+    return name[:cut].strip()
+
+
 def _counter_means(path):
     """Mean counter value per (kernel, counter) from a rocprofv3 counter_collection.csv."""
     import collections
@@ -118,25 +237,43 @@ def _counter_means(path):
     acc = collections.defaultdict(list)
     with open(path) as f:
         for row in csv.DictReader(f):
-            # the kernel with its template arguments, without its parameter list
-            name = row["Kernel_Name"].replace("void ", "").replace("(anonymous namespace)::", "")
-            name = name.strip()
-            depth, cut = 0, len(name)
-            for n, ch in enumerate(name):
-                depth += ch == "<"
-                depth -= ch == ">"
-                if ch == "(" and depth == 0:
-                    cut = n
-                    break
-            acc[(name[:cut].strip(), row["Counter_Name"])].append(float(row["Counter_Value"]))
+            acc[(_kernel_key(row["Kernel_Name"]), row["Counter_Name"])].append(
+                float(row["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+
+# the counter pass that says what bounds a kernel (one run: 2 TA, 2 TD, 1 GRBM, 4 SQ counters)
+BUSY_COUNTERS = ["TA_TA_BUSY_sum", "TD_TD_BUSY_sum", "TD_TC_STALL_sum", "GRBM_GUI_ACTIVE",
+                 "SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_LDS", "SQ_BUSY_CU_CYCLES"]
+
+
+def _busy(get):
+    """Busy shares from the busy pass.  GRBM_GUI_ACTIVE sums the 8 XCDs' clocks, so one XCD's
+    cycles are GRBM_GUI_ACTIVE / 8; TA and TD counters sum the 256 CUs' units; a wave64 VALU
+    instruction holds its SIMD for 4 cycles."""
+    cyc = get("GRBM_GUI_ACTIVE") / N_XCD
+    if cyc <= 0:
+        return {}
+    return {"ta_busy": get("TA_TA_BUSY_sum") / (N_CU * cyc),
+            "td_busy": get("TD_TD_BUSY_sum") / (N_CU * cyc),
+            "td_stalled_on_l2": get("TD_TC_STALL_sum") / (N_CU * cyc),
+            "valu_issue": 4.0 * get("SQ_INSTS_VALU") / (N_SIMD * cyc),
+            "vmem_rd_insts": get("SQ_INSTS_VMEM_RD"), "lds_insts": get("SQ_INSTS_LDS"),
+            "cycles": cyc}
+
+
+def profile_bench_cmd(w):
+    """The bench command each counter pass of a workload profiles: warm steps only."""
+    extra = " --no-cpu-baseline --cold-reps 0 --index-order-reps 0" if w != "eaas" else ""
+    return f"python -u bench.py --workload {w} --steps 3 --warmup 1{extra}"
 
 
 def summarize_profile(pmc_dir, workload, out_path):
     """Write the committed counter summary from a directory of rocprofv3 csv runs.
 
-    Expects sub-directories trace_<w>, fetch_<w>, write_<w>, hit_<w>, fetch_copy, write_copy
-    (each holding run_*.csv) as produced by the commands listed in the summary.
+    Expects sub-directories trace_<w>, fetch_<w>, write_<w>, fetch_copy, write_copy and,
+    optionally, hit_<w>, busy_<w>, mfma_<w> (each holding run_*.csv) as produced by the
+    commands listed in the summary.
     """
     import csv
     w = workload
@@ -144,30 +281,32 @@ def summarize_profile(pmc_dir, workload, out_path):
     stats = list(csv.DictReader(open(os.path.join(pmc_dir, f"trace_{w}", "run_kernel_stats.csv"))))
     fetch, nf = _counter_means(os.path.join(pmc_dir, f"fetch_{w}", "run_counter_collection.csv"))
     write, _ = _counter_means(os.path.join(pmc_dir, f"write_{w}", "run_counter_collection.csv"))
-    hit_path = os.path.join(pmc_dir, f"hit_{w}", "run_counter_collection.csv")
-    hit = _counter_means(hit_path)[0] if os.path.exists(hit_path) else {}
+
+    def optional(name):
+        path = os.path.join(pmc_dir, f"{name}_{w}", "run_counter_collection.csv")
+        return _counter_means(path)[0] if os.path.exists(path) else {}
+
+    hit, busy = optional("hit"), optional("busy")
     cf, _ = _counter_means(os.path.join(pmc_dir, "fetch_copy", "run_counter_collection.csv"))
     cw, _ = _counter_means(os.path.join(pmc_dir, "write_copy", "run_counter_collection.csv"))
     copy_bytes = CALIB_COPY_MIB << 20
     kf = copy_bytes / (cf[("__amd_rocclr_copyBuffer", "FETCH_SIZE")] * 1024)
     kw = copy_bytes / (cw[("__amd_rocclr_copyBuffer", "WRITE_SIZE")] * 1024)
+    avg_ns = {_kernel_key(r["Name"]): float(r["AverageNs"]) for r in stats}
     lines = [f"# rocprofv3 summary: {w} workload ({WORKLOADS[w]})", "",
              f"kernel source hash: {kernel_source_hash()}", "",
              "Commands (run from the repository root on an MI355X, TMPDIR=/tmp):", "```"]
-    extra = ""
-    bench_cmd = ("python -u bench.py --workload {w} --steps 3 --warmup 1 --no-cpu-baseline"
-                 "{x}").format(w=w, x=extra)
+    bench_cmd = profile_bench_cmd(w)
+    prof = "rocprofv3 --output-format csv"
     lines += [f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_{w} "
               f"-o run -- {bench_cmd}",
-              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch_{w} -o run "
-              f"-- {bench_cmd}",
-              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write_{w} -o run "
-              f"-- {bench_cmd}",
-              f"rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv -d "
-              f"{d}/hit_{w} -o run -- {bench_cmd}",
-              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch_copy -o run "
+              f"{prof} --pmc FETCH_SIZE -d {d}/fetch_{w} -o run -- {bench_cmd}",
+              f"{prof} --pmc WRITE_SIZE -d {d}/write_{w} -o run -- {bench_cmd}",
+              f"{prof} --pmc TCC_HIT_sum TCC_MISS_sum -d {d}/hit_{w} -o run -- {bench_cmd}",
+              f"{prof} --pmc {' '.join(BUSY_COUNTERS)} -d {d}/busy_{w} -o run -- {bench_cmd}",
+              f"{prof} --pmc FETCH_SIZE -d {d}/fetch_copy -o run "
               f"-- python -u bench.py --calib-copy-mib {CALIB_COPY_MIB} --steps 3",
-              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write_copy -o run "
+              f"{prof} --pmc WRITE_SIZE -d {d}/write_copy -o run "
               f"-- python -u bench.py --calib-copy-mib {CALIB_COPY_MIB} --steps 3",
               f"python bench.py --summarize-profile {d} --workload {w}", "```", "",
               "## Kernel trace (--kernel-trace --stats)", "",
@@ -185,18 +324,32 @@ def summarize_profile(pmc_dir, workload, out_path):
               f"- WRITE_SIZE reads {cw[('__amd_rocclr_copyBuffer', 'WRITE_SIZE')]:.0f} KiB per copy "
               f"of {copy_bytes} B written: write factor {kw:.4f}", "",
               "## Per-dispatch counters (mean over dispatches) and calibrated traffic", "",
-              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | TCC_HIT | TCC_MISS | L2 hit rate | "
-              "traffic bytes per launch |", "|---|---|---|---|---|---|---|"]
+              "Traffic = FETCH_SIZE x read factor + WRITE_SIZE x write factor: the bytes that "
+              "cross between L2 and the fabric (Infinity Cache and HBM).  Busy shares: "
+              "TA_TA_BUSY_sum and TD_TD_BUSY_sum over 256 CUs x (GRBM_GUI_ACTIVE / 8) cycles; "
+              "TD stalled on L2 = TD_TC_STALL_sum on the same base; VALU issue = 4 x "
+              "SQ_INSTS_VALU over 1024 SIMDs x (GRBM_GUI_ACTIVE / 8).", "",
+              "| kernel | avg ns | FETCH_SIZE KiB | WRITE_SIZE KiB | L2 hit rate | traffic bytes | "
+              "traffic GB/s | TA busy | TD busy | TD stalled on L2 | VALU issue | VMEM rd insts |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for k in sorted({k for (k, c) in fetch}):
         fb = fetch.get((k, "FETCH_SIZE"), 0.0)
         wb = write.get((k, "WRITE_SIZE"), 0.0)
         th = hit.get((k, "TCC_HIT_sum"), 0.0)
         tm = hit.get((k, "TCC_MISS_sum"), 0.0)
         traffic = fb * 1024 * kf + wb * 1024 * kw
+        b = _busy(lambda c: busy.get((k, c), 0.0)) if busy else {}
+        ns = avg_ns.get(k)
+        gbs = traffic / ns if ns else float("nan")
         kn = k if len(k) <= 200 else k.split("<")[0].strip() + "<...>"
-        lines.append(f"| `{kn}` | {fb:.0f} | {wb:.0f} | {th:.4g} | {tm:.4g} | "
-                     f"{th / max(th + tm, 1):.3f} | {traffic:.6g} |")
-        lines.append(f"<!-- traffic {kn} {traffic:.0f} -->")
+        fmt = lambda key: f"{b[key]:.2f}" if key in b else "-"
+        lines.append(f"| `{kn}` | {ns or 0:.0f} | {fb:.0f} | {wb:.0f} | "
+                     f"{th / max(th + tm, 1):.3f} | {traffic:.6g} | {gbs:.0f} | {fmt('ta_busy')} | "
+                     f"{fmt('td_busy')} | {fmt('td_stalled_on_l2')} | {fmt('valu_issue')} | "
+                     f"{b.get('vmem_rd_insts', float('nan')):.4g} |")
+        fields = [f"traffic={traffic:.0f}"] + ([f"avg_ns={ns:.0f}"] if ns else []) + \
+            [f"{key}={val:.6g}" for key, val in b.items()]
+        lines.append(f"<!-- kernel {kn} | {' '.join(fields)} -->")
     mfma_path = os.path.join(pmc_dir, f"mfma_{w}", "run_counter_collection.csv")
     if os.path.exists(mfma_path):
         mf, nm = _counter_means(mfma_path)
@@ -215,60 +368,106 @@ def summarize_profile(pmc_dir, workload, out_path):
         for k in sorted({k for (k, c) in mf if "k_proj_eaas" in k}):
             flops = 512.0 * (mf.get((k, "SQ_INSTS_VALU_MFMA_MOPS_F32"), 0.0)
                              + mf.get((k, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), 0.0))
-            busy = mf.get((k, "SQ_VALU_MFMA_BUSY_CYCLES"), 0.0)
+            bz = mf.get((k, "SQ_VALU_MFMA_BUSY_CYCLES"), 0.0)
             active = mf.get((k, "GRBM_GUI_ACTIVE"), 0.0)
-            share = busy / (1024.0 * active / 8.0) if active > 0 else float("nan")
+            share = bz / (1024.0 * active / 8.0) if active > 0 else float("nan")
             lines.append(f"| `{k}` | {nm.get((k, 'GRBM_GUI_ACTIVE'), 0)} | {flops:.4g} | "
                          f"{share:.2f} |")
-    if os.path.exists(os.path.join(pmc_dir, "trace_default", "run_kernel_trace.csv")) and \
-            os.path.exists(os.path.join(pmc_dir, "default.json")) and w == "large":
-        lines += _default_trace_section(pmc_dir, d)
+    if os.path.exists(os.path.join(pmc_dir, f"trace_default_{w}", "run_kernel_trace.csv")) and \
+            os.path.exists(os.path.join(pmc_dir, f"default_{w}.json")) and w != "eaas":
+        lines += _default_trace_section(pmc_dir, d, w)
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(out_path)
 
 
-def _default_trace_section(pmc_dir, d):
+def _default_trace_section(pmc_dir, d, w):
     """The timed steps of the default command under --kernel-trace, beside the bench's own
     HIP-event timing of the same steps in the same run."""
     import csv
-    rows = list(csv.DictReader(open(os.path.join(pmc_dir, "trace_default",
+    rows = list(csv.DictReader(open(os.path.join(pmc_dir, f"trace_default_{w}",
                                                  "run_kernel_trace.csv"))))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    with open(os.path.join(pmc_dir, "default.json")) as f:
+    with open(os.path.join(pmc_dir, f"default_{w}.json")) as f:
         line = json.loads(f.read().strip().splitlines()[-1])
     warmup, steps = line["warmup"], line["steps"]
-    # the plain (no envelope) instance of the shared-row aggregate
-    is_plain = lambda n: "k_aggregate_mt<" in n and n.split(">(")[0].endswith("false")
-    plain = next((r["Kernel_Name"].split("(")[0].replace("void ", "") for r in rows
-                  if is_plain(r["Kernel_Name"])), "k_aggregate_mt")
-    kern, span, sched_start = [], [], None
+    # one step: the pre-coupling, the schedule kernels, then the plain aggregate
+    step_k1 = lambda n: "k_eaas<" in n and _kernel_key(n).endswith("true>")
+    agg = lambda n: _plain_aggregate(_kernel_key(n))
+    spans, k1s, k2s, t_k1 = [], [], [], None
     for r in rows:
         name = r["Kernel_Name"]
         t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
-        if "k_sched_" in name and sched_start is None:
-            sched_start = t0
-        elif is_plain(name):
-            kern.append((t1 - t0) * 1e-6)
-            span.append((t1 - (sched_start if sched_start is not None else t0)) * 1e-6)
-            sched_start = None
-        elif "k_eaas" in name or "k_proj_eaas" in name:
-            sched_start = None
-    timed_k = kern[warmup:warmup + steps]
-    timed_s = span[warmup:warmup + steps]
+        if step_k1(name):
+            t_k1 = t0
+            k1s.append((t1 - t0) * 1e-6)
+        elif agg(name) and t_k1 is not None:
+            k2s.append((t1 - t0) * 1e-6)
+            spans.append((t1 - t_k1) * 1e-6)
+            t_k1 = None
+    sel = slice(warmup, warmup + steps)
     mean = lambda v: sum(v) / max(len(v), 1)
     return ["", "## The default command under the kernel trace", "", "```",
-            f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_default "
-            f"-o run -- python -u bench.py > {d}/default.json", "```", "",
-            f"The bench's own timing of its {steps} timed steps in this run (HIP events around "
-            f"the aggregate call, schedule kernels included): "
-            f"{line['kernels_ms']['aggregate']:.4f} ms.", "",
-            f"- `{plain}` dispatches {warmup + 1}-{warmup + steps} (the timed steps, after "
-            f"{warmup} warm-up steps): mean {mean(timed_k):.4f} ms, "
-            f"min {min(timed_k):.4f}, max {max(timed_k):.4f}",
-            f"- the same steps from the first schedule kernel's start to the aggregate's end: "
-            f"mean {mean(timed_s):.4f} ms",
-            f"- all {len(kern)} dispatches of `{plain}` in the run: mean {mean(kern):.4f} ms"]
+            f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_default_{w} "
+            f"-o run -- python -u bench.py --workload {w} --no-cpu-baseline "
+            f"> {d}/default_{w}.json", "```", "",
+            f"The bench's own timing of its {steps} timed steps in this run (HIP events on the "
+            f"launch stream): pre-coupling {line['kernels_ms']['precouple']:.4f} ms, aggregate "
+            f"with its schedule kernels {line['kernels_ms']['aggregate']:.4f} ms, step "
+            f"{line['ms_per_step']:.4f} ms.", "",
+            f"- the timed steps (dispatches {warmup + 1}-{warmup + steps}) under the trace: "
+            f"pre-coupling kernel mean {mean(k1s[sel]):.4f} ms, aggregate kernel mean "
+            f"{mean(k2s[sel]):.4f} ms (min {min(k2s[sel]):.4f}, max {max(k2s[sel]):.4f}), "
+            f"pre-coupling start to aggregate end {mean(spans[sel]):.4f} ms"]
+
+
+def _plain_aggregate(key):
+    """True for the aggregate instances without the distance envelope."""
+    if "<" not in key:
+        return False
+    args = [x.strip() for x in key[key.index("<") + 1:key.rindex(">")].split(",")]
+    if key.startswith("e2f::k_aggregate_mt<"):
+        return args[4] == "false"
+    if key.startswith("e2f::k_aggregate<"):
+        return args[6] == "false"
+    return False
+
+
+def step_kernel(key, workload):
+    """Whether a kernel (name with template arguments) is launched by one forward step."""
+    if workload == "eaas":
+        return key.startswith("e2f::k_eaas<") and key.endswith("false>")
+    return ((key.startswith("e2f::k_eaas<") and key.endswith("true>"))
+            or key.startswith("e2f::k_sched_")
+            or (key.startswith("e2f::k_aggregate") and _plain_aggregate(key)))
+
+
+def committed_counters(workload):
+    """{kernel: {traffic, avg_ns, ta_busy, ...}} from the committed summary, or None when the
+    kernel sources changed since it was taken."""
+    import re
+    base = "k_eaas" if workload == "eaas" else "k_aggregate"
+    path = os.path.join(ROOT, "profiles", f"{base}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if f"kernel source hash: {kernel_source_hash()}" not in text:
+        return None
+    out = {}
+    for name, fields in re.findall(r"<!-- kernel (.*?) \| (.*?) -->", text):
+        out[name] = {k: float(v) for k, v in (f.split("=") for f in fields.split())}
+    return out
+
+
+def committed_step_traffic(workload, prefixes=None):
+    """Calibrated L2-to-fabric bytes of one step's kernels (or of the kernels whose names start
+    with one of `prefixes`), or None without a current summary."""
+    cc = committed_counters(workload)
+    if not cc:
+        return None
+    keys = [k for k in cc if (step_kernel(k, workload) if prefixes is None
+                              else any(k.startswith(p) for p in prefixes))]
+    return sum(cc[k]["traffic"] for k in keys) if keys else None
 
 
 def aggregate_kernel(spec):
@@ -278,24 +477,6 @@ def aggregate_kernel(spec):
     shared = (spec.dtype == "f32" and spec.K <= 256 and d % 4 == 0 and d // 4 in (1, 2, 4)
               and C // 4 <= 64)
     return "e2f::k_aggregate_mt" if shared else "e2f::k_aggregate"
-
-
-def committed_traffic(workload, kernel="e2f::k_aggregate"):
-    """Calibrated HBM bytes per launch from the committed summary, if the kernel is unchanged."""
-    base = "k_eaas" if workload == "eaas" else "k_aggregate"
-    path = os.path.join(ROOT, "profiles", f"{base}_{workload}.md")
-    if not os.path.exists(path):
-        return None
-    text = open(path).read()
-    if f"kernel source hash: {kernel_source_hash()}" not in text:
-        return None
-    import re
-    # the plain instance: the envelope flag (the workspace flag of k_eaas) is false
-    flag = {"e2f::k_aggregate": 6, "e2f::k_aggregate_mt": 4, "e2f::k_eaas": 3}[kernel]
-    for args, val in re.findall(r"<!-- traffic %s<([^>]*)> (\d+) -->" % re.escape(kernel), text):
-        if [x.strip() for x in args.split(",")][flag] == "false":
-            return float(val)
-    return None
 
 
 def bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream):
@@ -464,7 +645,8 @@ def bench_envelope(args, e2f, cfg, pos, h, idx, mask, ws, out, stream, k2_ms):
 
 
 def bench_eaas(args, e2f, dev):
-    """The EAAS tensor product on its own (e2f_eaas_couple over 2^20 vectors)."""
+    """The EAAS tensor product on its own (e2f_eaas_couple over 2^20 vectors), timed beside the
+    dense Clebsch-Gordan contraction it replaces (e2f_dense_couple, the same product)."""
     import numpy as np
     import torch
 
@@ -476,20 +658,34 @@ def bench_eaas(args, e2f, dev):
     h = torch.from_numpy(h_np).to(dev)
     out = torch.empty_like(h)
     del h_np
-    for _ in range(args.warmup):
-        e2f.eaas_couple(r, h, out=out)
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for e in ev:
-        e[0].record(stream)
-        e2f.eaas_couple(r, h, out=out)
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn(r, h, out=out)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+              for _ in range(args.steps)]
+        for e in ev:
+            e[0].record(stream)
+            fn(r, h, out=out)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        t = [e[0].elapsed_time(e[1]) for e in ev]
+        return float(np.mean(t)), float(np.median(t))
+
+    ms, ms_med = timed(e2f.eaas_couple)
+    dense_ms, dense_med = timed(e2f.dense_couple)
     per_vec = 2 * S * C * 4 + 12
     gbs = B * per_vec / (ms * 1e-3) / 1e9
-    print(f"[bench] eaas: {B} vectors, {ms:.3f} ms, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    # multiply-adds per channel: EAAS (rotate in, sparse reindex, rotate back) against the
+    # dense contraction (every path's full tensor, plus the 81 products h[si] R[sf])
+    dense_fma = 615 + 81
+    dense_tflops = 2.0 * B * C * dense_fma / (dense_ms * 1e-3) / 1e12
+    print(f"[bench] eaas: {B} vectors, {ms:.3f} ms, {gbs:.0f} GB/s; dense CG {dense_ms:.3f} ms "
+          f"({dense_tflops:.1f} TFLOP/s); dense / EAAS = {dense_ms / ms:.2f}",
+          file=sys.stderr, flush=True)
+    traffic = committed_step_traffic("eaas", ["e2f::k_eaas<"])
     result = {
         "metric": "EAAS tensor-product vectors/s (lmax=2, C=128, all 15 paths)",
         "value": B / (ms * 1e-3), "unit": "vectors/s", "n_gpus": 1, "steps": args.steps,
@@ -497,9 +693,18 @@ def bench_eaas(args, e2f, dev):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded generator)",
         "config": {"workload": WORKLOADS["eaas"], "vectors": B, "lmax": 2, "channels": C},
         "roofline": {"kernel": "k_eaas", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": committed_traffic("eaas", "e2f::k_eaas"),
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": B * per_vec, "bytes_per_vector": per_vec},
+        "dense_vs_eaas": {
+            "kernel": "k_dense_tp (every path's full real CG tensor, 615 multiply-adds per "
+                      "channel + 81 products)",
+            "dense_ms": dense_ms, "eaas_ms": ms, "ratio": dense_ms / ms,
+            "dense_ms_median": dense_med, "eaas_ms_median": ms_med,
+            "dense_tflops": dense_tflops, "fp32_vector_peak_tflops": FP32_VECTOR_PEAK_TFLOPS,
+            "note": "the pages' 6.49x (write-up Fig. 3) is an operation-count ratio on other "
+                    "hardware; here EAAS runs at the HBM roofline and the dense kernel is bound "
+                    "by fp32 FMA issue",
+        },
     }
     print(json.dumps(result), flush=True)
     return 0
@@ -518,14 +723,22 @@ def main(argv=None):
                     help="skip the envelope variant and the neighbour-list build timed after it")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward pass (dL/dh, dL/dpos) timed after the forward")
-    ap.add_argument("--index-order-reference", action="store_true",
-                    help="also time the aggregate visiting targets in index order (no schedule)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--index-order-reps", type=int, default=5,
+                    help="reps of the aggregate visiting targets in index order (a reference)")
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="steps timed after a 1 GiB eviction write each (median reported)")
+    ap.add_argument("--cpu-budget", type=float, default=18.0, help="seconds of oracle time")
+    ap.add_argument("--cpu-baseline-dir", default=None,
+                    help="(internal) time the CPU oracle on the arrays saved in this directory")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
                     help="write profiles/k_aggregate_<workload>.md from rocprofv3 csv runs in DIR")
     args = ap.parse_args(argv)
+
+    if args.cpu_baseline_dir:
+        print(json.dumps(cpu_baseline_child(args.cpu_baseline_dir, args.cpu_budget)), flush=True)
+        return 0
 
     if args.summarize_profile:
         kernel = "k_eaas" if args.workload == "eaas" else "k_aggregate"
@@ -589,6 +802,7 @@ def main(argv=None):
                      dtype=torch.uint8, device=dev)
     out = torch.empty_like(h)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
 
     def step():
         e2f.attn_precouple(pos, h, ws)
@@ -598,7 +812,7 @@ def main(argv=None):
         step()
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream(dev)
+    # warm: K back-to-back steps, HIP events on the launch stream around each kernel group
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -614,14 +828,34 @@ def main(argv=None):
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    k2_ms_min = float(np.min([e[1].elapsed_time(e[2]) for e in ev]))
+    k1_all = [e[0].elapsed_time(e[1]) for e in ev]
+    k2_all = [e[1].elapsed_time(e[2]) for e in ev]
+    k1_ms, k2_ms = float(np.mean(k1_all)), float(np.mean(k2_all))
 
+    # cold: before each rep, a 1 GiB write evicts L2 and the 256 MB Infinity Cache, so the
+    # step's inputs and workspace start in HBM
+    cold_k1, cold_k2 = [], []
+    if args.cold_reps > 0:
+        evict = torch.empty(CALIB_COPY_MIB << 18, dtype=torch.float32, device=dev)
+        evc = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               for _ in range(args.cold_reps)]
+        for k, e in enumerate(evc):
+            evict.fill_(float(k))
+            e[0].record(stream)
+            e2f.attn_precouple(pos, h, ws)
+            e[1].record(stream)
+            e2f.attn_aggregate(pos, idx, mask, ws, H, s.lmax, C, tdt, out=out)
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        cold_k1 = [e[0].elapsed_time(e[1]) for e in evc]
+        cold_k2 = [e[1].elapsed_time(e[2]) for e in evc]
+        del evict
+
+    # reference: the same aggregate visiting targets in index order (no spatial schedule)
     k2_unsched_ms = None
-    if args.index_order_reference:
-        # reference only: the same aggregate visiting targets in index order (no schedule)
-        ev_u = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)]
+    if args.index_order_reps > 0:
+        ev_u = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                for _ in range(args.index_order_reps)]
         for e in ev_u:
             e[0].record(stream)
             e2f.attn_aggregate(pos, idx, mask, ws, H, s.lmax, C, tdt, out=out,
@@ -631,13 +865,23 @@ def main(argv=None):
         k2_unsched_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev_u]))
 
     k1_bytes, k2_bytes, per_edge, per_target = algorithmic_bytes(N, K, E, S, C, b)
-    k2_gbs = k2_bytes / (k2_ms * 1e-3) / 1e9
-    step_gbs = (k1_bytes + k2_bytes) / (ms_step * 1e-3) / 1e9
-    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; precouple {k1_ms:.3f} ms "
-          f"({k1_bytes / (k1_ms * 1e-3) / 1e9:.0f} GB/s), aggregate {k2_ms:.3f} ms "
-          f"(min {k2_ms_min:.3f}) = {k2_gbs:.0f} GB/s algorithmic", file=sys.stderr, flush=True)
+    alg_gbs = (k1_bytes + k2_bytes) / ((k1_ms + k2_ms) * 1e-3) / 1e9
+    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; precouple {k1_ms:.3f} ms, "
+          f"aggregate {k2_ms:.3f} ms (median {np.median(k2_all):.3f}); cold medians: "
+          f"precouple {np.median(cold_k1) if cold_k1 else float('nan'):.3f} ms, aggregate "
+          f"{np.median(cold_k2) if cold_k2 else float('nan'):.3f} ms; index order "
+          f"{k2_unsched_ms or float('nan'):.3f} ms", file=sys.stderr, flush=True)
 
-    traffic = committed_traffic(args.workload, aggregate_kernel(s))
+    # the roofline of the step's kernels from the committed counters of this workload:
+    # L2-to-fabric bytes (FETCH_SIZE + WRITE_SIZE, calibrated) over this run's kernel time
+    cc = committed_counters(args.workload)
+    traffic = committed_step_traffic(args.workload)
+    agg_key = next((k for k in (cc or {}) if step_kernel(k, args.workload)
+                    and k.startswith(aggregate_kernel(s))), None)
+    agg_c = cc[agg_key] if agg_key else {}
+    t_step = (k1_ms + k2_ms) * 1e-3
+    achieved = traffic / t_step / 1e9 if traffic else None
+    med = lambda v: float(np.median(v)) if v else None
     result = {
         "metric": "edges/s + achieved HBM GB/s, fused on-the-fly attention, N=32768 K=256",
         "value": E / (ms_step * 1e-3),
@@ -657,28 +901,43 @@ def main(argv=None):
             "heads": H, "cutoff_A": s.cutoff, "seed": s.seed,
         },
         "atoms_per_s": N / (ms_step * 1e-3),
-        "step_algorithmic_GBps": step_gbs,
         "kernels_ms": {"precouple": k1_ms, "aggregate": k2_ms,
+                       "precouple_median": med(k1_all), "aggregate_median": med(k2_all),
                        "aggregate_index_order_reference": k2_unsched_ms},
+        "cold": {
+            "reps": len(cold_k2),
+            "eviction": f"{CALIB_COPY_MIB} MiB device write before each rep",
+            "precouple_ms_median": med(cold_k1), "aggregate_ms_median": med(cold_k2),
+            "step_ms_median": med([a + c for a, c in zip(cold_k1, cold_k2)]),
+            "edges_per_s": (E / (med([a + c for a, c in zip(cold_k1, cold_k2)]) * 1e-3)
+                            if cold_k2 else None),
+        },
         "roofline": {
-            "kernel": (aggregate_kernel(s).split("::")[1]
-                       + (" (steps 2-3, three targets per wave sharing the rows they read)"
-                          if aggregate_kernel(s).endswith("_mt") else " (steps 2-3)")
-                       + ", timed with its target-schedule kernels"),
-            "bound": "hbm",
-            "achieved": k2_gbs,
+            "kernel": ("one step: k_eaas (step 1) + the target-schedule kernels + "
+                       + aggregate_kernel(s).split("::")[1] + " (steps 2-3)"),
+            # the counters show the gathered rows served by L2 and the per-CU vector-memory
+            # pipeline (TA/TD) as the busiest unit, not HBM
+            "bound": "vmem",
+            "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": k2_gbs / HBM_PEAK_GBS,
+            "frac": achieved / HBM_PEAK_GBS if achieved else None,
             "traffic": traffic,
-            # calibrated HBM/fabric bytes of the committed profile over this run's duration
-            "traffic_GBps": traffic / (k2_ms * 1e-3) / 1e9 if traffic else None,
-            "traffic_frac": traffic / (k2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS if traffic else None,
-            "algorithmic_bytes_per_launch": k2_bytes,
+            "traffic_source": (f"profiles/k_aggregate_{args.workload}.md (calibrated FETCH_SIZE "
+                               "+ WRITE_SIZE per dispatch, summed over the step's kernels), over "
+                               "this run's mean warm step kernel time"
+                               if traffic else "no current counter summary for these sources"),
+            "algorithmic_bytes_per_step": k1_bytes + k2_bytes,
+            "algorithmic_GBps": alg_gbs,
+            "algorithmic_frac": alg_gbs / HBM_PEAK_GBS,
+            "cache_reuse_factor": (k1_bytes + k2_bytes) / traffic if traffic else None,
             "bytes_per_edge": per_edge,
             "bytes_per_target": per_target,
-            "vmem_path_peak": VMEM_PATH_PEAK_GBS,
-            "vmem_path_frac": k2_gbs / VMEM_PATH_PEAK_GBS,
+            "aggregate_counters": {k: agg_c[k] for k in ("ta_busy", "td_busy",
+                                                         "td_stalled_on_l2", "valu_issue")
+                                   if k in agg_c} or None,
+            "aggregate_traffic_GBps": (agg_c["traffic"] / (k2_ms * 1e-3) / 1e9
+                                       if "traffic" in agg_c else None),
         },
     }
     if not args.no_proj:

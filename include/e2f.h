@@ -118,6 +118,23 @@ int e2f_eaas_couple(hipStream_t stream, int64_t n, int lmax, int C, int dtype,
                     const float* r, const void* h_in, const float* path_w, void* h_out);
 
 /*
+ * e2f_dense_couple -- the same product h_out_a = h_in_a (x) R(r_a) as
+ * e2f_eaas_couple, computed the way EAAS avoids: for every path the full real
+ * Clebsch-Gordan tensor C_p[mi, mf, mo] (zeros included) is contracted with
+ * the feature block and the solid harmonics,
+ *   y[lo, mo] = sum_p w_p sum_{mi, mf} C_p[mi, mf, mo] h[li, mi] R_lf(r)[mf],
+ * 615 multiply-adds per channel at lmax = 2 (write-up section 2.2, Fig. 3:
+ * the dense baseline of the EAAS speed-up; gist.science summary 2.1: dense
+ * CG at O(L^6)).  Real basis: spherical components T_0 = x_0,
+ * T_{+m} = (-1)^m (x_m + i x_{-m}) / sqrt2, T_{-m} = (x_m - i x_{-m}) / sqrt2,
+ * Condon-Shortley coefficients, odd li + lf + lo tensors times -i.  By
+ * Proposition 4.3 the result equals e2f_eaas_couple's up to rounding.
+ * Arguments, layouts, in-place use and errors as for e2f_eaas_couple.
+ */
+int e2f_dense_couple(hipStream_t stream, int64_t n, int lmax, int C, int dtype,
+                     const float* r, const void* h_in, const float* path_w, void* h_out);
+
+/*
  * Workspace bytes that e2f_attn_precouple / _aggregate / _forward need for
  * N atoms, 0 on bad arguments.  Layout, each part 256-byte aligned:
  *   - the pre-coupled values of step 1, stored per atom as S + 1 rows of C

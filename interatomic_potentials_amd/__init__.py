@@ -17,7 +17,8 @@ import os
 from typing import Optional
 
 __all__ = [
-    "E2FError", "lib", "status_string", "path_count", "eaas_couple", "attn_workspace_bytes",
+    "E2FError", "lib", "status_string", "path_count", "eaas_couple", "dense_couple",
+    "attn_workspace_bytes",
     "attn_precouple", "attn_aggregate", "attn_forward", "attn_backward",
     "attn_backward_workspace_bytes", "neighbour_workspace_bytes", "neighbour_list", "frames",
     "F32", "BF16",
@@ -48,6 +49,7 @@ SIGNATURES = {
     "e2f_last_hip_error": (_i32, []),
     "e2f_last_hip_error_name": (ctypes.c_char_p, []),
     "e2f_eaas_couple": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "e2f_dense_couple": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "e2f_attn_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
     "e2f_attn_precouple": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz]),
     "e2f_attn_precouple_proj": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -256,6 +258,15 @@ def _nbr_dims(nbr_idx, nbr_mask, N):
 
 def eaas_couple(r, h, path_w=None, out=None):
     """h (x) R(r) through EAAS: r [n,3] fp32, h [n,S,C] fp32|bf16 -> [n,S,C]."""
+    return _couple(lib.e2f_eaas_couple, "e2f_eaas_couple", r, h, path_w, out)
+
+
+def dense_couple(r, h, path_w=None, out=None):
+    """h (x) R(r) by the dense Clebsch-Gordan contraction (the baseline EAAS replaces)."""
+    return _couple(lib.e2f_dense_couple, "e2f_dense_couple", r, h, path_w, out)
+
+
+def _couple(fn, where, r, h, path_w, out):
     torch = _torch()
     n, S, C = _dims(h)
     lmax = _lmax_of(S)
@@ -268,8 +279,8 @@ def eaas_couple(r, h, path_w=None, out=None):
     _dev(out, "out", h.dtype)
     _same_device(r=r, h=h, out=out)
     pw = _path_w(path_w, h.device)
-    _check(lib.e2f_eaas_couple(_stream(h), n, lmax, C, _dtype_code(h), _ptr(r), _ptr(h), _ptr(pw),
-                               _ptr(out)), "e2f_eaas_couple")
+    _check(fn(_stream(h), n, lmax, C, _dtype_code(h), _ptr(r), _ptr(h), _ptr(pw), _ptr(out)),
+           where)
     return out
 
 

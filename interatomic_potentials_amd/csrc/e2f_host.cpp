@@ -10,6 +10,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <complex>
 #include <mutex>
 
 #include <hip/hip_runtime_api.h>
@@ -137,6 +138,62 @@ EaasCoef make_coef(int lmax, const float* path_w) {
         const int mmax = li < lo ? li : lo;
         for (int m = 0; m <= mmax; ++m)
           cf.c[p][m] = (float)(w * clebsch_gordan(li, m, lf, 0, lo, m));
+        ++p;
+      }
+  return cf;
+}
+
+// Real-basis coupling tensors for the dense product, from the Condon-Shortley
+// coefficients above and the change of basis between real components x and
+// spherical components T of degree l:
+//   T_0 = x_0;  T_{+m} = (-1)^m (x_m + i x_{-m}) / sqrt2;  T_{-m} = (x_m - i x_{-m}) / sqrt2.
+// The coupled spherical components sum_{m1 + m2 = M} <li m1 lf m2 | lo M> A_m1 B_m2,
+// taken back to real components, give a tensor that is real when li + lf + lo is
+// even and imaginary when it is odd; odd tensors are multiplied by -i.  Factor
+// order: feature (li) first, harmonic (lf) second.
+std::complex<double> real_to_sph(int l, int m_sph, int m_real) {
+  const double s = 1.0 / sqrt(2.0);
+  if (m_sph == 0) return m_real == 0 ? 1.0 : 0.0;
+  const int m = abs(m_sph);
+  const double sg = (m % 2) ? -1.0 : 1.0;
+  (void)l;
+  if (m_sph > 0) {
+    if (m_real == m) return {sg * s, 0.0};
+    if (m_real == -m) return {0.0, sg * s};
+  } else {
+    if (m_real == m) return {s, 0.0};
+    if (m_real == -m) return {0.0, -s};
+  }
+  return 0.0;
+}
+
+double real_cg(int li, int lf, int lo, int a, int b, int c) {  // a, b, c real m values
+  std::complex<double> acc = 0.0;
+  for (int m1 = -li; m1 <= li; ++m1)
+    for (int m2 = -lf; m2 <= lf; ++m2) {
+      const int M = m1 + m2;
+      if (abs(M) > lo) continue;
+      const double cg = clebsch_gordan(li, m1, lf, m2, lo, M);
+      if (cg == 0.0) continue;
+      acc += std::conj(real_to_sph(lo, M, c)) * cg * real_to_sph(li, m1, a) *
+             real_to_sph(lf, m2, b);
+    }
+  if ((li + lf + lo) % 2) acc *= std::complex<double>(0.0, -1.0);
+  return acc.real();
+}
+
+e2f::DenseCoef make_dense_coef(int lmax, const float* path_w) {
+  e2f::DenseCoef cf;
+  memset(&cf, 0, sizeof(cf));
+  int p = 0, off = 0;
+  for (int li = 0; li <= lmax; ++li)
+    for (int lf = 0; lf <= lmax; ++lf)
+      for (int lo = 0; lo <= lmax; ++lo) {
+        if (lo < abs(li - lf) || lo > li + lf) continue;
+        const double w = path_w ? (double)path_w[p] : 1.0;
+        for (int a = -li; a <= li; ++a)
+          for (int b = -lf; b <= lf; ++b)
+            for (int c = -lo; c <= lo; ++c) cf.c[off++] = (float)(w * real_cg(li, lf, lo, a, b, c));
         ++p;
       }
   return cf;
@@ -440,6 +497,33 @@ int e2f_eaas_couple(hipStream_t stream, int64_t n, int lmax, int C, int dtype, c
   return hip_status(e2f::launch_eaas(lmax, dtype, V, false, a, cf, stream));
 }
 
+int e2f_dense_couple(hipStream_t stream, int64_t n, int lmax, int C, int dtype, const float* r,
+                     const void* h_in, const float* path_w, void* h_out) {
+  if (const int rt = check_runtime()) return rt;
+  int st = check_shape_common(n, lmax, C, dtype);
+  if (st != E2F_OK) return st;
+  if (n == 0) return E2F_OK;
+  if (!r || !h_in || !h_out) return E2F_ERR_NULL;
+  if (!aligned(r, 4) || !aligned(h_in, 16) || !aligned(h_out, 16) ||
+      (path_w && !aligned(path_w, 4)))
+    return E2F_ERR_ALIGN;
+  const size_t hb = (size_t)n * ncomp(lmax) * C * esize(dtype);
+  if (h_out != h_in && overlap({h_out, hb}, {h_in, hb})) return E2F_ERR_ALIAS;
+  if (overlap({h_out, hb}, {r, (size_t)n * 12})) return E2F_ERR_ALIAS;
+  const int V = C % 4 == 0 ? 4 : 1;   // the widths the dense kernel is built for
+  e2f::EaasArgs a;
+  a.r = r;
+  a.h_in = h_in;
+  a.h_out = h_out;
+  a.q_out = nullptr;
+  a.n = n;
+  a.C = C;
+  const int lanes = (C + V - 1) / V;
+  a.lane_log = ceil_log2(lanes > 64 ? 64 : lanes);
+  const e2f::DenseCoef cf = make_dense_coef(lmax, path_w);
+  return hip_status(e2f::launch_dense(lmax, dtype, V, a, cf, stream));
+}
+
 size_t e2f_attn_workspace_bytes(int64_t N, int lmax, int C, int dtype) {
   if (check_shape_common(N, lmax, C, dtype) != E2F_OK) return 0;
   return ws_body_bytes(N, lmax, C, dtype) + 256 + sched_bytes(N);
@@ -587,6 +671,14 @@ int forward_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, i
 }
 
 }  // namespace
+
+namespace e2f {
+
+int runtime_status() { return check_runtime(); }
+
+int hip_error_status(int err) { return hip_status(err); }
+
+}  // namespace e2f
 
 extern "C" {
 

@@ -107,15 +107,32 @@ struct ProjArgs {
 };
 constexpr int kProjTileAtoms = 16;  // atoms per MFMA row tile
 
+// Dense real Clebsch-Gordan tensors of every path (lexicographic (li, lf, lo)),
+// each [2li+1][2lf+1][2lo+1] row-major, path weights folded in: 615 entries
+// at lmax = 2 (the O(L^6) contraction EAAS replaces).
+constexpr int kDenseCoefs = 615;
+struct DenseCoef {
+  float c[kDenseCoefs];
+};
+
 // launchers (kernels file); return 0 or a hipError_t value
 int launch_eaas(int lmax, int dtype, int V, bool to_workspace, const EaasArgs& a,
                 const EaasCoef& cf, hipStream_t s);
 int launch_aggregate(int lmax, int dtype, int V, const AggArgs& a, const EaasCoef& cf,
                      hipStream_t s);
+// the aggregate with 16 targets a workgroup sharing rows through LDS (its own file):
+// C = 128, K <= kWgMaxK, 2 channels a lane with d / 2 lanes a head in {1, ..., 16}
+constexpr int kWgMaxK = 256;
+bool aggregate_wg_supported(int64_t N, int K, int C, int H, int dtype);
+int launch_aggregate_wg(int lmax, int dtype, const AggArgs& a, const EaasCoef& cf,
+                        hipStream_t s);
 // fused projection + pre-coupling; C in {16, 32, 64, 128} (fp32) or {32, 64, 128} (bf16)
 bool proj_supported(int C, int dtype);
 int launch_proj(int lmax, int dtype, int C, const ProjArgs& a, const EaasCoef& cf, hipStream_t s);
 int launch_frames(int lmax, int64_t n, const float* r, float* Q, float* D, hipStream_t s);
+// the dense-CG product (dense file): EaasArgs without the workspace fields
+int launch_dense(int lmax, int dtype, int V, const EaasArgs& a, const DenseCoef& cf,
+                 hipStream_t s);
 int launch_validate(int64_t N, int K, const int32_t* idx, const uint8_t* mask, int32_t* flag,
                     hipStream_t s);
 int launch_schedule(int64_t N, const float* pos, const SchedScratch& sc, hipStream_t s);
@@ -131,6 +148,11 @@ constexpr int kScanTile = 4096;     // elements per block of the generic scan
 // caller last cleared them.
 int launch_scan_exclusive(int64_t n, int32_t* a, int32_t* tile_sums, int32_t* cur,
                           hipStream_t s);
+
+// host file: E2F_OK, or E2F_ERR_RUNTIME while two HIP runtimes are mapped; and the status
+// of a HIP error (recorded for e2f_last_hip_error)
+int runtime_status();
+int hip_error_status(int err);
 
 // padded neighbour lists (cell list) and the Morton order of the atoms
 constexpr int kNlMaxBits = 7;        // Morton bits per axis of the cell grid, at most

@@ -111,11 +111,11 @@ def _fwd(**kw):
                                 a["flags"])
 
 
-def _eaas(**kw):
+def _eaas(fn=None, **kw):
     a = dict(stream=None, n=1000, lmax=2, C=128, dt=0, r=fake(1), h=fake(2), pw=None, out=fake(3))
     a.update(kw)
-    return lib.e2f_eaas_couple(a["stream"], a["n"], a["lmax"], a["C"], a["dt"], a["r"], a["h"],
-                               a["pw"], a["out"])
+    fn = fn or lib.e2f_eaas_couple
+    return fn(a["stream"], a["n"], a["lmax"], a["C"], a["dt"], a["r"], a["h"], a["pw"], a["out"])
 
 
 def _pre(**kw):
@@ -165,6 +165,21 @@ def test_forward_specific_errors():
     assert _fwd(h=ctypes.c_void_p(BASE + 9 * 64 * MB + 4)) == C["E2F_ERR_ALIGN"]
     assert _fwd(out=fake(9)) == C["E2F_ERR_ALIAS"]           # out over h
     assert _fwd(ws=fake(9)) == C["E2F_ERR_ALIAS"]            # workspace over h
+
+
+@pytest.mark.parametrize("fn", ["e2f_eaas_couple", "e2f_dense_couple"])
+def test_coupling_errors(fn):
+    f = getattr(lib, fn)
+    assert _eaas(f, dt=9) == C["E2F_ERR_DTYPE"]
+    assert _eaas(f, n=-2) == C["E2F_ERR_SHAPE"]
+    assert _eaas(f, lmax=3) == C["E2F_ERR_SHAPE"]
+    assert _eaas(f, C=0) == C["E2F_ERR_SHAPE"]
+    assert _eaas(f, n=0, r=None, h=None, out=None) == C["E2F_OK"]
+    assert _eaas(f, r=None) == C["E2F_ERR_NULL"]
+    assert _eaas(f, out=None) == C["E2F_ERR_NULL"]
+    assert _eaas(f, h=ctypes.c_void_p(BASE + 2 * 64 * MB + 8)) == C["E2F_ERR_ALIGN"]
+    assert _eaas(f, out=ctypes.c_void_p(BASE + 2 * 64 * MB + 4096)) == C["E2F_ERR_ALIAS"]
+    assert _eaas(f, out=fake(1)) == C["E2F_ERR_ALIAS"]
 
 
 def test_eaas_and_precouple_errors():
