@@ -239,6 +239,32 @@ int e2f_attn_forward_proj(hipStream_t stream, int64_t N, int K, int lmax, int C,
                           size_t ws_bytes, void* out, void* out_msg, float* lse, uint32_t flags);
 
 /*
+ * e2f_attn_forward_noalloc -- e2f_attn_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): no workspace argument; the workspace is
+ * the library's own static device array of e2f_attn_noalloc_max_bytes()
+ * bytes (64 MiB), one per GPU, created when the library's code is loaded on
+ * that GPU and held until the process ends.  The call allocates nothing.
+ *   - Arguments, outputs, flags and errors as for e2f_attn_forward; N with
+ *     e2f_attn_workspace_bytes(N, lmax, C, dtype) above the array's size gives
+ *     E2F_ERR_WORKSPACE (at lmax 2, C 128: about 10,900 atoms at fp32,
+ *     21,800 at bf16).
+ *   - Every call on one GPU uses that GPU's one array, which keeps the last
+ *     call's contents: calls that overlap on one GPU (other streams, other
+ *     threads) race on it and must be serialised by the caller.
+ *   - The array's device address is looked up on the first call on each
+ *     device (the stream's device); that first call is not capturable.
+ */
+int e2f_attn_forward_noalloc(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
+                             int dtype, const float* pos, const void* h, const int32_t* nbr_idx,
+                             const uint8_t* nbr_mask, float scale, float env_cutoff,
+                             const float* path_w, void* out, void* out_msg, float* lse,
+                             uint32_t flags);
+
+/* Size in bytes of the static workspace of e2f_attn_forward_noalloc. */
+size_t e2f_attn_noalloc_max_bytes(void);
+
+/*
  * Backward pass (vector-Jacobian product) of the attention, for forces as
  * derivatives of an energy with respect to positions (the write-up's
  * "Conservative" variant, section 4.2): given G = dL/d out it returns

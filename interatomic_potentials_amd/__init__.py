@@ -21,6 +21,7 @@ __all__ = [
     "attn_workspace_bytes",
     "attn_precouple", "attn_aggregate", "attn_forward", "attn_backward",
     "attn_backward_workspace_bytes", "neighbour_workspace_bytes", "neighbour_list", "frames",
+    "attn_forward_noalloc", "attn_noalloc_max_bytes",
     "F32", "BF16",
     "VALIDATE_INDICES", "TARGETS_IN_ORDER",
 ]
@@ -61,6 +62,9 @@ SIGNATURES = {
                                   _f32, _vp, _vp, _sz, _vp, _vp, _vp, _u32]),
     "e2f_attn_forward": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                 _f32, _f32, _vp, _vp, _sz, _vp, _vp, _vp, _u32]),
+    "e2f_attn_forward_noalloc": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                        _vp, _f32, _f32, _vp, _vp, _vp, _vp, _u32]),
+    "e2f_attn_noalloc_max_bytes": (_sz, []),
     "e2f_attn_backward_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32]),
     "e2f_attn_backward": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                  _f32, _f32, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
@@ -441,6 +445,46 @@ def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] =
                                          _nbytes(ws), _ptr(out), _ptr(msg),
                                          _ptr(lse), _flags(validate, targets_in_order)),
                "e2f_attn_forward_proj")
+    return _results(out, msg, lse)
+
+
+def attn_noalloc_max_bytes() -> int:
+    """Size of the static per-GPU workspace of attn_forward_noalloc."""
+    return int(lib.e2f_attn_noalloc_max_bytes())
+
+
+def attn_forward_noalloc(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] = None,
+                         path_w=None, out=None, return_msg: bool = False,
+                         validate: bool = False, targets_in_order: bool = False,
+                         return_lse: bool = False, env_cutoff: Optional[float] = None):
+    """attn_forward with the library's static per-GPU workspace instead of a caller's one.
+
+    The library call allocates nothing; pass ``out`` (and use no return_msg / return_lse)
+    for a call in which torch allocates nothing either.  Calls overlapping on one GPU race.
+    """
+    torch = _torch()
+    N, S, C = _dims(h)
+    lmax = _lmax_of(S)
+    K = _nbr_dims(nbr_idx, nbr_mask, N)
+    _shape(pos, "pos", (N, 3))
+    _shape(out, "out", (N, S, C))
+    _dev(pos, "pos", torch.float32)
+    _dev(h, "h")
+    _dev(nbr_idx, "nbr_idx", torch.int32)
+    _dev(nbr_mask, "nbr_mask", torch.uint8)
+    dt = _dtype_code(h)
+    if out is None:
+        out = torch.empty_like(h)
+    _dev(out, "out", h.dtype)
+    _same_device(pos=pos, h=h, nbr_idx=nbr_idx, nbr_mask=nbr_mask, out=out)
+    msg = torch.empty_like(h) if return_msg else None
+    lse = torch.empty((N, heads), dtype=torch.float32, device=h.device) if return_lse else None
+    pw = _path_w(path_w, h.device)
+    _check(lib.e2f_attn_forward_noalloc(_stream(h), N, K, lmax, C, heads, dt, _ptr(pos), _ptr(h),
+                                        _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0),
+                                        float(env_cutoff or 0.0), _ptr(pw), _ptr(out), _ptr(msg),
+                                        _ptr(lse), _flags(validate, targets_in_order)),
+           "e2f_attn_forward_noalloc")
     return _results(out, msg, lse)
 
 

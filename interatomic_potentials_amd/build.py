@@ -38,6 +38,7 @@ SOURCES = [
     ("e2f_project.hip", True),
     ("e2f_neighbours.hip", True),
     ("e2f_dense.hip", True),
+    ("e2f_noalloc.hip", True),
     ("e2f_host.cpp", False),
 ]
 
