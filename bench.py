@@ -195,7 +195,7 @@ def cpu_baseline(cfg, budget_s=15.0):
 # a workload stay valid while these are unchanged (the backward, projection and neighbour-list
 # files do not touch those kernels).
 KERNEL_SOURCES = ["interatomic_potentials_amd/csrc/e2f_kernels.hip",
-                  "interatomic_potentials_amd/csrc/e2f_aggregate_wg.hip",
+                  "interatomic_potentials_amd/csrc/e2f_aggregate_generic.hip",
                   "interatomic_potentials_amd/csrc/e2f_dense.hip",
                   "interatomic_potentials_amd/csrc/e2f_device.hpp",
                   "interatomic_potentials_amd/csrc/e2f_internal.hpp"]
@@ -486,18 +486,18 @@ def bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream):
 
     s = cfg.spec
     N, K, S, C, H, E = cfg.N, s.K, cfg.S, s.C, s.H, cfg.nl.n_edges
-    if h.dtype != torch.float32:
-        return {"skipped": "backward is fp32-only"}
-    g = torch.randn_like(out)
-    bws = torch.empty(e2f.attn_backward_workspace_bytes(N, K, s.lmax, C, H), dtype=torch.uint8,
-                      device=h.device)
+    bf16 = h.dtype == torch.bfloat16
+    dt_code = e2f.BF16 if bf16 else e2f.F32
+    g = torch.randn(out.shape, device=out.device).to(out.dtype)
+    bws = torch.empty(e2f.attn_backward_workspace_bytes(N, K, s.lmax, C, H, dt_code),
+                      dtype=torch.uint8, device=h.device)
     gh = torch.empty_like(h)
     gp = torch.empty_like(pos)
 
     def timed(env_cutoff):
-        _, msg, lse = e2f.attn_aggregate(pos, idx, mask, ws, H, s.lmax, C, torch.float32,
+        _, msg, lse = e2f.attn_aggregate(pos, idx, mask, ws, H, s.lmax, C, h.dtype,
                                          out=out, return_msg=True, return_lse=True,
-                                         env_cutoff=env_cutoff)
+                                         env_cutoff=env_cutoff, msg_f32=True)
 
         def run():
             e2f.attn_backward(pos, h, idx, mask, H, ws, msg, lse, g, bwd_ws=bws, grad_h=gh,
@@ -524,11 +524,17 @@ def bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream):
     b_q = E * row + N * (K * 5 + row + C * 4 + 2 * H * 4)
     b_src = E * (row + 2 * 4) + N * (row + S * C * 4 + S * C * 4 + C * 4 + 12 + 12)
     total = b_prep + b_q + b_src
+    if bf16:
+        # bf16 storage: h, the workspace rows and G are widened to fp32 once (read 2 B,
+        # write 4 B each) and dL/dh narrowed at the end; the passes then move fp32 rows
+        feat = N * S * C
+        total += 6 * (2 * feat + N * (S + 1) * C) + 6 * feat
     print(f"[bench] backward: {ms:.3f} ms, {total / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic; "
           f"with the envelope {env_ms:.3f} ms", file=sys.stderr, flush=True)
     return {"ms": ms, "edges_per_s": E / (ms * 1e-3), "algorithmic_bytes": total,
             "algorithmic_GBps": total / (ms * 1e-3) / 1e9,
-            "bytes_per_edge": 2 * row + 8, "envelope_ms": env_ms}
+            "bytes_per_edge": 2 * row + 8, "envelope_ms": env_ms,
+            "storage": "bf16 (widened to fp32 copies, fp32 passes)" if bf16 else "fp32"}
 
 
 # published dense peaks of MI355X (TFLOP/s) for the matrix-core dtypes used here

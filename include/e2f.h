@@ -49,10 +49,13 @@
  *   synchronisation, as usual for HIP.
  * - n = 0 (or N = 0) is a successful no-op.
  * - Supported sizes: lmax in {0, 1, 2}; C >= 1, H >= 1, C % H == 0.  The
- *   attention kernels also need a per-lane channel count V in {1, 2, 4}
- *   (fp32) or {1, 2, 4, 8} (bf16) with V | d, d / V a power of two and
- *   C / V <= 64 (so C <= 256 at fp32 when d is a multiple of 4, C <= 512 at
- *   bf16 when d is a multiple of 8); otherwise E2F_ERR_UNSUPPORTED.
+ *   attention forward serves every such layout up to C = 512 (wider rows:
+ *   E2F_ERR_UNSUPPORTED): layouts with a per-lane channel count V in {1, 2,
+ *   4} (fp32) or {1, 2, 4, 8} (bf16) with V | d, d / V a power of two and
+ *   C / V <= 64 take the vectorised kernels, every other one (head widths
+ *   d = 3, 5, 6, 12, ..., fp32 rows above 256 channels) a general kernel with
+ *   one channel a lane.  The backward needs such a V (E2F_ERR_UNSUPPORTED
+ *   otherwise).
  */
 #ifndef E2F_H_
 #define E2F_H_
@@ -92,6 +95,8 @@ typedef enum e2f_dtype {
 #define E2F_VALIDATE_INDICES 1u  /* check every valid slot's index before running; synchronises */
 #define E2F_TARGETS_IN_ORDER 2u  /* visit targets in index order: skip the spatial schedule, for
                                     atoms already stored in a spatially coherent order */
+#define E2F_MSG_F32 4u           /* out_msg is stored fp32 whatever the dtype (the message
+                                    before any rounding to the storage type) */
 
 /* Name of a status code ("E2F_OK", "E2F_ERR_SHAPE", ...); never NULL. */
 const char* e2f_status_string(int status);
@@ -168,8 +173,10 @@ int e2f_attn_precouple(hipStream_t stream, int64_t N, int lmax, int C, int dtype
  *   w_q, w_k  [C, C] device arrays of the storage type, row-major
  *             [C_in, C_out], applied from the right
  *   w_v       [lmax + 1, C, C] device array, one matrix per degree
- * Supported C: 16, 32, 64, 128 (fp32) and 32, 64, 128 (bf16); other C give
- * E2F_ERR_UNSUPPORTED.  Weights must be 16-byte aligned and must not overlap
+ * C = 16, 32, 64, 128 (fp32) and 32, 64, 128 (bf16) run on the matrix cores;
+ * any other C up to 1024 on the vector ALUs (same products, fp32 accumulation,
+ * input channels summed in order); above 1024: E2F_ERR_UNSUPPORTED.
+ * Weights must be 16-byte aligned and must not overlap
  * the workspace.
  */
 int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int dtype,
@@ -213,11 +220,12 @@ int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int 
  *             stretch, so that waves sharing an L2 share neighbours; the
  *             visiting order never changes any target's result.
  *   out       [N, S, C] T    out_i; exactly 0 for a target with no valid slot
- *   out_msg   [N, S, C] T or NULL: also store the normalised message m_i
+ *   out_msg   [N, S, C] T (fp32 under E2F_MSG_F32) or NULL: also store the
+ *             normalised message m_i
  *   lse       [N, H] fp32 or NULL: also store each head's natural log-sum-exp
  *             of the logits over the valid slots (-inf with no valid slot);
  *             with out_msg, this is what e2f_attn_backward needs
- *   flags     0 or E2F_VALIDATE_INDICES | E2F_TARGETS_IN_ORDER
+ *   flags     0 or E2F_VALIDATE_INDICES | E2F_TARGETS_IN_ORDER | E2F_MSG_F32
  */
 int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                        const float* pos, const int32_t* nbr_idx, const uint8_t* nbr_mask,
@@ -275,23 +283,35 @@ size_t e2f_attn_noalloc_max_bytes(void);
  *
  * e2f_attn_backward_workspace_bytes -- scratch bytes for N atoms and K slots:
  * (S + 1) C + C + H floats per atom, the reverse neighbour list (8 N + 4 N K
- * bytes) and the target schedule scratch.  0 on bad arguments.
+ * bytes) and the target schedule scratch; with bf16 storage also fp32 copies
+ * of h, G and dL/dh, the recomputed message and log-sum-exp, and an fp32
+ * attention workspace (e2f_attn_workspace_bytes at E2F_F32).  0 on bad
+ * arguments.
  */
 size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int H, int dtype);
 
 /*
- * e2f_attn_backward -- fp32 storage only (E2F_ERR_UNSUPPORTED for bf16, for
- * N above 2^24, K above 2048 or N K at or above 2^31).
+ * e2f_attn_backward -- fp32 or bf16 storage, fp32 arithmetic.  With bf16
+ * storage, h and G are widened exactly into fp32 copies in the backward
+ * workspace, the forward (step 1, message, log-sum-exp) is recomputed from
+ * them in fp32, and the gradients of that are taken; dL/dh is rounded to bf16
+ * at the end.  (The stored bf16 workspace and message would carry a 2^-9
+ * rounding into the softmax backward's <dm_i, h'_j> - <dm_i, m_i>, which
+ * cancels.)  E2F_ERR_UNSUPPORTED for N above 2^24, K above 2048, N K at or
+ * above 2^31, or a layout without an fp32 lane width.
  *   pos, h, nbr_idx, nbr_mask, scale, env_cutoff, path_w: as given to the
  *               forward (with an envelope, dL/dpos includes its derivative
  *               through each pair distance)
  *   workspace   the forward's workspace after e2f_attn_precouple (read only;
  *               the layer without projections is differentiated)
- *   msg, lse    the forward's out_msg and lse outputs
- *   grad_out    [N, S, C] fp32  dL/d out
- *   grad_h      [N, S, C] fp32  dL/dh (written)
+ *   msg, lse    the forward's out_msg ([N, S, C] fp32) and lse ([N, H] fp32)
+ *               outputs; with bf16 storage they are recomputed and these are
+ *               not read (NULL allowed)
+ *   grad_out    [N, S, C] T     dL/d out
+ *   grad_h      [N, S, C] T     dL/dh (written)
  *   grad_pos    [N, 3] fp32     dL/dpos (written)
  *   bwd_workspace, bwd_ws_bytes  scratch of e2f_attn_backward_workspace_bytes
+ *               (with bf16 storage it also holds the fp32 copies)
  *   flags       0 or E2F_TARGETS_IN_ORDER (index order; also taken for
  *               N <= 2048)
  * The result does not depend on the order of a target's slots, nor on the

@@ -23,7 +23,7 @@ __all__ = [
     "attn_backward_workspace_bytes", "neighbour_workspace_bytes", "neighbour_list", "frames",
     "attn_forward_noalloc", "attn_noalloc_max_bytes",
     "F32", "BF16",
-    "VALIDATE_INDICES", "TARGETS_IN_ORDER",
+    "VALIDATE_INDICES", "TARGETS_IN_ORDER", "MSG_F32",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +33,7 @@ F32 = 0
 BF16 = 1
 VALIDATE_INDICES = 1
 TARGETS_IN_ORDER = 2
+MSG_F32 = 4
 
 _STATUS = {
     0: "E2F_OK", -1: "E2F_ERR_NULL", -2: "E2F_ERR_SHAPE", -3: "E2F_ERR_DTYPE",
@@ -147,8 +148,9 @@ def path_count(lmax: int) -> int:
     return lib.e2f_path_count(lmax)
 
 
-def _flags(validate: bool, targets_in_order: bool) -> int:
-    return (VALIDATE_INDICES if validate else 0) | (TARGETS_IN_ORDER if targets_in_order else 0)
+def _flags(validate: bool, targets_in_order: bool, msg_f32: bool = False) -> int:
+    return ((VALIDATE_INDICES if validate else 0) | (TARGETS_IN_ORDER if targets_in_order else 0)
+            | (MSG_F32 if msg_f32 else 0))
 
 
 def _check(code: int, where: str) -> None:
@@ -364,10 +366,11 @@ def attn_aggregate(pos, nbr_idx, nbr_mask, ws, heads: int, lmax: int, C: int, dt
                    scale: Optional[float] = None, path_w=None, out=None,
                    return_msg: bool = False, validate: bool = False,
                    targets_in_order: bool = False, return_lse: bool = False,
-                   env_cutoff: Optional[float] = None):
+                   env_cutoff: Optional[float] = None, msg_f32: bool = False):
     """Steps 2-3 from a filled workspace; returns out, or (out[, m][, lse]) when asked.
 
-    ``env_cutoff`` = r_env switches on the smooth distance envelope of the weights.
+    ``env_cutoff`` = r_env switches on the smooth distance envelope of the weights;
+    ``msg_f32`` stores m in float32 whatever the storage type (what attn_backward takes).
     """
     torch = _torch()
     if nbr_idx.dim() != 2:
@@ -385,14 +388,16 @@ def attn_aggregate(pos, nbr_idx, nbr_mask, ws, heads: int, lmax: int, C: int, dt
         out = torch.empty((N, S, C), dtype=dtype, device=ws.device)
     _dev(out, "out", dtype)
     _same_device(pos=pos, nbr_idx=nbr_idx, nbr_mask=nbr_mask, ws=ws, out=out)
-    msg = torch.empty_like(out) if return_msg else None
+    msg = None
+    if return_msg:
+        msg = torch.empty_like(out, dtype=torch.float32 if msg_f32 else out.dtype)
     lse = torch.empty((N, heads), dtype=torch.float32, device=ws.device) if return_lse else None
     pw = _path_w(path_w, ws.device)
     _check(lib.e2f_attn_aggregate(_stream(ws), N, K, lmax, C, heads, _dtype_code(out), _ptr(pos),
                                   _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0),
                                   float(env_cutoff or 0.0), _ptr(pw),
                                   _ptr(ws), _nbytes(ws), _ptr(out), _ptr(msg),
-                                  _ptr(lse), _flags(validate, targets_in_order)),
+                                  _ptr(lse), _flags(validate, targets_in_order, msg_f32)),
            "e2f_attn_aggregate")
     return _results(out, msg, lse)
 
@@ -496,7 +501,11 @@ def attn_backward_workspace_bytes(N: int, K: int, lmax: int, C: int, H: int,
 def attn_backward(pos, h, nbr_idx, nbr_mask, heads: int, ws, msg, lse, grad_out,
                   scale: Optional[float] = None, path_w=None, targets_in_order: bool = False,
                   bwd_ws=None, grad_h=None, grad_pos=None, env_cutoff: Optional[float] = None):
-    """(dL/dh, dL/dpos) for L = <grad_out, out>; ws, msg, lse from the forward."""
+    """(dL/dh, dL/dpos) for L = <grad_out, out>; ws, msg, lse from the forward.
+
+    With bf16 storage the library recomputes the message and the log-sum-exp in fp32, so
+    msg and lse may be None (they are not read).
+    """
     torch = _torch()
     N, S, C = _dims(h)
     lmax = _lmax_of(S)
@@ -512,8 +521,10 @@ def attn_backward(pos, h, nbr_idx, nbr_mask, heads: int, ws, msg, lse, grad_out,
     _dev(nbr_idx, "nbr_idx", torch.int32)
     _dev(nbr_mask, "nbr_mask", torch.uint8)
     _dev(ws, "ws")
-    _dev(msg, "msg", h.dtype)
-    _dev(lse, "lse", torch.float32)
+    if dt == F32 or msg is not None:
+        _dev(msg, "msg", torch.float32)
+    if dt == F32 or lse is not None:
+        _dev(lse, "lse", torch.float32)
     _dev(grad_out, "grad_out", h.dtype)
     if bwd_ws is None:
         nbytes = attn_backward_workspace_bytes(N, K, lmax, C, heads, dt)

@@ -1,4 +1,6 @@
-// e2f_backward.hip -- vector-Jacobian product of the on-the-fly attention (fp32).
+// e2f_backward.hip -- vector-Jacobian product of the on-the-fly attention (fp32
+// arithmetic; bf16 storage is widened exactly into fp32 copies first, and dL/dh
+// is rounded back at the end).
 //
 // For L = <G, out> with out_i = T(r_i) m_i, m_i = sum_j a_ij h'_j and
 // h'_j = T(r_j) h_j (T(r) = the EAAS coupling with R(r)), the gradients are
@@ -1127,6 +1129,57 @@ int launch_reverse_list(int64_t N, int K, const int32_t* idx, const uint8_t* mas
   if (st != 0) return st;
   hipLaunchKernelGGL(k_rev_pass<true>, dim3(gr), dim3(256), 0, s, N, K, per, idx, mask, sched,
                      cur, entries);
+  return last_err();
+}
+
+namespace {
+
+// eight elements a thread, 16-byte loads of bf16; tails element by element
+__global__ __launch_bounds__(256) void k_widen_bf16(int64_t n, const uint16_t* src, float* dst) {
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (e0 + 8 <= n) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src + e0);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float4* o = reinterpret_cast<float4*>(dst + e0);
+    o[0] = make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                       __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u));
+    o[1] = make_float4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
+                       __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u));
+  } else {
+    for (int64_t e = e0; e < n; ++e) dst[e] = bf16_to_f32(src[e]);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_narrow_bf16(int64_t n, const float* src, uint16_t* dst) {
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (e0 + 8 <= n) {
+    const float4 a = reinterpret_cast<const float4*>(src + e0)[0];
+    const float4 b = reinterpret_cast<const float4*>(src + e0)[1];
+    auto pk = [](float lo, float hi) {
+      return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+    };
+    *reinterpret_cast<uint4*>(dst + e0) = make_uint4(pk(a.x, a.y), pk(a.z, a.w), pk(b.x, b.y),
+                                                     pk(b.z, b.w));
+  } else {
+    for (int64_t e = e0; e < n; ++e) dst[e] = f32_to_bf16(src[e]);
+  }
+}
+
+}  // namespace
+
+int launch_widen_bf16(int64_t n, const uint16_t* src, float* dst, hipStream_t s) {
+  if (n <= 0) return 0;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_widen_bf16, dim3((unsigned)((n + 2047) / 2048)), dim3(256), 0, s, n, src,
+                     dst);
+  return last_err();
+}
+
+int launch_narrow_bf16(int64_t n, const float* src, uint16_t* dst, hipStream_t s) {
+  if (n <= 0) return 0;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_narrow_bf16, dim3((unsigned)((n + 2047) / 2048)), dim3(256), 0, s, n, src,
+                     dst);
   return last_err();
 }
 

@@ -473,11 +473,15 @@ struct VecIO<float, V> {
     }
   }
   static __device__ inline void store(float* p, const float* o) {
-    if constexpr (V == 4) {
+    if constexpr (V == 8) {   // fp32 copies of 8-channel bf16 lanes (the fp32 message)
+      *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(p + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    } else if constexpr (V == 4) {
       *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
     } else if constexpr (V == 2) {
       *reinterpret_cast<float2*>(p) = make_float2(o[0], o[1]);
     } else {
+      static_assert(V == 1, "fp32 vector width");
       *p = o[0];
     }
   }

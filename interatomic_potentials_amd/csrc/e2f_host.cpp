@@ -274,11 +274,16 @@ size_t sched_bytes(int64_t N) {
 
 // backward workspace: [q / dm rows][dq][per-head D][reverse list offsets, cursors,
 // scan tile sums, entries][schedule scratch]; every part 256-byte aligned
+// With bf16 storage the backward widens h and G exactly into fp32 copies, recomputes the
+// forward in fp32 from them (workspace, message, log-sum-exp) and differentiates that with
+// the fp32 passes: [h][fp32 attention workspace][m][lse][G][dL/dh, narrowed at the end].
 struct BwdLayout {
-  size_t brows, dq, dh, off, cur, tiles, entries, sched, cell, counts, partial, total;
+  size_t brows, dq, dh, off, cur, tiles, entries, sched, cell, counts, partial;
+  size_t h32, ws32, msg32, lse32, g32, gh32;   // bf16 storage only
+  size_t total;
 };
 
-BwdLayout bwd_layout(int64_t N, int K, int lmax, int C, int H) {
+BwdLayout bwd_layout(int64_t N, int K, int lmax, int C, int H, int dt) {
   BwdLayout L;
   size_t p = 0;
   auto take = [&p](size_t bytes) {
@@ -286,6 +291,14 @@ BwdLayout bwd_layout(int64_t N, int K, int lmax, int C, int H) {
     p += round256(bytes);
     return at;
   };
+  const size_t feat = (size_t)N * ncomp(lmax) * C * 4;
+  const bool wide = dt == E2F_BF16;
+  L.h32 = take(wide ? feat : 0);
+  L.ws32 = take(wide ? e2f_attn_workspace_bytes(N, lmax, C, E2F_F32) : 0);
+  L.msg32 = take(wide ? feat : 0);
+  L.lse32 = take(wide ? (size_t)N * H * 4 : 0);
+  L.g32 = take(wide ? feat : 0);
+  L.gh32 = take(wide ? feat : 0);
   L.brows = take((size_t)N * (ncomp(lmax) + 1) * C * 4);
   L.dq = take((size_t)N * C * 4);
   L.dh = take((size_t)N * H * 4);
@@ -362,13 +375,23 @@ float env_inv(float env_cutoff) {
   return env_cutoff > 0.0f ? (float)(1.0 / (double)env_cutoff) : 0.0f;
 }
 
+// attention forward: any C % H == 0 layout up to kGenericMaxC channels (layouts without a
+// lane-vector width go to the generic kernel)
 int check_attn_shape(int64_t N, int K, int lmax, int C, int H, int dt, uint32_t flags) {
   const int st = check_shape_common(N, lmax, C, dt);
   if (st != E2F_OK) return st;
   if (K < 1 || H < 1 || C % H != 0) return E2F_ERR_SHAPE;
-  if (flags & ~(E2F_VALIDATE_INDICES | E2F_TARGETS_IN_ORDER)) return E2F_ERR_SHAPE;
-  if (attn_width(C, H, dt) == 0) return E2F_ERR_UNSUPPORTED;
+  if (flags & ~(E2F_VALIDATE_INDICES | E2F_TARGETS_IN_ORDER | E2F_MSG_F32)) return E2F_ERR_SHAPE;
+  if (attn_width(C, H, dt) == 0 && C > e2f::kGenericMaxC) return E2F_ERR_UNSUPPORTED;
   return E2F_OK;
+}
+
+// the backward's lane mapping: its passes run in fp32 (bf16 storage is widened first), so
+// they need an fp32 per-lane vector width (see attn_width)
+int check_bwd_shape(int64_t N, int K, int lmax, int C, int H, int dt, uint32_t flags) {
+  const int st = check_attn_shape(N, K, lmax, C, H, dt, flags);
+  if (st != E2F_OK) return st;
+  return attn_width(C, H, E2F_F32) == 0 ? E2F_ERR_UNSUPPORTED : E2F_OK;
 }
 
 int precouple_impl(hipStream_t stream, int64_t N, int lmax, int C, int dt, const float* pos,
@@ -405,7 +428,7 @@ int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
     if (st != E2F_OK) return st;
     if (host_flag != 0) return E2F_ERR_INDEX;
   }
-  const int V = attn_width(C, H, dt);
+  const int V = attn_width(C, H, dt);   // 0: no lane-vector layout, the generic kernel
   const int d = C / H;
   const int32_t* sched = nullptr;
   if (!(flags & E2F_TARGETS_IN_ORDER) && N > kSchedMinAtoms) {
@@ -425,8 +448,8 @@ int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
   a.N = N;
   a.K = K;
   a.C = C;
-  a.lane_log = ceil_log2(C / V);
-  a.head_lanes = d / V;
+  a.lane_log = V ? ceil_log2(C / V) : 6;
+  a.head_lanes = V ? d / V : 0;
   const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)d);
   a.scale_log2e = (float)(sc * 1.4426950408889634);  // log2(e)
   a.sched = sched;
@@ -434,7 +457,9 @@ int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
   a.heads = H;
   a.env_inv_rc = env_inv(env_cutoff);
   a.env_rc = env_cutoff > 0.0f ? env_cutoff : 0.0f;
+  a.msg_f32 = (flags & E2F_MSG_F32) ? 1 : 0;
   const EaasCoef cf = make_coef(lmax, path_w);
+  if (V == 0) return hip_status(e2f::launch_aggregate_generic(lmax, dt, a, cf, stream));
   return hip_status(e2f::launch_aggregate(lmax, dt, V, a, cf, stream));
 }
 
@@ -565,6 +590,7 @@ int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, in
   const size_t need = e2f_attn_workspace_bytes(N, lmax, C, dtype);
   if (ws_bytes < need) return E2F_ERR_WORKSPACE;
   const size_t ob = (size_t)N * ncomp(lmax) * C * esize(dtype);
+  const size_t mb = (flags & E2F_MSG_F32) ? (size_t)N * ncomp(lmax) * C * 4 : ob;
   const size_t lb = (size_t)N * H * 4;
   const Range ins[4] = {{pos, (size_t)N * 12},
                         {nbr_idx, (size_t)N * K * 4},
@@ -572,11 +598,11 @@ int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, in
                         {workspace, need}};
   for (const Range& r : ins) {
     if (overlap({out, ob}, r)) return E2F_ERR_ALIAS;
-    if (out_msg && overlap({out_msg, ob}, r)) return E2F_ERR_ALIAS;
+    if (out_msg && overlap({out_msg, mb}, r)) return E2F_ERR_ALIAS;
     if (lse && overlap({lse, lb}, r)) return E2F_ERR_ALIAS;
   }
-  if (out_msg && overlap({out, ob}, {out_msg, ob})) return E2F_ERR_ALIAS;
-  if (lse && (overlap({lse, lb}, {out, ob}) || (out_msg && overlap({lse, lb}, {out_msg, ob}))))
+  if (out_msg && overlap({out, ob}, {out_msg, mb})) return E2F_ERR_ALIAS;
+  if (lse && (overlap({lse, lb}, {out, ob}) || (out_msg && overlap({lse, lb}, {out_msg, mb}))))
     return E2F_ERR_ALIAS;
   return aggregate_impl(stream, N, K, lmax, C, H, dtype, pos, nbr_idx, nbr_mask, scale,
                         env_cutoff, path_w, workspace, out, out_msg, lse, flags);
@@ -630,7 +656,8 @@ int forward_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, i
   if (!h) return E2F_ERR_NULL;
   if (!aligned(h, 16)) return E2F_ERR_ALIGN;
   const size_t hb = (size_t)N * ncomp(lmax) * C * esize(dtype);
-  if (overlap({out, hb}, {h, hb}) || (out_msg && overlap({out_msg, hb}, {h, hb})))
+  const size_t mb = (flags & E2F_MSG_F32) ? (size_t)N * ncomp(lmax) * C * 4 : hb;
+  if (overlap({out, hb}, {h, hb}) || (out_msg && overlap({out_msg, mb}, {h, hb})))
     return E2F_ERR_ALIAS;
   // all remaining checks (and the workspace / h overlap) happen in the two stages,
   // the aggregate's before anything is enqueued
@@ -650,11 +677,11 @@ int forward_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, i
                         {h, hb}};
   for (const Range& r : ins) {
     if (overlap({out, hb}, r)) return E2F_ERR_ALIAS;
-    if (out_msg && overlap({out_msg, hb}, r)) return E2F_ERR_ALIAS;
+    if (out_msg && overlap({out_msg, mb}, r)) return E2F_ERR_ALIAS;
     if (lse && overlap({lse, lb}, r)) return E2F_ERR_ALIAS;
   }
-  if (out_msg && overlap({out, hb}, {out_msg, hb})) return E2F_ERR_ALIAS;
-  if (lse && (overlap({lse, lb}, {out, hb}) || (out_msg && overlap({lse, lb}, {out_msg, hb}))))
+  if (out_msg && overlap({out, hb}, {out_msg, mb})) return E2F_ERR_ALIAS;
+  if (lse && (overlap({lse, lb}, {out, hb}) || (out_msg && overlap({lse, lb}, {out_msg, mb}))))
     return E2F_ERR_ALIAS;
   if (overlap({workspace, need}, {pos, (size_t)N * 12})) return E2F_ERR_ALIAS;
   if (proj) {
@@ -726,8 +753,8 @@ int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int 
 }
 
 size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int H, int dtype) {
-  if (check_attn_shape(N, K, lmax, C, H, dtype, 0) != E2F_OK) return 0;
-  return bwd_layout(N, K, lmax, C, H).total;
+  if (check_bwd_shape(N, K, lmax, C, H, dtype, 0) != E2F_OK) return 0;
+  return bwd_layout(N, K, lmax, C, H, dtype).total;
 }
 
 int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
@@ -738,29 +765,31 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
                       float* grad_pos, void* bwd_workspace, size_t bwd_ws_bytes,
                       uint32_t flags) {
   if (const int rt = check_runtime()) return rt;
-  int st = check_attn_shape(N, K, lmax, C, H, dtype, flags);
+  int st = check_bwd_shape(N, K, lmax, C, H, dtype, flags);
   if (st != E2F_OK) return st;
   if (bad_env(env_cutoff)) return E2F_ERR_SHAPE;
-  if (flags & E2F_VALIDATE_INDICES) return E2F_ERR_SHAPE;  // not offered for the backward
-  if (dtype != E2F_F32) return E2F_ERR_UNSUPPORTED;         // fp32 storage only
+  if (flags & (E2F_VALIDATE_INDICES | E2F_MSG_F32)) return E2F_ERR_SHAPE;  // forward-only flags
   if (N == 0) return E2F_OK;
   if (N > (int64_t)e2f::kScanTile * e2f::kScanTile || N * (int64_t)K >= ((int64_t)1 << 31) ||
       K > e2f::kRevMaxK)
     return E2F_ERR_UNSUPPORTED;
-  if (!pos || !h || !nbr_idx || !nbr_mask || !workspace || !msg || !lse || !grad_out || !grad_h ||
-      !grad_pos || !bwd_workspace)
+  const bool recompute = dtype == E2F_BF16;   // msg and lse are recomputed in fp32 (may be NULL)
+  if (!pos || !h || !nbr_idx || !nbr_mask || !workspace || (!recompute && (!msg || !lse)) ||
+      !grad_out || !grad_h || !grad_pos || !bwd_workspace)
     return E2F_ERR_NULL;
   if (!aligned(pos, 4) || !aligned(h, 16) || !aligned(nbr_idx, 4) || !aligned(workspace, 16) ||
-      !aligned(msg, 16) || !aligned(lse, 4) || !aligned(grad_out, 16) || !aligned(grad_h, 16) ||
+      (msg && !aligned(msg, 16)) || (lse && !aligned(lse, 4)) || !aligned(grad_out, 16) ||
+      !aligned(grad_h, 16) ||
       !aligned(grad_pos, 4) || !aligned(bwd_workspace, 16) || (path_w && !aligned(path_w, 4)))
     return E2F_ERR_ALIGN;
   const size_t need = e2f_attn_workspace_bytes(N, lmax, C, dtype);
   if (ws_bytes < need) return E2F_ERR_WORKSPACE;
-  const BwdLayout L = bwd_layout(N, K, lmax, C, H);
+  const BwdLayout L = bwd_layout(N, K, lmax, C, H, dtype);
   if (bwd_ws_bytes < L.total) return E2F_ERR_WORKSPACE;
-  const size_t hb = (size_t)N * ncomp(lmax) * C * 4;
+  const size_t hb = (size_t)N * ncomp(lmax) * C * esize(dtype);
+  const size_t mb = recompute ? 0 : hb;   // unused with bf16 storage
   const Range ins[8] = {{pos, (size_t)N * 12}, {h, hb},       {nbr_idx, (size_t)N * K * 4},
-                        {nbr_mask, (size_t)N * K}, {workspace, need}, {msg, hb},
+                        {nbr_mask, (size_t)N * K}, {workspace, need}, {msg, mb},
                         {lse, (size_t)N * H * 4}, {grad_out, hb}};
   const Range outs[3] = {{grad_h, hb}, {grad_pos, (size_t)N * 12}, {bwd_workspace, L.total}};
   for (const Range& o : outs)
@@ -781,6 +810,37 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
   a.gout = static_cast<const float*>(grad_out);
   a.grad_h = static_cast<float*>(grad_h);
   a.grad_pos = grad_pos;
+  const bool wide = dtype == E2F_BF16;
+  const int64_t n_feat = N * (int64_t)ncomp(lmax) * C;
+  if (wide) {
+    // exact fp32 copies of h and G, and the forward recomputed from them in fp32: the
+    // gradients of the layer at the bf16 inputs, without the rounding of the stored
+    // workspace and message (the softmax backward's <dm_i, h'_j> - <dm_i, m_i> cancels)
+    float* h32 = reinterpret_cast<float*>(b + L.h32);
+    void* ws32 = b + L.ws32;
+    float* msg32 = reinterpret_cast<float*>(b + L.msg32);
+    float* lse32 = reinterpret_cast<float*>(b + L.lse32);
+    float* g32 = reinterpret_cast<float*>(b + L.g32);
+    float* gh32 = reinterpret_cast<float*>(b + L.gh32);
+    st = hip_status(e2f::launch_widen_bf16(n_feat, static_cast<const uint16_t*>(h), h32, stream));
+    if (st == E2F_OK)
+      st = hip_status(
+          e2f::launch_widen_bf16(n_feat, static_cast<const uint16_t*>(grad_out), g32, stream));
+    const size_t ws32_bytes = e2f_attn_workspace_bytes(N, lmax, C, E2F_F32);
+    if (st == E2F_OK)
+      st = precouple_impl(stream, N, lmax, C, E2F_F32, pos, h32, path_w, ws32, ws32_bytes);
+    if (st == E2F_OK)   // out goes to the dL/dh buffer, which the passes overwrite
+      st = aggregate_impl(stream, N, K, lmax, C, H, E2F_F32, pos, nbr_idx, nbr_mask, scale,
+                          env_cutoff, path_w, ws32, gh32, msg32, lse32,
+                          flags & E2F_TARGETS_IN_ORDER);
+    if (st != E2F_OK) return st;
+    a.h = h32;
+    a.ws = static_cast<const float*>(ws32);
+    a.msg = msg32;
+    a.lse = lse32;
+    a.gout = g32;
+    a.grad_h = gh32;
+  }
   a.brows = reinterpret_cast<float*>(b + L.brows);
   a.dq = reinterpret_cast<float*>(b + L.dq);
   a.dh = reinterpret_cast<float*>(b + L.dh);
@@ -805,7 +865,7 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
   st = hip_status(e2f::launch_reverse_list(N, K, nbr_idx, nbr_mask, a.sched, off, cur, tiles,
                                            entries, stream));
   if (st != E2F_OK) return st;
-  const int V = attn_width(C, H, dtype);
+  const int V = attn_width(C, H, E2F_F32);   // the fp32 passes' lane mapping
   const int d = C / H;
   a.N = N;
   a.K = K;
@@ -819,7 +879,10 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
   a.env_inv_rc = env_inv(env_cutoff);
   a.env_rc = env_cutoff > 0.0f ? env_cutoff : 0.0f;
   const EaasCoef cf = make_coef(lmax, path_w);
-  return hip_status(e2f::launch_backward(lmax, V, a, cf, stream));
+  st = hip_status(e2f::launch_backward(lmax, V, a, cf, stream));
+  if (st != E2F_OK || !wide) return st;
+  return hip_status(e2f::launch_narrow_bf16(n_feat, a.grad_h, static_cast<uint16_t*>(grad_h),
+                                            stream));
 }
 
 size_t e2f_neighbour_workspace_bytes(int64_t N) {

@@ -61,6 +61,7 @@ struct AggArgs {
   int heads;               // H
   float env_inv_rc;        // 1 / r_env of the distance envelope (kernels with the envelope only)
   float env_rc;            // r_env itself
+  int msg_f32;             // out_msg is fp32 whatever T is
 };
 
 // Backward pass (vector-Jacobian product) arguments, fp32 storage.
@@ -120,13 +121,14 @@ int launch_eaas(int lmax, int dtype, int V, bool to_workspace, const EaasArgs& a
                 const EaasCoef& cf, hipStream_t s);
 int launch_aggregate(int lmax, int dtype, int V, const AggArgs& a, const EaasCoef& cf,
                      hipStream_t s);
-// the aggregate with 16 targets a workgroup sharing rows through LDS (its own file):
-// C = 128, K <= kWgMaxK, 2 channels a lane with d / 2 lanes a head in {1, ..., 16}
-constexpr int kWgMaxK = 256;
-bool aggregate_wg_supported(int64_t N, int K, int C, int H, int dtype);
-int launch_aggregate_wg(int lmax, int dtype, const AggArgs& a, const EaasCoef& cf,
-                        hipStream_t s);
-// fused projection + pre-coupling; C in {16, 32, 64, 128} (fp32) or {32, 64, 128} (bf16)
+// the aggregate for any layout with C % H == 0 and C <= kGenericMaxC (its own file): one
+// target a wave, lane l owning channels l + 64 k, per-head sums through LDS
+constexpr int kGenericMaxC = 512;
+int launch_aggregate_generic(int lmax, int dtype, const AggArgs& a, const EaasCoef& cf,
+                             hipStream_t s);
+// fused projection + pre-coupling: on the matrix cores for C in {16, 32, 64, 128} (fp32) or
+// {32, 64, 128} (bf16), on the vector ALUs for any other C up to kProjMaxC
+constexpr int kProjMaxC = 1024;
 bool proj_supported(int C, int dtype);
 int launch_proj(int lmax, int dtype, int C, const ProjArgs& a, const EaasCoef& cf, hipStream_t s);
 int launch_frames(int lmax, int64_t n, const float* r, float* Q, float* D, hipStream_t s);
@@ -142,6 +144,9 @@ int launch_reverse_list(int64_t N, int K, const int32_t* idx, const uint8_t* mas
                         int32_t* entries, hipStream_t s);
 constexpr int kRevMaxK = 2048;      // longest neighbour row the reverse-list build takes
 int launch_backward(int lmax, int V, const BwdArgs& a, const EaasCoef& cf, hipStream_t s);
+// exact bf16 -> fp32 widening and round-to-nearest-even fp32 -> bf16 narrowing of n elements
+int launch_widen_bf16(int64_t n, const uint16_t* src, float* dst, hipStream_t s);
+int launch_narrow_bf16(int64_t n, const float* src, uint16_t* dst, hipStream_t s);
 constexpr int kScanTile = 4096;     // elements per block of the generic scan
 // exclusive scan of a[0, n) in place (n <= kScanTile^2), a[n] = total, cur = copy of the
 // scanned values; tile_sums holds kScanTile ints.  Returns the first launch error since the

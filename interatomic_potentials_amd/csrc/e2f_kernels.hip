@@ -396,9 +396,15 @@ __global__ __launch_bounds__(64 * kAggWaves) void k_aggregate(AggArgs a, EaasCoe
       for (int k = 0; k < 2; ++k) m2[r][k] *= inv;
     const int cs = c0 + 2 * sub;
     if (a.out_msg != nullptr) {
-      T* mp = static_cast<T*>(a.out_msg) + i * (int64_t)S * C + cs;
+      if (a.msg_f32) {   // the message in fp32 whatever the storage type
+        float* mp = static_cast<float*>(a.out_msg) + i * (int64_t)S * C + cs;
 #pragma unroll
-      for (int r = 0; r < S; ++r) VecIO<T, 2>::store(mp + r * C, m2[r]);
+        for (int r = 0; r < S; ++r) VecIO<float, 2>::store(mp + r * C, m2[r]);
+      } else {
+        T* mp = static_cast<T*>(a.out_msg) + i * (int64_t)S * C + cs;
+#pragma unroll
+        for (int r = 0; r < S; ++r) VecIO<T, 2>::store(mp + r * C, m2[r]);
+      }
     }
     const Frame f = make_frame(a.pos[3 * i], a.pos[3 * i + 1], a.pos[3 * i + 2]);
     const Dy2 d = make_dy2(f);
@@ -434,9 +440,15 @@ __global__ __launch_bounds__(64 * kAggWaves) void k_aggregate(AggArgs a, EaasCoe
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[r][v] *= inv;
   if (a.out_msg != nullptr) {
-    T* mp = static_cast<T*>(a.out_msg) + i * (int64_t)S * C + c0;
+    if (a.msg_f32) {   // the message in fp32 whatever the storage type
+      float* mp = static_cast<float*>(a.out_msg) + i * (int64_t)S * C + c0;
 #pragma unroll
-    for (int r = 0; r < S; ++r) VecIO<T, V>::store(mp + r * C, acc[r]);
+      for (int r = 0; r < S; ++r) VecIO<float, V>::store(mp + r * C, acc[r]);
+    } else {
+      T* mp = static_cast<T*>(a.out_msg) + i * (int64_t)S * C + c0;
+#pragma unroll
+      for (int r = 0; r < S; ++r) VecIO<T, V>::store(mp + r * C, acc[r]);
+    }
   }
   const Frame f = make_frame(a.pos[3 * i], a.pos[3 * i + 1], a.pos[3 * i + 2]);
   const Dy2 d = make_dy2(f);

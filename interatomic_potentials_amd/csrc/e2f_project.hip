@@ -27,6 +27,9 @@
 //  4. every thread takes (atom, channel) pairs, applies EAAS to the pair's S
 //     components and stores the h' rows, consecutive threads on consecutive
 //     channels.
+// Channel counts this kernel is not built for (any other C up to kProjMaxC)
+// take a plain vector-ALU kernel, k_proj_generic, with the same arithmetic
+// order per output (input channels in order, fp32 accumulation).
 // The contraction index is split over the four 16-lane groups of a wave:
 // group g covers k in [g C/4, (g+1) C/4).  Any split is valid as long as the
 // A and B operands use the same one; this one makes every operand read a
@@ -237,6 +240,61 @@ __global__ __launch_bounds__(C / 16 * 64) void k_proj_eaas(ProjArgs a, EaasCoef 
   }
 }
 
+// ---------------------------------------------------------- any C: vector ALU
+//
+// The same products and coupling for channel counts the matrix-core kernel is
+// not built for (C not in its list, or too wide for its register-held weight
+// slices).  One workgroup per atom: the atom's S rows are staged in LDS; thread
+// c computes output channel c of q, k and every value row, summing over the
+// input channels in order (fp32 accumulation), then applies EAAS to channel c.
+template <int LMAX, typename T>
+__global__ __launch_bounds__(256) void k_proj_generic(ProjArgs a, EaasCoef cf, int C) {
+  constexpr int S = ncomp(LMAX);
+  extern __shared__ float s_h[];   // [S, C] of this atom, widened to fp32
+  const int64_t atom = blockIdx.x;
+  if (atom >= a.n) return;
+  const T* h = static_cast<const T*>(a.h) + atom * (int64_t)S * C;
+  for (int e = threadIdx.x; e < S * C; e += blockDim.x) {
+    float v;
+    VecIO<T, 1>::load(h + e, &v);
+    s_h[e] = v;
+  }
+  __syncthreads();
+  const T* wq = static_cast<const T*>(a.w_q);
+  const T* wk = static_cast<const T*>(a.w_k);
+  const T* wv = static_cast<const T*>(a.w_v);
+  const Frame f = make_frame(a.r[3 * atom], a.r[3 * atom + 1], a.r[3 * atom + 2]);
+  const Dy2 d = make_dy2(f);
+  const Reindex<LMAX> R = make_reindex<LMAX>(cf, f);
+  T* ws = static_cast<T*>(a.ws) + atom * (int64_t)(S + 1) * C;
+  T* qo = static_cast<T*>(a.q_out) + atom * (int64_t)C;
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    float q = 0.0f, k = 0.0f, v[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) v[s] = 0.0f;
+    for (int i = 0; i < C; ++i) {
+      float w_q, w_k;
+      VecIO<T, 1>::load(wq + (int64_t)i * C + c, &w_q);
+      VecIO<T, 1>::load(wk + (int64_t)i * C + c, &w_k);
+      q = fmaf(s_h[i], w_q, q);
+      k = fmaf(s_h[i], w_k, k);
+#pragma unroll
+      for (int l = 0; l <= LMAX; ++l) {
+        float w_v;
+        VecIO<T, 1>::load(wv + ((int64_t)l * C + i) * C + c, &w_v);
+#pragma unroll
+        for (int m = 0; m < 2 * l + 1; ++m) v[l * l + m] = fmaf(s_h[(l * l + m) * C + i], w_v, v[l * l + m]);
+      }
+    }
+    VecIO<T, 1>::store(qo + c, &q);
+    VecIO<T, 1>::store(ws + c, &k);
+    float y[S];
+    eaas_channel<LMAX>(v, y, f, d, R);
+#pragma unroll
+    for (int s = 0; s < S; ++s) VecIO<T, 1>::store(ws + (s + 1) * C + c, &y[s]);
+  }
+}
+
 template <int LMAX, typename T, int C>
 int go(const ProjArgs& a, const EaasCoef& cf, hipStream_t s) {
   const int64_t ntiles = (a.n + kProjTileAtoms - 1) / kProjTileAtoms;
@@ -270,20 +328,37 @@ int go_c(int C, const ProjArgs& a, const EaasCoef& cf, hipStream_t s) {
   }
 }
 
+template <int LMAX, typename T>
+int go_generic(int C, const ProjArgs& a, const EaasCoef& cf, hipStream_t s) {
+  const int threads = C < 256 ? (C + 63) / 64 * 64 : 256;
+  const size_t lds = (size_t)ncomp(LMAX) * C * sizeof(float);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((k_proj_generic<LMAX, T>), dim3((unsigned)a.n), dim3(threads), lds, s, a, cf,
+                     C);
+  return (int)hipGetLastError();
+}
+
+// the matrix-core kernel's channel counts
+bool proj_mfma(int C, int dtype) {
+  if (dtype == 0) return C == 16 || C == 32 || C == 64 || C == 128;
+  return C == 32 || C == 64 || C == 128;
+}
+
 template <typename T>
 int go_l(int lmax, int C, const ProjArgs& a, const EaasCoef& cf, hipStream_t s) {
+  const bool mfma = proj_mfma(C, sizeof(T) == 4 ? 0 : 1);
   switch (lmax) {
-    case 0: return go_c<0, T>(C, a, cf, s);
-    case 1: return go_c<1, T>(C, a, cf, s);
-    default: return go_c<2, T>(C, a, cf, s);
+    case 0: return mfma ? go_c<0, T>(C, a, cf, s) : go_generic<0, T>(C, a, cf, s);
+    case 1: return mfma ? go_c<1, T>(C, a, cf, s) : go_generic<1, T>(C, a, cf, s);
+    default: return mfma ? go_c<2, T>(C, a, cf, s) : go_generic<2, T>(C, a, cf, s);
   }
 }
 
 }  // namespace
 
 bool proj_supported(int C, int dtype) {
-  if (dtype == 0) return C == 16 || C == 32 || C == 64 || C == 128;
-  return C == 32 || C == 64 || C == 128;
+  (void)dtype;
+  return C >= 1 && C <= kProjMaxC;
 }
 
 int launch_proj(int lmax, int dtype, int C, const ProjArgs& a, const EaasCoef& cf,

@@ -136,10 +136,15 @@ def test_attention_argument_errors(fn):
     assert fn(C=0) == C["E2F_ERR_SHAPE"]
     assert fn(H=0) == C["E2F_ERR_SHAPE"]
     assert fn(C=128, H=3) == C["E2F_ERR_SHAPE"]
-    assert fn(C=12, H=4) == C["E2F_ERR_UNSUPPORTED"]    # d = 3: heads cannot align to lanes
-    assert fn(C=512, H=4) == C["E2F_ERR_UNSUPPORTED"]   # fp32: 128 lanes per row
-    assert fn(C=1024, H=8, dt=1) == C["E2F_ERR_UNSUPPORTED"]   # bf16: 128 lanes per row
-    assert fn(flags=4) == C["E2F_ERR_SHAPE"]                  # unknown flag bit
+    # any C % H == 0 layout up to 512 channels is served (the general kernel where no
+    # lane-vector width fits): the call gets as far as the pointer checks
+    assert fn(C=12, H=4, out=None) == C["E2F_ERR_NULL"]          # d = 3
+    assert fn(C=96, H=16, out=None) == C["E2F_ERR_NULL"]         # d = 6
+    assert fn(C=512, H=4, out=None) == C["E2F_ERR_NULL"]         # fp32, 512 channels
+    assert fn(C=1024, H=8) == C["E2F_ERR_UNSUPPORTED"]           # wider rows
+    assert fn(C=1024, H=8, dt=1) == C["E2F_ERR_UNSUPPORTED"]
+    assert fn(flags=8) == C["E2F_ERR_SHAPE"]                  # unknown flag bit
+    assert fn(flags=4, out=None) == C["E2F_ERR_NULL"]         # E2F_MSG_F32 is known
     assert fn(N=0, pos=None, idx=None, mask=None, ws=None, out=None) == C["E2F_OK"]
     assert fn(pos=None) == C["E2F_ERR_NULL"]
     assert fn(idx=None) == C["E2F_ERR_NULL"]
@@ -230,10 +235,12 @@ def test_backward_argument_errors():
     wb = lib.e2f_attn_backward_workspace_bytes
     assert wb(1000, 64, 2, 128, 16, 0) > 1000 * 11 * 128 * 4 + 1000 * 64 * 4
     assert wb(1000, 64, 3, 128, 16, 0) == 0
-    assert _bwd(dt=1) == C["E2F_ERR_UNSUPPORTED"]            # bf16 backward not offered
+    assert _bwd(dt=1, gh=None) == C["E2F_ERR_NULL"]           # bf16 storage is served
+    assert wb(1000, 64, 2, 128, 16, 1) > wb(1000, 64, 2, 128, 16, 0)   # + fp32 copies
     assert _bwd(dt=5) == C["E2F_ERR_DTYPE"]
     assert _bwd(K=0) == C["E2F_ERR_SHAPE"]
     assert _bwd(flags=1) == C["E2F_ERR_SHAPE"]               # no index validation here
+    assert _bwd(flags=4) == C["E2F_ERR_SHAPE"]               # nor a message dtype flag
     assert _bwd(N=0, pos=None, h=None) == C["E2F_OK"]
     for name in ("pos", "h", "idx", "mask", "ws", "msg", "lse", "gout", "gh", "gp", "bws"):
         assert _bwd(**{name: None}) == C["E2F_ERR_NULL"], name
@@ -284,9 +291,11 @@ def test_projection_argument_errors(fn):
     assert fn(wk=fake(4)) == C["E2F_ERR_ALIAS"]                  # weights inside the workspace
     assert fn(dt=7) == C["E2F_ERR_DTYPE"]
     assert fn(lmax=3) == C["E2F_ERR_SHAPE"]
-    # MFMA tiles: C in {16, 32, 64, 128} for fp32, {32, 64, 128} for bf16
-    assert fn(C=96, **({"H": 12} if fn is _fproj else {})) == C["E2F_ERR_UNSUPPORTED"]
-    assert fn(C=16, dt=1, **({"H": 2} if fn is _fproj else {})) == C["E2F_ERR_UNSUPPORTED"]
+    # any C up to 1024 (the matrix cores for C in {16, 32, 64, 128} fp32, {32, 64, 128} bf16,
+    # the vector ALUs otherwise): other widths get as far as the pointer checks
+    assert fn(C=96, wq=None, **({"H": 12} if fn is _fproj else {})) == C["E2F_ERR_NULL"]
+    assert fn(C=16, dt=1, wq=None, **({"H": 2} if fn is _fproj else {})) == C["E2F_ERR_NULL"]
+    assert fn(C=2048, **({"H": 16} if fn is _fproj else {})) == C["E2F_ERR_UNSUPPORTED"]
 
 
 def _nl(**kw):

@@ -11,7 +11,7 @@ import pytest
 
 from gen import make_config
 from oracle.grad import attn_backward as oracle_backward
-from tests.helpers import TOL_F32, block_rel_err
+from tests.helpers import TOL_BF16, TOL_F32, block_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -178,3 +178,72 @@ def test_backward_sources_listed_many_times(e2f, dev, lmax, C, H, r_env):
     rh, rp = oracle_backward(pos, h, idx, mask, H, lmax, g, **kw)
     assert block_rel_err(res[0][0], rh, lmax) <= TOL_F32
     assert pos_err(res[0][1], rp) <= TOL_F32
+
+
+# ------------------------------------------------ bf16 storage, fp32 arithmetic
+
+def gpu_backward_bf16(e2f, dev, pos, h, idx, mask, H, g, env_cutoff=None, pass_msg=True):
+    """Forward and backward with bf16 features, workspace, upstream gradient and dL/dh (the
+    backward recomputes the message and log-sum-exp in fp32: passing them is optional)."""
+    p, ii, mm = T(pos, dev), T(idx, dev), T(mask, dev)
+    hh = T(h, dev).to(torch.bfloat16)
+    ws = e2f.attn_precouple(p, hh)
+    lmax = int(round(h.shape[1] ** 0.5)) - 1
+    out, msg, lse = e2f.attn_aggregate(p, ii, mm, ws, H, lmax, h.shape[2], torch.bfloat16,
+                                       return_msg=True, return_lse=True, env_cutoff=env_cutoff,
+                                       msg_f32=True)
+    if not pass_msg:
+        msg = lse = None
+    gb = T(g, dev).to(torch.bfloat16)
+    gh, gp = e2f.attn_backward(p, hh, ii, mm, H, ws, msg, lse, gb, env_cutoff=env_cutoff)
+    torch.cuda.synchronize()
+    assert gh.dtype == torch.bfloat16
+    return gh.float().cpu().numpy(), gp.cpu().numpy()
+
+
+def _bf16(x):
+    from gen import bf16_bits_to_f32, f32_to_bf16_bits
+    return bf16_bits_to_f32(f32_to_bf16_bits(x))
+
+
+@pytest.mark.parametrize("lmax,C,H,K", [(2, 128, 16, 64), (1, 32, 4, 20), (2, 64, 8, 300)])
+def test_backward_bf16_random_graphs(e2f, dev, lmax, C, H, K):
+    """bf16 storage: the oracle's gradients of the bf16-rounded inputs, at the bf16 bar."""
+    say(f"backward bf16 random graph: lmax={lmax} C={C} H={H} K={K}")
+    rng = np.random.default_rng(500 + lmax * 31 + C + K)
+    N = 80
+    S = (lmax + 1) ** 2
+    pos = (rng.standard_normal((N, 3)) * 3).astype(np.float32)
+    h = _bf16(rng.standard_normal((N, S, C)).astype(np.float32))
+    idx = rng.integers(0, N, size=(N, K)).astype(np.int32)
+    mask = (rng.random((N, K)) < 0.6).astype(np.uint8)
+    mask[7] = 0
+    g = _bf16(rng.standard_normal((N, S, C)).astype(np.float32))
+    gh, gp = gpu_backward_bf16(e2f, dev, pos, h, idx, mask, H, g, pass_msg=K != 20)
+    rh, rp = oracle_backward(pos, h, idx, mask, H, lmax, g)
+    assert block_rel_err(gh, rh, lmax) <= TOL_BF16
+    assert pos_err(gp, rp) <= TOL_BF16
+
+
+@pytest.mark.parametrize("envelope", [False, True])
+def test_backward_scaleout_sampled_bf16(e2f, dev, envelope):
+    """Scale-out workload (100,000 atoms, bf16 storage): the upstream gradient lives on a few
+    targets, so the oracle needs only their edges; plain and with the envelope."""
+    cfg = make_config("scaleout")
+    s = cfg.spec
+    r_env = float(np.float32(s.cutoff)) if envelope else None
+    rng = np.random.default_rng(19)
+    tg = rng.choice(cfg.N, 24, replace=False)
+    g = np.zeros(cfg.h.shape, np.float32)
+    g[tg] = _bf16(rng.standard_normal((tg.size,) + cfg.h.shape[1:]).astype(np.float32))
+    say(f"backward scale-out bf16, gradient on {tg.size} targets, envelope {r_env}")
+    gh, gp = gpu_backward_bf16(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g,
+                               env_cutoff=r_env)
+    mask_t = np.zeros_like(cfg.mask)
+    mask_t[tg] = cfg.mask[tg]
+    rh, rp = oracle_backward(cfg.pos, cfg.h, cfg.idx, mask_t, s.H, s.lmax, g, env_cutoff=r_env)
+    touched = np.unique(np.concatenate([tg, cfg.idx[tg][cfg.mask[tg] != 0]]))
+    assert block_rel_err(gh[touched], rh[touched], s.lmax) <= TOL_BF16
+    assert pos_err(gp[touched], rp[touched]) <= TOL_BF16
+    untouched = np.setdiff1d(np.arange(cfg.N), touched)
+    assert np.all(gh[untouched] == 0) and np.all(gp[untouched] == 0)

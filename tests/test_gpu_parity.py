@@ -15,7 +15,7 @@ from gen import bf16_bits_to_f32, f32_to_bf16_bits, make_config, make_micro
 from oracle import tp
 from oracle import wigner as owig
 from oracle.attn import attn_forward as oracle_attn
-from tests.helpers import TOL_BF16, TOL_F32, block_rel_err, to_host
+from tests.helpers import TOL_BF16, TOL_F32, block_rel_err, head_rel_err, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -146,6 +146,8 @@ def test_attention_small_configs_full(e2f, dev, name):
                                chunk_edges=4096)
     assert block_rel_err(to_host(msg), ref_msg, s.lmax) <= TOL_F32
     assert block_rel_err(to_host(out), ref, s.lmax) <= TOL_F32
+    # the stricter per-head metric: the message's heads are independent softmaxes
+    assert head_rel_err(to_host(msg), ref_msg, s.lmax, s.H) <= TOL_F32
 
 
 def _sample_targets(cfg, n, seed):
@@ -172,6 +174,7 @@ def test_attention_big_configs_sampled(e2f, dev, name):
     tol = TOL_BF16 if s.dtype == "bf16" else TOL_F32
     assert block_rel_err(got_msg, ref_msg, s.lmax) <= tol
     assert block_rel_err(got, ref, s.lmax) <= tol
+    assert head_rel_err(got_msg, ref_msg, s.lmax, s.H) <= tol
     assert torch.isfinite(out.float()).all()
 
 
@@ -370,9 +373,9 @@ def test_attention_bf16_shapes_vs_oracle(e2f, dev, lmax, C, H, K):
     assert (out[3].float() == 0).all()
 
 
-def test_unsupported_head_layout_is_reported(e2f, dev):
-    """d = 3 channels per head cannot align heads to lanes: a clear error, nothing launched."""
-    h = torch.zeros((4, 9, 24), device=dev)
+def test_unsupported_row_width_is_reported(e2f, dev):
+    """Rows wider than 512 channels: a clear error, nothing launched."""
+    h = torch.zeros((4, 9, 1024), device=dev)
     with pytest.raises(e2f.E2FError) as ei:
         e2f.attn_forward(torch.zeros((4, 3), device=dev), h,
                          torch.zeros((4, 2), dtype=torch.int32, device=dev),
@@ -406,3 +409,28 @@ def test_targets_sharing_a_wave_stay_independent(e2f, dev):
     others = np.setdiff1d(np.arange(N + 1), [1])
     assert torch.isnan(with_nan[1]).any()
     assert torch.equal(with_nan[others], without[others])
+
+
+@pytest.mark.parametrize("C,H", [(128, 16), (24, 8)])
+def test_message_in_fp32_with_bf16_storage(e2f, dev, C, H):
+    """E2F_MSG_F32: the message m leaves the kernel in fp32; rounded to bf16 it equals the
+    bf16-stored message bit for bit (the same value, rounded once), and out is unchanged."""
+    say(f"bf16 storage, message in fp32: C={C} H={H}")
+    rng = np.random.default_rng(31 + C)
+    N, K, lmax = 90, 48, 2
+    pos = (rng.standard_normal((N, 3)) * 3).astype(np.float32)
+    h = bf16_bits_to_f32(f32_to_bf16_bits(rng.standard_normal((N, 9, C)).astype(np.float32)))
+    idx = rng.integers(0, N, size=(N, K)).astype(np.int32)
+    mask = (rng.random((N, K)) < 0.6).astype(np.uint8)
+    args = (T(pos, dev), T(h, dev, torch.bfloat16), T(idx, dev), T(mask, dev), H)
+    p, hh, ii, mm = args[:4]
+    ws = e2f.attn_precouple(p, hh)
+    out_a, msg_b = e2f.attn_aggregate(p, ii, mm, ws, H, lmax, C, torch.bfloat16, return_msg=True)
+    out_b, msg_f = e2f.attn_aggregate(p, ii, mm, ws, H, lmax, C, torch.bfloat16, return_msg=True,
+                                      msg_f32=True)
+    assert msg_f.dtype == torch.float32 and msg_b.dtype == torch.bfloat16
+    assert torch.equal(out_a, out_b)
+    got = f32_to_bf16_bits(msg_f.cpu().numpy())
+    assert np.array_equal(got, msg_b.cpu().view(torch.int16).numpy().view(np.uint16))
+    _, ref_msg = oracle_attn(pos, h, idx, mask, H, lmax, return_msg=True)
+    assert block_rel_err(to_host(msg_f), ref_msg, lmax) <= TOL_BF16

@@ -65,7 +65,10 @@ def _weights_dev(w, dev, dt):
 
 
 CASES = [(0, 16, "f32"), (1, 32, "f32"), (2, 64, "f32"), (2, 128, "f32"), (1, 128, "f32"),
-         (2, 16, "f32"), (2, 32, "bf16"), (1, 64, "bf16"), (2, 128, "bf16"), (0, 128, "bf16")]
+         (2, 16, "f32"), (2, 32, "bf16"), (1, 64, "bf16"), (2, 128, "bf16"), (0, 128, "bf16"),
+         # widths the matrix-core kernel is not built for: the vector-ALU kernel
+         (2, 48, "f32"), (2, 96, "f32"), (1, 80, "bf16"), (2, 256, "f32"), (2, 16, "bf16"),
+         (0, 48, "bf16"), (2, 20, "f32")]
 
 
 @pytest.mark.parametrize("lmax,C,dt", CASES)
@@ -161,9 +164,9 @@ def test_identity_weights_reproduce_the_unprojected_path(e2f, dev):
 
 
 def test_unsupported_projection_width_is_reported(e2f, dev):
-    h = torch.zeros((4, 9, 48), device=dev)
-    w = torch.zeros((48, 48), device=dev)
+    h = torch.zeros((4, 9, 2048), device=dev)
+    w = torch.zeros((2048, 2048), device=dev)
     with pytest.raises(e2f.E2FError) as ei:
         e2f.attn_precouple(torch.zeros((4, 3), device=dev), h,
-                           proj=(w, w, torch.zeros((3, 48, 48), device=dev)))
+                           proj=(w, w, torch.zeros((3, 2048, 2048), device=dev)))
     assert ei.value.name == "E2F_ERR_UNSUPPORTED"
