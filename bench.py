@@ -197,8 +197,7 @@ def cpu_baseline(cfg, budget_s=15.0):
 KERNEL_SOURCES = ["interatomic_potentials_amd/csrc/e2f_kernels.hip",
                   "interatomic_potentials_amd/csrc/e2f_aggregate_generic.hip",
                   "interatomic_potentials_amd/csrc/e2f_dense.hip",
-                  "interatomic_potentials_amd/csrc/e2f_device.hpp",
-                  "interatomic_potentials_amd/csrc/e2f_internal.hpp"]
+                  "interatomic_potentials_amd/csrc/e2f_device.hpp"]
 
 N_CU, N_XCD, N_SIMD = 256, 8, 1024   # MI355X
 
