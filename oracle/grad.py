@@ -62,8 +62,12 @@ def envelope_torch(x: torch.Tensor) -> torch.Tensor:
 def attn_forward_torch(pos: torch.Tensor, h: torch.Tensor, nbr_idx: np.ndarray, nbr_mask: np.ndarray,
                        heads: int, lmax: int, scale: Optional[float] = None,
                        path_w: Optional[np.ndarray] = None,
-                       env_cutoff: Optional[float] = None) -> torch.Tensor:
-    """The three steps of ``oracle.attn.attn_forward`` for all targets, in torch."""
+                       env_cutoff: Optional[float] = None, proj=None) -> torch.Tensor:
+    """The three steps of ``oracle.attn.attn_forward`` for all targets, in torch.
+
+    ``proj`` = (W_Q, W_K, W_V) torch tensors: the learned projections of
+    ``oracle.attn.project`` (q = h[l=0] W_Q, k = h[l=0] W_K, v[l] = h[l] W_V[l], h' = v (x) R).
+    """
     N, S, C = h.shape
     d = C // heads
     if scale is None:
@@ -72,9 +76,15 @@ def attn_forward_torch(pos: torch.Tensor, h: torch.Tensor, nbr_idx: np.ndarray, 
     e_src = np.asarray(nbr_idx)[e_row, e_slot].astype(np.int64)
     er = torch.from_numpy(e_row)
     es = torch.from_numpy(e_src)
-    hp = tp_dense_torch(h, pos, lmax, path_w)                      # step 1
-    q = h[:, 0, :].reshape(N, heads, d)
-    k = h[:, 0, :].reshape(N, heads, d)
+    if proj is None:
+        v, q0, k0 = h, h[:, 0, :], h[:, 0, :]
+    else:
+        w_q, w_k, w_v = proj
+        q0, k0 = h[:, 0, :] @ w_q, h[:, 0, :] @ w_k
+        v = torch.cat([h[:, l * l:(l + 1) ** 2, :] @ w_v[l] for l in range(lmax + 1)], dim=1)
+    hp = tp_dense_torch(v, pos, lmax, path_w)                      # step 1
+    q = q0.reshape(N, heads, d)
+    k = k0.reshape(N, heads, d)
     s = scale * (q[er] * k[es]).sum(-1)                            # [E, H]
     mx_np = np.full((N, heads), -np.inf)
     np.maximum.at(mx_np, e_row, s.detach().numpy())
@@ -103,6 +113,21 @@ def attn_backward(pos: np.ndarray, h: np.ndarray, nbr_idx: np.ndarray, nbr_mask:
     if dpos is None:            # lmax = 0: the harmonics are constant, positions do not enter
         dpos = torch.zeros_like(pt)
     return dh.numpy(), dpos.numpy()
+
+
+def attn_backward_proj(pos: np.ndarray, h: np.ndarray, nbr_idx: np.ndarray, nbr_mask: np.ndarray,
+                       heads: int, lmax: int, grad_out: np.ndarray, proj, scale: Optional[float] = None,
+                       path_w: Optional[np.ndarray] = None, env_cutoff: Optional[float] = None):
+    """(dL/dh, dL/dpos, dL/dW_Q, dL/dW_K, dL/dW_V) of the projected layer, float64."""
+    pt = torch.tensor(np.asarray(pos, dtype=np.float64), requires_grad=True)
+    ht = torch.tensor(np.asarray(h, dtype=np.float64), requires_grad=True)
+    ws = [torch.tensor(np.asarray(w, dtype=np.float64), requires_grad=True) for w in proj]
+    out = attn_forward_torch(pt, ht, nbr_idx, nbr_mask, heads, lmax, scale, path_w, env_cutoff,
+                             proj=tuple(ws))
+    g = torch.from_numpy(np.asarray(grad_out, dtype=np.float64))
+    grads = torch.autograd.grad((out * g).sum(), (ht, pt, *ws), allow_unused=True)
+    grads = [torch.zeros_like(t) if d is None else d for d, t in zip(grads, (ht, pt, *ws))]
+    return tuple(d.numpy() for d in grads)
 
 
 def eaas_vjp(x: np.ndarray, r: np.ndarray, g: np.ndarray, lmax: int,

@@ -85,3 +85,51 @@ def test_lmax0_position_gradient_is_zero():
     _, dpos = attn_backward(rng.standard_normal((N, 3)), rng.standard_normal((N, 1, C)), idx, mask,
                             H, 0, rng.standard_normal((N, 1, C)))
     assert np.all(dpos == 0)
+
+
+@pytest.mark.parametrize("lmax", [0, 2])
+def test_projected_gradients_match_finite_differences(lmax):
+    """dL/dW_Q, dL/dW_K, dL/dW_V, dL/dh and dL/dpos of the projected layer against central finite
+    differences of the numpy oracle's projected forward."""
+    from oracle.grad import attn_backward_proj
+    rng = np.random.default_rng(40 + lmax)
+    N, K, C, H = 7, 5, 4, 2
+    S = (lmax + 1) ** 2
+    pos = rng.standard_normal((N, 3)) * 1.5
+    h = rng.standard_normal((N, S, C))
+    w = (rng.standard_normal((C, C)) / 2, rng.standard_normal((C, C)) / 2,
+         rng.standard_normal((lmax + 1, C, C)) / 2)
+    idx, mask = _graph(rng, N, K)
+    g = rng.standard_normal((N, S, C))
+    dh, dpos, dwq, dwk, dwv = attn_backward_proj(pos, h, idx, mask, H, lmax, g, w)
+
+    def loss(p, hh, ww):
+        return float((attn_forward(p, hh, idx, mask, H, lmax, proj=ww) * g).sum())
+
+    eps = 1e-6
+
+    def fd_check(arr_index, grad, make):
+        for k in arr_index:
+            plus, minus = make(k, eps), make(k, -eps)
+            fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+            assert abs(fd - grad[k]) <= 1e-6 * (1 + abs(fd)), (k, fd, grad[k])
+
+    def w_at(which, k, e):
+        ww = [x.copy() for x in w]
+        ww[which][k] += e
+        return pos, h, tuple(ww)
+
+    for which, grad in ((0, dwq), (1, dwk), (2, dwv)):
+        keys = list(np.ndindex(grad.shape))
+        picks = [keys[i] for i in rng.choice(len(keys), min(12, len(keys)), replace=False)]
+        fd_check(picks, grad, lambda k, e, which=which: w_at(which, k, e))
+    hk = list(np.ndindex(h.shape))
+    fd_check([hk[i] for i in rng.choice(len(hk), 12, replace=False)], dh,
+             lambda k, e: (pos, h + np.where(np.arange(h.size).reshape(h.shape) ==
+                                             np.ravel_multi_index(k, h.shape), e, 0.0), w))
+    if lmax > 0:
+        fd_check([(i, a) for i in range(N) for a in range(3)], dpos,
+                 lambda k, e: (pos + np.where(np.arange(pos.size).reshape(pos.shape) ==
+                                              np.ravel_multi_index(k, pos.shape), e, 0.0), h, w))
+    else:
+        assert np.all(dpos == 0)
