@@ -24,9 +24,12 @@
 //     atom) and its weight slices as B, for all S rows and for q and k;
 //  3. q and k go to memory from the accumulators; the value rows go back
 //     to LDS as fp32;
-//  4. every thread takes (atom, channel) pairs, applies EAAS to the pair's S
+//  4. each atom's frame, Wigner blocks and reindex weights are computed once
+//     (one thread per atom, during step 3) into an LDS table; every thread
+//     then takes (atom, channel) pairs, applies EAAS to the pair's S
 //     components and stores the h' rows, consecutive threads on consecutive
-//     channels.
+//     channels.  With C a multiple of 64 a wave takes whole atoms, and holds
+//     the atom's table entry in scalar registers.
 // Channel counts this kernel is not built for (any other C up to kProjMaxC)
 // take a plain vector-ALU kernel, k_proj_generic, with the same arithmetic
 // order per output (input channels in order, fp32 accumulation).
@@ -89,6 +92,28 @@ __device__ inline float uni(float x) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
+// one atom's coupling data, computed once per tile and read by every channel
+template <int LMAX>
+struct __align__(16) AtomFrame {
+  Frame f;
+  Dy2 d;
+  Reindex<LMAX> R;
+};
+
+template <int LMAX>
+__device__ inline AtomFrame<LMAX> uni(const AtomFrame<LMAX>& e) {
+  AtomFrame<LMAX> u;
+  u.f.ct = uni(e.f.ct); u.f.st = uni(e.f.st); u.f.c1 = uni(e.f.c1); u.f.s1 = uni(e.f.s1);
+  u.f.c2 = uni(e.f.c2); u.f.s2 = uni(e.f.s2); u.f.r1 = uni(e.f.r1); u.f.r2 = uni(e.f.r2);
+  u.d.d00 = uni(e.d.d00); u.d.d01 = uni(e.d.d01); u.d.d02 = uni(e.d.d02);
+  u.d.d11 = uni(e.d.d11); u.d.d12 = uni(e.d.d12); u.d.d22 = uni(e.d.d22);
+#pragma unroll
+  for (int q = 0; q < kMaxPaths; ++q)
+#pragma unroll
+    for (int m = 0; m <= LMAX; ++m) u.R.k[q][m] = uni(e.R.k[q][m]);
+  return u;
+}
+
 __device__ inline void store_elem(float* p, float v) { *p = v; }
 __device__ inline void store_elem(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 
@@ -110,6 +135,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_proj_eaas(ProjArgs a, EaasCoef 
 
   __shared__ __align__(16) T sa[TA * PA];
   __shared__ __align__(16) float sv[TA * PV];
+  __shared__ AtomFrame<LMAX> sf[TA];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -204,36 +230,52 @@ __global__ __launch_bounds__(C / 16 * 64) void k_proj_eaas(ProjArgs a, EaasCoef 
       for (int s = 0; s < S; ++s) sv[i * PV + s * C + c0 + col] = acc[s][r];
     }
     if (AHEAD && tile + gridDim.x < ntiles) fetch(tile + gridDim.x);
+    // the tile's frames, once per atom (sf was last read in step 4 of the
+    // previous tile, before this tile's first barrier)
+    if (tid < na) {
+      const int64_t atom = a0 + tid;
+      AtomFrame<LMAX> e;
+      e.f = make_frame(a.r[3 * atom], a.r[3 * atom + 1], a.r[3 * atom + 2]);
+      e.d = make_dy2(e.f);
+      e.R = make_reindex<LMAX>(cf, e.f);
+      sf[tid] = e;
+    }
     __syncthreads();
 
     // 4. EAAS per (atom, channel); stores coalesced along the channels
-    for (int p = tid; p < TA * C; p += NT) {
-      const int i = p / C;
-      const int c = p - i * C;
-      if (i >= na) break;
-      const int64_t atom = a0 + i;
-      Frame f = make_frame(a.r[3 * atom], a.r[3 * atom + 1], a.r[3 * atom + 2]);
-      Dy2 d = make_dy2(f);
-      Reindex<LMAX> R = make_reindex<LMAX>(cf, f);
-      if constexpr (C % 64 == 0) {
-        // the wave's 64 lanes share one atom: hold its frame and reindex
-        // weights in scalar registers (the weight slices fill the vector file)
-        f.ct = uni(f.ct); f.st = uni(f.st); f.c1 = uni(f.c1); f.s1 = uni(f.s1);
-        f.c2 = uni(f.c2); f.s2 = uni(f.s2); f.r1 = uni(f.r1); f.r2 = uni(f.r2);
-        d.d00 = uni(d.d00); d.d01 = uni(d.d01); d.d02 = uni(d.d02);
-        d.d11 = uni(d.d11); d.d12 = uni(d.d12); d.d22 = uni(d.d22);
+    if constexpr (C % 64 == 0) {
+      // a wave takes whole atoms: their table entries go to scalar registers
+      // (the weight slices fill the vector file)
+      constexpr int NW = NT / 64;
+      for (int i = tid >> 6; i < na; i += NW) {
+        const AtomFrame<LMAX> e = uni<LMAX>(sf[i]);
+        const int64_t atom = a0 + i;
+        T* dst = ws + atom * (int64_t)((S + 1) * C) + C;
 #pragma unroll
-        for (int q = 0; q < kMaxPaths; ++q)
+        for (int c = lane; c < C; c += 64) {
+          float x[S], y[S];
 #pragma unroll
-          for (int m = 0; m <= LMAX; ++m) R.k[q][m] = uni(R.k[q][m]);
+          for (int s = 0; s < S; ++s) x[s] = sv[i * PV + s * C + c];
+          eaas_channel<LMAX>(x, y, e.f, e.d, e.R);
+#pragma unroll
+          for (int s = 0; s < S; ++s) store_elem(dst + s * C + c, y[s]);
+        }
       }
-      float x[S], y[S];
+    } else {
+      for (int p = tid; p < TA * C; p += NT) {
+        const int i = p / C;
+        const int c = p - i * C;
+        if (i >= na) break;
+        const int64_t atom = a0 + i;
+        const AtomFrame<LMAX> e = sf[i];
+        float x[S], y[S];
 #pragma unroll
-      for (int s = 0; s < S; ++s) x[s] = sv[i * PV + s * C + c];
-      eaas_channel<LMAX>(x, y, f, d, R);
-      T* dst = ws + atom * (int64_t)((S + 1) * C) + C + c;
+        for (int s = 0; s < S; ++s) x[s] = sv[i * PV + s * C + c];
+        eaas_channel<LMAX>(x, y, e.f, e.d, e.R);
+        T* dst = ws + atom * (int64_t)((S + 1) * C) + C + c;
 #pragma unroll
-      for (int s = 0; s < S; ++s) store_elem(dst + s * C, y[s]);
+        for (int s = 0; s < S; ++s) store_elem(dst + s * C, y[s]);
+      }
     }
     // the next tile's step 1 overwrites sa, last read in step 2 above (before
     // the barrier that preceded step 4), so no further barrier is needed here
