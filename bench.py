@@ -493,14 +493,21 @@ def bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream):
     gh = torch.empty_like(h)
     gp = torch.empty_like(pos)
 
-    def timed(env_cutoff):
-        _, msg, lse = e2f.attn_aggregate(pos, idx, mask, ws, H, s.lmax, C, h.dtype,
+    def timed(env_cutoff, proj=None):
+        wsp = ws
+        if proj is not None:   # the forward's workspace built with the projections
+            wsp = e2f.attn_precouple(pos, h, ws=torch.empty_like(ws), proj=proj)
+        _, msg, lse = e2f.attn_aggregate(pos, idx, mask, wsp, H, s.lmax, C, h.dtype,
                                          out=out, return_msg=True, return_lse=True,
                                          env_cutoff=env_cutoff, msg_f32=True)
+        bw = bws
+        if proj is not None:
+            bw = torch.empty(e2f.attn_backward_proj_workspace_bytes(N, K, s.lmax, C, H, dt_code),
+                             dtype=torch.uint8, device=h.device)
 
         def run():
-            e2f.attn_backward(pos, h, idx, mask, H, ws, msg, lse, g, bwd_ws=bws, grad_h=gh,
-                              grad_pos=gp, env_cutoff=env_cutoff)
+            e2f.attn_backward(pos, h, idx, mask, H, wsp, msg, lse, g, bwd_ws=bw, grad_h=gh,
+                              grad_pos=gp, env_cutoff=env_cutoff, proj=proj)
 
         for _ in range(args.warmup):
             run()
@@ -515,6 +522,12 @@ def bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream):
 
     ms = timed(None)
     env_ms = timed(float(s.cutoff))      # the envelope-weighted softmax, radius = list cutoff
+    proj_ms = None
+    if not args.no_proj:                 # through the learned projections (weight gradients too)
+        from gen import proj_weights
+        w = tuple(torch.from_numpy(x).to(h.device).to(h.dtype)
+                  for x in proj_weights(s.lmax, C, seed=13, dtype=s.dtype))
+        proj_ms = timed(None, proj=w)
     row = (S + 1) * C * 4
     # prep reads G, m, h row 0 and writes q + dm rows; each stream reads one row block per edge
     # (k + h' for the target pass; q + dm plus lse and D for the source pass) and per atom
@@ -529,10 +542,15 @@ def bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream):
         feat = N * S * C
         total += 6 * (2 * feat + N * (S + 1) * C) + 6 * feat
     print(f"[bench] backward: {ms:.3f} ms, {total / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic; "
-          f"with the envelope {env_ms:.3f} ms", file=sys.stderr, flush=True)
+          f"with the envelope {env_ms:.3f} ms; through the projections {proj_ms} ms",
+          file=sys.stderr, flush=True)
+    # the projections' backward products: v = h W_V (S rows), dL/dh (S rows + dq, dk), and the
+    # weight gradients (S rows + 2), C^2 multiply-adds per row each
+    proj_flops = 2 * N * C * C * (3 * S + 4)
     return {"ms": ms, "edges_per_s": E / (ms * 1e-3), "algorithmic_bytes": total,
             "algorithmic_GBps": total / (ms * 1e-3) / 1e9,
             "bytes_per_edge": 2 * row + 8, "envelope_ms": env_ms,
+            "projected_ms": proj_ms, "projected_extra_flops": proj_flops,
             "storage": "bf16 (widened to fp32 copies, fp32 passes)" if bf16 else "fp32"}
 
 

@@ -303,7 +303,8 @@ size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int 
  *               forward (with an envelope, dL/dpos includes its derivative
  *               through each pair distance)
  *   workspace   the forward's workspace after e2f_attn_precouple (read only;
- *               the layer without projections is differentiated)
+ *               the layer without projections is differentiated, with q_i read
+ *               from the workspace's query rows)
  *   msg, lse    the forward's out_msg ([N, S, C] fp32) and lse ([N, H] fp32)
  *               outputs; with bf16 storage they are recomputed and these are
  *               not read (NULL allowed)
@@ -325,6 +326,44 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
                       const void* msg, const float* lse, const void* grad_out, void* grad_h,
                       float* grad_pos, void* bwd_workspace, size_t bwd_ws_bytes,
                       uint32_t flags);
+
+/*
+ * e2f_attn_backward_proj -- the backward pass of the layer with learned
+ * projections (e2f_attn_precouple_proj's q, k and v; gist.science summary,
+ * technical summary 2.2, Eq. 6): besides dL/dh and dL/dpos it returns the
+ * weight gradients
+ *   dL/dW_Q = sum_i h_i[0]^T dq_i,  dL/dW_K = sum_i h_i[0]^T dk_i,
+ *   dL/dW_V[l] = sum_i sum_m h_i[l, m]^T dv_i[l, m],
+ * and dL/dh flows through the projections:
+ *   dL/dh_i[0] = dv_i[0] W_V[0]^T + dq_i W_Q^T + dk_i W_K^T,
+ *   dL/dh_i[l] = dv_i[l] W_V[l]^T (l > 0),
+ * where dq, dk are the logit gradients and dv the adjoint pre-coupling of the
+ * value gradients.  The value rows v = h W_V are recomputed (the position
+ * gradient of the pre-coupling needs them).  Arguments as e2f_attn_backward,
+ * plus:
+ *   w_q, w_k, w_v     the forward's weights (storage type, 16-byte aligned);
+ *                     workspace must come from e2f_attn_precouple_proj with them
+ *   grad_w_q, grad_w_k  [C, C] fp32, written (not accumulated)
+ *   grad_w_v          [lmax + 1, C, C] fp32, written
+ *   bwd_workspace     e2f_attn_backward_proj_workspace_bytes(...) bytes: that
+ *                     of e2f_attn_backward plus v, dv and dk, fp32 weight copies
+ *                     (bf16), and the weight gradients' partial sums (one [C, C]
+ *                     matrix per chunk of about 512 rows, at most 128 MiB)
+ * The weight gradients are sums over chunks of rows, the chunks added in a
+ * fixed order: the same bits on every run.  The products run on the matrix
+ * cores for C = 16, 32, 64, 128, on the vector ALUs for other C up to 1024.
+ * E2F_ERR_UNSUPPORTED where e2f_attn_backward or the projections are.
+ */
+size_t e2f_attn_backward_proj_workspace_bytes(int64_t N, int K, int lmax, int C, int H,
+                                              int dtype);
+int e2f_attn_backward_proj(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
+                           int dtype, const float* pos, const void* h, const void* w_q,
+                           const void* w_k, const void* w_v, const int32_t* nbr_idx,
+                           const uint8_t* nbr_mask, float scale, float env_cutoff,
+                           const float* path_w, const void* workspace, size_t ws_bytes,
+                           const void* msg, const float* lse, const void* grad_out, void* grad_h,
+                           float* grad_pos, float* grad_w_q, float* grad_w_k, float* grad_w_v,
+                           void* bwd_workspace, size_t bwd_ws_bytes, uint32_t flags);
 
 /*
  * Padded neighbour lists, built on the GPU: the list that the attention

@@ -70,6 +70,10 @@ SIGNATURES = {
     "e2f_attn_backward": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                  _f32, _f32, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                  _u32]),
+    "e2f_attn_backward_proj_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32]),
+    "e2f_attn_backward_proj": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _f32, _f32, _vp, _vp, _sz, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _u32]),
     "e2f_neighbour_workspace_bytes": (_sz, [_i64]),
     "e2f_neighbour_list": (_i32, [_vp, _i64, _i32, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _sz]),
@@ -498,17 +502,26 @@ def attn_backward_workspace_bytes(N: int, K: int, lmax: int, C: int, H: int,
     return int(lib.e2f_attn_backward_workspace_bytes(N, K, lmax, C, H, dtype))
 
 
+def attn_backward_proj_workspace_bytes(N: int, K: int, lmax: int, C: int, H: int,
+                                       dtype: int = F32) -> int:
+    return int(lib.e2f_attn_backward_proj_workspace_bytes(N, K, lmax, C, H, dtype))
+
+
 def attn_backward(pos, h, nbr_idx, nbr_mask, heads: int, ws, msg, lse, grad_out,
                   scale: Optional[float] = None, path_w=None, targets_in_order: bool = False,
-                  bwd_ws=None, grad_h=None, grad_pos=None, env_cutoff: Optional[float] = None):
+                  bwd_ws=None, grad_h=None, grad_pos=None, env_cutoff: Optional[float] = None,
+                  proj=None):
     """(dL/dh, dL/dpos) for L = <grad_out, out>; ws, msg, lse from the forward.
 
     With bf16 storage the library recomputes the message and the log-sum-exp in fp32, so
-    msg and lse may be None (they are not read).
+    msg and lse may be None (they are not read).  ``proj`` = (w_q, w_k, w_v), the weights
+    the forward's workspace was built with: the gradients go through the projections, and
+    (dL/dh, dL/dpos, dL/dW_Q, dL/dW_K, dL/dW_V) is returned, the weight gradients in fp32.
     """
     torch = _torch()
     N, S, C = _dims(h)
     lmax = _lmax_of(S)
+    w = _proj_weights(proj, h, lmax)
     K = _nbr_dims(nbr_idx, nbr_mask, N)
     _shape(pos, "pos", (N, 3))
     for t, name in ((msg, "msg"), (grad_out, "grad_out"), (grad_h, "grad_h")):
@@ -527,7 +540,8 @@ def attn_backward(pos, h, nbr_idx, nbr_mask, heads: int, ws, msg, lse, grad_out,
         _dev(lse, "lse", torch.float32)
     _dev(grad_out, "grad_out", h.dtype)
     if bwd_ws is None:
-        nbytes = attn_backward_workspace_bytes(N, K, lmax, C, heads, dt)
+        nbytes = (attn_backward_workspace_bytes if w is None
+                  else attn_backward_proj_workspace_bytes)(N, K, lmax, C, heads, dt)
         bwd_ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=h.device)
     _dev(bwd_ws, "bwd_ws")
     grad_h = torch.empty_like(h) if grad_h is None else _dev(grad_h, "grad_h", h.dtype)
@@ -536,13 +550,24 @@ def attn_backward(pos, h, nbr_idx, nbr_mask, heads: int, ws, msg, lse, grad_out,
     _same_device(pos=pos, h=h, nbr_idx=nbr_idx, nbr_mask=nbr_mask, ws=ws, msg=msg, lse=lse,
                  grad_out=grad_out, bwd_ws=bwd_ws, grad_h=grad_h, grad_pos=grad_pos)
     pw = _path_w(path_w, h.device)
+    flags = TARGETS_IN_ORDER if targets_in_order else 0
+    if w is not None:
+        gw = (torch.empty((C, C), dtype=torch.float32, device=h.device),
+              torch.empty((C, C), dtype=torch.float32, device=h.device),
+              torch.empty((lmax + 1, C, C), dtype=torch.float32, device=h.device))
+        _check(lib.e2f_attn_backward_proj(
+            _stream(h), N, K, lmax, C, heads, dt, _ptr(pos), _ptr(h), _ptr(w[0]), _ptr(w[1]),
+            _ptr(w[2]), _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0),
+            float(env_cutoff or 0.0), _ptr(pw), _ptr(ws), _nbytes(ws), _ptr(msg), _ptr(lse),
+            _ptr(grad_out), _ptr(grad_h), _ptr(grad_pos), _ptr(gw[0]), _ptr(gw[1]), _ptr(gw[2]),
+            _ptr(bwd_ws), _nbytes(bwd_ws), flags), "e2f_attn_backward_proj")
+        return (grad_h, grad_pos) + gw
     _check(lib.e2f_attn_backward(_stream(h), N, K, lmax, C, heads, dt, _ptr(pos), _ptr(h),
                                  _ptr(nbr_idx), _ptr(nbr_mask), float(scale or 0.0),
                                  float(env_cutoff or 0.0), _ptr(pw),
                                  _ptr(ws), _nbytes(ws), _ptr(msg), _ptr(lse),
                                  _ptr(grad_out), _ptr(grad_h), _ptr(grad_pos), _ptr(bwd_ws),
-                                 _nbytes(bwd_ws),
-                                 TARGETS_IN_ORDER if targets_in_order else 0),
+                                 _nbytes(bwd_ws), flags),
            "e2f_attn_backward")
     return grad_h, grad_pos
 

@@ -37,6 +37,7 @@ SOURCES = [
     ("e2f_aggregate_generic.hip", True),
     ("e2f_backward.hip", True),
     ("e2f_project.hip", True),
+    ("e2f_project_bwd.hip", True),
     ("e2f_neighbours.hip", True),
     ("e2f_dense.hip", True),
     ("e2f_noalloc.hip", True),

@@ -13,6 +13,10 @@
 //   dpos_i = grad_r <G_i, T(r) m_i> at r_i + grad_r <dh'_i, T(r) h_i> at r_i
 // with a_ij recomputed from the forward's saved log-sum-exp, as in the
 // recompute scheme of FlashAttention-2, so no per-edge tensor is stored.
+// q_i is read from the forward workspace's query rows.  Through learned
+// projections (BwdArgs::dk set) h is the value rows v = h W_V, and the source
+// pass stores dk_j and dv_j = T(r_j)^T dh'_j apart; the projections' own
+// backward follows in e2f_project_bwd.hip.
 //
 // k_bwd_prep    per atom: dm, D, the step-3 part of dpos
 // k_bwd_q       per target, streaming its sorted neighbours: dq
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a, EaasCoef cf) {
     ld<V>(a.gout + base + s * C + cl, g[s]);
     ld<V>(a.msg + base + s * C + cl, m[s]);
   }
-  ld<V>(a.h + base + cl, q);
+  ld<V>(a.q + atom * C + cl, q);
   float Dp = 0.0f;
   float acc[3] = {0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -523,10 +527,11 @@ __device__ __forceinline__ void src_finish(const BwdArgs& a, const EaasCoef& cf,
   Reindex<LMAX> Rrad, Rhat;
   make_grad_reindex<LMAX>(cf, f, Rrad, Rhat);
   const int64_t base = j * (int64_t)S * C;
+  const bool split = a.dk != nullptr;   // dk apart, and dh' only (the projections follow)
   float hj[S][V], dqj[V], gh[S][V];
 #pragma unroll
   for (int s2 = 0; s2 < S; ++s2) ld<V>(a.h + base + s2 * C + cl, hj[s2]);
-  ld<V>(a.dq + j * C + cl, dqj);
+  if (!split) ld<V>(a.dq + j * C + cl, dqj);
   float acc[3] = {0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int v = 0; v < V; ++v) {
@@ -537,7 +542,7 @@ __device__ __forceinline__ void src_finish(const BwdArgs& a, const EaasCoef& cf,
       xv[s2] = hj[s2][v];
     }
     eaas_channel_t<LMAX>(gv, out, f, d, R);  // gv is rotated in place
-    out[0] += dqj[v] + gdk[v];
+    if (!split) out[0] += dqj[v] + gdk[v];
 #pragma unroll
     for (int s2 = 0; s2 < S; ++s2) gh[s2][v] = out[s2];
     rotate_in<LMAX>(xv, f, d);
@@ -552,6 +557,7 @@ __device__ __forceinline__ void src_finish(const BwdArgs& a, const EaasCoef& cf,
   if (act) {
 #pragma unroll
     for (int s2 = 0; s2 < S; ++s2) st<V>(a.grad_h + base + s2 * C + c0, gh[s2]);
+    if (split) st<V>(a.dk + j * C + c0, gdk);
   }
   if (gl == 0) {
     float gp[3];

@@ -277,13 +277,53 @@ size_t sched_bytes(int64_t N) {
 // With bf16 storage the backward widens h and G exactly into fp32 copies, recomputes the
 // forward in fp32 from them (workspace, message, log-sum-exp) and differentiates that with
 // the fp32 passes: [h][fp32 attention workspace][m][lse][G][dL/dh, narrowed at the end].
+// Through the learned projections it also holds the recomputed value rows v, dv, dk, the
+// weight-gradient partial sums and (bf16) fp32 copies of the weights.
 struct BwdLayout {
   size_t brows, dq, dh, off, cur, tiles, entries, sched, cell, counts, partial;
   size_t h32, ws32, msg32, lse32, g32, gh32;   // bf16 storage only
+  size_t v32, dv32, dk32, w32, wpart;          // projections only
   size_t total;
 };
 
-BwdLayout bwd_layout(int64_t N, int K, int lmax, int C, int H, int dt) {
+// Rows of the weight gradients' partial sums: about kDwChunk rows a chunk, at most
+// 2^25 floats of partial matrices in all (wide channel counts take longer chunks).
+constexpr int64_t kDwChunk = 512;
+struct DwPlan {
+  int njobs;
+  int mult[e2f::kDwMaxJobs];
+  int chunks[e2f::kDwMaxJobs];
+  int64_t rows[e2f::kDwMaxJobs], chunk_rows[e2f::kDwMaxJobs], part_off[e2f::kDwMaxJobs];
+  int64_t total;   // partial matrices
+};
+
+// jobs: 0 = W_Q, 1 = W_K, 2 + l = W_V[l]
+DwPlan dw_plan(int64_t N, int lmax, int C) {
+  DwPlan P;
+  P.njobs = lmax + 3;
+  P.total = 0;
+  int64_t cap = ((int64_t)1 << 25) / ((int64_t)C * C) / P.njobs;
+  if (cap < 1) cap = 1;
+  for (int j = 0; j < P.njobs; ++j) {
+    P.mult[j] = j < 2 ? 1 : 2 * (j - 2) + 1;
+    P.rows[j] = N * P.mult[j];
+    int64_t chunks = (P.rows[j] + kDwChunk - 1) / kDwChunk;
+    if (chunks > cap) chunks = cap;
+    if (chunks < 1) chunks = 1;
+    int64_t cr = (P.rows[j] + chunks - 1) / chunks;
+    cr = (cr + 3) / 4 * 4;
+    if (cr < 4) cr = 4;
+    chunks = (P.rows[j] + cr - 1) / cr;
+    if (chunks < 1) chunks = 1;
+    P.chunk_rows[j] = cr;
+    P.chunks[j] = (int)chunks;
+    P.part_off[j] = P.total;
+    P.total += chunks;
+  }
+  return P;
+}
+
+BwdLayout bwd_layout(int64_t N, int K, int lmax, int C, int H, int dt, bool proj) {
   BwdLayout L;
   size_t p = 0;
   auto take = [&p](size_t bytes) {
@@ -298,7 +338,12 @@ BwdLayout bwd_layout(int64_t N, int K, int lmax, int C, int H, int dt) {
   L.msg32 = take(wide ? feat : 0);
   L.lse32 = take(wide ? (size_t)N * H * 4 : 0);
   L.g32 = take(wide ? feat : 0);
-  L.gh32 = take(wide ? feat : 0);
+  L.gh32 = take(wide && !proj ? feat : 0);
+  L.v32 = take(proj ? feat : 0);
+  L.dv32 = take(proj ? feat : 0);
+  L.dk32 = take(proj ? (size_t)N * C * 4 : 0);
+  L.w32 = take(proj && wide ? (size_t)(lmax + 3) * C * C * 4 : 0);
+  L.wpart = take(proj ? (size_t)dw_plan(N, lmax, C).total * C * C * 4 : 0);
   L.brows = take((size_t)N * (ncomp(lmax) + 1) * C * 4);
   L.dq = take((size_t)N * C * 4);
   L.dh = take((size_t)N * H * 4);
@@ -754,21 +799,34 @@ int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int 
 
 size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int H, int dtype) {
   if (check_bwd_shape(N, K, lmax, C, H, dtype, 0) != E2F_OK) return 0;
-  return bwd_layout(N, K, lmax, C, H, dtype).total;
+  return bwd_layout(N, K, lmax, C, H, dtype, false).total;
 }
 
-int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
-                      const float* pos, const void* h, const int32_t* nbr_idx,
-                      const uint8_t* nbr_mask, float scale, float env_cutoff,
-                      const float* path_w, const void* workspace, size_t ws_bytes,
-                      const void* msg, const float* lse, const void* grad_out, void* grad_h,
-                      float* grad_pos, void* bwd_workspace, size_t bwd_ws_bytes,
-                      uint32_t flags) {
+size_t e2f_attn_backward_proj_workspace_bytes(int64_t N, int K, int lmax, int C, int H,
+                                              int dtype) {
+  if (check_bwd_shape(N, K, lmax, C, H, dtype, 0) != E2F_OK) return 0;
+  if (!e2f::proj_supported(C, dtype)) return 0;
+  return bwd_layout(N, K, lmax, C, H, dtype, true).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// e2f_attn_backward and e2f_attn_backward_proj (proj: through the learned projections)
+int backward_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
+                  const float* pos, const void* h, const void* w_q, const void* w_k,
+                  const void* w_v, const int32_t* nbr_idx, const uint8_t* nbr_mask, float scale,
+                  float env_cutoff, const float* path_w, const void* workspace, size_t ws_bytes,
+                  const void* msg, const float* lse, const void* grad_out, void* grad_h,
+                  float* grad_pos, float* grad_w_q, float* grad_w_k, float* grad_w_v,
+                  void* bwd_workspace, size_t bwd_ws_bytes, uint32_t flags, bool proj) {
   if (const int rt = check_runtime()) return rt;
   int st = check_bwd_shape(N, K, lmax, C, H, dtype, flags);
   if (st != E2F_OK) return st;
   if (bad_env(env_cutoff)) return E2F_ERR_SHAPE;
   if (flags & (E2F_VALIDATE_INDICES | E2F_MSG_F32)) return E2F_ERR_SHAPE;  // forward-only flags
+  if (proj && !e2f::proj_supported(C, dtype)) return E2F_ERR_UNSUPPORTED;
   if (N == 0) return E2F_OK;
   if (N > (int64_t)e2f::kScanTile * e2f::kScanTile || N * (int64_t)K >= ((int64_t)1 << 31) ||
       K > e2f::kRevMaxK)
@@ -777,26 +835,36 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
   if (!pos || !h || !nbr_idx || !nbr_mask || !workspace || (!recompute && (!msg || !lse)) ||
       !grad_out || !grad_h || !grad_pos || !bwd_workspace)
     return E2F_ERR_NULL;
+  if (proj && (!w_q || !w_k || !w_v || !grad_w_q || !grad_w_k || !grad_w_v)) return E2F_ERR_NULL;
   if (!aligned(pos, 4) || !aligned(h, 16) || !aligned(nbr_idx, 4) || !aligned(workspace, 16) ||
       (msg && !aligned(msg, 16)) || (lse && !aligned(lse, 4)) || !aligned(grad_out, 16) ||
       !aligned(grad_h, 16) ||
       !aligned(grad_pos, 4) || !aligned(bwd_workspace, 16) || (path_w && !aligned(path_w, 4)))
     return E2F_ERR_ALIGN;
+  if (proj && (!aligned(w_q, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) ||
+               !aligned(grad_w_q, 4) || !aligned(grad_w_k, 4) || !aligned(grad_w_v, 4)))
+    return E2F_ERR_ALIGN;
   const size_t need = e2f_attn_workspace_bytes(N, lmax, C, dtype);
   if (ws_bytes < need) return E2F_ERR_WORKSPACE;
-  const BwdLayout L = bwd_layout(N, K, lmax, C, H, dtype);
+  const BwdLayout L = bwd_layout(N, K, lmax, C, H, dtype, proj);
   if (bwd_ws_bytes < L.total) return E2F_ERR_WORKSPACE;
   const size_t hb = (size_t)N * ncomp(lmax) * C * esize(dtype);
   const size_t mb = recompute ? 0 : hb;   // unused with bf16 storage
-  const Range ins[8] = {{pos, (size_t)N * 12}, {h, hb},       {nbr_idx, (size_t)N * K * 4},
-                        {nbr_mask, (size_t)N * K}, {workspace, need}, {msg, mb},
-                        {lse, (size_t)N * H * 4}, {grad_out, hb}};
-  const Range outs[3] = {{grad_h, hb}, {grad_pos, (size_t)N * 12}, {bwd_workspace, L.total}};
+  const size_t wb = proj ? (size_t)C * C * esize(dtype) : 0;
+  const size_t gwb = proj ? (size_t)C * C * 4 : 0;
+  const Range ins[11] = {{pos, (size_t)N * 12}, {h, hb},       {nbr_idx, (size_t)N * K * 4},
+                         {nbr_mask, (size_t)N * K}, {workspace, need}, {msg, mb},
+                         {lse, (size_t)N * H * 4}, {grad_out, hb}, {w_q, wb}, {w_k, wb},
+                         {w_v, (size_t)(lmax + 1) * wb}};
+  const Range outs[6] = {{grad_h, hb},        {grad_pos, (size_t)N * 12},
+                         {bwd_workspace, L.total}, {grad_w_q, gwb},
+                         {grad_w_k, gwb},     {grad_w_v, (size_t)(lmax + 1) * gwb}};
   for (const Range& o : outs)
     for (const Range& r : ins)
       if (overlap(o, r)) return E2F_ERR_ALIAS;
-  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
-    return E2F_ERR_ALIAS;
+  for (int x = 0; x < 6; ++x)
+    for (int y = x + 1; y < 6; ++y)
+      if (overlap(outs[x], outs[y])) return E2F_ERR_ALIAS;
 
   char* b = static_cast<char*>(bwd_workspace);
   e2f::BwdArgs a;
@@ -805,6 +873,8 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
   a.idx = nbr_idx;
   a.mask = nbr_mask;
   a.ws = static_cast<const float*>(workspace);
+  a.q = static_cast<const float*>(ws_query_rows(const_cast<void*>(workspace), N, lmax, C, dtype));
+  a.dk = nullptr;
   a.msg = static_cast<const float*>(msg);
   a.lse = lse;
   a.gout = static_cast<const float*>(grad_out);
@@ -812,6 +882,12 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
   a.grad_pos = grad_pos;
   const bool wide = dtype == E2F_BF16;
   const int64_t n_feat = N * (int64_t)ncomp(lmax) * C;
+  const int64_t cc = (int64_t)C * C;
+  // fp32 weights (the caller's, or exact copies of the bf16 ones)
+  const float* wq32 = static_cast<const float*>(w_q);
+  const float* wk32 = static_cast<const float*>(w_k);
+  const float* wv32 = static_cast<const float*>(w_v);
+  float* dv32 = proj ? reinterpret_cast<float*>(b + L.dv32) : nullptr;
   if (wide) {
     // exact fp32 copies of h and G, and the forward recomputed from them in fp32: the
     // gradients of the layer at the bf16 inputs, without the rounding of the stored
@@ -821,25 +897,65 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
     float* msg32 = reinterpret_cast<float*>(b + L.msg32);
     float* lse32 = reinterpret_cast<float*>(b + L.lse32);
     float* g32 = reinterpret_cast<float*>(b + L.g32);
-    float* gh32 = reinterpret_cast<float*>(b + L.gh32);
+    // the aggregate's out is scratch here: the buffer it lands in is overwritten later
+    float* out32 = proj ? dv32 : reinterpret_cast<float*>(b + L.gh32);
     st = hip_status(e2f::launch_widen_bf16(n_feat, static_cast<const uint16_t*>(h), h32, stream));
     if (st == E2F_OK)
       st = hip_status(
           e2f::launch_widen_bf16(n_feat, static_cast<const uint16_t*>(grad_out), g32, stream));
     const size_t ws32_bytes = e2f_attn_workspace_bytes(N, lmax, C, E2F_F32);
-    if (st == E2F_OK)
+    if (proj) {
+      float* w32 = reinterpret_cast<float*>(b + L.w32);
+      if (st == E2F_OK)
+        st = hip_status(e2f::launch_widen_bf16(cc, static_cast<const uint16_t*>(w_q), w32, stream));
+      if (st == E2F_OK)
+        st = hip_status(
+            e2f::launch_widen_bf16(cc, static_cast<const uint16_t*>(w_k), w32 + cc, stream));
+      if (st == E2F_OK)
+        st = hip_status(e2f::launch_widen_bf16((lmax + 1) * cc,
+                                               static_cast<const uint16_t*>(w_v), w32 + 2 * cc,
+                                               stream));
+      wq32 = w32;
+      wk32 = w32 + cc;
+      wv32 = w32 + 2 * cc;
+      if (st == E2F_OK)
+        st = precouple_proj_impl(stream, N, lmax, C, E2F_F32, pos, h32, wq32, wk32, wv32, path_w,
+                                 ws32);
+    } else if (st == E2F_OK) {
       st = precouple_impl(stream, N, lmax, C, E2F_F32, pos, h32, path_w, ws32, ws32_bytes);
-    if (st == E2F_OK)   // out goes to the dL/dh buffer, which the passes overwrite
+    }
+    if (st == E2F_OK)
       st = aggregate_impl(stream, N, K, lmax, C, H, E2F_F32, pos, nbr_idx, nbr_mask, scale,
-                          env_cutoff, path_w, ws32, gh32, msg32, lse32,
+                          env_cutoff, path_w, ws32, out32, msg32, lse32,
                           flags & E2F_TARGETS_IN_ORDER);
     if (st != E2F_OK) return st;
     a.h = h32;
     a.ws = static_cast<const float*>(ws32);
+    a.q = static_cast<const float*>(ws_query_rows(ws32, N, lmax, C, E2F_F32));
     a.msg = msg32;
     a.lse = lse32;
     a.gout = g32;
-    a.grad_h = gh32;
+    a.grad_h = out32;
+  }
+  const float* h_in = a.h;   // fp32 h: the caller's, or its exact copy
+  if (proj) {
+    // the passes differentiate the pre-coupling of v = h W_V: recompute v, take dv and
+    // dk apart, and finish through the projections afterwards
+    float* v32 = reinterpret_cast<float*>(b + L.v32);
+    e2f::RowsArgs r;
+    r.x = h_in;
+    r.dq = nullptr;
+    r.dk = nullptr;
+    r.w_q = wq32;
+    r.w_k = wk32;
+    r.w_v = wv32;
+    r.out = v32;
+    r.n = N;
+    st = hip_status(e2f::launch_value_rows(lmax, C, r, stream));
+    if (st != E2F_OK) return st;
+    a.h = v32;
+    a.dk = reinterpret_cast<float*>(b + L.dk32);
+    a.grad_h = dv32;
   }
   a.brows = reinterpret_cast<float*>(b + L.brows);
   a.dq = reinterpret_cast<float*>(b + L.dq);
@@ -880,9 +996,78 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
   a.env_rc = env_cutoff > 0.0f ? env_cutoff : 0.0f;
   const EaasCoef cf = make_coef(lmax, path_w);
   st = hip_status(e2f::launch_backward(lmax, V, a, cf, stream));
-  if (st != E2F_OK || !wide) return st;
-  return hip_status(e2f::launch_narrow_bf16(n_feat, a.grad_h, static_cast<uint16_t*>(grad_h),
-                                            stream));
+  if (st != E2F_OK) return st;
+  if (!proj) {
+    if (!wide) return E2F_OK;
+    return hip_status(e2f::launch_narrow_bf16(n_feat, a.grad_h, static_cast<uint16_t*>(grad_h),
+                                              stream));
+  }
+  // dL/dh through the projections, in the storage type
+  e2f::RowsArgs r;
+  r.x = dv32;
+  r.dq = a.dq;
+  r.dk = a.dk;
+  r.w_q = wq32;
+  r.w_k = wk32;
+  r.w_v = wv32;
+  r.out = grad_h;
+  r.n = N;
+  st = hip_status(e2f::launch_grad_rows(lmax, C, dtype, r, stream));
+  if (st != E2F_OK) return st;
+  // weight gradients: X = h rows, dY = dq, dk, dv rows
+  const DwPlan P = dw_plan(N, lmax, C);
+  e2f::DwArgs w;
+  w.partial = reinterpret_cast<float*>(b + L.wpart);
+  w.njobs = P.njobs;
+  w.C = C;
+  const int64_t row = (int64_t)ncomp(lmax) * C;
+  for (int j = 0; j < P.njobs; ++j) {
+    e2f::DwJob& J = w.job[j];
+    const int l = j - 2;
+    J.x = j < 2 ? h_in : h_in + (int64_t)l * l * C;
+    J.xs = row;
+    J.dy = j == 0 ? a.dq : (j == 1 ? a.dk : dv32 + (int64_t)l * l * C);
+    J.ys = j < 2 ? C : row;
+    J.rows = P.rows[j];
+    J.chunk_rows = P.chunk_rows[j];
+    J.part_off = P.part_off[j];
+    J.out = j == 0 ? grad_w_q : (j == 1 ? grad_w_k : grad_w_v + (int64_t)l * cc);
+    J.mult = P.mult[j];
+    J.C = C;
+    J.chunks = P.chunks[j];
+  }
+  return hip_status(e2f::launch_weight_grads(w, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
+                      const float* pos, const void* h, const int32_t* nbr_idx,
+                      const uint8_t* nbr_mask, float scale, float env_cutoff,
+                      const float* path_w, const void* workspace, size_t ws_bytes,
+                      const void* msg, const float* lse, const void* grad_out, void* grad_h,
+                      float* grad_pos, void* bwd_workspace, size_t bwd_ws_bytes,
+                      uint32_t flags) {
+  return backward_impl(stream, N, K, lmax, C, H, dtype, pos, h, nullptr, nullptr, nullptr,
+                       nbr_idx, nbr_mask, scale, env_cutoff, path_w, workspace, ws_bytes, msg,
+                       lse, grad_out, grad_h, grad_pos, nullptr, nullptr, nullptr, bwd_workspace,
+                       bwd_ws_bytes, flags, false);
+}
+
+int e2f_attn_backward_proj(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
+                           int dtype, const float* pos, const void* h, const void* w_q,
+                           const void* w_k, const void* w_v, const int32_t* nbr_idx,
+                           const uint8_t* nbr_mask, float scale, float env_cutoff,
+                           const float* path_w, const void* workspace, size_t ws_bytes,
+                           const void* msg, const float* lse, const void* grad_out, void* grad_h,
+                           float* grad_pos, float* grad_w_q, float* grad_w_k, float* grad_w_v,
+                           void* bwd_workspace, size_t bwd_ws_bytes, uint32_t flags) {
+  return backward_impl(stream, N, K, lmax, C, H, dtype, pos, h, w_q, w_k, w_v, nbr_idx, nbr_mask,
+                       scale, env_cutoff, path_w, workspace, ws_bytes, msg, lse, grad_out, grad_h,
+                       grad_pos, grad_w_q, grad_w_k, grad_w_v, bwd_workspace, bwd_ws_bytes, flags,
+                       true);
 }
 
 size_t e2f_neighbour_workspace_bytes(int64_t N) {

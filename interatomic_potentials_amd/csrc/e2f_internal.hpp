@@ -76,6 +76,8 @@ struct BwdArgs {
   const float* gout;       // [N, S, C] upstream gradient of out
   float* grad_h;           // [N, S, C]
   float* grad_pos;         // [N, 3]
+  const float* q;          // [N, C] query rows (the forward workspace's)
+  float* dk;               // [N, C] or NULL: dk_j stored apart, grad_h then holds dv_j only
   float* brows;            // [N, S + 1, C] scratch: row 0 = q_i, rows 1..S = dm_i
   float* dq;               // [N, C] scratch
   float* dh;               // [N, H] scratch: per-head <dm_i, m_i>
@@ -93,6 +95,45 @@ struct BwdArgs {
   float env_inv_rc;        // 1 / r_env of the distance envelope, 0 = none
   float env_rc;            // r_env itself
 };
+
+// Row products of the projections' backward (fp32): values x W_V, or
+// gradients x W^T (+ dq W_Q^T + dk W_K^T on the l = 0 row).
+struct RowsArgs {
+  const float* x;          // [n, S, C] h (values) or dv (gradients)
+  const float* dq;         // [n, C] (gradients)
+  const float* dk;         // [n, C] (gradients)
+  const float* w_q;        // [C, C] fp32
+  const float* w_k;        // [C, C] fp32
+  const float* w_v;        // [lmax + 1, C, C] fp32
+  void* out;               // [n, S, C]: fp32 values, or dL/dh in the storage type
+  int64_t n;
+};
+
+// One weight gradient sum_r X_r^T dY_r over rows r = (atom r / mult, component
+// r % mult): row r of X starts at x + (r / mult) xs + (r % mult) C.
+struct DwJob {
+  const float* x;
+  const float* dy;
+  int64_t xs, ys;          // atom strides (floats)
+  int64_t rows;
+  int64_t chunk_rows;      // rows per partial sum (a multiple of 4)
+  int64_t part_off;        // first partial matrix of the job
+  float* out;              // [C, C]
+  int mult;
+  int C;
+  int chunks;
+};
+constexpr int kDwMaxJobs = kMaxLmax + 3;   // W_Q, W_K, W_V[0..lmax]
+struct DwArgs {
+  DwJob job[kDwMaxJobs];
+  float* partial;          // [sum of chunks, C, C]
+  int njobs;
+  int C;
+};
+bool rows_mfma(int C);
+int launch_value_rows(int lmax, int C, const RowsArgs& a, hipStream_t s);
+int launch_grad_rows(int lmax, int C, int dtype, const RowsArgs& a, hipStream_t s);
+int launch_weight_grads(const DwArgs& a, hipStream_t s);
 
 // Learned projections fused with the pre-coupling (storage type T for h and
 // the weights, row-major [C_in, C_out] matrices applied from the right).

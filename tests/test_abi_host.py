@@ -459,3 +459,41 @@ def test_binding_rejects_mismatched_shapes_before_any_launch():
     # matching shapes on the CPU stop at the device check instead
     with pytest.raises(ValueError, match="GPU"):
         e2f.attn_forward(pos, h, idx, mask, H)
+
+
+def _bproj(**kw):
+    a = dict(stream=None, N=1000, K=64, lmax=2, C=128, H=16, dt=0, pos=fake(1), h=fake(9),
+             wq=fake(20), wk=fake(21), wv=fake(22), idx=fake(2), mask=fake(3), scale=0.0, env=0.0,
+             pw=None, ws=fake(4), ws_bytes=1 << 30, msg=fake(10), lse=fake(11), gout=fake(12),
+             gh=fake(13), gp=fake(14), gwq=fake(23), gwk=fake(24), gwv=fake(25), bws=fake(16),
+             bws_bytes=1 << 30, flags=0)
+    a.update(kw)
+    return lib.e2f_attn_backward_proj(
+        a["stream"], a["N"], a["K"], a["lmax"], a["C"], a["H"], a["dt"], a["pos"], a["h"], a["wq"],
+        a["wk"], a["wv"], a["idx"], a["mask"], a["scale"], a["env"], a["pw"], a["ws"],
+        a["ws_bytes"], a["msg"], a["lse"], a["gout"], a["gh"], a["gp"], a["gwq"], a["gwk"],
+        a["gwv"], a["bws"], a["bws_bytes"], a["flags"])
+
+
+def test_backward_proj_argument_errors():
+    wb = lib.e2f_attn_backward_proj_workspace_bytes
+    plain = lib.e2f_attn_backward_workspace_bytes(1000, 64, 2, 128, 16, 0)
+    # + v, dv (2 N S C floats), dk (N C) and the weight gradients' partial sums
+    assert wb(1000, 64, 2, 128, 16, 0) >= plain + (2 * 9 + 1) * 1000 * 128 * 4 + 5 * 128 * 128 * 4
+    assert wb(1000, 64, 2, 128, 16, 1) > wb(1000, 64, 2, 128, 16, 0)   # + fp32 copies
+    assert wb(1000, 64, 3, 128, 16, 0) == 0
+    assert wb(1000, 64, 2, 2048, 16, 0) == 0
+    assert _bproj(N=0, pos=None, h=None) == C["E2F_OK"]
+    for name in ("pos", "h", "wq", "wk", "wv", "idx", "mask", "ws", "msg", "lse", "gout", "gh",
+                 "gp", "gwq", "gwk", "gwv", "bws"):
+        assert _bproj(**{name: None}) == C["E2F_ERR_NULL"], name
+    assert _bproj(dt=1, msg=None, lse=None, gh=None) == C["E2F_ERR_NULL"]   # bf16: msg, lse optional
+    assert _bproj(wv=ctypes.c_void_p(BASE + 22 * 64 * MB + 4)) == C["E2F_ERR_ALIGN"]
+    assert _bproj(gwk=ctypes.c_void_p(BASE + 24 * 64 * MB + 2)) == C["E2F_ERR_ALIGN"]
+    assert _bproj(bws_bytes=wb(1000, 64, 2, 128, 16, 0) - 1) == C["E2F_ERR_WORKSPACE"]
+    assert _bproj(gwq=fake(20)) == C["E2F_ERR_ALIAS"]          # dW_Q over W_Q
+    assert _bproj(gwv=fake(16)) == C["E2F_ERR_ALIAS"]          # dW_V inside the scratch
+    assert _bproj(gwk=fake(23)) == C["E2F_ERR_ALIAS"]          # dW_K over dW_Q
+    assert _bproj(flags=4) == C["E2F_ERR_SHAPE"]
+    assert _bproj(C=2048) == C["E2F_ERR_UNSUPPORTED"]
+    assert _bproj(C=96, H=6, wq=None) == C["E2F_ERR_NULL"]    # vector-ALU widths are served

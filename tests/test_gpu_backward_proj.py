@@ -1,0 +1,180 @@
+"""GPU backward pass through the learned projections against the oracle's float64 autograd.
+
+The oracle (oracle.grad.attn_backward_proj) differentiates the projected forward
+(q = h[l=0] W_Q, k = h[l=0] W_K, v[l] = h[l] W_V[l], h' = v (x) R) with respect to h,
+pos and the three weights; finite differences of the numpy forward pin it on the CPU.
+Errors: dL/dh block-relative, dL/dpos per atom (as the plain backward's tests), each
+weight gradient max|gpu - ref| / max|ref| over the matrix.  fp32 at 1e-4; with bf16
+storage the inputs are the bf16-rounded values, the arithmetic is fp32 from their exact
+widening, and only dL/dh is rounded back to bf16 (2e-2 for it, 1e-4 for the rest).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from gen import make_config, proj_weights
+from oracle.grad import attn_backward_proj as oracle_backward_proj
+from tests.helpers import TOL_BF16, TOL_F32, block_rel_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def e2f():
+    import interatomic_potentials_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return torch.device("cuda:0")
+
+
+def T(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def pos_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    nr = np.linalg.norm(ref, axis=1)
+    den = np.maximum(nr, 1e-3 * nr.max() + 1e-300)
+    return float((np.linalg.norm(got - ref, axis=1) / den).max())
+
+
+def mat_err(got, ref):
+    ref = np.asarray(ref, np.float64)
+    return float(np.abs(np.asarray(got, np.float64) - ref).max() / np.abs(ref).max())
+
+
+def bf16_round(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).float().numpy()
+
+
+def gpu_backward_proj(e2f, dev, pos, h, idx, mask, H, g, w, dt="f32", env_cutoff=None, **kw):
+    """Projected forward (workspace, message, lse) then the projected backward on the GPU."""
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    p, ii, mm = T(pos, dev), T(idx, dev), T(mask, dev)
+    hh = T(h, dev).to(tdt)
+    wt = tuple(T(x, dev).to(tdt) for x in w)
+    lmax = int(round(h.shape[1] ** 0.5)) - 1
+    ws = e2f.attn_precouple(p, hh, proj=wt)
+    _, msg, lse = e2f.attn_aggregate(p, ii, mm, ws, H, lmax, h.shape[2], tdt, return_msg=True,
+                                     return_lse=True, env_cutoff=env_cutoff,
+                                     msg_f32=dt == "bf16")
+    res = e2f.attn_backward(p, hh, ii, mm, H, ws, msg, lse, T(g, dev).to(tdt), proj=wt,
+                            env_cutoff=env_cutoff, **kw)
+    torch.cuda.synchronize()
+    assert res[0].dtype == tdt and all(x.dtype == torch.float32 for x in res[1:])
+    return [x.float().cpu().numpy() for x in res]
+
+
+def check(got, ref, lmax, dt):
+    gh, gp, gq, gk, gv = got
+    rh, rp, rq, rk, rv = ref
+    eh = block_rel_err(gh, rh, lmax)
+    ep = pos_err(gp, rp) if lmax > 0 else float(np.abs(gp).max())
+    ew = max(mat_err(gq, rq), mat_err(gk, rk), max(mat_err(gv[l], rv[l]) for l in range(lmax + 1)))
+    say(f"  dh {eh:.2e}  dpos {ep:.2e}  dW {ew:.2e}")
+    assert eh <= (TOL_BF16 if dt == "bf16" else TOL_F32)
+    assert ep <= TOL_F32
+    assert ew <= TOL_F32
+
+
+# matrix-core channel counts (16, 32, 64, 128) and vector-ALU ones (20, 48, 96)
+@pytest.mark.parametrize("lmax,C,H,K,dt", [(0, 16, 2, 12, "f32"), (1, 32, 4, 20, "f32"),
+                                           (2, 64, 4, 24, "f32"), (2, 128, 16, 40, "f32"),
+                                           (2, 48, 3, 16, "f32"), (2, 20, 5, 12, "f32"),
+                                           (1, 96, 6, 10, "f32"), (2, 128, 16, 30, "bf16"),
+                                           (1, 32, 4, 16, "bf16"), (2, 48, 3, 12, "bf16")])
+def test_backward_proj_random_graphs(e2f, dev, lmax, C, H, K, dt):
+    say(f"projected backward: lmax={lmax} C={C} H={H} K={K} {dt}")
+    rng = np.random.default_rng(lmax * 7 + C + K)
+    N = 70
+    S = (lmax + 1) ** 2
+    pos = (rng.standard_normal((N, 3)) * 3).astype(np.float32)
+    h = rng.standard_normal((N, S, C)).astype(np.float32)
+    idx = rng.integers(0, N, size=(N, K)).astype(np.int32)
+    mask = (rng.random((N, K)) < 0.6).astype(np.uint8)
+    mask[5] = 0                                          # a target with no valid slot
+    g = rng.standard_normal((N, S, C)).astype(np.float32)
+    w = proj_weights(lmax, C, seed=C + lmax, dtype=dt)
+    if dt == "bf16":
+        h, g = bf16_round(h), bf16_round(g)
+    got = gpu_backward_proj(e2f, dev, pos, h, idx, mask, H, g, w, dt)
+    ref = oracle_backward_proj(pos, h, idx, mask, H, lmax, g, w)
+    check(got, ref, lmax, dt)
+
+
+def test_backward_proj_envelope_and_order(e2f, dev):
+    """With the distance envelope, in schedule and in index order: identical bits, and
+    within tolerance of the oracle (N above the schedule threshold, so both orders differ)."""
+    lmax, C, H, K, r_env = 2, 64, 8, 32, 3.0
+    say("projected backward with the envelope, schedule vs index order")
+    rng = np.random.default_rng(77)
+    N = 2500
+    S = (lmax + 1) ** 2
+    pos = (rng.random((N, 3)) * 2.2).astype(np.float32)   # most pairs inside r_env, some not
+    h = rng.standard_normal((N, S, C)).astype(np.float32)
+    idx = rng.integers(0, N, size=(N, K)).astype(np.int32)
+    mask = (rng.random((N, K)) < 0.7).astype(np.uint8)
+    g = np.zeros((N, S, C), np.float32)
+    tg = rng.choice(N, 40, replace=False)
+    g[tg] = rng.standard_normal((tg.size, S, C)).astype(np.float32)
+    w = proj_weights(lmax, C, seed=3)
+    a = gpu_backward_proj(e2f, dev, pos, h, idx, mask, H, g, w, env_cutoff=r_env)
+    b = gpu_backward_proj(e2f, dev, pos, h, idx, mask, H, g, w, env_cutoff=r_env,
+                          targets_in_order=True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    mask_t = np.zeros_like(mask)
+    mask_t[tg] = mask[tg]
+    ref = oracle_backward_proj(pos, h, idx, mask_t, H, lmax, g, w, env_cutoff=r_env)
+    check(a, ref, lmax, "f32")
+
+
+def test_backward_proj_deterministic_and_linear(e2f, dev):
+    cfg = make_config("water")
+    s = cfg.spec
+    say("projected backward determinism, zero and doubled upstream gradients")
+    w = proj_weights(s.lmax, s.C, seed=21)
+    g = np.random.default_rng(8).standard_normal(cfg.h.shape).astype(np.float32)
+    args = (cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H)
+    a = gpu_backward_proj(e2f, dev, *args, g, w)
+    b = gpu_backward_proj(e2f, dev, *args, g, w)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    z = gpu_backward_proj(e2f, dev, *args, np.zeros_like(g), w)
+    assert all(np.all(x == 0) for x in z)
+    two = gpu_backward_proj(e2f, dev, *args, 2 * g, w)
+    assert all(np.array_equal(x, 2 * y) for x, y in zip(two, a))
+
+
+def test_backward_proj_large_sampled(e2f, dev):
+    """Large workload (N = 32,768, K = 256, C = 128): the upstream gradient lives on a few
+    targets, so the oracle needs only their edges; the weight gradients collect every
+    listed source's rows."""
+    cfg = make_config("large")
+    s = cfg.spec
+    rng = np.random.default_rng(12)
+    tg = rng.choice(cfg.N, 16, replace=False)
+    g = np.zeros(cfg.h.shape, np.float32)
+    g[tg] = rng.standard_normal((tg.size,) + cfg.h.shape[1:]).astype(np.float32)
+    w = proj_weights(s.lmax, s.C, seed=13)
+    say(f"projected backward large, gradient on {tg.size} targets")
+    got = gpu_backward_proj(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g, w)
+    mask_t = np.zeros_like(cfg.mask)
+    mask_t[tg] = cfg.mask[tg]
+    ref = oracle_backward_proj(cfg.pos, cfg.h, cfg.idx, mask_t, s.H, s.lmax, g, w)
+    touched = np.unique(np.concatenate([tg, cfg.idx[tg][cfg.mask[tg] != 0]]))
+    check([got[0][touched], got[1][touched]] + got[2:],
+          [ref[0][touched], ref[1][touched]] + list(ref[2:]), s.lmax, "f32")
+    untouched = np.setdiff1d(np.arange(cfg.N), touched)
+    assert np.all(got[0][untouched] == 0) and np.all(got[1][untouched] == 0)
