@@ -348,7 +348,8 @@ int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int
  *   bwd_workspace     e2f_attn_backward_proj_workspace_bytes(...) bytes: that
  *                     of e2f_attn_backward plus v, dv and dk, fp32 weight copies
  *                     (bf16), and the weight gradients' partial sums (one [C, C]
- *                     matrix per chunk of about 512 rows, at most 128 MiB)
+ *                     matrix per chunk of rows, chunks sized for about 4,096
+ *                     waves and at least 512 rows, at most 128 MiB in all)
  * The weight gradients are sums over chunks of rows, the chunks added in a
  * fixed order: the same bits on every run.  The products run on the matrix
  * cores for C = 16, 32, 64, 128, on the vector ALUs for other C up to 1024.

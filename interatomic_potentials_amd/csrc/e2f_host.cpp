@@ -286,9 +286,11 @@ struct BwdLayout {
   size_t total;
 };
 
-// Rows of the weight gradients' partial sums: about kDwChunk rows a chunk, at most
-// 2^25 floats of partial matrices in all (wide channel counts take longer chunks).
+// Rows of the weight gradients' partial sums: chunks sized for about kDwWaves waves
+// (chunk x output tile) over all jobs, at least kDwChunk rows, and at most 2^25 floats of
+// partial matrices in all (wide channel counts take longer chunks).
 constexpr int64_t kDwChunk = 512;
+constexpr int64_t kDwWaves = 4096;
 struct DwPlan {
   int njobs;
   int mult[e2f::kDwMaxJobs];
@@ -304,10 +306,14 @@ DwPlan dw_plan(int64_t N, int lmax, int C) {
   P.total = 0;
   int64_t cap = ((int64_t)1 << 25) / ((int64_t)C * C) / P.njobs;
   if (cap < 1) cap = 1;
+  const int64_t tpd = e2f::rows_mfma(C) ? (C < 64 ? 1 : C / 64) : (C + 15) / 16;
+  const int64_t total_rows = N * (2 + (int64_t)(lmax + 1) * (lmax + 1));
+  int64_t target = (total_rows * tpd * tpd + kDwWaves - 1) / kDwWaves;
+  if (target < kDwChunk) target = kDwChunk;
   for (int j = 0; j < P.njobs; ++j) {
     P.mult[j] = j < 2 ? 1 : 2 * (j - 2) + 1;
     P.rows[j] = N * P.mult[j];
-    int64_t chunks = (P.rows[j] + kDwChunk - 1) / kDwChunk;
+    int64_t chunks = (P.rows[j] + target - 1) / target;
     if (chunks > cap) chunks = cap;
     if (chunks < 1) chunks = 1;
     int64_t cr = (P.rows[j] + chunks - 1) / chunks;

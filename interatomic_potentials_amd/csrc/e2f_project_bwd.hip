@@ -207,6 +207,8 @@ __device__ inline int64_t dw_row(const DwJob& j, int64_t r, int64_t stride) {
   return n * stride + (r - n * j.mult) * j.C;
 }
 
+constexpr int kDwAhead = 4;   // row steps in flight per wave
+
 // TM x TM output tile a wave (TM = min(C, 64)), 4 rows per MFMA
 template <int C>
 __global__ __launch_bounds__(256) void k_dw(DwArgs a) {
@@ -233,22 +235,47 @@ __global__ __launch_bounds__(256) void k_dw(DwArgs a) {
   for (int e = 0; e < FB; ++e)
 #pragma unroll
     for (int f = 0; f < FB; ++f) acc[e][f] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t r0 = r_begin; r0 < r_end; r0 += 4) {
-    const int64_t r = r0 + g;
-    float xa[VW], yb[VW];
+  // The next row this lane fetches, r = (atom n, component m), advanced 4 rows a step
+  // without a division: the row offsets move by 4 C inside an atom and by the atom
+  // stride less mult C at each wrap (at most four wraps a step, at mult = 1).
+  int64_t r = r_begin + g;
+  int64_t n = r / J.mult;
+  int m = (int)(r - n * J.mult);
+  int64_t ox = n * J.xs + (int64_t)m * J.C + a0;
+  int64_t oy = n * J.ys + (int64_t)m * J.C + b0;
+  const int64_t wx = J.xs - (int64_t)J.mult * J.C, wy = J.ys - (int64_t)J.mult * J.C;
+  auto fetch = [&](float (&xa)[VW], float (&yb)[VW]) {
     if (r < r_end) {
-      const float* xp = J.x + dw_row(J, r, J.xs) + a0;
-      const float* yp = J.dy + dw_row(J, r, J.ys) + b0;
-      VecIO<float, VW>::load(xp, xa);
-      VecIO<float, VW>::load(yp, yb);
+      VecIO<float, VW>::load(J.x + ox, xa);
+      VecIO<float, VW>::load(J.dy + oy, yb);
     } else {
 #pragma unroll
       for (int e = 0; e < VW; ++e) xa[e] = yb[e] = 0.0f;
     }
+    r += 4;
+    m += 4;
+    ox += 4 * J.C;
+    oy += 4 * J.C;
+    while (m >= J.mult) {
+      m -= J.mult;
+      ox += wx;
+      oy += wy;
+    }
+  };
+  // kDwAhead steps of 4 rows in flight: step p of a group is used, then refilled with the
+  // step kDwAhead later
+  float xa[kDwAhead][VW], yb[kDwAhead][VW];
 #pragma unroll
-    for (int e = 0; e < FB; ++e)
+  for (int p = 0; p < kDwAhead; ++p) fetch(xa[p], yb[p]);
+  for (int64_t r0 = r_begin; r0 < r_end; r0 += 4 * kDwAhead) {
 #pragma unroll
-      for (int f = 0; f < FB; ++f) acc[e][f] = mfma4(xa[e], yb[f], acc[e][f]);
+    for (int p = 0; p < kDwAhead; ++p) {
+#pragma unroll
+      for (int e = 0; e < FB; ++e)
+#pragma unroll
+        for (int f = 0; f < FB; ++f) acc[e][f] = mfma4(xa[p][e], yb[p][f], acc[e][f]);
+      fetch(xa[p], yb[p]);
+    }
   }
   // block (e, f), element r of lane (col, g): row 4g + r of block e is column
   // VW (4g + r) + e of the tile's X side; column col of block f is VW col + f
@@ -291,8 +318,17 @@ __global__ __launch_bounds__(256) void k_dw_reduce(DwArgs a) {
   if (e >= cc || jb >= a.njobs) return;
   const DwJob& J = a.job[jb];
   const float* p = a.partial + J.part_off * cc + e;
+  // eight loads in flight, added in chunk order
   float s = 0.0f;
-  for (int c = 0; c < J.chunks; ++c) s += p[(int64_t)c * cc];
+  int c = 0;
+  for (; c + 8 <= J.chunks; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = p[(int64_t)(c + k) * cc];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += v[k];
+  }
+  for (; c < J.chunks; ++c) s += p[(int64_t)c * cc];
   J.out[e] = s;
 }
 
