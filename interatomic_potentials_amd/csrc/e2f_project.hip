@@ -117,8 +117,10 @@ __device__ inline AtomFrame<LMAX> uni(const AtomFrame<LMAX>& e) {
 __device__ inline void store_elem(float* p, float v) { *p = v; }
 __device__ inline void store_elem(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 
+// Two waves a SIMD: the weight slices, accumulators and next-tile registers fit in 256
+// registers, and the compiler is held to that (it would otherwise spill into AGPRs at C = 64).
 template <int LMAX, typename T, int C>
-__global__ __launch_bounds__(C / 16 * 64) void k_proj_eaas(ProjArgs a, EaasCoef cf) {
+__global__ __launch_bounds__(C / 16 * 64, 2) void k_proj_eaas(ProjArgs a, EaasCoef cf) {
   constexpr int S = ncomp(LMAX);
   constexpr int NT = C / 16 * 64;           // threads per workgroup
   constexpr int KG = C / 4;                 // contraction values per lane group
