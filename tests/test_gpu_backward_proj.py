@@ -178,3 +178,25 @@ def test_backward_proj_large_sampled(e2f, dev):
           [ref[0][touched], ref[1][touched]] + list(ref[2:]), s.lmax, "f32")
     untouched = np.setdiff1d(np.arange(cfg.N), touched)
     assert np.all(got[0][untouched] == 0) and np.all(got[1][untouched] == 0)
+
+
+def test_backward_proj_scaleout_sampled_bf16(e2f, dev):
+    """Scale-out workload (N = 100,000, K = 64, bf16 storage): gradient on a few targets, the
+    weights bf16; the projected forward is recomputed in fp32 from the exact widening."""
+    cfg = make_config("scaleout")
+    s = cfg.spec
+    rng = np.random.default_rng(23)
+    tg = rng.choice(cfg.N, 16, replace=False)
+    g = np.zeros(cfg.h.shape, np.float32)
+    g[tg] = bf16_round(rng.standard_normal((tg.size,) + cfg.h.shape[1:]).astype(np.float32))
+    w = proj_weights(s.lmax, s.C, seed=13, dtype="bf16")
+    say(f"projected backward scale-out bf16, gradient on {tg.size} targets")
+    got = gpu_backward_proj(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g, w, dt="bf16")
+    mask_t = np.zeros_like(cfg.mask)
+    mask_t[tg] = cfg.mask[tg]
+    ref = oracle_backward_proj(cfg.pos, cfg.h, cfg.idx, mask_t, s.H, s.lmax, g, w)
+    touched = np.unique(np.concatenate([tg, cfg.idx[tg][cfg.mask[tg] != 0]]))
+    check([got[0][touched], got[1][touched]] + got[2:],
+          [ref[0][touched], ref[1][touched]] + list(ref[2:]), s.lmax, "bf16")
+    untouched = np.setdiff1d(np.arange(cfg.N), touched)
+    assert np.all(got[0][untouched] == 0) and np.all(got[1][untouched] == 0)
