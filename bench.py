@@ -432,13 +432,27 @@ def _plain_aggregate(key):
     return False
 
 
+# storage type of each workload's step kernels (their template argument)
+WORKLOAD_STORAGE = {"scaleout": "unsigned short"}
+
+
 def step_kernel(key, workload):
-    """Whether a kernel (name with template arguments) is launched by one forward step."""
+    """Whether a kernel (name with template arguments) is launched by one forward step.
+
+    The storage type must match the workload's: with bf16 storage the backward also runs the
+    fp32 forward kernels (its recompute), which are not part of a step."""
     if workload == "eaas":
         return key.startswith("e2f::k_eaas<") and key.endswith("false>")
-    return ((key.startswith("e2f::k_eaas<") and key.endswith("true>"))
-            or key.startswith("e2f::k_sched_")
-            or (key.startswith("e2f::k_aggregate") and _plain_aggregate(key)))
+    if key.startswith("e2f::k_sched_"):
+        return True
+    if not (key.startswith("e2f::k_eaas<") and key.endswith("true>")
+            or key.startswith("e2f::k_aggregate") and _plain_aggregate(key)):
+        return False
+    storage = WORKLOAD_STORAGE.get(workload, "float")
+    if key.startswith("e2f::k_aggregate_mt<"):   # fp32 storage only
+        return storage == "float"
+    args = [x.strip() for x in key[key.index("<") + 1:key.rindex(">")].split(",")]
+    return args[2] == storage
 
 
 def committed_counters(workload):
