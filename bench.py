@@ -681,6 +681,62 @@ def bench_envelope(args, e2f, cfg, pos, h, idx, mask, ws, out, stream, k2_ms):
             "overhead_vs_plain": ms / k2_ms - 1.0}
 
 
+def bench_graph(args, e2f, dev):
+    """A launch-bound step (the water workload, 648 atoms: no schedule, two kernels) run eagerly
+    and replayed from a HIP graph captured through torch.cuda.graph; wall-clock per step over
+    back-to-back steps, and whether a replay reproduces the eager result bit for bit."""
+    import numpy as np
+    import torch
+
+    from gen import make_config
+
+    cfg = make_config("water")
+    s = cfg.spec
+    T = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    pos, h, idx, mask = T(cfg.pos), T(cfg.h), T(cfg.idx), T(cfg.mask)
+    ws = e2f.attn_precouple(pos, h)
+    out = torch.empty_like(h)
+
+    def step():
+        e2f.attn_precouple(pos, h, ws)
+        e2f.attn_aggregate(pos, idx, mask, ws, s.H, s.lmax, s.C, torch.float32, out=out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    n = max(args.steps, 100)
+
+    def wall(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n * 1e3
+
+    eager_ms = wall(step)
+    ref = out.clone()
+    graph_ms = wall(g.replay)
+    same = bool(torch.equal(out, ref))
+    print(f"[bench] graph: water step eager {eager_ms:.4f} ms, replayed {graph_ms:.4f} ms "
+          f"(wall clock, {n} steps), replay equals eager: {same}", file=sys.stderr, flush=True)
+    return {"workload": "water (648 atoms, K=64, lmax=2, C=128, H=16, fp32)",
+            "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
+            "edges_per_s_graph": cfg.nl.n_edges / (graph_ms * 1e-3),
+            "replay_equals_eager": same, "steps": n,
+            "note": "precouple + aggregate captured once with torch.cuda.graph (HIP graph), "
+                    "then replayed; wall-clock including launch"}
+
+
 def bench_eaas(args, e2f, dev):
     """The EAAS tensor product on its own (e2f_eaas_couple over 2^20 vectors), timed beside the
     dense Clebsch-Gordan contraction it replaces (e2f_dense_couple, the same product)."""
@@ -983,6 +1039,7 @@ def main(argv=None):
         result["envelope"] = bench_envelope(args, e2f, cfg, pos, h, idx, mask, ws, out, stream,
                                             k2_ms)
         result["neighbour_list"] = bench_neighbours(args, e2f, cfg, pos, stream)
+        result["graph"] = bench_graph(args, e2f, dev)
     if not args.no_backward:
         result["backward"] = bench_backward(args, e2f, cfg, pos, h, idx, mask, ws, out, stream)
     if not args.no_cpu_baseline:
