@@ -97,6 +97,11 @@ typedef enum e2f_dtype {
                                     atoms already stored in a spatially coherent order */
 #define E2F_MSG_F32 4u           /* out_msg is stored fp32 whatever the dtype (the message
                                     before any rounding to the storage type) */
+#define E2F_SHARED_ROWS 8u       /* fp32 layouts: run the kernels in which several atoms of a
+                                    wave share the rows they read whatever N.  Without it they
+                                    run above 4,096 atoms only, where N/3 waves fill the chip;
+                                    below, one atom a wave is faster.  Either way the result is
+                                    the same function, rounded in another order. */
 
 /* Name of a status code ("E2F_OK", "E2F_ERR_SHAPE", ...); never NULL. */
 const char* e2f_status_string(int status);
@@ -225,7 +230,8 @@ int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int 
  *   lse       [N, H] fp32 or NULL: also store each head's natural log-sum-exp
  *             of the logits over the valid slots (-inf with no valid slot);
  *             with out_msg, this is what e2f_attn_backward needs
- *   flags     0 or E2F_VALIDATE_INDICES | E2F_TARGETS_IN_ORDER | E2F_MSG_F32
+ *   flags     0 or E2F_VALIDATE_INDICES | E2F_TARGETS_IN_ORDER | E2F_MSG_F32 |
+ *             E2F_SHARED_ROWS
  */
 int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                        const float* pos, const int32_t* nbr_idx, const uint8_t* nbr_mask,
@@ -313,7 +319,7 @@ size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int 
  *   grad_pos    [N, 3] fp32     dL/dpos (written)
  *   bwd_workspace, bwd_ws_bytes  scratch of e2f_attn_backward_workspace_bytes
  *               (with bf16 storage it also holds the fp32 copies)
- *   flags       0 or E2F_TARGETS_IN_ORDER (index order; also taken for
+ *   flags       0 or E2F_TARGETS_IN_ORDER | E2F_SHARED_ROWS (index order; also taken for
  *               N <= 2048)
  * The result does not depend on the order of a target's slots, nor on the
  * order in which the reverse list is filled for sources listed by at most

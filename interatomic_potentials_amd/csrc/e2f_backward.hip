@@ -1053,9 +1053,10 @@ int bwd_go(const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
   const bool buf = a.N * (ncomp(L) + 1) * (int64_t)a.C * 4 < ((int64_t)1 << 32);
   hipLaunchKernelGGL((k_bwd_prep<L, V, HL>), grid_prep, dim3(256), 0, s, a, cf);
   if constexpr (V == 4 && HL > 0) {
-    // several atoms per wave sharing every row they read: the target pass for rows
-    // of at most kShareMaxK slots, the source pass when each source gets a subgroup
-    if (buf && a.N < ((int64_t)1 << 30)) {
+    // several atoms per wave sharing every row they read (enough atoms to fill the
+    // chip): the target pass for rows of at most kShareMaxK slots, the source pass
+    // when each source gets a subgroup
+    if (buf && (a.N > kMtMinAtoms || a.shared) && a.N < ((int64_t)1 << 30)) {
       if (a.K <= kShareMaxK) {
         constexpr int TQ = E ? kBqTargetsEnv : kBqTargets;
         const int64_t qb = (a.N + kBwWaves * TQ - 1) / (kBwWaves * TQ);

@@ -11,6 +11,11 @@ constexpr int kMaxLmax = 2;
 constexpr int kMaxPaths = 15;       // triangle-allowed (li, lf, lo) with all <= 2
 constexpr int kWavesPerBlock = 4;   // 256-thread workgroups of the one-target-a-wave kernels
 constexpr int kTile = 256;          // neighbour slots compacted per pass
+// Up to this many atoms the kernels that share rows between several atoms of a
+// wave launch too few waves to fill the chip (N/3 of them): one atom a wave is
+// faster there (measured crossover on MI355X, 256 CUs: about 4,096 atoms at
+// K = 256; at 1,024 atoms one a wave takes 0.044 ms against 0.147).
+constexpr int64_t kMtMinAtoms = 4096;
 constexpr int kXcds = 8;            // gfx950 (MI350 series): 8 XCDs, workgroups dealt round-robin
 constexpr int kBboxBlocks = 256;    // partial bounding boxes reduced by the schedule builder
 constexpr int kSchedMaxBits = 5;    // Morton bits per axis of the schedule grid, at most
@@ -62,6 +67,7 @@ struct AggArgs {
   float env_inv_rc;        // 1 / r_env of the distance envelope (kernels with the envelope only)
   float env_rc;            // r_env itself
   int msg_f32;             // out_msg is fp32 whatever T is
+  int shared;              // row-sharing kernels whatever N (else above kMtMinAtoms only)
 };
 
 // Backward pass (vector-Jacobian product) arguments, fp32 storage.
@@ -94,6 +100,7 @@ struct BwdArgs {
   float scale_log2e;
   float env_inv_rc;        // 1 / r_env of the distance envelope, 0 = none
   float env_rc;            // r_env itself
+  int shared;              // row-sharing kernels whatever N (else above kMtMinAtoms only)
 };
 
 // Row products of the projections' backward (fp32): values x W_V, or

@@ -985,9 +985,10 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
     }
   }
   if constexpr (sizeof(T) == 4) {
-    // fp32, 4 channels per lane, rows of at most kMtMaxK slots: several targets
-    // per wave share every row they read
-    if (V == 4 && buf && a.K <= kMtMaxK && a.N < ((int64_t)1 << 30) &&
+    // fp32, 4 channels per lane, rows of at most kMtMaxK slots, more than
+    // kMtMinAtoms targets: several targets per wave share every row they read
+    if (V == 4 && buf && a.K <= kMtMaxK && (a.N > kMtMinAtoms || a.shared) &&
+        a.N < ((int64_t)1 << 30) &&
         (a.head_lanes == 1 || a.head_lanes == 2 || a.head_lanes == 4)) {
       constexpr int TM = kMtTargets;
       constexpr int UM = kMtInflight;

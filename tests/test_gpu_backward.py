@@ -50,7 +50,8 @@ def gpu_backward(e2f, dev, pos, h, idx, mask, H, g, env_cutoff=None, **kw):
     ws = e2f.attn_precouple(p, hh)
     out, msg, lse = e2f.attn_aggregate(p, ii, mm, ws, H, int(round(h.shape[1] ** 0.5)) - 1,
                                        h.shape[2], torch.float32, return_msg=True, return_lse=True,
-                                       env_cutoff=env_cutoff)
+                                       env_cutoff=env_cutoff,
+                                       shared_rows=kw.get("shared_rows", False))
     gh, gp = e2f.attn_backward(p, hh, ii, mm, H, ws, msg, lse, T(g, dev), env_cutoff=env_cutoff,
                                **kw)
     torch.cuda.synchronize()
@@ -60,8 +61,9 @@ def gpu_backward(e2f, dev, pos, h, idx, mask, H, g, env_cutoff=None, **kw):
 @pytest.mark.parametrize("lmax,C,H,K", [(0, 16, 2, 12), (1, 16, 2, 20), (2, 32, 4, 24),
                                         (2, 128, 16, 64), (2, 64, 4, 300), (1, 8, 8, 10),
                                         (2, 128, 16, 300)])
-def test_backward_random_graphs(e2f, dev, lmax, C, H, K):
-    say(f"backward random graph: lmax={lmax} C={C} H={H} K={K}")
+@pytest.mark.parametrize("shared", [False, True])
+def test_backward_random_graphs(e2f, dev, lmax, C, H, K, shared):
+    say(f"backward random graph: lmax={lmax} C={C} H={H} K={K} shared rows {shared}")
     rng = np.random.default_rng(lmax * 31 + C + K)
     N = 80
     S = (lmax + 1) ** 2
@@ -71,19 +73,21 @@ def test_backward_random_graphs(e2f, dev, lmax, C, H, K):
     mask = (rng.random((N, K)) < 0.6).astype(np.uint8)
     mask[7] = 0                                          # a target with no valid slot
     g = rng.standard_normal((N, S, C)).astype(np.float32)
-    gh, gp, _ = gpu_backward(e2f, dev, pos, h, idx, mask, H, g)
+    gh, gp, _ = gpu_backward(e2f, dev, pos, h, idx, mask, H, g, shared_rows=shared)
     rh, rp = oracle_backward(pos, h, idx, mask, H, lmax, g)
     assert block_rel_err(gh, rh, lmax) <= TOL_F32
     assert pos_err(gp, rp) <= TOL_F32
 
 
+@pytest.mark.parametrize("shared", [False, True])
 @pytest.mark.parametrize("name", ["tiny", "water"])
-def test_backward_small_configs(e2f, dev, name):
+def test_backward_small_configs(e2f, dev, name, shared):
     cfg = make_config(name)
     s = cfg.spec
-    say(f"backward {name}: N={cfg.N} E={cfg.nl.n_edges}")
+    say(f"backward {name}: N={cfg.N} E={cfg.nl.n_edges} shared rows {shared}")
     g = np.random.default_rng(5).standard_normal(cfg.h.shape).astype(np.float32)
-    gh, gp, lse = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g)
+    gh, gp, lse = gpu_backward(e2f, dev, cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, g,
+                               shared_rows=shared)
     rh, rp = oracle_backward(cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, s.lmax, g)
     assert block_rel_err(gh, rh, s.lmax) <= TOL_F32
     assert pos_err(gp, rp) <= TOL_F32
@@ -169,9 +173,9 @@ def test_backward_sources_listed_many_times(e2f, dev, lmax, C, H, r_env):
     _, msg, lse = e2f.attn_aggregate(p, ii, mm, ws, H, lmax, C, torch.float32, return_msg=True,
                                      return_lse=True, **kw)
     res = []
-    for order in (False, True):
+    for order in (False, True):   # the shared-row passes, forced at this size
         gh, gp = e2f.attn_backward(p, hh, ii, mm, H, ws, msg, lse, T(g, dev),
-                                   targets_in_order=order, **kw)
+                                   targets_in_order=order, shared_rows=True, **kw)
         torch.cuda.synchronize()
         res.append((gh.cpu().numpy(), gp.cpu().numpy()))
     assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])

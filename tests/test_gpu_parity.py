@@ -136,12 +136,16 @@ def run_attn(e2f, dev, cfg, h=None, idx=None, mask=None, dtype=None, return_msg=
                             return_msg=return_msg, **kw)
 
 
+# shared: the kernels in which several targets of a wave share rows, forced at these sizes
+# (by default they run above 4,096 atoms only)
+@pytest.mark.parametrize("shared", [False, True])
 @pytest.mark.parametrize("name", ["tiny", "water"])
-def test_attention_small_configs_full(e2f, dev, name):
+def test_attention_small_configs_full(e2f, dev, name, shared):
     cfg = make_config(name)
     s = cfg.spec
-    say(f"attention {name}: N={cfg.N} K={s.K} lmax={s.lmax} C={s.C} H={s.H} E={cfg.nl.n_edges}")
-    out, msg = run_attn(e2f, dev, cfg, return_msg=True)
+    say(f"attention {name}: N={cfg.N} K={s.K} lmax={s.lmax} C={s.C} H={s.H} E={cfg.nl.n_edges} "
+        f"shared rows {shared}")
+    out, msg = run_attn(e2f, dev, cfg, return_msg=True, shared_rows=shared)
     ref, ref_msg = oracle_attn(cfg.pos, cfg.h, cfg.idx, cfg.mask, s.H, s.lmax, return_msg=True,
                                chunk_edges=4096)
     assert block_rel_err(to_host(msg), ref_msg, s.lmax) <= TOL_F32
@@ -181,9 +185,10 @@ def test_attention_big_configs_sampled(e2f, dev, name):
 @pytest.mark.parametrize("lmax,C,H,K", [(0, 32, 4, 10), (1, 16, 2, 32), (2, 64, 4, 300),
                                         (2, 128, 16, 64), (1, 8, 8, 7), (2, 256, 8, 40),
                                         (2, 128, 16, 300), (2, 96, 12, 300)])
-def test_attention_shapes_vs_oracle(e2f, dev, lmax, C, H, K):
+@pytest.mark.parametrize("shared", [False, True])
+def test_attention_shapes_vs_oracle(e2f, dev, lmax, C, H, K, shared):
     """Ragged sizes: K not a multiple of 64, K above one LDS tile, d = 1, 16, 32."""
-    say(f"attention shapes: lmax={lmax} C={C} H={H} K={K}")
+    say(f"attention shapes: lmax={lmax} C={C} H={H} K={K} shared rows {shared}")
     rng = np.random.default_rng(lmax * 1000 + C + K)
     N = 150
     S = (lmax + 1) ** 2
@@ -193,7 +198,7 @@ def test_attention_shapes_vs_oracle(e2f, dev, lmax, C, H, K):
     mask = (rng.random((N, K)) < 0.7).astype(np.uint8)
     mask[5] = 0                                    # a target with no valid slot
     out, msg = e2f.attn_forward(T(pos, dev), T(h, dev), T(idx, dev), T(mask, dev), H,
-                                return_msg=True)
+                                return_msg=True, shared_rows=shared)
     ref, ref_msg = oracle_attn(pos, h, idx, mask, H, lmax, return_msg=True)
     assert block_rel_err(to_host(msg), ref_msg, lmax) <= TOL_F32
     assert block_rel_err(to_host(out), ref, lmax) <= TOL_F32
@@ -235,17 +240,19 @@ def test_aggregate_with_given_values(e2f, dev):
 
 # ----------------------------------------------- integer path, bit-exact
 
-def test_mask_semantics_bit_exact(e2f, dev):
+@pytest.mark.parametrize("shared", [False, True])
+def test_mask_semantics_bit_exact(e2f, dev, shared):
     """Masked slots are never read; out-of-range indices at valid slots are skipped."""
     cfg = make_config("water")
     s = cfg.spec
-    say("mask semantics on water")
-    base = run_attn(e2f, dev, cfg).cpu()
+    say(f"mask semantics on water, shared rows {shared}")
+    kw = {"shared_rows": shared}
+    base = run_attn(e2f, dev, cfg, **kw).cpu()
     rng = np.random.default_rng(3)
     # poison every masked slot with garbage / out-of-range indices
     idx_p = np.where(cfg.mask != 0, cfg.idx, rng.integers(-2**31, 2**31 - 1, size=cfg.idx.shape)
                      ).astype(np.int32)
-    poisoned = run_attn(e2f, dev, cfg, idx=idx_p).cpu()
+    poisoned = run_attn(e2f, dev, cfg, idx=idx_p, **kw).cpu()
     assert torch.equal(base, poisoned)
     # a NaN atom that only appears behind masked slots changes nothing
     N = cfg.N
@@ -254,13 +261,13 @@ def test_mask_semantics_bit_exact(e2f, dev):
     extra_idx = np.concatenate([np.where(cfg.mask != 0, cfg.idx, N), np.zeros((1, s.K), np.int32)])
     extra_mask = np.concatenate([cfg.mask, np.zeros((1, s.K), np.uint8)])
     out = e2f.attn_forward(T(extra_pos, dev), T(extra_h, dev), T(extra_idx.astype(np.int32), dev),
-                           T(extra_mask, dev), s.H).cpu()
+                           T(extra_mask, dev), s.H, **kw).cpu()
     assert torch.equal(out[:N], base)
     assert (out[N] == 0).all()
     # all-masked targets give exact zeros
     m2 = cfg.mask.copy()
     m2[::7] = 0
-    out2 = run_attn(e2f, dev, cfg, mask=m2).cpu()
+    out2 = run_attn(e2f, dev, cfg, mask=m2, **kw).cpu()
     assert (out2[::7] == 0).all()
     # an out-of-range index at a valid slot is skipped, or reported under validation
     idx_bad = cfg.idx.copy()
@@ -268,22 +275,24 @@ def test_mask_semantics_bit_exact(e2f, dev):
     idx_bad[row, 0] = N + 5
     m3 = cfg.mask.copy()
     m3[row, 0] = 0
-    skipped = run_attn(e2f, dev, cfg, idx=idx_bad).cpu()
-    masked = run_attn(e2f, dev, cfg, mask=m3).cpu()
+    skipped = run_attn(e2f, dev, cfg, idx=idx_bad, **kw).cpu()
+    masked = run_attn(e2f, dev, cfg, mask=m3, **kw).cpu()
     assert torch.equal(skipped, masked)
     with pytest.raises(e2f.E2FError) as ei:
-        run_attn(e2f, dev, cfg, idx=idx_bad, validate=True)
+        run_attn(e2f, dev, cfg, idx=idx_bad, validate=True, **kw)
     assert ei.value.name == "E2F_ERR_INDEX"
-    ok = run_attn(e2f, dev, cfg, validate=True).cpu()
+    ok = run_attn(e2f, dev, cfg, validate=True, **kw).cpu()
     assert torch.equal(ok, base)
 
 
-def test_slot_order_and_layout_invariance(e2f, dev):
+@pytest.mark.parametrize("shared", [False, True])
+def test_slot_order_and_layout_invariance(e2f, dev, shared):
     cfg = make_config("water")
     s = cfg.spec
-    say("slot shuffle, atom permutation, run twice")
-    base = run_attn(e2f, dev, cfg).cpu()
-    again = run_attn(e2f, dev, cfg).cpu()
+    say(f"slot shuffle, atom permutation, run twice, shared rows {shared}")
+    kw = {"shared_rows": shared}
+    base = run_attn(e2f, dev, cfg, **kw).cpu()
+    again = run_attn(e2f, dev, cfg, **kw).cpu()
     assert torch.equal(base, again)                   # deterministic: no atomics
     rng = np.random.default_rng(11)
     # shuffled slots (valid slots scattered through the row): the kernel visits a
@@ -291,7 +300,7 @@ def test_slot_order_and_layout_invariance(e2f, dev):
     perm_slots = np.argsort(rng.random(cfg.idx.shape), axis=1)
     idx_s = np.take_along_axis(cfg.idx, perm_slots, 1)
     mask_s = np.take_along_axis(cfg.mask, perm_slots, 1)
-    shuf = run_attn(e2f, dev, cfg, idx=idx_s, mask=mask_s).cpu()
+    shuf = run_attn(e2f, dev, cfg, idx=idx_s, mask=mask_s, **kw).cpu()
     assert torch.equal(shuf, base)
     # atom relabelling with remapped indices: same neighbour sets, visited in
     # another order, so equal up to rounding (a wrong neighbour would be O(1))
@@ -299,7 +308,7 @@ def test_slot_order_and_layout_invariance(e2f, dev):
     inv = np.argsort(perm)
     idx_p = np.where(cfg.mask[perm] != 0, inv[np.maximum(cfg.idx[perm], 0)], -1).astype(np.int32)
     out_p = e2f.attn_forward(T(cfg.pos[perm], dev), T(cfg.h[perm], dev), T(idx_p, dev),
-                             T(cfg.mask[perm], dev), s.H).cpu()
+                             T(cfg.mask[perm], dev), s.H, **kw).cpu()
     assert block_rel_err(to_host(out_p), to_host(base[torch.from_numpy(perm)]), s.lmax) <= 1e-5
 
 
@@ -403,7 +412,8 @@ def test_targets_sharing_a_wave_stay_independent(e2f, dev):
     idx_nan[1, free] = N                             # only target 1 lists the NaN atom
     mask_nan[1, free] = 1
     run = lambda i, m: e2f.attn_forward(T(pos, dev), T(h, dev), T(i, dev), T(m, dev), s.H,
-                                        targets_in_order=True).cpu()  # noqa: E731
+                                        targets_in_order=True,
+                                        shared_rows=True).cpu()  # noqa: E731
     with_nan = run(idx_nan, mask_nan)
     without = run(idx, mask)
     others = np.setdiff1d(np.arange(N + 1), [1])
