@@ -500,3 +500,25 @@ def test_backward_proj_argument_errors():
     assert _bproj(flags=4) == C["E2F_ERR_SHAPE"]
     assert _bproj(C=2048) == C["E2F_ERR_UNSUPPORTED"]
     assert _bproj(C=96, H=6, wq=None) == C["E2F_ERR_NULL"]    # vector-ALU widths are served
+
+
+@pytest.mark.parametrize("N,C,H", [(1000, 128, 16), (100000, 128, 16), (50000, 256, 16),
+                                   (7, 16, 2)])
+def test_backward_proj_workspace_bounds(N, C, H):
+    """The projected backward's extra scratch: v and dv ([N, S, C] fp32), dk ([N, C]), and the
+    weight gradients' partial sums, at least one [C, C] matrix per weight and at most 2^25 floats
+    in all (plus one matrix per weight when the cap leaves a job a single chunk)."""
+    wb = lib.e2f_attn_backward_proj_workspace_bytes
+    plain = lib.e2f_attn_backward_workspace_bytes(N, 64, 2, C, H, 0)
+    extra = wb(N, 64, 2, C, H, 0) - plain
+    rows = (2 * 9 + 1) * N * C * 4
+    parts = extra - rows
+    jobs = 5
+    assert parts >= jobs * C * C * 4 - 5 * 256
+    assert parts <= max(4 << 25, jobs * C * C * 4) + 8 * 256
+
+
+def test_backward_proj_needs_an_fp32_lane_width():
+    # C = 1024 projects, but the backward's passes have no fp32 lane layout for it
+    assert lib.e2f_attn_backward_proj_workspace_bytes(1000, 64, 2, 1024, 16, 0) == 0
+    assert _bproj(C=1024, H=16) == C["E2F_ERR_UNSUPPORTED"]
