@@ -323,7 +323,7 @@ size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int 
  *               N <= 2048)
  * The result does not depend on the order of a target's slots, nor on the
  * order in which the reverse list is filled for sources listed by at most
- * 1024 targets (each source's list is sorted before it is summed).
+ * 16,384 targets (each source's list is sorted before it is summed).
  */
 int e2f_attn_backward(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                       const float* pos, const void* h, const int32_t* nbr_idx,

@@ -28,8 +28,8 @@
 //               reverse lists (sources listed at most kSrcShareMaxL times)
 // The reverse list is a CSR built with a count, a scan and a fill (atomics
 // aggregated in LDS per group of spatially adjacent targets); the per-source
-// sort makes the summation order independent of the fill order for sources
-// listed by up to kRevTile targets.  Rows are read through buffer resources
+// sort makes the summation order independent of the fill order (lists longer
+// than kRevTile, read in tiles, are sorted whole first, up to kRevSortMax).  Rows are read through buffer resources
 // (32-bit offsets) when the row arrays fit 4 GiB.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -991,6 +991,57 @@ __global__ __launch_bounds__(256) void k_rev_pass(int64_t N, int K, int per, con
   }
 }
 
+// Sources listed by more than kRevTile targets: their lists are read in tiles of
+// kRevTile in list order, so the fill's (atomic, run-dependent) order would leak
+// into the summation order.  Each workgroup checks 256 sources; every long list
+// among them (up to kRevSortMax entries) is sorted ascending by the whole
+// workgroup in LDS (bitonic), so that the tiles are consecutive runs of the
+// sorted list and the sums depend on the graph alone.
+constexpr int kRevSortMax = 16384;
+
+__global__ __launch_bounds__(256) void k_rev_sort_long(int64_t N, const int32_t* off,
+                                                       int32_t* entries) {
+  __shared__ int32_t s_key[kRevSortMax];
+  __shared__ int32_t s_long[256];
+  __shared__ int s_nlong;
+  const int t = threadIdx.x;
+  const int64_t j = (int64_t)blockIdx.x * 256 + t;
+  if (t == 0) s_nlong = 0;
+  __syncthreads();
+  if (j < N) {
+    const int len = off[j + 1] - off[j];
+    if (len > kRevTile && len <= kRevSortMax) s_long[atomicAdd(&s_nlong, 1)] = (int32_t)j;
+  }
+  __syncthreads();
+  const int nl = s_nlong;
+  for (int q = 0; q < nl; ++q) {   // uniform: every thread reads the same count
+    const int32_t src = s_long[q];
+    const int beg = off[src], len = off[src + 1] - beg;
+    int n2 = 1;
+    while (n2 < len) n2 <<= 1;
+    for (int e = t; e < n2; e += 256) s_key[e] = e < len ? entries[beg + e] : 0x7fffffff;
+    __syncthreads();
+    for (int kk = 2; kk <= n2; kk <<= 1) {
+      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+        for (int e = t; e < n2; e += 256) {
+          const int p = e ^ jj;
+          if (p > e) {
+            const int32_t a = s_key[e], b = s_key[p];
+            const bool up = (e & kk) == 0;
+            if ((a > b) == up) {
+              s_key[e] = b;
+              s_key[p] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int e = t; e < len; e += 256) entries[beg + e] = s_key[e];
+    __syncthreads();   // s_key is rewritten for the next long list
+  }
+}
+
 // exclusive scan, pass 1: each 1024-thread block scans kScanTile elements in place
 __global__ __launch_bounds__(1024) void k_scan_tiles(int64_t n, int32_t* a, int32_t* tile_sums) {
   __shared__ int32_t part[16];
@@ -1136,6 +1187,7 @@ int launch_reverse_list(int64_t N, int K, const int32_t* idx, const uint8_t* mas
   if (st != 0) return st;
   hipLaunchKernelGGL(k_rev_pass<true>, dim3(gr), dim3(256), 0, s, N, K, per, idx, mask, sched,
                      cur, entries);
+  hipLaunchKernelGGL(k_rev_sort_long, dim3(gn), dim3(256), 0, s, N, off, entries);
   return last_err();
 }
 

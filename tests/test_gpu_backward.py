@@ -251,3 +251,28 @@ def test_backward_scaleout_sampled_bf16(e2f, dev, envelope):
     assert pos_err(gp[touched], rp[touched]) <= TOL_BF16
     untouched = np.setdiff1d(np.arange(cfg.N), touched)
     assert np.all(gh[untouched] == 0) and np.all(gp[untouched] == 0)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_backward_long_reverse_list_reproducible(e2f, dev, shared):
+    """A source listed by every one of 3,000 targets: its reverse list, filled in an order that
+    depends on the visiting order, is sorted whole before it is summed, so the schedule and index
+    orders (different fills) give the same bits, within tolerance of the oracle."""
+    lmax, C, H, K = 2, 32, 4, 8
+    say(f"backward, a source listed 3,000 times, shared rows {shared}")
+    rng = np.random.default_rng(41)
+    N = 3000
+    S = (lmax + 1) ** 2
+    pos = (rng.random((N, 3)) * 30).astype(np.float32)
+    h = rng.standard_normal((N, S, C)).astype(np.float32)
+    idx = rng.integers(1, N, size=(N, K)).astype(np.int32)
+    mask = (rng.random((N, K)) < 0.7).astype(np.uint8)
+    idx[:, 0] = 0                                        # every target lists source 0
+    mask[:, 0] = 1
+    g = rng.standard_normal((N, S, C)).astype(np.float32)
+    res = [gpu_backward(e2f, dev, pos, h, idx, mask, H, g, targets_in_order=order,
+                        shared_rows=shared)[:2] for order in (False, True)]
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+    rh, rp = oracle_backward(pos, h, idx, mask, H, lmax, g)
+    assert block_rel_err(res[0][0], rh, lmax) <= TOL_F32
+    assert pos_err(res[0][1], rp) <= TOL_F32
