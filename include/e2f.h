@@ -102,6 +102,9 @@ typedef enum e2f_dtype {
                                     run above 4,096 atoms only, where N/3 waves fill the chip;
                                     below, one atom a wave is faster.  Either way the result is
                                     the same function, rounded in another order. */
+#define E2F_MATRIX_TILES 16u     /* the 16-atom matrix-core aggregate whatever N, where its
+                                    layout is served (fp32, C = 128, H = 16, K <= 256, no
+                                    envelope); ignored elsewhere and under E2F_SHARED_ROWS */
 
 /* Name of a status code ("E2F_OK", "E2F_ERR_SHAPE", ...); never NULL. */
 const char* e2f_status_string(int status);
@@ -231,7 +234,7 @@ int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int 
  *             of the logits over the valid slots (-inf with no valid slot);
  *             with out_msg, this is what e2f_attn_backward needs
  *   flags     0 or E2F_VALIDATE_INDICES | E2F_TARGETS_IN_ORDER | E2F_MSG_F32 |
- *             E2F_SHARED_ROWS
+ *             E2F_SHARED_ROWS | E2F_MATRIX_TILES
  */
 int e2f_attn_aggregate(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, int dtype,
                        const float* pos, const int32_t* nbr_idx, const uint8_t* nbr_mask,
@@ -319,8 +322,8 @@ size_t e2f_attn_backward_workspace_bytes(int64_t N, int K, int lmax, int C, int 
  *   grad_pos    [N, 3] fp32     dL/dpos (written)
  *   bwd_workspace, bwd_ws_bytes  scratch of e2f_attn_backward_workspace_bytes
  *               (with bf16 storage it also holds the fp32 copies)
- *   flags       0 or E2F_TARGETS_IN_ORDER | E2F_SHARED_ROWS (index order; also taken for
- *               N <= 2048)
+ *   flags       0 or E2F_TARGETS_IN_ORDER | E2F_SHARED_ROWS | E2F_MATRIX_TILES (index
+ *               order, also taken for N <= 2048; the kernels of a recomputed forward)
  * The result does not depend on the order of a target's slots, nor on the
  * order in which the reverse list is filled for sources listed by at most
  * 16,384 targets (each source's list is sorted before it is summed).

@@ -35,6 +35,7 @@ VALIDATE_INDICES = 1
 TARGETS_IN_ORDER = 2
 MSG_F32 = 4
 SHARED_ROWS = 8
+MATRIX_TILES = 16
 
 _STATUS = {
     0: "E2F_OK", -1: "E2F_ERR_NULL", -2: "E2F_ERR_SHAPE", -3: "E2F_ERR_DTYPE",
@@ -154,9 +155,10 @@ def path_count(lmax: int) -> int:
 
 
 def _flags(validate: bool, targets_in_order: bool, msg_f32: bool = False,
-           shared_rows: bool = False) -> int:
+           shared_rows: bool = False, matrix_tiles: bool = False) -> int:
     return ((VALIDATE_INDICES if validate else 0) | (TARGETS_IN_ORDER if targets_in_order else 0)
-            | (MSG_F32 if msg_f32 else 0) | (SHARED_ROWS if shared_rows else 0))
+            | (MSG_F32 if msg_f32 else 0) | (SHARED_ROWS if shared_rows else 0)
+            | (MATRIX_TILES if matrix_tiles else 0))
 
 
 def _check(code: int, where: str) -> None:
@@ -373,7 +375,7 @@ def attn_aggregate(pos, nbr_idx, nbr_mask, ws, heads: int, lmax: int, C: int, dt
                    return_msg: bool = False, validate: bool = False,
                    targets_in_order: bool = False, return_lse: bool = False,
                    env_cutoff: Optional[float] = None, msg_f32: bool = False,
-                   shared_rows: bool = False):
+                   shared_rows: bool = False, matrix_tiles: bool = False):
     """Steps 2-3 from a filled workspace; returns out, or (out[, m][, lse]) when asked.
 
     ``env_cutoff`` = r_env switches on the smooth distance envelope of the weights;
@@ -405,7 +407,8 @@ def attn_aggregate(pos, nbr_idx, nbr_mask, ws, heads: int, lmax: int, C: int, dt
                                   float(env_cutoff or 0.0), _ptr(pw),
                                   _ptr(ws), _nbytes(ws), _ptr(out), _ptr(msg),
                                   _ptr(lse),
-                                  _flags(validate, targets_in_order, msg_f32, shared_rows)),
+                                  _flags(validate, targets_in_order, msg_f32, shared_rows,
+                                         matrix_tiles)),
            "e2f_attn_aggregate")
     return _results(out, msg, lse)
 
@@ -414,14 +417,15 @@ def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] =
                  path_w=None, ws=None, out=None, return_msg: bool = False,
                  validate: bool = False, targets_in_order: bool = False,
                  return_lse: bool = False, proj=None, env_cutoff: Optional[float] = None,
-                 shared_rows: bool = False):
+                 shared_rows: bool = False, matrix_tiles: bool = False):
     """Full path (steps 1-3): pos [N,3] fp32, h [N,S,C], nbr_idx [N,K] int32, nbr_mask [N,K] uint8.
 
     Returns out, or (out[, m][, lse]) when return_msg / return_lse ask for them.
     ``proj`` = (w_q, w_k, w_v) adds the learned projections (see attn_precouple);
     ``env_cutoff`` = r_env the smooth distance envelope of the weights;
     ``shared_rows`` runs the kernels in which several targets of a wave share rows at any N
-    (E2F_SHARED_ROWS; by default above 4,096 atoms only).
+    (E2F_SHARED_ROWS; by default above 4,096 atoms only); ``matrix_tiles`` the 16-target
+    matrix-core aggregate at any N where it serves the layout (E2F_MATRIX_TILES).
     """
     torch = _torch()
     N, S, C = _dims(h)
@@ -452,7 +456,8 @@ def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] =
                                     float(env_cutoff or 0.0), _ptr(pw),
                                     _ptr(ws), _nbytes(ws), _ptr(out), _ptr(msg),
                                     _ptr(lse),
-                                    _flags(validate, targets_in_order, shared_rows=shared_rows)),
+                                    _flags(validate, targets_in_order, shared_rows=shared_rows,
+                                           matrix_tiles=matrix_tiles)),
                "e2f_attn_forward")
     else:
         _check(lib.e2f_attn_forward_proj(_stream(h), N, K, lmax, C, heads, dt, _ptr(pos), _ptr(h),
@@ -462,7 +467,8 @@ def attn_forward(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[float] =
                                          _nbytes(ws), _ptr(out), _ptr(msg),
                                          _ptr(lse),
                                          _flags(validate, targets_in_order,
-                                                shared_rows=shared_rows)),
+                                                shared_rows=shared_rows,
+                                                matrix_tiles=matrix_tiles)),
                "e2f_attn_forward_proj")
     return _results(out, msg, lse)
 
@@ -476,7 +482,7 @@ def attn_forward_noalloc(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[
                          path_w=None, out=None, return_msg: bool = False,
                          validate: bool = False, targets_in_order: bool = False,
                          return_lse: bool = False, env_cutoff: Optional[float] = None,
-                         shared_rows: bool = False):
+                         shared_rows: bool = False, matrix_tiles: bool = False):
     """attn_forward with the library's static per-GPU workspace instead of a caller's one.
 
     The library call allocates nothing; pass ``out`` (and use no return_msg / return_lse)
@@ -505,7 +511,8 @@ def attn_forward_noalloc(pos, h, nbr_idx, nbr_mask, heads: int, scale: Optional[
                                         float(env_cutoff or 0.0), _ptr(pw), _ptr(out), _ptr(msg),
                                         _ptr(lse),
                                         _flags(validate, targets_in_order,
-                                               shared_rows=shared_rows)),
+                                               shared_rows=shared_rows,
+                                               matrix_tiles=matrix_tiles)),
            "e2f_attn_forward_noalloc")
     return _results(out, msg, lse)
 
@@ -523,7 +530,7 @@ def attn_backward_proj_workspace_bytes(N: int, K: int, lmax: int, C: int, H: int
 def attn_backward(pos, h, nbr_idx, nbr_mask, heads: int, ws, msg, lse, grad_out,
                   scale: Optional[float] = None, path_w=None, targets_in_order: bool = False,
                   bwd_ws=None, grad_h=None, grad_pos=None, env_cutoff: Optional[float] = None,
-                  proj=None, shared_rows: bool = False):
+                  proj=None, shared_rows: bool = False, matrix_tiles: bool = False):
     """(dL/dh, dL/dpos) for L = <grad_out, out>; ws, msg, lse from the forward.
 
     With bf16 storage the library recomputes the message and the log-sum-exp in fp32, so
@@ -564,7 +571,7 @@ def attn_backward(pos, h, nbr_idx, nbr_mask, heads: int, ws, msg, lse, grad_out,
                  grad_out=grad_out, bwd_ws=bwd_ws, grad_h=grad_h, grad_pos=grad_pos)
     pw = _path_w(path_w, h.device)
     flags = ((TARGETS_IN_ORDER if targets_in_order else 0)
-             | (SHARED_ROWS if shared_rows else 0))
+             | (SHARED_ROWS if shared_rows else 0) | (MATRIX_TILES if matrix_tiles else 0))
     if w is not None:
         gw = (torch.empty((C, C), dtype=torch.float32, device=h.device),
               torch.empty((C, C), dtype=torch.float32, device=h.device),

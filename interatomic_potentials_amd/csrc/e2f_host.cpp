@@ -432,7 +432,8 @@ int check_attn_shape(int64_t N, int K, int lmax, int C, int H, int dt, uint32_t 
   const int st = check_shape_common(N, lmax, C, dt);
   if (st != E2F_OK) return st;
   if (K < 1 || H < 1 || C % H != 0) return E2F_ERR_SHAPE;
-  if (flags & ~(E2F_VALIDATE_INDICES | E2F_TARGETS_IN_ORDER | E2F_MSG_F32 | E2F_SHARED_ROWS))
+  if (flags & ~(E2F_VALIDATE_INDICES | E2F_TARGETS_IN_ORDER | E2F_MSG_F32 | E2F_SHARED_ROWS |
+                E2F_MATRIX_TILES))
     return E2F_ERR_SHAPE;
   if (attn_width(C, H, dt) == 0 && C > e2f::kGenericMaxC) return E2F_ERR_UNSUPPORTED;
   return E2F_OK;
@@ -511,8 +512,11 @@ int aggregate_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H,
   a.env_rc = env_cutoff > 0.0f ? env_cutoff : 0.0f;
   a.msg_f32 = (flags & E2F_MSG_F32) ? 1 : 0;
   a.shared = (flags & E2F_SHARED_ROWS) ? 1 : 0;
+  a.tile = (flags & E2F_MATRIX_TILES) ? 1 : 0;
   const EaasCoef cf = make_coef(lmax, path_w);
   if (V == 0) return hip_status(e2f::launch_aggregate_generic(lmax, dt, a, cf, stream));
+  if (!a.shared && a.tile && e2f::tile_supported(lmax, dt, a))
+    return hip_status(e2f::launch_aggregate_tile(lmax, a, cf, stream));
   return hip_status(e2f::launch_aggregate(lmax, dt, V, a, cf, stream));
 }
 
@@ -935,7 +939,7 @@ int backward_impl(hipStream_t stream, int64_t N, int K, int lmax, int C, int H, 
     if (st == E2F_OK)
       st = aggregate_impl(stream, N, K, lmax, C, H, E2F_F32, pos, nbr_idx, nbr_mask, scale,
                           env_cutoff, path_w, ws32, out32, msg32, lse32,
-                          flags & (E2F_TARGETS_IN_ORDER | E2F_SHARED_ROWS));
+                          flags & (E2F_TARGETS_IN_ORDER | E2F_SHARED_ROWS | E2F_MATRIX_TILES));
     if (st != E2F_OK) return st;
     a.h = h32;
     a.ws = static_cast<const float*>(ws32);

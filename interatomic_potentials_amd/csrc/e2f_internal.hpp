@@ -68,6 +68,7 @@ struct AggArgs {
   float env_rc;            // r_env itself
   int msg_f32;             // out_msg is fp32 whatever T is
   int shared;              // row-sharing kernels whatever N (else above kMtMinAtoms only)
+  int tile;                // the 16-target matrix-core kernel whatever N, where it serves the layout
 };
 
 // Backward pass (vector-Jacobian product) arguments, fp32 storage.
@@ -169,6 +170,11 @@ int launch_eaas(int lmax, int dtype, int V, bool to_workspace, const EaasArgs& a
                 const EaasCoef& cf, hipStream_t s);
 int launch_aggregate(int lmax, int dtype, int V, const AggArgs& a, const EaasCoef& cf,
                      hipStream_t s);
+// the 16-target matrix-core aggregate (its own file): fp32, C = 128, H = 16, rows of at most
+// kTileMaxK slots, no envelope
+constexpr int kTileMaxK = 256;
+bool tile_supported(int lmax, int dtype, const AggArgs& a);
+int launch_aggregate_tile(int lmax, const AggArgs& a, const EaasCoef& cf, hipStream_t s);
 // the aggregate for any layout with C % H == 0 and C <= kGenericMaxC (its own file): one
 // target a wave, lane l owning channels l + 64 k, per-head sums through LDS
 constexpr int kGenericMaxC = 512;

@@ -143,9 +143,10 @@ def test_attention_argument_errors(fn):
     assert fn(C=512, H=4, out=None) == C["E2F_ERR_NULL"]         # fp32, 512 channels
     assert fn(C=1024, H=8) == C["E2F_ERR_UNSUPPORTED"]           # wider rows
     assert fn(C=1024, H=8, dt=1) == C["E2F_ERR_UNSUPPORTED"]
-    assert fn(flags=16) == C["E2F_ERR_SHAPE"]                 # unknown flag bit
+    assert fn(flags=32) == C["E2F_ERR_SHAPE"]                 # unknown flag bit
     assert fn(flags=4, out=None) == C["E2F_ERR_NULL"]         # E2F_MSG_F32 is known
     assert fn(flags=8, out=None) == C["E2F_ERR_NULL"]         # E2F_SHARED_ROWS too
+    assert fn(flags=16, out=None) == C["E2F_ERR_NULL"]        # E2F_MATRIX_TILES too
     assert fn(N=0, pos=None, idx=None, mask=None, ws=None, out=None) == C["E2F_OK"]
     assert fn(pos=None) == C["E2F_ERR_NULL"]
     assert fn(idx=None) == C["E2F_ERR_NULL"]
@@ -242,8 +243,9 @@ def test_backward_argument_errors():
     assert _bwd(K=0) == C["E2F_ERR_SHAPE"]
     assert _bwd(flags=1) == C["E2F_ERR_SHAPE"]               # no index validation here
     assert _bwd(flags=4) == C["E2F_ERR_SHAPE"]               # nor a message dtype flag
-    assert _bwd(flags=16) == C["E2F_ERR_SHAPE"]              # nor an unknown bit
+    assert _bwd(flags=32) == C["E2F_ERR_SHAPE"]              # nor an unknown bit
     assert _bwd(flags=8, gh=None) == C["E2F_ERR_NULL"]       # E2F_SHARED_ROWS is known
+    assert _bwd(flags=16, gh=None) == C["E2F_ERR_NULL"]      # so is E2F_MATRIX_TILES
     assert _bwd(N=0, pos=None, h=None) == C["E2F_OK"]
     for name in ("pos", "h", "idx", "mask", "ws", "msg", "lse", "gout", "gh", "gp", "bws"):
         assert _bwd(**{name: None}) == C["E2F_ERR_NULL"], name
