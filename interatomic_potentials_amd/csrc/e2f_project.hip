@@ -137,7 +137,12 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_proj_eaas(ProjArgs a, EaasCo
 
   __shared__ __align__(16) T sa[TA * PA];
   __shared__ __align__(16) float sv[TA * PV];
-  __shared__ AtomFrame<LMAX> sf[TA];
+  // frames of FB consecutive tiles of this workgroup: computed by one wave's lanes at
+  // once every FB tiles (the computation is a long dependent chain, so 64 frames take
+  // hardly longer than 16); two tiles where the tiles' own LDS is largest (fp32, C = 128)
+  constexpr int FB = (sizeof(T) == 4 && C >= 128) ? 2 : 4;
+  static_assert(FB * TA <= 64, "one wave computes a batch");
+  __shared__ AtomFrame<LMAX> sf[FB * TA];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -182,7 +187,8 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_proj_eaas(ProjArgs a, EaasCo
       buf[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + p * NT) * 16, 0, 0);
   };
   if (AHEAD && (int64_t)blockIdx.x < ntiles) fetch(blockIdx.x);
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  int kb = 0;   // this tile's place in its batch of FB frame tiles
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x, kb = (kb + 1) % FB) {
     const int64_t a0 = tile * TA;
     const int na = (int)(a.n - a0 < TA ? a.n - a0 : TA);
 
@@ -232,35 +238,57 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_proj_eaas(ProjArgs a, EaasCo
       for (int s = 0; s < S; ++s) sv[i * PV + s * C + c0 + col] = acc[s][r];
     }
     if (AHEAD && tile + gridDim.x < ntiles) fetch(tile + gridDim.x);
-    // the tile's frames, once per atom (sf was last read in step 4 of the
-    // previous tile, before this tile's first barrier)
-    if (tid < na) {
-      const int64_t atom = a0 + tid;
-      AtomFrame<LMAX> e;
-      e.f = make_frame(a.r[3 * atom], a.r[3 * atom + 1], a.r[3 * atom + 2]);
-      e.d = make_dy2(e.f);
-      e.R = make_reindex<LMAX>(cf, e.f);
-      sf[tid] = e;
+    // the frames of this tile and the next FB - 1 of the workgroup, once per atom, at
+    // the first tile of each batch (sf was last read in step 4 of the previous tile,
+    // before this tile's first barrier)
+    if (kb == 0 && tid < FB * TA) {
+      const int64_t ft = tile + (int64_t)(tid / TA) * gridDim.x;
+      const int64_t atom = ft * TA + tid % TA;
+      if (ft < ntiles && atom < a.n) {
+        AtomFrame<LMAX> e;
+        e.f = make_frame(a.r[3 * atom], a.r[3 * atom + 1], a.r[3 * atom + 2]);
+        e.d = make_dy2(e.f);
+        e.R = make_reindex<LMAX>(cf, e.f);
+        sf[tid] = e;
+      }
     }
     __syncthreads();
+    const AtomFrame<LMAX>* tf = sf + kb * TA;   // this tile's frames
 
     // 4. EAAS per (atom, channel); stores coalesced along the channels
     if constexpr (C % 64 == 0) {
       // a wave takes whole atoms: their table entries go to scalar registers
-      // (the weight slices fill the vector file)
+      // (the weight slices fill the vector file).  Lane l owns the VPL adjacent
+      // channels VPL l .. VPL l + VPL - 1, so each component is one LDS read and
+      // one store of VPL values a lane.
       constexpr int NW = NT / 64;
+      constexpr int VPL = C / 64;
+      static_assert(VPL == 1 || VPL == 2, "64 or 128 channels");
+      const int c0 = lane * VPL;
       for (int i = tid >> 6; i < na; i += NW) {
-        const AtomFrame<LMAX> e = uni<LMAX>(sf[i]);
+        const AtomFrame<LMAX> e = uni<LMAX>(tf[i]);
         const int64_t atom = a0 + i;
-        T* dst = ws + atom * (int64_t)((S + 1) * C) + C;
+        T* dst = ws + atom * (int64_t)((S + 1) * C) + C + c0;
+        float x[VPL][S], y[VPL][S];
 #pragma unroll
-        for (int c = lane; c < C; c += 64) {
-          float x[S], y[S];
+        for (int s = 0; s < S; ++s) {
+          const float* src = &sv[i * PV + s * C + c0];
+          if constexpr (VPL == 2) {
+            const float2 v = *reinterpret_cast<const float2*>(src);
+            x[0][s] = v.x;
+            x[1][s] = v.y;
+          } else {
+            x[0][s] = src[0];
+          }
+        }
 #pragma unroll
-          for (int s = 0; s < S; ++s) x[s] = sv[i * PV + s * C + c];
-          eaas_channel<LMAX>(x, y, e.f, e.d, e.R);
+        for (int v = 0; v < VPL; ++v) eaas_channel<LMAX>(x[v], y[v], e.f, e.d, e.R);
 #pragma unroll
-          for (int s = 0; s < S; ++s) store_elem(dst + s * C + c, y[s]);
+        for (int s = 0; s < S; ++s) {
+          float o[VPL];
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) o[v] = y[v][s];
+          VecIO<T, VPL>::store(dst + s * C, o);
         }
       }
     } else {
@@ -269,7 +297,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_proj_eaas(ProjArgs a, EaasCo
         const int c = p - i * C;
         if (i >= na) break;
         const int64_t atom = a0 + i;
-        const AtomFrame<LMAX> e = sf[i];
+        const AtomFrame<LMAX> e = tf[i];
         float x[S], y[S];
 #pragma unroll
         for (int s = 0; s < S; ++s) x[s] = sv[i * PV + s * C + c];
