@@ -260,3 +260,46 @@ def test_tile_flag_ignored_where_not_served(e2f, dev):
                          matrix_tiles=True).cpu()
     b = e2f.attn_forward(T(pos, dev), T(h, dev), T(idx, dev), T(mask, dev), hd).cpu()
     assert torch.equal(a, b)
+
+
+def test_tile_allocation_free_entry_point(e2f, dev):
+    """The static-workspace entry point runs the same kernel: the same bits, twice in a row."""
+    cfg = make_config("water")
+    s = cfg.spec
+    say("matrix tiles through the allocation-free entry point")
+    args = (T(cfg.pos, dev), T(cfg.h, dev), T(cfg.idx, dev), T(cfg.mask, dev), s.H)
+    ref = e2f.attn_forward(*args, matrix_tiles=True)
+    for _ in range(2):
+        got = e2f.attn_forward_noalloc(*args, matrix_tiles=True)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref)
+
+
+def test_tile_graph_replay(e2f, dev):
+    """The forward with matrix tiles captured in a HIP graph, replayed on new values."""
+    cfg = make_config("water")
+    s = cfg.spec
+    say("matrix tiles: graph capture and replay")
+    pos, h, idx, mask = T(cfg.pos, dev), T(cfg.h, dev), T(cfg.idx, dev), T(cfg.mask, dev)
+
+    def step():
+        return e2f.attn_forward(pos, h, idx, mask, s.H, matrix_tiles=True)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = step()
+    rng = np.random.default_rng(4)
+    for _ in range(3):
+        h.copy_(T(rng.standard_normal(cfg.h.shape).astype(np.float32), dev))
+        g.replay()
+        torch.cuda.synchronize()
+        eager = step()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
