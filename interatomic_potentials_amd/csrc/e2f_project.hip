@@ -30,6 +30,11 @@
 //     components and stores the h' rows, consecutive threads on consecutive
 //     channels.  With C a multiple of 64 a wave takes whole atoms, and holds
 //     the atom's table entry in scalar registers.
+// Where the registers allow (every layout but fp32 with C = 128, whose weight
+// slices fill the vector file), step 2 runs with the operands swapped,
+// D = W^T h^T: each lane then ends with four consecutive output channels of
+// one atom, all S components, so steps 3 and 4 run from the accumulators with
+// the atom's table entry, without the value rows' trip through LDS.
 // Channel counts this kernel is not built for (any other C up to kProjMaxC)
 // take a plain vector-ALU kernel, k_proj_generic, with the same arithmetic
 // order per output (input channels in order, fp32 accumulation).
@@ -131,12 +136,18 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_proj_eaas(ProjArgs a, EaasCo
   constexpr int PA = S * C + 16 / (int)sizeof(T);   // LDS pitch of an h row block (elements)
   constexpr int PV = S * C + 4;                     // LDS pitch of a value row block (floats)
   constexpr int CPA = S * C * (int)sizeof(T) / 16;  // 16-byte chunks per atom
+  // Where registers allow (all but fp32 with C = 128, whose weight slices fill the vector
+  // file), the products run transposed so that each lane ends with whole (atom, channel)
+  // columns, and the coupling runs from registers; there the next tile's rows are loaded
+  // ahead too.
+  constexpr bool TRANS = !(sizeof(T) == 4 && C >= 128);
   constexpr int PER = (TA * CPA + NT - 1) / NT;     // chunks per thread
   static_assert(KG % KPL == 0, "channel count does not fit the MFMA shape");
   using Frag = typename Mma<T>::Frag;
 
   __shared__ __align__(16) T sa[TA * PA];
-  __shared__ __align__(16) float sv[TA * PV];
+  // value rows through LDS on the path that keeps the original MFMA layout (fp32, C = 128)
+  __shared__ __align__(16) float sv[TRANS ? 1 : TA * PV];
   // frames of FB consecutive tiles of this workgroup: computed by one wave's lanes at
   // once every FB tiles (the computation is a long dependent chain, so 64 frames take
   // hardly longer than 16); two tiles where the tiles' own LDS is largest (fp32, C = 128)
@@ -175,7 +186,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_proj_eaas(ProjArgs a, EaasCo
   // leave no registers for it: there the loads are issued at the tile's start.
   // The buffer range ends at the tile's last atom, so reads past it (a partial
   // last tile) return zeros without a branch.
-  constexpr bool AHEAD = !(sizeof(T) == 4 && C >= 128);
+  constexpr bool AHEAD = TRANS;
   v4u buf[PER];
   auto fetch = [&](int64_t t) {
     const int64_t b0 = t * TA;
@@ -205,106 +216,172 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_proj_eaas(ProjArgs a, EaasCo
     }
     __syncthreads();
 
-    // 2. products: acc[s] = v rows, acc[S] = q, acc[S + 1] = k
-    v4f acc[S + 2];
+    if constexpr (TRANS) {
+      // 2. products with the operands swapped (D = W^T h^T): lane (col, g) ends with
+      //    output channels c0 + 4g + r (r < 4) of atom col; acc[s] = value row s,
+      //    acc[S] = q, acc[S + 1] = k
+      v4f acc[S + 2];
 #pragma unroll
-    for (int s = 0; s < S + 2; ++s) acc[s] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int s = 0; s < S + 2; ++s) acc[s] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int l = s < 1 ? 0 : (s < 4 ? 1 : 2);
-      const T* arow = sa + col * PA + s * C + g * KG;
+      for (int s = 0; s < S; ++s) {
+        const int l = s < 1 ? 0 : (s < 4 ? 1 : 2);
+        const T* arow = sa + col * PA + s * C + g * KG;
 #pragma unroll
-      for (int t = 0; t < NI; ++t) {
-        const Frag af = Mma<T>::load(arow + t * KPL);
-        acc[s] = Mma<T>::mma(af, wf[2 + l][t], acc[s]);
-        if (s == 0) {
-          acc[S] = Mma<T>::mma(af, wf[0][t], acc[S]);
-          acc[S + 1] = Mma<T>::mma(af, wf[1][t], acc[S + 1]);
-        }
-      }
-    }
-
-    // 3. q and k straight out; value rows to LDS (fp32).  sv was last read in
-    //    step 4 of the previous tile, before this tile's barrier.
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 4 * g + r;              // output row = atom of the tile
-      if (i < na) {
-        const int64_t atom = a0 + i;
-        store_elem(qo + atom * C + c0 + col, acc[S][r]);
-        store_elem(ws + atom * (int64_t)((S + 1) * C) + c0 + col, acc[S + 1][r]);
-      }
-#pragma unroll
-      for (int s = 0; s < S; ++s) sv[i * PV + s * C + c0 + col] = acc[s][r];
-    }
-    if (AHEAD && tile + gridDim.x < ntiles) fetch(tile + gridDim.x);
-    // the frames of this tile and the next FB - 1 of the workgroup, once per atom, at
-    // the first tile of each batch (sf was last read in step 4 of the previous tile,
-    // before this tile's first barrier)
-    if (kb == 0 && tid < FB * TA) {
-      const int64_t ft = tile + (int64_t)(tid / TA) * gridDim.x;
-      const int64_t atom = ft * TA + tid % TA;
-      if (ft < ntiles && atom < a.n) {
-        AtomFrame<LMAX> e;
-        e.f = make_frame(a.r[3 * atom], a.r[3 * atom + 1], a.r[3 * atom + 2]);
-        e.d = make_dy2(e.f);
-        e.R = make_reindex<LMAX>(cf, e.f);
-        sf[tid] = e;
-      }
-    }
-    __syncthreads();
-    const AtomFrame<LMAX>* tf = sf + kb * TA;   // this tile's frames
-
-    // 4. EAAS per (atom, channel); stores coalesced along the channels
-    if constexpr (C % 64 == 0) {
-      // a wave takes whole atoms: their table entries go to scalar registers
-      // (the weight slices fill the vector file).  Lane l owns the VPL adjacent
-      // channels VPL l .. VPL l + VPL - 1, so each component is one LDS read and
-      // one store of VPL values a lane.
-      constexpr int NW = NT / 64;
-      constexpr int VPL = C / 64;
-      static_assert(VPL == 1 || VPL == 2, "64 or 128 channels");
-      const int c0 = lane * VPL;
-      for (int i = tid >> 6; i < na; i += NW) {
-        const AtomFrame<LMAX> e = uni<LMAX>(tf[i]);
-        const int64_t atom = a0 + i;
-        T* dst = ws + atom * (int64_t)((S + 1) * C) + C + c0;
-        float x[VPL][S], y[VPL][S];
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const float* src = &sv[i * PV + s * C + c0];
-          if constexpr (VPL == 2) {
-            const float2 v = *reinterpret_cast<const float2*>(src);
-            x[0][s] = v.x;
-            x[1][s] = v.y;
-          } else {
-            x[0][s] = src[0];
+        for (int t = 0; t < NI; ++t) {
+          const Frag af = Mma<T>::load(arow + t * KPL);
+          acc[s] = Mma<T>::mma(wf[2 + l][t], af, acc[s]);
+          if (s == 0) {
+            acc[S] = Mma<T>::mma(wf[0][t], af, acc[S]);
+            acc[S + 1] = Mma<T>::mma(wf[1][t], af, acc[S + 1]);
           }
         }
+      }
+      // the frames of this tile and the next FB - 1 of the workgroup, at the first tile
+      // of each batch (sf was last read in step 4 of the previous tile, before this
+      // tile's first barrier)
+      if (kb == 0 && tid < FB * TA) {
+        const int64_t ft = tile + (int64_t)(tid / TA) * gridDim.x;
+        const int64_t atom = ft * TA + tid % TA;
+        if (ft < ntiles && atom < a.n) {
+          AtomFrame<LMAX> e;
+          e.f = make_frame(a.r[3 * atom], a.r[3 * atom + 1], a.r[3 * atom + 2]);
+          e.d = make_dy2(e.f);
+          e.R = make_reindex<LMAX>(cf, e.f);
+          sf[tid] = e;
+        }
+      }
+      __syncthreads();   // sa is free for the next tile's rows; sf is written
+      if (tile + gridDim.x < ntiles) fetch(tile + gridDim.x);
+      // 3-4. q, k and EAAS straight from the accumulators: four consecutive channels of
+      //      atom col a lane, one store of the four per row
+      if (col < na) {
+        const int64_t atom = a0 + col;
+        const int cl = c0 + 4 * g;
+        T* wrow = ws + atom * (int64_t)((S + 1) * C) + cl;
+        {
+          float o[4] = {acc[S][0], acc[S][1], acc[S][2], acc[S][3]};
+          VecIO<T, 4>::store(qo + atom * C + cl, o);
+          float kk[4] = {acc[S + 1][0], acc[S + 1][1], acc[S + 1][2], acc[S + 1][3]};
+          VecIO<T, 4>::store(wrow, kk);
+        }
+        const AtomFrame<LMAX> e = sf[kb * TA + col];
+        float y[4][S];
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) eaas_channel<LMAX>(x[v], y[v], e.f, e.d, e.R);
+        for (int r = 0; r < 4; ++r) {
+          float x[S];
+#pragma unroll
+          for (int s = 0; s < S; ++s) x[s] = acc[s][r];
+          eaas_channel<LMAX>(x, y[r], e.f, e.d, e.R);
+        }
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          float o[VPL];
-#pragma unroll
-          for (int v = 0; v < VPL; ++v) o[v] = y[v][s];
-          VecIO<T, VPL>::store(dst + s * C, o);
+          float o[4] = {y[0][s], y[1][s], y[2][s], y[3][s]};
+          VecIO<T, 4>::store(wrow + (s + 1) * C, o);
         }
       }
     } else {
-      for (int p = tid; p < TA * C; p += NT) {
-        const int i = p / C;
-        const int c = p - i * C;
-        if (i >= na) break;
-        const int64_t atom = a0 + i;
-        const AtomFrame<LMAX> e = tf[i];
-        float x[S], y[S];
-#pragma unroll
-        for (int s = 0; s < S; ++s) x[s] = sv[i * PV + s * C + c];
-        eaas_channel<LMAX>(x, y, e.f, e.d, e.R);
-        T* dst = ws + atom * (int64_t)((S + 1) * C) + C + c;
-#pragma unroll
-        for (int s = 0; s < S; ++s) store_elem(dst + s * C, y[s]);
+      // 2. products: acc[s] = v rows, acc[S] = q, acc[S + 1] = k
+      v4f acc[S + 2];
+  #pragma unroll
+      for (int s = 0; s < S + 2; ++s) acc[s] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  #pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int l = s < 1 ? 0 : (s < 4 ? 1 : 2);
+        const T* arow = sa + col * PA + s * C + g * KG;
+  #pragma unroll
+        for (int t = 0; t < NI; ++t) {
+          const Frag af = Mma<T>::load(arow + t * KPL);
+          acc[s] = Mma<T>::mma(af, wf[2 + l][t], acc[s]);
+          if (s == 0) {
+            acc[S] = Mma<T>::mma(af, wf[0][t], acc[S]);
+            acc[S + 1] = Mma<T>::mma(af, wf[1][t], acc[S + 1]);
+          }
+        }
+      }
+
+      // 3. q and k straight out; value rows to LDS (fp32).  sv was last read in
+      //    step 4 of the previous tile, before this tile's barrier.
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g + r;              // output row = atom of the tile
+        if (i < na) {
+          const int64_t atom = a0 + i;
+          store_elem(qo + atom * C + c0 + col, acc[S][r]);
+          store_elem(ws + atom * (int64_t)((S + 1) * C) + c0 + col, acc[S + 1][r]);
+        }
+  #pragma unroll
+        for (int s = 0; s < S; ++s) sv[i * PV + s * C + c0 + col] = acc[s][r];
+      }
+      if (AHEAD && tile + gridDim.x < ntiles) fetch(tile + gridDim.x);
+      // the frames of this tile and the next FB - 1 of the workgroup, once per atom, at
+      // the first tile of each batch (sf was last read in step 4 of the previous tile,
+      // before this tile's first barrier)
+      if (kb == 0 && tid < FB * TA) {
+        const int64_t ft = tile + (int64_t)(tid / TA) * gridDim.x;
+        const int64_t atom = ft * TA + tid % TA;
+        if (ft < ntiles && atom < a.n) {
+          AtomFrame<LMAX> e;
+          e.f = make_frame(a.r[3 * atom], a.r[3 * atom + 1], a.r[3 * atom + 2]);
+          e.d = make_dy2(e.f);
+          e.R = make_reindex<LMAX>(cf, e.f);
+          sf[tid] = e;
+        }
+      }
+      __syncthreads();
+      const AtomFrame<LMAX>* tf = sf + kb * TA;   // this tile's frames
+
+      // 4. EAAS per (atom, channel); stores coalesced along the channels
+      if constexpr (C % 64 == 0) {
+        // a wave takes whole atoms: their table entries go to scalar registers
+        // (the weight slices fill the vector file).  Lane l owns the VPL adjacent
+        // channels VPL l .. VPL l + VPL - 1, so each component is one LDS read and
+        // one store of VPL values a lane.
+        constexpr int NW = NT / 64;
+        constexpr int VPL = C / 64;
+        static_assert(VPL == 1 || VPL == 2, "64 or 128 channels");
+        const int c0 = lane * VPL;
+        for (int i = tid >> 6; i < na; i += NW) {
+          const AtomFrame<LMAX> e = uni<LMAX>(tf[i]);
+          const int64_t atom = a0 + i;
+          T* dst = ws + atom * (int64_t)((S + 1) * C) + C + c0;
+          float x[VPL][S], y[VPL][S];
+  #pragma unroll
+          for (int s = 0; s < S; ++s) {
+            const float* src = &sv[i * PV + s * C + c0];
+            if constexpr (VPL == 2) {
+              const float2 v = *reinterpret_cast<const float2*>(src);
+              x[0][s] = v.x;
+              x[1][s] = v.y;
+            } else {
+              x[0][s] = src[0];
+            }
+          }
+  #pragma unroll
+          for (int v = 0; v < VPL; ++v) eaas_channel<LMAX>(x[v], y[v], e.f, e.d, e.R);
+  #pragma unroll
+          for (int s = 0; s < S; ++s) {
+            float o[VPL];
+  #pragma unroll
+            for (int v = 0; v < VPL; ++v) o[v] = y[v][s];
+            VecIO<T, VPL>::store(dst + s * C, o);
+          }
+        }
+      } else {
+        for (int p = tid; p < TA * C; p += NT) {
+          const int i = p / C;
+          const int c = p - i * C;
+          if (i >= na) break;
+          const int64_t atom = a0 + i;
+          const AtomFrame<LMAX> e = tf[i];
+          float x[S], y[S];
+  #pragma unroll
+          for (int s = 0; s < S; ++s) x[s] = sv[i * PV + s * C + c];
+          eaas_channel<LMAX>(x, y, e.f, e.d, e.R);
+          T* dst = ws + atom * (int64_t)((S + 1) * C) + C + c;
+  #pragma unroll
+          for (int s = 0; s < S; ++s) store_elem(dst + s * C, y[s]);
+        }
       }
     }
     // the next tile's step 1 overwrites sa, last read in step 2 above (before
