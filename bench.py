@@ -822,6 +822,9 @@ def main(argv=None):
                     help="skip the backward pass (dL/dh, dL/dpos) timed after the forward")
     ap.add_argument("--index-order-reps", type=int, default=5,
                     help="reps of the aggregate visiting targets in index order (a reference)")
+    ap.add_argument("--matrix-tile-reps", type=int, default=10,
+                    help="reps of the opt-in matrix-core aggregate, where it serves the layout "
+                         "(median reported beside the default kernel's time)")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="steps timed after a 1 GiB eviction write each (median reported)")
     ap.add_argument("--cpu-budget", type=float, default=18.0, help="seconds of oracle time")
@@ -961,13 +964,27 @@ def main(argv=None):
         torch.cuda.synchronize()
         k2_unsched_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev_u]))
 
+    # the opt-in 16-target matrix-core aggregate (E2F_MATRIX_TILES), where it serves the layout
+    # (fp32, C = 128, H = 16, K <= 256): its time beside the default kernel's, median of the reps
+    k2_tiles_ms = None
+    if args.matrix_tile_reps > 0 and not bf16 and C == 128 and H == 16 and K <= 256:
+        ev_t = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                for _ in range(args.matrix_tile_reps + 2)]
+        for e in ev_t:
+            e[0].record(stream)
+            e2f.attn_aggregate(pos, idx, mask, ws, H, s.lmax, C, tdt, out=out, matrix_tiles=True)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        k2_tiles_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev_t[2:]]))
+
     k1_bytes, k2_bytes, per_edge, per_target = algorithmic_bytes(N, K, E, S, C, b)
     alg_gbs = (k1_bytes + k2_bytes) / ((k1_ms + k2_ms) * 1e-3) / 1e9
     print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; precouple {k1_ms:.3f} ms, "
           f"aggregate {k2_ms:.3f} ms (median {np.median(k2_all):.3f}); cold medians: "
           f"precouple {np.median(cold_k1) if cold_k1 else float('nan'):.3f} ms, aggregate "
           f"{np.median(cold_k2) if cold_k2 else float('nan'):.3f} ms; index order "
-          f"{k2_unsched_ms or float('nan'):.3f} ms", file=sys.stderr, flush=True)
+          f"{k2_unsched_ms or float('nan'):.3f} ms; matrix tiles (opt-in) "
+          f"{k2_tiles_ms or float('nan'):.3f} ms", file=sys.stderr, flush=True)
 
     # the roofline of the step's kernels from the committed counters of this workload:
     # L2-to-fabric bytes (FETCH_SIZE + WRITE_SIZE, calibrated) over this run's kernel time
@@ -1000,7 +1017,8 @@ def main(argv=None):
         "atoms_per_s": N / (ms_step * 1e-3),
         "kernels_ms": {"precouple": k1_ms, "aggregate": k2_ms,
                        "precouple_median": med(k1_all), "aggregate_median": med(k2_all),
-                       "aggregate_index_order_reference": k2_unsched_ms},
+                       "aggregate_index_order_reference": k2_unsched_ms,
+                       "aggregate_matrix_tiles": k2_tiles_ms},
         "cold": {
             "reps": len(cold_k2),
             "eviction": f"{CALIB_COPY_MIB} MiB device write before each rep",
