@@ -33,10 +33,10 @@
 //     registers meanwhile), then logits, weights and sums on the MFMA;
 //  5. per target and head: normalise (0 for an empty row), the target-side
 //     EAAS, one store.
-// A chunk holding a non-finite value (0 x inf would reach the targets that do
-// not list its source) is done on the vector ALUs instead: the same fused
-// multiply-adds in the same order, skipping non-members, so finite results keep
-// their bits and a non-finite source only reaches the targets that list it.
+// A tile in which some chunk holds a non-finite value (0 x inf would reach the
+// targets that do not list its source) is redone on the vector ALUs: the same
+// fused multiply-adds in the same order, skipping non-members, so finite results
+// keep their bits and a non-finite source only reaches the targets that list it.
 //
 // Served layout: fp32 storage, C = 128, H = 16 (d = 8), rows of at most 256
 // slots, N < 2^27; the host picks the other kernels for anything else.
