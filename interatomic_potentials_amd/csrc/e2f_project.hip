@@ -119,8 +119,8 @@ __device__ inline AtomFrame<LMAX> uni(const AtomFrame<LMAX>& e) {
   return u;
 }
 
+// one element of q or k on the fp32 C = 128 path (the only one that stores element-wise)
 __device__ inline void store_elem(float* p, float v) { *p = v; }
-__device__ inline void store_elem(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 
 // Two waves a SIMD: the weight slices, accumulators and next-tile registers fit in 256
 // registers, and the compiler is held to that (it would otherwise spill into AGPRs at C = 64).
