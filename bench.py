@@ -264,7 +264,7 @@ def _busy(get):
 def profile_bench_cmd(w):
     """The bench command each counter pass of a workload profiles: warm steps only."""
     extra = (" --no-cpu-baseline --cold-reps 0 --index-order-reps 0 --sorted-steps 0"
-             " --matrix-tile-reps 0" if w != "eaas" else "")
+             " --matrix-tile-reps 0 --no-other-workloads" if w != "eaas" else "")
     return f"python -u bench.py --workload {w} --steps 3 --warmup 1{extra}"
 
 
@@ -409,7 +409,7 @@ def _default_trace_section(pmc_dir, d, w):
     mean = lambda v: sum(v) / max(len(v), 1)
     return ["", "## The default command under the kernel trace", "", "```",
             f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_default_{w} "
-            f"-o run -- python -u bench.py --workload {w} --no-cpu-baseline "
+            f"-o run -- python -u bench.py --workload {w} --no-cpu-baseline --no-other-workloads "
             f"> {d}/default_{w}.json", "```", "",
             f"The bench's own timing of its {steps} timed steps in this run (HIP events on the "
             f"launch stream): pre-coupling {line['kernels_ms']['precouple']:.4f} ms, aggregate "
@@ -899,6 +899,9 @@ def main(argv=None):
                     help="skip the backward pass (dL/dh, dL/dpos) timed after the forward")
     ap.add_argument("--index-order-reps", type=int, default=5,
                     help="reps of the aggregate visiting targets in index order (a reference)")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="with the default workload: skip the Scale-out, Water and EAAS runs "
+                         "whose summaries the line carries")
     ap.add_argument("--sorted-steps", type=int, default=50,
                     help="steps timed with the atoms relabelled into Morton order (0: skip)")
     ap.add_argument("--matrix-tile-reps", type=int, default=10,
@@ -1150,8 +1153,49 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, budget_s=args.cpu_budget)
+    if args.workload == "large" and not args.no_other_workloads:
+        result["other_workloads"] = other_workloads(args)
     print(json.dumps(result), flush=True)
     return 0
+
+
+# fields of another workload's line kept beside the headline one
+_OTHER_KEYS = ("metric", "value", "unit", "ms_per_step", "steps", "warmup", "dtype", "config",
+               "atoms_per_s", "kernels_ms", "cold", "spatially_sorted", "backward", "projected")
+
+
+def other_workloads(args):
+    """The Scale-out, Water and EAAS workloads measured in the same run (each in a child process
+    of its own, the same K and W; no CPU baseline), so that their figures come from the run that
+    produces the headline line.  A compact copy of each child's line: the roofline's measured and
+    algorithmic rates and the step timings."""
+    import subprocess
+    out = {}
+    for w in ("scaleout", "water", "eaas"):
+        cmd = [sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--workload", w,
+               "--steps", str(args.steps), "--warmup", str(args.warmup), "--no-cpu-baseline",
+               "--no-other-workloads"]
+        print(f"[bench] other workload {w}: {' '.join(cmd[2:])}", file=sys.stderr, flush=True)
+        try:
+            run = subprocess.run(cmd, stdout=subprocess.PIPE, timeout=600, text=True)
+        except subprocess.TimeoutExpired:
+            out[w] = {"error": "timed out"}
+            continue
+        lines = [ln for ln in run.stdout.splitlines() if ln.startswith("{")]
+        if run.returncode != 0 or not lines:
+            out[w] = {"error": f"exit status {run.returncode}"}
+            continue
+        line = json.loads(lines[-1])
+        keep = {k: line[k] for k in _OTHER_KEYS if k in line}
+        rf = line.get("roofline")
+        if isinstance(rf, dict):
+            keep["roofline"] = {k: rf.get(k) for k in ("bound", "achieved", "peak", "unit", "frac",
+                                                      "traffic", "algorithmic_GBps")}
+        for k in ("dense_vs_eaas", "dense"):
+            if k in line:
+                keep[k] = line[k]
+        out[w] = keep
+    return out
 
 
 if __name__ == "__main__":
