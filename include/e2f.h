@@ -102,9 +102,14 @@ typedef enum e2f_dtype {
                                     run above 4,096 atoms only, where N/3 waves fill the chip;
                                     below, one atom a wave is faster.  Either way the result is
                                     the same function, rounded in another order. */
-#define E2F_MATRIX_TILES 16u     /* the 16-atom matrix-core aggregate whatever N, where its
-                                    layout is served (fp32, C = 128, H = 16, K <= 256, no
-                                    envelope); ignored elsewhere and under E2F_SHARED_ROWS */
+#define E2F_MATRIX_TILES 16u     /* run the aggregate on the matrix cores, 16 atoms a
+                                    workgroup sharing the rows they read, where that kernel
+                                    serves the layout (fp32, C = 128, H = 16, K <= 256, no
+                                    envelope); ignored elsewhere and under E2F_SHARED_ROWS.
+                                    Opt-in: slower than the default kernels at the measured
+                                    sizes.  The same function, rounded in another order; each
+                                    atom's result does not depend on the atoms sharing its
+                                    workgroup. */
 
 /* Name of a status code ("E2F_OK", "E2F_ERR_SHAPE", ...); never NULL. */
 const char* e2f_status_string(int status);
