@@ -268,6 +268,80 @@ def profile_bench_cmd(w):
     return f"python -u bench.py --workload {w} --steps 3 --warmup 1{extra}"
 
 
+TILE_MFMA_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE",
+                      "TCC_HIT_sum", "TCC_MISS_sum"]
+
+
+def tile_profile_cmd():
+    """The bench command the tile-kernel counter passes profile: the default step kernels and the
+    opt-in matrix-core aggregate, side by side in one run."""
+    return ("python -u bench.py --workload large --steps 3 --warmup 1 --no-cpu-baseline "
+            "--cold-reps 0 --index-order-reps 0 --sorted-steps 0 --no-other-workloads "
+            "--no-backward --no-proj --no-extras --matrix-tile-reps 5")
+
+
+def summarize_tile_profile(pmc_dir, out_path):
+    """Counters of the opt-in matrix-core aggregate beside the default shared-row kernel at
+    Large, per valid edge, from a directory with trace_tile, fetch_tile, write_tile, busy_tile,
+    mfma_tile, fetch_copy and write_copy runs (commands listed in the summary)."""
+    import csv
+    from gen import make_config
+    d = os.path.relpath(pmc_dir, ROOT) if os.path.isabs(pmc_dir) else pmc_dir
+    stats = list(csv.DictReader(open(os.path.join(pmc_dir, "trace_tile", "run_kernel_stats.csv"))))
+    avg_ns = {_kernel_key(r["Name"]): float(r["AverageNs"]) for r in stats}
+    calls = {_kernel_key(r["Name"]): int(r["Calls"]) for r in stats}
+    mean = {n: _counter_means(os.path.join(pmc_dir, f"{n}_tile", "run_counter_collection.csv"))[0]
+            for n in ("fetch", "write", "busy", "mfma")}
+    cf, _ = _counter_means(os.path.join(pmc_dir, "fetch_copy", "run_counter_collection.csv"))
+    cw, _ = _counter_means(os.path.join(pmc_dir, "write_copy", "run_counter_collection.csv"))
+    copy_bytes = CALIB_COPY_MIB << 20
+    kf = copy_bytes / (cf[("__amd_rocclr_copyBuffer", "FETCH_SIZE")] * 1024)
+    kw = copy_bytes / (cw[("__amd_rocclr_copyBuffer", "WRITE_SIZE")] * 1024)
+    cfg = make_config("large")
+    E = int(cfg.nl.n_edges)
+    cmd = tile_profile_cmd()
+    prof = "rocprofv3 --output-format csv"
+    lines = ["# rocprofv3 summary: the matrix-core aggregate (opt-in) beside the default one, large "
+             f"workload ({WORKLOADS['large']})", "",
+             f"kernel source hash: {kernel_source_hash()}", "",
+             "Commands (run from the repository root on an MI355X, TMPDIR=/tmp):", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_tile -o run -- {cmd}",
+             f"{prof} --pmc FETCH_SIZE -d {d}/fetch_tile -o run -- {cmd}",
+             f"{prof} --pmc WRITE_SIZE -d {d}/write_tile -o run -- {cmd}",
+             f"{prof} --pmc {' '.join(BUSY_COUNTERS)} -d {d}/busy_tile -o run -- {cmd}",
+             f"{prof} --pmc {' '.join(TILE_MFMA_COUNTERS)} -d {d}/mfma_tile -o run -- {cmd}",
+             f"{prof} --pmc FETCH_SIZE -d {d}/fetch_copy -o run -- python -u bench.py "
+             f"--calib-copy-mib {CALIB_COPY_MIB} --steps 3",
+             f"{prof} --pmc WRITE_SIZE -d {d}/write_copy -o run -- python -u bench.py "
+             f"--calib-copy-mib {CALIB_COPY_MIB} --steps 3",
+             f"python bench.py --summarize-tile-profile {d}", "```", "",
+             f"Valid edges E = {E:,}. Fabric bytes: FETCH_SIZE x {kf:.3f} + WRITE_SIZE x {kw:.3f} "
+             "(calibrated against a plain 1 GiB device copy); busy shares over 256 CUs (TA, TD) "
+             "or 1,024 SIMDs (VALU issue, MFMA busy) x GRBM_GUI_ACTIVE / 8; per-edge figures are "
+             "instructions summed over the whole chip divided by E.", "",
+             "| kernel | calls | average ms | fabric GB | TA busy | TD busy | TD waiting on L2 | "
+             "VALU issue | VMEM rd instr / edge | LDS instr / edge | MFMA busy | L2 hit rate |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(avg_ns):
+        if not (k.startswith("e2f::k_aggregate_mt<") or k.startswith("e2f::k_aggregate_tile<")):
+            continue
+        get = lambda name, src="busy": mean[src].get((k, name), 0.0)   # noqa: E731
+        fab = (mean["fetch"].get((k, "FETCH_SIZE"), 0.0) * kf
+               + mean["write"].get((k, "WRITE_SIZE"), 0.0) * kw) * 1024
+        b = _busy(get)
+        mcyc = get("GRBM_GUI_ACTIVE", "mfma") / N_XCD
+        mfma = get("SQ_VALU_MFMA_BUSY_CYCLES", "mfma") / (N_SIMD * mcyc) if mcyc > 0 else 0.0
+        hit, miss = get("TCC_HIT_sum", "mfma"), get("TCC_MISS_sum", "mfma")
+        lines.append(f"| `{k}` | {calls[k]} | {avg_ns[k] * 1e-6:.3f} | {fab * 1e-9:.2f} | "
+                     f"{b.get('ta_busy', 0):.2f} | {b.get('td_busy', 0):.2f} | "
+                     f"{b.get('td_stalled_on_l2', 0):.2f} | {b.get('valu_issue', 0):.2f} | "
+                     f"{get('SQ_INSTS_VMEM_RD') / E:.2f} | {get('SQ_INSTS_LDS') / E:.2f} | "
+                     f"{mfma:.2f} | {hit / max(hit + miss, 1.0):.2f} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out_path)
+
+
 def summarize_profile(pmc_dir, workload, out_path):
     """Write the committed counter summary from a directory of rocprofv3 csv runs.
 
@@ -914,6 +988,8 @@ def main(argv=None):
                     help="(internal) time the CPU oracle on the arrays saved in this directory")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-tile-profile", metavar="DIR", default=None,
+                    help="write profiles/k_aggregate_tile_large.md from rocprofv3 csv runs in DIR")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
                     help="write profiles/k_aggregate_<workload>.md from rocprofv3 csv runs in DIR")
     args = ap.parse_args(argv)
@@ -922,6 +998,10 @@ def main(argv=None):
         print(json.dumps(cpu_baseline_child(args.cpu_baseline_dir, args.cpu_budget)), flush=True)
         return 0
 
+    if args.summarize_tile_profile:
+        summarize_tile_profile(args.summarize_tile_profile,
+                               os.path.join(ROOT, "profiles", "k_aggregate_tile_large.md"))
+        return 0
     if args.summarize_profile:
         kernel = "k_eaas" if args.workload == "eaas" else "k_aggregate"
         summarize_profile(args.summarize_profile, args.workload,
