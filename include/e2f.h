@@ -227,8 +227,9 @@ int e2f_attn_precouple_proj(hipStream_t stream, int64_t N, int lmax, int C, int 
  *             E2F_ERR_SHAPE.
  *   workspace filled by e2f_attn_precouple (or _proj); its schedule scratch (and, under
  *             E2F_VALIDATE_INDICES, its flag) is rewritten here, hence not
- *             const.  Targets are visited in Morton order of their
- *             positions (built on the GPU each call unless
+ *             const.  Targets are visited in Hilbert-curve order of
+ *             their cells on a grid over the positions' bounding box (built
+ *             on the GPU each call unless
  *             E2F_TARGETS_IN_ORDER or N <= 2048), each XCD taking one contiguous
  *             stretch, so that waves sharing an L2 share neighbours; the
  *             visiting order never changes any target's result.

@@ -88,7 +88,7 @@ __device__ inline void sort_list(int* nb, int cnt, int lane) {
   wave_sort<MAXN>(reinterpret_cast<uint32_t*>(nb), cnt, lane, 0x7fffffffu);
 }
 
-// the target or source handled by this wave (Morton schedule, XCD-aware order)
+// the target or source handled by this wave (Hilbert-curve schedule, XCD-aware order)
 __device__ inline int64_t scheduled_atom(const int32_t* sched, int64_t N, int w) {
   const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
   const int64_t blk = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;

@@ -260,7 +260,7 @@ void* ws_query_rows(void* ws, int64_t N, int lmax, int C, int dt) {
 // order, and the four schedule launches would cost more than they save.
 constexpr int64_t kSchedMinAtoms = 2048;
 
-// Morton bits per axis of the target schedule: about one cell per atom, at most 2^15 cells
+// bits per axis of the target schedule's grid: about one cell per atom, at most 2^15 cells
 int sched_bits(int64_t N) {
   int bits = 1;
   while (bits < e2f::kSchedMaxBits && ((int64_t)1 << (3 * bits)) < N) ++bits;

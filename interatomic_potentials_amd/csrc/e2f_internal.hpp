@@ -18,17 +18,17 @@ constexpr int kTile = 256;          // neighbour slots compacted per pass
 constexpr int64_t kMtMinAtoms = 4096;
 constexpr int kXcds = 8;            // gfx950 (MI350 series): 8 XCDs, workgroups dealt round-robin
 constexpr int kBboxBlocks = 256;    // partial bounding boxes reduced by the schedule builder
-constexpr int kSchedMaxBits = 5;    // Morton bits per axis of the schedule grid, at most
+constexpr int kSchedMaxBits = 5;    // bits per axis of the schedule grid, at most
 constexpr int kSchedCells = 1 << (3 * kSchedMaxBits);  // count entries always scanned
 
 // Target schedule scratch, carved from the caller's workspace after the
 // pre-coupled rows and the validation flag.
 struct SchedScratch {
-  int32_t* sched;      // [N] target order: atoms sorted by Morton cell
+  int32_t* sched;      // [N] target order: atoms sorted by their cell's Hilbert index
   int32_t* cell;       // [N] cell of each atom
   int32_t* counts;     // [kSchedCells] per-cell counts, then running offsets
   float* partial;      // [kBboxBlocks][6] partial (min, max) of the positions
-  int bits;            // Morton bits per axis (<= kSchedMaxBits); cells used = 2^(3 bits)
+  int bits;            // grid bits per axis (<= kSchedMaxBits); cells used = 2^(3 bits)
 };
 
 // Sparse reindex weights, one row per path (lexicographic (li, lf, lo)):

@@ -803,13 +803,13 @@ __global__ __launch_bounds__(256) void k_validate(int64_t total, int64_t N, cons
 
 // ------------------------------------------------- target schedule
 //
-// Targets are visited in Morton (Z-curve) order of a grid of 2^bits cells
-// per axis over the bounding box of the positions, built with a counting
+// Targets are visited in Hilbert-curve order of a grid of 2^bits cells per
+// axis over the bounding box of the positions, built with a counting
 // sort: bounding box, per-cell counts, one scan, scatter.  The order inside
 // a cell is whatever the atomics produce; it only changes which wave takes
 // which target, never a target's arithmetic, so outputs do not depend on it.
 
-// spread the low 10 bits of v to every third bit (Morton interleave)
+// spread the low 10 bits of v to every third bit (three-way bit interleave)
 __device__ inline uint32_t spread3(uint32_t v) {
   v &= 0x3ffu;
   v = (v | (v << 16)) & 0x030000ffu;
@@ -817,6 +817,36 @@ __device__ inline uint32_t spread3(uint32_t v) {
   v = (v | (v << 4)) & 0x030c30c3u;
   v = (v | (v << 2)) & 0x09249249u;
   return v;
+}
+
+// Position along the Hilbert curve of the cell (x, y, z), each coordinate of
+// `bits` bits: J. Skilling's transform (Programming the Hilbert curve, AIP
+// Conf. Proc. 707, 2004) to the curve's transposed form, whose bits, taken
+// from the top level down and x, y, z within a level, spell the index.  Cells
+// adjacent in the index are adjacent in space (the Z-curve jumps at every
+// block boundary), so the targets in flight at once cover a more compact region.
+__device__ inline uint32_t hilbert3(uint32_t x, uint32_t y, uint32_t z, int bits) {
+  uint32_t X[3] = {x, y, z};
+  const uint32_t top = 1u << (bits - 1);
+  for (uint32_t q = top; q > 1u; q >>= 1) {   // undo the excess rotations, level by level
+    const uint32_t p = q - 1u;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      if (X[i] & q) {
+        X[0] ^= p;
+      } else {
+        const uint32_t t = (X[0] ^ X[i]) & p;
+        X[0] ^= t;
+        X[i] ^= t;
+      }
+    }
+  }
+  X[1] ^= X[0];   // Gray code
+  X[2] ^= X[1];
+  uint32_t t = 0;
+  for (uint32_t q = top; q > 1u; q >>= 1)
+    if (X[2] & q) t ^= q - 1u;
+  return (spread3(X[0] ^ t) << 2) | (spread3(X[1] ^ t) << 1) | spread3(X[2] ^ t);
 }
 
 __global__ __launch_bounds__(256) void k_sched_bbox(int64_t N, const float* pos, float* partial,
@@ -883,7 +913,7 @@ __global__ __launch_bounds__(256) void k_sched_count(int64_t N, const float* pos
     // comparisons keep NaN and infinities out of the integer conversion
     q[d] = u >= 1.0f ? (u < (float)(n - 1) ? (uint32_t)u : (uint32_t)(n - 1)) : 0u;
   }
-  const int32_t c = (int32_t)(spread3(q[0]) | (spread3(q[1]) << 1) | (spread3(q[2]) << 2));
+  const int32_t c = (int32_t)hilbert3(q[0], q[1], q[2], bits);
   cell[at] = c;
   atomicAdd(&counts[c], 1);
 }

@@ -342,7 +342,7 @@ def test_empty_and_single_atom(e2f, dev):
 
 @pytest.mark.parametrize("name", ["water", "large", "scaleout"])
 def test_schedule_covers_every_target_bit_exact(e2f, dev, name):
-    """The Morton schedule only reorders work: same bits as index order, every target written."""
+    """The spatial schedule only reorders work: same bits as index order, every target written."""
     cfg = make_config(name)
     s = cfg.spec
     say(f"schedule vs index order on {name}")
