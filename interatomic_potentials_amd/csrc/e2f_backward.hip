@@ -1214,9 +1214,7 @@ __global__ __launch_bounds__(256) void k_narrow_bf16(int64_t n, const float* src
   if (e0 + 8 <= n) {
     const float4 a = reinterpret_cast<const float4*>(src + e0)[0];
     const float4 b = reinterpret_cast<const float4*>(src + e0)[1];
-    auto pk = [](float lo, float hi) {
-      return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
-    };
+    auto pk = [](float lo, float hi) { return f32x2_to_bf16x2(lo, hi); };
     *reinterpret_cast<uint4*>(dst + e0) = make_uint4(pk(a.x, a.y), pk(a.z, a.w), pk(b.x, b.y),
                                                      pk(b.z, b.w));
   } else {

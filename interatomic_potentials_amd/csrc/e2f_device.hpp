@@ -388,12 +388,15 @@ __device__ inline void eaas_channel_t(float* y, float* x, const Frame& f, const 
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-__device__ inline uint16_t f32_to_bf16(float f) {  // round to nearest, ties to even
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+// Two fp32 values rounded to bf16 (nearest, ties to even; NaN stays a quiet NaN)
+// by gfx950's packed conversion, one instruction for the pair; a in the low half.
+__device__ inline uint32_t f32x2_to_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
+
+__device__ inline uint16_t f32_to_bf16(float f) { return uint16_t(f32x2_to_bf16x2(f, 0.0f)); }
 
 // One lane's V elements of a row exactly as loaded (fp32, or bf16 pairs packed
 // in 32-bit words), widened to fp32 only where they are used.
@@ -493,9 +496,7 @@ struct VecIO<uint16_t, V> {
     o[0] = __uint_as_float(w << 16);
     o[1] = __uint_as_float(w & 0xffff0000u);
   }
-  static __device__ inline uint32_t pack(float a, float b) {
-    return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
-  }
+  static __device__ inline uint32_t pack(float a, float b) { return f32x2_to_bf16x2(a, b); }
   static __device__ inline void load_raw(const uint16_t* p, Raw<uint16_t, V>& r) {
     if constexpr (V == 8) {
       const uint4 v = *reinterpret_cast<const uint4*>(p);
