@@ -94,6 +94,32 @@ def test_projected_workspace_rows_vs_oracle(e2f, dev, lmax, C, dt, N):
     assert block_rel_err(to_host(rows[:, 1:]), ref_hp, lmax) <= tol
 
 
+@pytest.mark.parametrize("lmax,C,dt", [(2, 128, "bf16"), (2, 64, "f32"), (1, 64, "bf16"),
+                                        (2, 32, "f32")])
+def test_projected_workspace_rows_many_tiles(e2f, dev, lmax, C, dt):
+    """Enough atoms (20,003: 1,251 tiles of 16, the last partial) that each persistent
+    workgroup runs several tiles, so every tile's rows come from the register sets
+    loaded one or two tile periods ahead."""
+    N = 20003
+    say(f"projected precouple, many tiles: lmax={lmax} C={C} {dt} N={N}")
+    rng = np.random.default_rng(lmax * 100 + C + 7)
+    S = (lmax + 1) ** 2
+    pos, h = _inputs(rng, N, lmax, C, dt)
+    w = proj_weights(lmax, C, seed=C + lmax + 1, dtype=dt)
+    ws = e2f.attn_precouple(T(pos, dev), T(h, dev, _tdt(dt)), proj=_weights_dev(w, dev, dt))
+    torch.cuda.synchronize()
+    b = 2 if dt == "bf16" else 4
+    rows = ws[:N * (S + 1) * C * b].view(_tdt(dt)).reshape(N, S + 1, C)
+    qoff = _r256(N * (S + 1) * C * b)
+    q = ws[qoff:qoff + N * C * b].view(_tdt(dt)).reshape(N, 1, C)
+    rq, rk, rv = oracle_project(h, *w)
+    ref_hp = tp.tp_dense(rv, pos, lmax)
+    tol = TOL_BF16 if dt == "bf16" else TOL_F32
+    assert block_rel_err(to_host(q), rq[:, None, :], 0) <= tol
+    assert block_rel_err(to_host(rows[:, :1]), rk[:, None, :], 0) <= tol
+    assert block_rel_err(to_host(rows[:, 1:]), ref_hp, lmax) <= tol
+
+
 @pytest.mark.parametrize("lmax,C,H,dt,K", [(0, 16, 2, "f32", 12), (1, 32, 4, "f32", 40),
                                            (2, 128, 16, "f32", 64), (2, 64, 8, "f32", 300),
                                            (2, 128, 16, "bf16", 64), (1, 64, 8, "bf16", 30)])
