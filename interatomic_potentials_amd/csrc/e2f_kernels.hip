@@ -486,13 +486,16 @@ __global__ __launch_bounds__(64 * kAggWaves) void k_aggregate(AggArgs a, EaasCoe
 // in which order -- depends on its own neighbour set alone: not on the other
 // targets sharing the wave, the schedule, or slot order.
 constexpr int kMtMaxK = kShareMaxK;   // longest neighbour row this kernel takes
-// Three targets per wave, two union sources per subgroup in flight: measured
-// against two targets with three in flight (the union of two rows is a larger
-// share of their lengths, and more rows go through the vector-memory path) and
-// three targets with three in flight (registers for one wave a SIMD only).  The
-// envelope variant takes the same (its log2 u table fits at one wave a workgroup).
-constexpr int kMtTargets = 3;     // targets per wave
-constexpr int kMtInflight = 2;    // union sources per subgroup in flight
+// Four targets per wave, one union source per subgroup in flight: on the
+// Hilbert-curve schedule the union of four adjacent targets' rows is a small
+// enough share of their lengths that it beats three targets with two in flight
+// (0.835 against 0.850 ms at Large) and two targets with one or two (0.93).
+// The envelope variant keeps three targets with two in flight: its log2 u table
+// grows with the targets, and at four it would hold a CU to four workgroups.
+constexpr int kMtTargets = 4;       // targets per wave
+constexpr int kMtInflight = 1;      // union sources per subgroup in flight
+constexpr int kMtTargetsEnv = 3;    // the same with the distance envelope
+constexpr int kMtInflightEnv = 2;
 
 // One wave a workgroup: the waves share nothing, and a workgroup's LDS and slot
 // are freed only when its last wave ends, so with four waves the early ones
@@ -1020,8 +1023,8 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
     if (V == 4 && buf && a.K <= kMtMaxK && (a.N > kMtMinAtoms || a.shared) &&
         a.N < ((int64_t)1 << 30) &&
         (a.head_lanes == 1 || a.head_lanes == 2 || a.head_lanes == 4)) {
-      constexpr int TM = kMtTargets;
-      constexpr int UM = kMtInflight;
+      constexpr int TM = E ? kMtTargetsEnv : kMtTargets;
+      constexpr int UM = E ? kMtInflightEnv : kMtInflight;
       const int64_t mblocks = (a.N + kMtWaves * TM - 1) / (kMtWaves * TM);
       const dim3 mgrid((unsigned)((mblocks + kXcds - 1) / kXcds * kXcds));
       const dim3 mblk(64 * kMtWaves);

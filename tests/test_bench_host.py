@@ -17,6 +17,7 @@ import bench  # noqa: E402
     # Large, fp32 storage: step 1, the schedule, the shared-row aggregate without the envelope
     ("e2f::k_eaas<2, 4, float, true>", "large", True),
     ("e2f::k_sched_count", "large", True),
+    ("e2f::k_aggregate_mt<2, 4, 1, 2, false>", "large", True),
     ("e2f::k_aggregate_mt<2, 3, 2, 2, false>", "large", True),
     ("e2f::k_aggregate_mt<2, 3, 2, 2, true>", "large", False),      # envelope variant
     ("e2f::k_bwd_q_mt<2, 3, 2, 2, false>", "large", False),
@@ -27,6 +28,7 @@ import bench  # noqa: E402
     ("e2f::k_aggregate<2, 8, unsigned short, 1, 1, true, true, true>", "scaleout", False),
     ("e2f::k_eaas<2, 4, float, true>", "scaleout", False),
     ("e2f::k_aggregate_mt<2, 3, 2, 2, false>", "scaleout", False),
+    ("e2f::k_aggregate_mt<2, 4, 1, 2, false>", "scaleout", False),
     ("e2f::k_sched_scatter", "scaleout", True),
     # the EAAS workload: the product alone, without the workspace's query rows
     ("e2f::k_eaas<2, 4, float, false>", "eaas", True),
