@@ -148,16 +148,20 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_proj_eaas(ProjArgs a, EaasCo
   __shared__ __align__(16) T sa[TA * PA];
   // value rows through LDS on the path that keeps the original MFMA layout (fp32, C = 128)
   __shared__ __align__(16) float sv[TRANS ? 1 : TA * PV];
-  // the transposed path's output tile: per atom its S + 1 workspace rows (k, h') and
-  // then its q row, in the storage type, POB bytes apart (32 bytes of padding spread
-  // the atoms over the LDS banks).  It goes to memory as whole rows: each wave
-  // instruction then writes 1 KB of consecutive bytes, where stores straight from
-  // the accumulators would write 32-byte pieces of 16 different atoms' rows.
+  // the transposed path's output tile at bf16 storage: per atom its S + 1 workspace
+  // rows (k, h') and then its q row, in the storage type, POB bytes apart (32 bytes of
+  // padding spread the atoms over the LDS banks).  It goes to memory as whole rows:
+  // each wave instruction then writes 1 KB of consecutive bytes, where stores straight
+  // from the accumulators would write 32-byte pieces of 16 different atoms' rows.  At
+  // fp32 those pieces are 64 bytes and the tile's LDS and registers (the compiler
+  // parks accumulators in AGPRs, one wave a SIMD) cost more than they save, so fp32
+  // stores straight from the accumulators.
+  constexpr bool OTILE = TRANS && sizeof(T) == 2;
   constexpr int CPW = (S + 1) * C * (int)sizeof(T) / 16;   // 16-byte chunks of an atom's rows
   constexpr int CPQ = C * (int)sizeof(T) / 16;             // 16-byte chunks of its q row
   constexpr int POB = (CPW + CPQ) * 16 + 32;
-  static_assert(!TRANS || (C * (int)sizeof(T)) % 16 == 0, "rows of whole 16-byte chunks");
-  __shared__ __align__(16) char so[TRANS ? TA * POB : 16];
+  static_assert(!OTILE || (C * (int)sizeof(T)) % 16 == 0, "rows of whole 16-byte chunks");
+  __shared__ __align__(16) char so[OTILE ? TA * POB : 16];
   // frames of FB consecutive tiles of this workgroup: computed by one wave's lanes at
   // once every FB tiles (the computation is a long dependent chain, so 64 frames take
   // hardly longer than 16); two tiles where the tiles' own LDS is largest (fp32, C = 128)
@@ -263,50 +267,80 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_proj_eaas(ProjArgs a, EaasCo
       }
       __syncthreads();   // sa is free for the next tile's rows; sf is written
       if (tile + gridDim.x < ntiles) fetch(tile + gridDim.x);
-      // 3-4. q, k and EAAS straight from the accumulators: four consecutive channels of
-      //      atom col a lane, into the output tile (so was last read before this
-      //      tile's first barrier)
-      {
-        const int cl = c0 + 4 * g;
-        T* orow = reinterpret_cast<T*>(so + col * POB) + cl;
+      if constexpr (OTILE) {
+        // 3-4. q, k and EAAS straight from the accumulators: four consecutive channels of
+        //      atom col a lane, into the output tile (so was last read before this
+        //      tile's first barrier)
         {
-          float o[4] = {acc[S][0], acc[S][1], acc[S][2], acc[S][3]};
-          VecIO<T, 4>::store(orow + (S + 1) * C, o);
-          float kk[4] = {acc[S + 1][0], acc[S + 1][1], acc[S + 1][2], acc[S + 1][3]};
-          VecIO<T, 4>::store(orow, kk);
+          const int cl = c0 + 4 * g;
+          T* orow = reinterpret_cast<T*>(so + col * POB) + cl;
+          {
+            float o[4] = {acc[S][0], acc[S][1], acc[S][2], acc[S][3]};
+            VecIO<T, 4>::store(orow + (S + 1) * C, o);
+            float kk[4] = {acc[S + 1][0], acc[S + 1][1], acc[S + 1][2], acc[S + 1][3]};
+            VecIO<T, 4>::store(orow, kk);
+          }
+          const AtomFrame<LMAX> e = sf[kb * TA + col];
+          float y[4][S];
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x[S];
+  #pragma unroll
+            for (int s = 0; s < S; ++s) x[s] = acc[s][r];
+            eaas_channel<LMAX>(x, y[r], e.f, e.d, e.R);
+          }
+  #pragma unroll
+          for (int s = 0; s < S; ++s) {
+            float o[4] = {y[0][s], y[1][s], y[2][s], y[3][s]};
+            VecIO<T, 4>::store(orow + (s + 1) * C, o);
+          }
         }
-        const AtomFrame<LMAX> e = sf[kb * TA + col];
-        float y[4][S];
+        __syncthreads();   // the output tile is complete
+        // 5. the tile's rows to memory, 16 bytes a lane: the workspace rows of its
+        //    na atoms are one contiguous block, and so are their q rows
+        {
+          char* wdst = reinterpret_cast<char*>(ws + a0 * (int64_t)((S + 1) * C));
+          for (int q = tid; q < na * CPW; q += NT) {
+            const int at = q / CPW;
+            const int ch = q - at * CPW;
+            *reinterpret_cast<v4u*>(wdst + (int64_t)q * 16) =
+                *reinterpret_cast<const v4u*>(so + at * POB + ch * 16);
+          }
+          char* qdst = reinterpret_cast<char*>(qo + a0 * (int64_t)C);
+          for (int q = tid; q < na * CPQ; q += NT) {
+            const int at = q / CPQ;
+            const int ch = q - at * CPQ;
+            *reinterpret_cast<v4u*>(qdst + (int64_t)q * 16) =
+                *reinterpret_cast<const v4u*>(so + at * POB + (CPW + ch) * 16);
+          }
+        }
+      } else {
+        // 3-4. q, k and EAAS straight from the accumulators: four consecutive channels
+        //      of atom col a lane, one store of the four per row
+        if (col < na) {
+          const int64_t atom = a0 + col;
+          const int cl = c0 + 4 * g;
+          T* wrow = ws + atom * (int64_t)((S + 1) * C) + cl;
+          {
+            float o[4] = {acc[S][0], acc[S][1], acc[S][2], acc[S][3]};
+            VecIO<T, 4>::store(qo + atom * C + cl, o);
+            float kk[4] = {acc[S + 1][0], acc[S + 1][1], acc[S + 1][2], acc[S + 1][3]};
+            VecIO<T, 4>::store(wrow, kk);
+          }
+          const AtomFrame<LMAX> e = sf[kb * TA + col];
+          float y[4][S];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x[S];
+          for (int r = 0; r < 4; ++r) {
+            float x[S];
 #pragma unroll
-          for (int s = 0; s < S; ++s) x[s] = acc[s][r];
-          eaas_channel<LMAX>(x, y[r], e.f, e.d, e.R);
-        }
+            for (int s = 0; s < S; ++s) x[s] = acc[s][r];
+            eaas_channel<LMAX>(x, y[r], e.f, e.d, e.R);
+          }
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-          float o[4] = {y[0][s], y[1][s], y[2][s], y[3][s]};
-          VecIO<T, 4>::store(orow + (s + 1) * C, o);
-        }
-      }
-      __syncthreads();   // the output tile is complete
-      // 5. the tile's rows to memory, 16 bytes a lane: the workspace rows of its
-      //    na atoms are one contiguous block, and so are their q rows
-      {
-        char* wdst = reinterpret_cast<char*>(ws + a0 * (int64_t)((S + 1) * C));
-        for (int q = tid; q < na * CPW; q += NT) {
-          const int at = q / CPW;
-          const int ch = q - at * CPW;
-          *reinterpret_cast<v4u*>(wdst + (int64_t)q * 16) =
-              *reinterpret_cast<const v4u*>(so + at * POB + ch * 16);
-        }
-        char* qdst = reinterpret_cast<char*>(qo + a0 * (int64_t)C);
-        for (int q = tid; q < na * CPQ; q += NT) {
-          const int at = q / CPQ;
-          const int ch = q - at * CPQ;
-          *reinterpret_cast<v4u*>(qdst + (int64_t)q * 16) =
-              *reinterpret_cast<const v4u*>(so + at * POB + (CPW + ch) * 16);
+          for (int s = 0; s < S; ++s) {
+            float o[4] = {y[0][s], y[1][s], y[2][s], y[3][s]};
+            VecIO<T, 4>::store(wrow + (s + 1) * C, o);
+          }
         }
       }
     } else {
