@@ -502,6 +502,32 @@ constexpr int kMtInflightEnv = 2;
 // idled (one: 0.93 ms at Large against 0.98 with four).
 constexpr int kMtWaves = 1;   // waves per workgroup
 
+// Work units (one wave each).  XCD x takes the x-th contiguous stretch of sx
+// schedule slots, in `head` units of T targets and then, with `tail`, units of
+// kMtTailT targets for the last eighth of the stretch: a wave's time grows with
+// its targets, so the closing units are short and the XCD's waves run out
+// closer together (at 32,768 atoms the stretch is four units per wave slot).
+// Every slot lands in exactly one unit; a unit's targets past the stretch or N
+// are empty (-1).
+constexpr int kMtTailDen = 8;   // 1/kMtTailDen of each stretch in the closing units
+constexpr int kMtTailT = 2;     // targets per closing unit
+struct MtUnits {
+  int64_t sx;        // schedule slots per XCD
+  int64_t head;      // units of T targets per XCD
+  int64_t per_xcd;   // units per XCD (grid = kXcds * per_xcd)
+};
+__host__ __device__ inline MtUnits mt_units(int64_t N, int T, bool tail) {
+  const int64_t base = (N + T - 1) / T;
+  const int64_t per0 = (base + kXcds - 1) / kXcds;
+  MtUnits u;
+  u.sx = per0 * T;
+  const int64_t q = (int64_t)T * kMtTailT;   // the closing part holds whole units of both sizes
+  const int64_t tl = (tail && kMtTailDen > 0) ? u.sx / kMtTailDen / q * q : 0;
+  u.head = (u.sx - tl) / T;
+  u.per_xcd = u.head + tl / kMtTailT;
+  return u;
+}
+
 template <int LMAX, int T, int U, int HL, bool ENV>
 __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
   constexpr int S = ncomp(LMAX);
@@ -513,9 +539,23 @@ __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasC
   __shared__ float s_le[kMtWaves][ENV ? T : 1][ENV ? EN : 1];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
-  const int64_t blk = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int64_t slot0 = (blk * kMtWaves + w) * T;
+  // Workgroups are dealt to the XCDs round-robin: XCD x runs units x, x + kXcds, ...
+  // of the grid, in order, over its own stretch of the schedule (closing units with
+  // the envelope off; its variant keeps equal units)
+  static_assert(kMtWaves == 1, "one wave a workgroup");
+  (void)w;
+  const MtUnits un_ = mt_units(a.N, T, !ENV);
+  const int64_t xcd = blockIdx.x % kXcds, b = blockIdx.x / kXcds;
+  const int64_t xend = (xcd + 1) * un_.sx;
+  int64_t slot0;
+  int cnt;   // targets of this unit
+  if (b < un_.head) {
+    slot0 = xcd * un_.sx + b * T;
+    cnt = T;
+  } else {
+    slot0 = xcd * un_.sx + un_.head * T + (b - un_.head) * kMtTailT;
+    cnt = kMtTailT;
+  }
   if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
   const int64_t N = a.N;
   const int C = a.C;
@@ -524,7 +564,7 @@ __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasC
   for (int t = 0; t < T; ++t) {
     const int64_t sl = slot0 + t;
     int64_t i = -1;
-    if (sl < N) i = a.sched ? (int64_t)a.sched[sl] : sl;
+    if (t < cnt && sl < N && sl < xend) i = a.sched ? (int64_t)a.sched[sl] : sl;
     tg[t] = (i >= 0 && i < N) ? i : -1;
   }
   const int lg = a.lane_log;
@@ -1025,8 +1065,7 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
         (a.head_lanes == 1 || a.head_lanes == 2 || a.head_lanes == 4)) {
       constexpr int TM = E ? kMtTargetsEnv : kMtTargets;
       constexpr int UM = E ? kMtInflightEnv : kMtInflight;
-      const int64_t mblocks = (a.N + kMtWaves * TM - 1) / (kMtWaves * TM);
-      const dim3 mgrid((unsigned)((mblocks + kXcds - 1) / kXcds * kXcds));
+      const dim3 mgrid((unsigned)(mt_units(a.N, TM, !E).per_xcd * kXcds));
       const dim3 mblk(64 * kMtWaves);
       switch (a.head_lanes) {
         case 1: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 1, E>), mgrid, mblk, 0, s, a, cf); break;
