@@ -504,12 +504,14 @@ constexpr int kMtWaves = 1;   // waves per workgroup
 
 // Work units (one wave each).  XCD x takes the x-th contiguous stretch of sx
 // schedule slots, in `head` units of T targets and then, with `tail`, units of
-// kMtTailT targets for the last eighth of the stretch: a wave's time grows with
+// kMtTailT targets for the last sixteenth of the stretch: a wave's time grows with
 // its targets, so the closing units are short and the XCD's waves run out
-// closer together (at 32,768 atoms the stretch is four units per wave slot).
+// closer together (at 32,768 atoms the stretch is about four units per wave
+// slot; an eighth, a quarter, a twenty-fourth and a thirty-second in units of two,
+// a sixteenth in units of one and an eighth in units of three measured slower).
 // Every slot lands in exactly one unit; a unit's targets past the stretch or N
 // are empty (-1).
-constexpr int kMtTailDen = 8;   // 1/kMtTailDen of each stretch in the closing units
+constexpr int kMtTailDen = 16;  // 1/kMtTailDen of each stretch in the closing units
 constexpr int kMtTailT = 2;     // targets per closing unit
 struct MtUnits {
   int64_t sx;        // schedule slots per XCD
