@@ -337,6 +337,10 @@ __global__ __launch_bounds__(256) void k_bwd_q(BwdArgs a) {
 // workgroup's LDS is freed only when its last wave ends (backward 2.62 -> 2.51
 // ms at Large against four waves).
 constexpr int kBwWaves = 1;   // waves per workgroup of the shared passes
+// closing units of both shared passes (unit_map): the last 1/kBwTailDen of each XCD's
+// stretch in units of kBwTailT targets (target pass) or of one source (source pass)
+constexpr int kBwTailDen = 16;
+constexpr int kBwTailT = 2;
 constexpr int kBqTargets = 3;      // targets per wave
 constexpr int kBqTargetsEnv = 2;   // targets per wave, envelope variant
 constexpr int kBqInflight = 2;     // union sources per subgroup in flight
@@ -354,9 +358,11 @@ __global__ __launch_bounds__(64 * kBwWaves) void k_bwd_q_mt(BwdArgs a) {
   __shared__ float2 s_env[kBwWaves][ENV ? T : 1][ENV ? EN : 1];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
-  const int64_t blk = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int64_t slot0 = (blk * kBwWaves + w) * T;
+  static_assert(kBwWaves == 1, "one wave a workgroup");
+  (void)w;
+  int64_t slot0, xend;
+  int cnt;   // targets of this unit
+  unit_of_block(unit_map(a.N, T, ENV ? 0 : kBwTailDen, kBwTailT), T, kBwTailT, slot0, cnt, xend);
   if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
   const int64_t N = a.N;
   const int C = a.C;
@@ -365,7 +371,7 @@ __global__ __launch_bounds__(64 * kBwWaves) void k_bwd_q_mt(BwdArgs a) {
   for (int t = 0; t < T; ++t) {
     const int64_t sl = slot0 + t;
     int64_t i = -1;
-    if (sl < N) i = a.sched ? (int64_t)a.sched[sl] : sl;
+    if (t < cnt && sl < N && sl < xend) i = a.sched ? (int64_t)a.sched[sl] : sl;
     tg[t] = (i >= 0 && i < N) ? i : -1;
   }
   const int lg = a.lane_log;
@@ -731,9 +737,11 @@ __global__ __launch_bounds__(64 * kBwWaves) void k_bwd_src_mt(BwdArgs a, EaasCoe
   __shared__ float4 s_hp[kBwWaves][T][S][32];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
-  const int64_t blk = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  const int64_t slot0 = (blk * kBwWaves + w) * T;
+  static_assert(kBwWaves == 1, "one wave a workgroup");
+  (void)w;
+  int64_t slot0, xend;
+  int cnt;   // sources of this unit
+  unit_of_block(unit_map(a.N, T, kBwTailDen, 1), T, 1, slot0, cnt, xend);
   if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
   const int64_t N = a.N;
   const int C = a.C;
@@ -744,7 +752,7 @@ __global__ __launch_bounds__(64 * kBwWaves) void k_bwd_src_mt(BwdArgs a, EaasCoe
   for (int t = 0; t < T; ++t) {
     const int64_t sl = slot0 + t;
     int64_t j = -1;
-    if (sl < N) j = a.sched ? (int64_t)a.sched[sl] : sl;
+    if (t < cnt && sl < N && sl < xend) j = a.sched ? (int64_t)a.sched[sl] : sl;
     beg[t] = 0;
     len[t] = 0;
     if (j >= 0 && j < N) {
@@ -1110,16 +1118,14 @@ int bwd_go(const BwdArgs& a, const EaasCoef& cf, hipStream_t s) {
     if (buf && (a.N > kMtMinAtoms || a.shared) && a.N < ((int64_t)1 << 30)) {
       if (a.K <= kShareMaxK) {
         constexpr int TQ = E ? kBqTargetsEnv : kBqTargets;
-        const int64_t qb = (a.N + kBwWaves * TQ - 1) / (kBwWaves * TQ);
-        const dim3 qgrid((unsigned)((qb + kXcds - 1) / kXcds * kXcds));
+        const dim3 qgrid((unsigned)(unit_map(a.N, TQ, E ? 0 : kBwTailDen, kBwTailT).per_xcd * kXcds));
         hipLaunchKernelGGL((k_bwd_q_mt<L, TQ, kBqInflight, HL, E>), qgrid, dim3(64 * kBwWaves),
                            0, s, a);
       } else {
         hipLaunchKernelGGL((k_bwd_q<L, V, UQ, HL, true, E>), grid, dim3(256), 0, s, a);
       }
       if (!E && (64 >> a.lane_log) >= kBsSources) {
-        const int64_t sb = (a.N + kBwWaves * kBsSources - 1) / (kBwWaves * kBsSources);
-        const dim3 sgrid((unsigned)((sb + kXcds - 1) / kXcds * kXcds));
+        const dim3 sgrid((unsigned)(unit_map(a.N, kBsSources, kBwTailDen, 1).per_xcd * kXcds));
         hipLaunchKernelGGL((k_bwd_src_mt<L, kBsSources, kBsInflight, HL>), sgrid,
                            dim3(64 * kBwWaves), 0, s, a, cf);
         // sources listed by more targets than the shared union holds

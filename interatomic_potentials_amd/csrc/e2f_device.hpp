@@ -384,6 +384,47 @@ __device__ inline void eaas_channel_t(float* y, float* x, const Frame& f, const 
   rotate_out<LMAX>(x, f, d);
 }
 
+// ------------------------------------------------ work units of the shared-row kernels
+//
+// One wave a unit.  XCD x takes the x-th contiguous stretch of sx schedule slots
+// (workgroups are dealt to the XCDs round-robin, so XCD x runs blocks x, x + 8,
+// ... in order), in `head` units of T slots and then, with tail_den > 0, units
+// of tail_t slots for the last 1/tail_den of the stretch: a wave's time grows
+// with its slots, so short closing units let the XCD's waves run out closer
+// together.  Every slot lands in exactly one unit; a unit's slots past the
+// stretch or N are empty.
+struct UnitMap {
+  int64_t sx;        // schedule slots per XCD
+  int64_t head;      // units of T slots per XCD
+  int64_t per_xcd;   // units per XCD (grid = kXcds * per_xcd)
+};
+
+__host__ __device__ inline UnitMap unit_map(int64_t N, int T, int tail_den, int tail_t) {
+  const int64_t base = (N + T - 1) / T;
+  const int64_t per0 = (base + kXcds - 1) / kXcds;
+  UnitMap u;
+  u.sx = per0 * T;
+  const int64_t q = (int64_t)T * tail_t;   // the closing part holds whole units of both sizes
+  const int64_t tl = tail_den > 0 ? u.sx / tail_den / q * q : 0;
+  u.head = (u.sx - tl) / T;
+  u.per_xcd = u.head + tl / tail_t;
+  return u;
+}
+
+// this workgroup's unit: its first slot, its number of slots, the end of its stretch
+__device__ inline void unit_of_block(const UnitMap& u, int T, int tail_t, int64_t& slot0,
+                                     int& cnt, int64_t& xend) {
+  const int64_t xcd = blockIdx.x % kXcds, b = blockIdx.x / kXcds;
+  xend = (xcd + 1) * u.sx;
+  if (b < u.head) {
+    slot0 = xcd * u.sx + b * T;
+    cnt = T;
+  } else {
+    slot0 = xcd * u.sx + u.head * T + (b - u.head) * tail_t;
+    cnt = tail_t;
+  }
+}
+
 // ------------------------------------------------------ storage types
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }

@@ -502,33 +502,12 @@ constexpr int kMtInflightEnv = 2;
 // idled (one: 0.93 ms at Large against 0.98 with four).
 constexpr int kMtWaves = 1;   // waves per workgroup
 
-// Work units (one wave each).  XCD x takes the x-th contiguous stretch of sx
-// schedule slots, in `head` units of T targets and then, with `tail`, units of
-// kMtTailT targets for the last sixteenth of the stretch: a wave's time grows with
-// its targets, so the closing units are short and the XCD's waves run out
-// closer together (at 32,768 atoms the stretch is about four units per wave
-// slot; an eighth, a quarter, a twenty-fourth and a thirty-second in units of two,
-// a sixteenth in units of one and an eighth in units of three measured slower).
-// Every slot lands in exactly one unit; a unit's targets past the stretch or N
-// are empty (-1).
-constexpr int kMtTailDen = 16;  // 1/kMtTailDen of each stretch in the closing units
-constexpr int kMtTailT = 2;     // targets per closing unit
-struct MtUnits {
-  int64_t sx;        // schedule slots per XCD
-  int64_t head;      // units of T targets per XCD
-  int64_t per_xcd;   // units per XCD (grid = kXcds * per_xcd)
-};
-__host__ __device__ inline MtUnits mt_units(int64_t N, int T, bool tail) {
-  const int64_t base = (N + T - 1) / T;
-  const int64_t per0 = (base + kXcds - 1) / kXcds;
-  MtUnits u;
-  u.sx = per0 * T;
-  const int64_t q = (int64_t)T * kMtTailT;   // the closing part holds whole units of both sizes
-  const int64_t tl = (tail && kMtTailDen > 0) ? u.sx / kMtTailDen / q * q : 0;
-  u.head = (u.sx - tl) / T;
-  u.per_xcd = u.head + tl / kMtTailT;
-  return u;
-}
+// The last sixteenth of each XCD's stretch in closing units of two targets (see
+// unit_map): at 32,768 atoms the stretch is about four units per wave slot; an
+// eighth, a quarter, a twenty-fourth and a thirty-second in units of two, a
+// sixteenth in units of one and an eighth in units of three measured slower.
+constexpr int kMtTailDen = 16;
+constexpr int kMtTailT = 2;
 
 template <int LMAX, int T, int U, int HL, bool ENV>
 __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasCoef cf) {
@@ -546,18 +525,9 @@ __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasC
   // the envelope off; its variant keeps equal units)
   static_assert(kMtWaves == 1, "one wave a workgroup");
   (void)w;
-  const MtUnits un_ = mt_units(a.N, T, !ENV);
-  const int64_t xcd = blockIdx.x % kXcds, b = blockIdx.x / kXcds;
-  const int64_t xend = (xcd + 1) * un_.sx;
-  int64_t slot0;
+  int64_t slot0, xend;
   int cnt;   // targets of this unit
-  if (b < un_.head) {
-    slot0 = xcd * un_.sx + b * T;
-    cnt = T;
-  } else {
-    slot0 = xcd * un_.sx + un_.head * T + (b - un_.head) * kMtTailT;
-    cnt = kMtTailT;
-  }
+  unit_of_block(unit_map(a.N, T, ENV ? 0 : kMtTailDen, kMtTailT), T, kMtTailT, slot0, cnt, xend);
   if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
   const int64_t N = a.N;
   const int C = a.C;
@@ -1067,7 +1037,7 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
         (a.head_lanes == 1 || a.head_lanes == 2 || a.head_lanes == 4)) {
       constexpr int TM = E ? kMtTargetsEnv : kMtTargets;
       constexpr int UM = E ? kMtInflightEnv : kMtInflight;
-      const dim3 mgrid((unsigned)(mt_units(a.N, TM, !E).per_xcd * kXcds));
+      const dim3 mgrid((unsigned)(unit_map(a.N, TM, E ? 0 : kMtTailDen, kMtTailT).per_xcd * kXcds));
       const dim3 mblk(64 * kMtWaves);
       switch (a.head_lanes) {
         case 1: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 1, E>), mgrid, mblk, 0, s, a, cf); break;
