@@ -521,13 +521,12 @@ __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasC
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   // Workgroups are dealt to the XCDs round-robin: XCD x runs units x, x + kXcds, ...
-  // of the grid, in order, over its own stretch of the schedule (closing units with
-  // the envelope off; its variant keeps equal units)
+  // of the grid, in order, over its own stretch of the schedule, closing units last
   static_assert(kMtWaves == 1, "one wave a workgroup");
   (void)w;
   int64_t slot0, xend;
   int cnt;   // targets of this unit
-  unit_of_block(unit_map(a.N, T, ENV ? 0 : kMtTailDen, kMtTailT), T, kMtTailT, slot0, cnt, xend);
+  unit_of_block(unit_map(a.N, T, kMtTailDen, kMtTailT), T, kMtTailT, slot0, cnt, xend);
   if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
   const int64_t N = a.N;
   const int C = a.C;
@@ -1037,7 +1036,7 @@ int agg_go(int V, const AggArgs& a, const EaasCoef& cf, hipStream_t s) {
         (a.head_lanes == 1 || a.head_lanes == 2 || a.head_lanes == 4)) {
       constexpr int TM = E ? kMtTargetsEnv : kMtTargets;
       constexpr int UM = E ? kMtInflightEnv : kMtInflight;
-      const dim3 mgrid((unsigned)(unit_map(a.N, TM, E ? 0 : kMtTailDen, kMtTailT).per_xcd * kXcds));
+      const dim3 mgrid((unsigned)(unit_map(a.N, TM, kMtTailDen, kMtTailT).per_xcd * kXcds));
       const dim3 mblk(64 * kMtWaves);
       switch (a.head_lanes) {
         case 1: hipLaunchKernelGGL((k_aggregate_mt<L, TM, UM, 1, E>), mgrid, mblk, 0, s, a, cf); break;
