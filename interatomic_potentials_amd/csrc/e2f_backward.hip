@@ -362,7 +362,8 @@ __global__ __launch_bounds__(64 * kBwWaves) void k_bwd_q_mt(BwdArgs a) {
   (void)w;
   int64_t slot0, xend;
   int cnt;   // targets of this unit
-  unit_of_block(unit_map(a.N, T, ENV ? 0 : kBwTailDen, kBwTailT), T, kBwTailT, slot0, cnt, xend);
+  unit_of_block(unit_map(a.N, T, ENV ? 0 : kBwTailDen, kBwTailT), blockIdx.x, T, kBwTailT, slot0,
+                cnt, xend);
   if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
   const int64_t N = a.N;
   const int C = a.C;
@@ -741,7 +742,7 @@ __global__ __launch_bounds__(64 * kBwWaves) void k_bwd_src_mt(BwdArgs a, EaasCoe
   (void)w;
   int64_t slot0, xend;
   int cnt;   // sources of this unit
-  unit_of_block(unit_map(a.N, T, kBwTailDen, 1), T, 1, slot0, cnt, xend);
+  unit_of_block(unit_map(a.N, T, kBwTailDen, 1), blockIdx.x, T, 1, slot0, cnt, xend);
   if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
   const int64_t N = a.N;
   const int C = a.C;

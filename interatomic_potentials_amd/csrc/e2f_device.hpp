@@ -411,10 +411,10 @@ __host__ __device__ inline UnitMap unit_map(int64_t N, int T, int tail_den, int 
   return u;
 }
 
-// this workgroup's unit: its first slot, its number of slots, the end of its stretch
-__device__ inline void unit_of_block(const UnitMap& u, int T, int tail_t, int64_t& slot0,
-                                     int& cnt, int64_t& xend) {
-  const int64_t xcd = blockIdx.x % kXcds, b = blockIdx.x / kXcds;
+// block `blk`'s unit: its first slot, its number of slots, the end of its stretch
+__host__ __device__ inline void unit_of_block(const UnitMap& u, int64_t blk, int T, int tail_t,
+                                              int64_t& slot0, int& cnt, int64_t& xend) {
+  const int64_t xcd = blk % kXcds, b = blk / kXcds;
   xend = (xcd + 1) * u.sx;
   if (b < u.head) {
     slot0 = xcd * u.sx + b * T;

@@ -526,7 +526,8 @@ __global__ __launch_bounds__(64 * kMtWaves) void k_aggregate_mt(AggArgs a, EaasC
   (void)w;
   int64_t slot0, xend;
   int cnt;   // targets of this unit
-  unit_of_block(unit_map(a.N, T, kMtTailDen, kMtTailT), T, kMtTailT, slot0, cnt, xend);
+  unit_of_block(unit_map(a.N, T, kMtTailDen, kMtTailT), blockIdx.x, T, kMtTailT, slot0, cnt,
+                xend);
   if (slot0 >= a.N) return;  // whole wave: no workgroup barrier below
   const int64_t N = a.N;
   const int C = a.C;
